@@ -1,0 +1,253 @@
+"""Seeded synthetic decode workloads (raw draws only).
+
+The pages measure a trained Qwen3 model on public long-context suites; none of
+that is available here, so these seeded Gaussian-plus-needle inputs stand in
+for them.  They keep the structure the pages describe: a head partition into
+retrieval and local heads ("Full Attention Strikes Back", section 3.1/3.2),
+concentrated versus diffuse retrieval queries (same paper, section 2.3 and
+Figure 3) and a roughly five-fold spread of the active token budget between
+the two (DeepRead summary of RTPurbo, "Key Results", niah-S vs multi-K).
+
+Everything here is input plumbing: Gaussian draws, needle planting in the
+pre-RoPE key space, rounding of the draws to bf16.  RoPE, the indexer
+projection and everything downstream belong to the two implementations under
+test and are not computed here.
+
+Draw order for ``make_workload`` (one ``numpy.random.default_rng(seed)``):
+  1. W_q for every retrieval q head r (ascending), each (D, R) ~ N(0, 1/D);
+     then W_k the same way unless the spec shares one draw (W_k = W_q).
+  2. u = the unscaled pre-RoPE queries, (B, Hq, nq, D) ~ N(0, 1).
+  3. For b, then KV group g: the group's pre-RoPE keys.  Retrieval groups get
+     (N, D) ~ N(0, 1) followed by one draw of all needle positions of the
+     group's retrieval heads (without replacement, split in head order);
+     a needle key is alpha * sqrt(D) * u_hat + its background draw.  Local
+     groups get draws only on the rows a local head reads (window + sinks).
+  4. For b, then g: values, on the same rows as the keys.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_SCALES_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "query_scales.json")
+
+
+# ----------------------------------------------------------------------------- bf16 plumbing
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 input draws to bf16 (nearest, ties to even); returns uint16 bits."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (b >> np.uint32(16)) & np.uint32(1)
+    return ((b + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bits to float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ----------------------------------------------------------------------------- specs
+@dataclass(frozen=True)
+class WorkloadSpec:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    nq: int = 1
+    ret_groups: tuple = (0,)
+    D: int = 128
+    R: int = 16
+    p: float = 0.9
+    window: int = 4096
+    n_sink: int = 4
+    rope_theta: float = 1.0e6
+    # needle recipe: "fixed" -> every retrieval query plants n_needles at alpha;
+    # "classes" -> class (b*Hr + r) % 2: 0 concentrated, 1 diffuse
+    needle_mode: str = "fixed"
+    n_needles: int = 32
+    alpha: float = 3.0
+    conc: tuple = (16, 4.0)
+    diffuse: tuple = (8192, 0.5)
+    budget_targets: tuple = (500, 2500)
+    # "unit": q = u; "table": q = s_(b,r) * u with s from the calibration table
+    query_scale: str = "unit"
+    shared_w: bool = True
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    def head_mode(self) -> np.ndarray:
+        """1 = retrieval q head, 0 = local (sliding window) q head."""
+        hm = np.zeros(self.Hq, dtype=np.int8)
+        for g in self.ret_groups:
+            hm[g * self.G:(g + 1) * self.G] = 1
+        return hm
+
+    def retrieval_heads(self) -> list:
+        return [int(h) for h in np.nonzero(self.head_mode())[0]]
+
+    @property
+    def Hr(self) -> int:
+        return len(self.ret_groups) * self.G
+
+    def needle_recipe(self, b: int, r: int) -> tuple:
+        """(count, alpha, class) of the needles planted for retrieval head r of batch b."""
+        if self.needle_mode == "fixed":
+            return self.n_needles, self.alpha, 0
+        cls = (b * self.Hr + r) % 2
+        cnt, alpha = self.conc if cls == 0 else self.diffuse
+        return cnt, alpha, cls
+
+    def local_rows(self) -> np.ndarray:
+        """Cache rows any local head can read: the union of all queries' windows and sinks."""
+        lo = max(0, self.N - self.nq - self.window + 1)
+        rows = set(range(lo, self.N))
+        rows.update(range(min(self.n_sink, self.N)))
+        return np.array(sorted(rows), dtype=np.int64)
+
+
+# The five workloads of the benchmark description, by number.
+CONFIGS = {
+    1: WorkloadSpec("needle-4k", B=1, Hq=1, Hkv=1, N=4096, ret_groups=(0,),
+                    needle_mode="fixed", n_needles=32, alpha=3.0),
+    2: WorkloadSpec("qwen3-8b-layer-32k-b8", B=8, Hq=32, Hkv=8, N=32768, ret_groups=(0,),
+                    needle_mode="fixed", n_needles=64, alpha=3.0),
+    3: WorkloadSpec("qwen3-8b-layer-128k-b4", B=4, Hq=32, Hkv=8, N=131072, ret_groups=(0,),
+                    needle_mode="classes", query_scale="table"),
+    4: WorkloadSpec("qwen3-32b-layer-1m-b1", B=1, Hq=64, Hkv=8, N=1048576, ret_groups=(0, 1),
+                    needle_mode="classes", query_scale="table"),
+}
+
+
+def spec_for(cfg: int, **overrides) -> WorkloadSpec:
+    """The spec of benchmark workload ``cfg``, optionally shrunk for tests."""
+    base = CONFIGS[cfg]
+    if not overrides:
+        return base
+    d = {k: getattr(base, k) for k in base.__dataclass_fields__}
+    d.update(overrides)
+    if "name" not in overrides:
+        d["name"] = base.name + "-" + "-".join(f"{k}{v}" for k, v in sorted(overrides.items()))
+    return WorkloadSpec(**d)
+
+
+def default_seed(cfg: int) -> int:
+    return 1000 + cfg
+
+
+# ----------------------------------------------------------------------------- workload
+@dataclass
+class Workload:
+    spec: WorkloadSpec
+    seed: int
+    q_pre: np.ndarray            # uint16 bf16 bits [B, Hq, nq, D]
+    w_q: np.ndarray              # uint16 [Hr, D, R]
+    w_k: np.ndarray              # uint16 [Hr, D, R]
+    k_pre: np.ndarray            # uint16 [B, Hkv, N, D] pre-RoPE keys (zero rows never read)
+    v: np.ndarray                # uint16 [B, Hkv, N, D]
+    head_mode: np.ndarray        # int8 [Hq]
+    u: np.ndarray = None         # float32 [B, Hq, nq, D] unscaled query draws
+    needles: dict = field(default_factory=dict)   # (b, r) -> int64 positions
+    classes: dict = field(default_factory=dict)   # (b, r) -> 0 concentrated / 1 diffuse
+    scales: dict = field(default_factory=dict)    # (b, r) -> query scale
+
+    @property
+    def positions(self) -> np.ndarray:
+        """Query positions m of the nq queries (the last nq cache rows)."""
+        return np.arange(self.spec.N - self.spec.nq, self.spec.N, dtype=np.int64)
+
+
+def load_scale_table() -> dict:
+    if not os.path.exists(_SCALES_FILE):
+        return {}
+    with open(_SCALES_FILE) as f:
+        return json.load(f)
+
+
+def scale_key(spec: WorkloadSpec, seed: int) -> str:
+    return f"{spec.name}/{seed}"
+
+
+def make_workload(spec: WorkloadSpec, seed: int, scales: dict | None = None) -> Workload:
+    """Draw one seeded workload.
+
+    ``scales`` maps (b, r) -> query scale and overrides the spec's mode; with
+    ``query_scale == "table"`` the scales come from ``query_scales.json``.
+    """
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, N, nq, D, R = spec.B, spec.Hq, spec.Hkv, spec.N, spec.nq, spec.D, spec.R
+    G = spec.G
+    rheads = spec.retrieval_heads()
+    Hr = len(rheads)
+    inv_sqrt_d = 1.0 / math.sqrt(D)
+
+    # 1. projections
+    w_q = np.empty((Hr, D, R), dtype=np.uint16)
+    for r in range(Hr):
+        w_q[r] = f32_to_bf16_bits(rng.standard_normal((D, R), dtype=np.float32) * np.float32(inv_sqrt_d))
+    if spec.shared_w:
+        w_k = w_q.copy()
+    else:
+        w_k = np.empty_like(w_q)
+        for r in range(Hr):
+            w_k[r] = f32_to_bf16_bits(rng.standard_normal((D, R), dtype=np.float32) * np.float32(inv_sqrt_d))
+
+    # 2. unscaled queries
+    u = rng.standard_normal((B, Hq, nq, D), dtype=np.float32)
+
+    # query scales
+    if scales is None:
+        scales = {}
+        if spec.query_scale == "table":
+            tab = load_scale_table().get(scale_key(spec, seed))
+            if tab is None:
+                raise KeyError(f"no calibrated query scales for {scale_key(spec, seed)} in {_SCALES_FILE}")
+            for b, r, s, *_ in tab:
+                scales[(int(b), int(r))] = float(s)
+    q = u.astype(np.float64)
+    for (b, r), s in scales.items():
+        q[b, rheads[r]] *= s
+    q_pre = f32_to_bf16_bits(q.astype(np.float32))
+
+    # 3. keys (+ needles), 4. values
+    k_pre = np.zeros((B, Hkv, N, D), dtype=np.uint16)
+    v = np.zeros((B, Hkv, N, D), dtype=np.uint16)
+    lrows = spec.local_rows()
+    needles, classes = {}, {}
+    n_avail = N - nq + 1 if nq > 1 else N   # needles must lie in every query's prefix
+    for b in range(B):
+        for g in range(Hkv):
+            if g in spec.ret_groups:
+                kg = rng.standard_normal((N, D), dtype=np.float32)
+                rs = [r for r in range(Hr) if rheads[r] // G == g]
+                recipes = [spec.needle_recipe(b, r) for r in rs]
+                total = sum(c for c, _, _ in recipes)
+                pos_all = rng.choice(n_avail, size=total, replace=False).astype(np.int64)
+                off = 0
+                for r, (cnt, alpha, cls) in zip(rs, recipes):
+                    pos = np.sort(pos_all[off:off + cnt])
+                    off += cnt
+                    direction = u[b, rheads[r], 0].astype(np.float64)
+                    direction /= np.linalg.norm(direction)
+                    kg[pos] += (alpha * math.sqrt(D) * direction).astype(np.float32)
+                    needles[(b, r)] = pos
+                    classes[(b, r)] = cls
+                k_pre[b, g] = f32_to_bf16_bits(kg)
+                del kg
+            else:
+                k_pre[b, g, lrows] = f32_to_bf16_bits(rng.standard_normal((len(lrows), D), dtype=np.float32))
+    for b in range(B):
+        for g in range(Hkv):
+            if g in spec.ret_groups:
+                v[b, g] = f32_to_bf16_bits(rng.standard_normal((N, D), dtype=np.float32))
+            else:
+                v[b, g, lrows] = f32_to_bf16_bits(rng.standard_normal((len(lrows), D), dtype=np.float32))
+
+    return Workload(spec=spec, seed=seed, q_pre=q_pre, w_q=w_q, w_k=w_k, k_pre=k_pre, v=v,
+                    head_mode=spec.head_mode(), u=u, needles=needles, classes=classes,
+                    scales={k: float(s) for k, s in scales.items()})

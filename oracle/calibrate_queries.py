@@ -1,0 +1,86 @@
+"""Write gen/query_scales.json: per-query scales of the 128K and 1M decode workloads.
+
+TEST INFRASTRUCTURE (calls only the oracle and the input generator).
+
+The budget of a retrieval query depends on how sharp its indexer logits are.
+To reproduce the pages' spread of active token budgets (about 470 tokens for
+a needle query versus about 2460 for a multi-key query at p = 0.9, DeepRead
+summary of RTPurbo, "Key Results"), each retrieval query q = s * u of the
+128K and 1M workloads gets the scale s whose oracle Top-P set (p = 0.9) has
+about 500 tokens (concentrated class) or 2500 tokens (diffuse class).  The
+scale is found by bisection on log s; the set size is non-increasing in s up
+to bf16 rounding of q.
+
+Usage:  python oracle/calibrate_queries.py [cfg ...]     (default: 3 4)
+"""
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import gen  # noqa: E402
+from gen.workload import _SCALES_FILE, default_seed, f32_to_bf16_bits, scale_key  # noqa: E402
+import oracle as O  # noqa: E402
+
+
+def calibrate(cfg: int, iters: int = 34):
+    spec = gen.spec_for(cfg)
+    seed = default_seed(cfg)
+    wl = gen.make_workload(spec, seed, scales={})
+    rheads = spec.retrieval_heads()
+    entries = []
+    for b in range(spec.B):
+        for r, h in enumerate(rheads):
+            t0 = time.time()
+            g = h // spec.G
+            m = spec.N - 1
+            kidx = O.index_project(wl.k_pre[b, g, :m + 1], wl.w_k[r])
+            cnt_needles, alpha, cls = spec.needle_recipe(b, r)
+            target = spec.budget_targets[cls]
+            u = wl.u[b, h, 0].astype(np.float64)
+
+            def count(s):
+                q = f32_to_bf16_bits((u * s).astype(np.float32))
+                s_idx = O.indexer_logits(O.index_project(q, wl.w_q[r]), kidx)
+                return len(O.topp_select(s_idx, spec.p)["sel"])
+
+            lo, hi = math.log(1e-3), math.log(1e2)
+            best = None
+            for _ in range(iters):
+                mid = 0.5 * (lo + hi)
+                c = count(math.exp(mid))
+                if best is None or abs(c - target) < abs(best[1] - target):
+                    best = (math.exp(mid), c)
+                if c > target:
+                    lo = mid
+                else:
+                    hi = mid
+                if c == target:
+                    break
+            entries.append([b, r, float(f"{best[0]:.9g}"), int(count(float(f"{best[0]:.9g}"))), cls])
+            print(f"cfg{cfg} b={b} r={r} cls={cls} target={target} scale={best[0]:.5g} count={entries[-1][3]} "
+                  f"({time.time() - t0:.1f}s)", flush=True)
+    return scale_key(spec, seed), entries
+
+
+def main(cfgs):
+    table = {}
+    if os.path.exists(_SCALES_FILE):
+        with open(_SCALES_FILE) as f:
+            table = json.load(f)
+    for cfg in cfgs:
+        key, entries = calibrate(cfg)
+        table[key] = entries
+        with open(_SCALES_FILE, "w") as f:
+            json.dump(table, f, indent=1)
+            f.write("\n")
+
+
+if __name__ == "__main__":
+    main([int(a) for a in sys.argv[1:]] or [3, 4])
