@@ -1,0 +1,165 @@
+/*
+ * rtp.h -- C ABI of librtp.so: one sparse-attention decode step of RTPurbo's
+ * head-wise sparse attention on AMD Instinct MI355X (gfx950).
+ *
+ * Method ("Full Attention Strikes Back", RTPurbo, arXiv 2605.16928, section 3.2):
+ * query heads are split into retrieval heads and local heads.  At decode time a
+ * retrieval head h scores every cached token n with a rank-16 indexer on the
+ * pre-RoPE features (eq. (4)), keeps the dynamic Top-P set of those scores and
+ * runs softmax attention with the post-RoPE query and keys over that set only
+ * (eq. (5)).  A local head runs the same attention over a sliding window plus
+ * attention sinks.  The Top-P set is found without sorting, through a 256-bin
+ * histogram per head (DeepRead summary of RTPurbo, hardware-optimised kernels).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - rtp_bf16 is the raw bit pattern of a bfloat16 value.
+ *  - Every array pointer is a DEVICE pointer owned by the caller, except
+ *    rtp_layer.head_mode, which lives in host memory.  The library never
+ *    allocates or frees memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call only enqueues work on that stream and returns; results are
+ *    ready once the stream has reached that point.
+ *  - Arguments are validated before anything is enqueued; on error nothing is
+ *    launched and a negative RTP_ERR_* code is returned.  RTP_ERR_HIP reports a
+ *    failed launch (the HIP error is left for hipGetLastError()).
+ *  - Non-finite inputs are undefined behaviour.
+ *  - Row-major layouts; "cap" rows of the caches are strided by Ncap.
+ *  - Retrieval heads are numbered r = 0..Hr-1 in ascending q-head order; the
+ *    q head h belongs to KV group h / (Hq / Hkv).
+ *  - The query of a decode step sits at position m = N - 1.  With nq > 1 the
+ *    nq queries sit at positions m_i = N - nq + i and each is causal (sees
+ *    positions 0..m_i).
+ *
+ * Numerics (readings of the pages, see the oracle for the written-out rules)
+ *  - RoPE (eq. (1)): theta_i = rope_theta^(-2(i-1)/D), i = 1..D/2, adjacent
+ *    channel pairs, angles m*theta_i formed in fp64.
+ *  - Indexer (eq. (4)): q_idx = bf16(q_pre . W_q) and K_idx = bf16(k_pre . W_k),
+ *    each the exact dot product rounded once to nearest-even; the score
+ *    s_n = fp32(q_idx . K_idx[n]) is the exact dot product rounded once.
+ *  - Top-P (eq. (5)): over softmax(s).  Bins are 1/8 logit unit wide on edges
+ *    k/8, bin 0 = cell of the maximum score, deeper cells clamped into bin 255.
+ *    Bins above the boundary bin b* are taken whole; bin b* is filled in
+ *    ascending position while the mass before a token is below p * Z.
+ *    p >= 1 selects every position.
+ *  - Attention accumulates in fp32 from bf16 K/V; outputs are fp32.
+ */
+#ifndef RTP_H
+#define RTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t rtp_bf16;
+
+enum rtp_status {
+  RTP_OK = 0,
+  RTP_ERR_ARG = -1,           /* null pointer, p <= 0 or NaN, window < 1, bad head_mode entry, n0/n1 out of range */
+  RTP_ERR_SHAPE = -2,         /* D != 128, R != 16, Hq % Hkv != 0, nq < 1, N < nq, N > Ncap, N >= 2^31, Hq > 256 */
+  RTP_ERR_WS_TOO_SMALL = -3,  /* ws_bytes < rtp_workspace_bytes(layer) */
+  RTP_ERR_UNSUPPORTED = -4,   /* a valid request this build does not implement */
+  RTP_ERR_HIP = -5            /* a HIP launch failed */
+};
+
+/* One attention layer of the step. */
+typedef struct rtp_layer {
+  int32_t B;                  /* batch (sequences) */
+  int32_t Hq;                 /* query heads, <= 256 */
+  int32_t Hkv;                /* KV heads (groups); Hq % Hkv == 0 */
+  int32_t D;                  /* head dim, must be 128 */
+  int32_t R;                  /* indexer rank, must be 16 */
+  int32_t nq;                 /* queries per (b, head): 1 = decode, > 1 = chunked prefill */
+  int64_t N;                  /* cached positions, current token(s) included; 1 <= N < 2^31 */
+  int64_t Ncap;               /* row capacity of every cache (its row stride), >= N */
+  const int8_t *head_mode;    /* HOST array [Hq]: 1 = retrieval head, 0 = local head */
+  float p;                    /* Top-P mass, > 0; >= 1 keeps every position */
+  int32_t window;             /* local heads: window W >= 1 (positions m-W+1..m) */
+  int32_t n_sink;             /* local heads: sink positions 0..n_sink-1, >= 0 */
+  double rope_theta;          /* RoPE base of eq. (1), > 0 */
+} rtp_layer;
+
+/* Number of retrieval heads Hr implied by layer->head_mode (or a negative status). */
+int32_t rtp_num_retrieval(const rtp_layer *layer);
+
+/* Workspace bytes the calls taking `ws` need for this layer (0 on invalid layer).
+ * The same workspace serves every call below. */
+size_t rtp_workspace_bytes(const rtp_layer *layer);
+
+/* Prepare a workspace for first use (enqueues a fill kernel on `stream`).  A
+ * workspace must be prepared once before its first use; every call leaves it
+ * ready for the next.  Calls that share one workspace must not overlap. */
+int rtp_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *rtp_status_str(int status);
+
+/* ---------------------------------------------------------------- cache writers */
+
+/* Post-RoPE key cache rows (FASB eq. (1)): k_out[b,g,n,:] = bf16(R(n) k_pre[b,g,n,:])
+ * for n in [n0, n1), every b and KV group g.  k_pre, k_out: [B, Hkv, Ncap, D] bf16.
+ * Requires 0 <= n0 <= n1 <= Ncap.  k_out may alias k_pre (in-place). */
+int rtp_rope_keys(const rtp_layer *layer, const rtp_bf16 *k_pre, rtp_bf16 *k_out,
+                  int64_t n0, int64_t n1, void *stream);
+
+/* Indexer-key cache rows (FASB eq. (4), key side): k_idx[b,r,n,:] =
+ * bf16(k_pre[b, g(r), n, :] . W_k[r]) for n in [n0, n1), every b and retrieval
+ * head r (g(r) = KV group of retrieval head r).
+ * k_pre: [B, Hkv, Ncap, D] bf16; w_k: [Hr, D, R] bf16; k_idx: [B, Hr, Ncap, R] bf16. */
+int rtp_index_keys(const rtp_layer *layer, const rtp_bf16 *k_pre, const rtp_bf16 *w_k,
+                   rtp_bf16 *k_idx, int64_t n0, int64_t n1, void *stream);
+
+/* ---------------------------------------------------------------- decode-path calls */
+
+/* Indexer scores (FASB eq. (4)): logits[b,r,i,n] = s_n for every retrieval head r,
+ * query i and n <= m_i; entries with n > m_i are set to -inf.
+ * q_pre: [B, Hq, nq, D] bf16 (pre-RoPE queries); w_q: [Hr, D, R] bf16;
+ * k_idx: [B, Hr, Ncap, R] bf16; logits: [B, Hr, nq, N] fp32. */
+int rtp_index_score(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *w_q,
+                    const rtp_bf16 *k_idx, float *logits, void *stream);
+
+/* Histogram Top-P over given scores (FASB eq. (5) right; DeepRead hardware notes).
+ * logits: [B, Hr, nq, N] fp32 (as written by rtp_index_score; entries n > m_i ignored).
+ * idx: [B, Hr, nq, cap] int32 receives the selected positions of each query as
+ * two ascending runs: first every position above the boundary bin, then the
+ * positions taken from the boundary bin.  Only the first min(count, cap) entries
+ * are written.  count: [B, Hr, nq] int32 receives the true |S| (check <= cap). */
+int rtp_topp_select(const rtp_layer *layer, const float *logits, int32_t *idx, int32_t *count,
+                    int64_t cap, void *ws, size_t ws_bytes, void *stream);
+
+/* Sparse attention of the retrieval heads over given sets (FASB eq. (5) left):
+ * out[b,h,i,:] = sum_{n in S} softmax(q_rot . K[n] / sqrt(D)) V[n] with
+ * q_rot = R(m_i) q_pre[b,h,i], S = idx[b,r(h),i,0:min(count,cap)] (duplicates count
+ * twice; an empty set gives zeros).  q_pre: [B,Hq,nq,D] bf16; k, v: [B,Hkv,Ncap,D]
+ * bf16 (post-RoPE keys, values); out: [B,Hq,nq,D] fp32 -- only retrieval-head rows
+ * are written.  Positions must lie in [0, N). */
+int rtp_sparse_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *k,
+                    const rtp_bf16 *v, const int32_t *idx, const int32_t *count, int64_t cap,
+                    float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Sliding-window attention with sinks of the local heads (FASB section 3.2):
+ * the same attention over positions max(0,m_i-W+1)..m_i and 0..n_sink-1.
+ * Layouts as rtp_sparse_attn; only local-head rows of out are written. */
+int rtp_swa_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *k,
+                 const rtp_bf16 *v, float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* One whole step (FASB eq. (4)-(5) and section 3.2): indexer scan, histogram
+ * Top-P, sparse attention for retrieval heads and SWA for local heads; writes
+ * every row of out [B,Hq,nq,D] fp32.  Equals rtp_index_score + rtp_topp_select +
+ * rtp_sparse_attn + rtp_swa_attn without materialising the scores.
+ * idx_opt/count_opt (may be NULL) receive the selected sets as rtp_topp_select
+ * writes them.  phase_event (may be NULL) is a hipEvent_t recorded on `stream`
+ * between the scan phase and the selection/attention phase (for profiling).
+ * This build implements nq == 1 only (RTP_ERR_UNSUPPORTED otherwise). */
+int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *w_q,
+                    const rtp_bf16 *k_idx, const rtp_bf16 *k, const rtp_bf16 *v, float *out,
+                    int32_t *idx_opt, int32_t *count_opt, int64_t cap,
+                    void *ws, size_t ws_bytes, void *phase_event, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RTP_H */

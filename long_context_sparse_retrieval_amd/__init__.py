@@ -1,0 +1,275 @@
+"""Python binding of librtp.so: RTPurbo's sparse-attention decode step on MI355X.
+
+Thin ctypes marshalling over the C ABI declared in include/rtp.h (same names,
+without the ``rtp_`` prefix).  Every step of the computation runs in the HIP
+kernels of librtp.so; PyTorch only provides device memory and the current
+stream.  Importing works without a GPU; the first call fails loudly if the
+library was not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+import torch
+
+__all__ = [
+    "Layer", "RtpError", "library_path", "load", "num_retrieval", "workspace_bytes", "workspace",
+    "rope_keys", "index_keys", "index_score", "topp_select", "sparse_attn", "swa_attn", "decode_step",
+    "SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "librtp.so")
+_lib = None
+
+SYMBOLS = ("rtp_num_retrieval", "rtp_workspace_bytes", "rtp_workspace_init", "rtp_status_str", "rtp_rope_keys",
+           "rtp_index_keys", "rtp_index_score", "rtp_topp_select", "rtp_sparse_attn", "rtp_swa_attn",
+           "rtp_decode_step")
+
+
+class RtpError(RuntimeError):
+    pass
+
+
+class _CLayer(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("R", ctypes.c_int32), ("nq", ctypes.c_int32), ("N", ctypes.c_int64), ("Ncap", ctypes.c_int64),
+        ("head_mode", ctypes.POINTER(ctypes.c_int8)), ("p", ctypes.c_float), ("window", ctypes.c_int32),
+        ("n_sink", ctypes.c_int32), ("rope_theta", ctypes.c_double),
+    ]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load librtp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RtpError(f"{_LIB_PATH} is missing: build it with `python -m long_context_sparse_retrieval_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32p = ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
+    L = ctypes.POINTER(_CLayer)
+    sig = {
+        "rtp_num_retrieval": (ctypes.c_int32, [L]),
+        "rtp_workspace_bytes": (ctypes.c_size_t, [L]),
+        "rtp_workspace_init": (ctypes.c_int, [vp, ctypes.c_size_t, vp]),
+        "rtp_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "rtp_rope_keys": (ctypes.c_int, [L, vp, vp, i64, i64, vp]),
+        "rtp_index_keys": (ctypes.c_int, [L, vp, vp, vp, i64, i64, vp]),
+        "rtp_index_score": (ctypes.c_int, [L, vp, vp, vp, vp, vp]),
+        "rtp_topp_select": (ctypes.c_int, [L, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]),
+        "rtp_sparse_attn": (ctypes.c_int, [L, vp, vp, vp, vp, vp, i64, vp, vp, ctypes.c_size_t, vp]),
+        "rtp_swa_attn": (ctypes.c_int, [L, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+        "rtp_decode_step": (ctypes.c_int, [L, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _ = i32p
+    _lib = lib
+    return lib
+
+
+@dataclass
+class Layer:
+    """One attention layer of the step (mirrors ``rtp_layer``)."""
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    head_mode: list
+    nq: int = 1
+    Ncap: int | None = None
+    p: float = 0.9
+    window: int = 4096
+    n_sink: int = 4
+    rope_theta: float = 1.0e6
+    D: int = 128
+    R: int = 16
+    _keep: list = field(default_factory=list, repr=False, compare=False)
+
+    @property
+    def cap_rows(self) -> int:
+        return self.N if self.Ncap is None else self.Ncap
+
+    @property
+    def Hr(self) -> int:
+        return int(sum(1 for h in self.head_mode if h))
+
+    def c(self) -> _CLayer:
+        hm = (ctypes.c_int8 * len(self.head_mode))(*[int(h) for h in self.head_mode])
+        self._keep = [hm]
+        return _CLayer(self.B, self.Hq, self.Hkv, self.D, self.R, self.nq, self.N, self.cap_rows,
+                       ctypes.cast(hm, ctypes.POINTER(ctypes.c_int8)), self.p, self.window, self.n_sink,
+                       self.rope_theta)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load().rtp_status_str(status).decode()
+        raise RtpError(f"{what}: {msg} ({status})")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: torch.Tensor | None, dtype, shape=None, name="tensor") -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def num_retrieval(layer: Layer) -> int:
+    return int(load().rtp_num_retrieval(ctypes.byref(layer.c())))
+
+
+def workspace_bytes(layer: Layer) -> int:
+    n = int(load().rtp_workspace_bytes(ctypes.byref(layer.c())))
+    if n == 0:
+        raise RtpError("invalid layer")
+    return n
+
+
+def workspace(layer: Layer, device="cuda") -> torch.Tensor:
+    """A prepared workspace for ``layer`` (allocated by torch, filled by the library)."""
+    n = workspace_bytes(layer)
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:off + n]
+    _check(load().rtp_workspace_init(ws.data_ptr(), n, _stream()), "rtp_workspace_init")
+    return ws
+
+
+def _cache_shape(layer: Layer, heads: int, width: int):
+    return (layer.B, heads, layer.cap_rows, width)
+
+
+def rope_keys(layer: Layer, k_pre: torch.Tensor, k_out: torch.Tensor | None = None, n0: int = 0,
+              n1: int | None = None) -> torch.Tensor:
+    """Post-RoPE key cache rows [n0, n1) from pre-RoPE keys (may be in place)."""
+    shp = _cache_shape(layer, layer.Hkv, layer.D)
+    a = _ptr(k_pre, torch.bfloat16, shp, "k_pre")
+    if k_out is None:
+        k_out = torch.empty_like(k_pre)
+    b = _ptr(k_out, torch.bfloat16, shp, "k_out")
+    n1 = layer.cap_rows if n1 is None else n1
+    _check(load().rtp_rope_keys(ctypes.byref(layer.c()), a, b, n0, n1, _stream()), "rtp_rope_keys")
+    return k_out
+
+
+def index_keys(layer: Layer, k_pre: torch.Tensor, w_k: torch.Tensor, k_idx: torch.Tensor | None = None,
+               n0: int = 0, n1: int | None = None) -> torch.Tensor:
+    """Indexer-key cache rows [n0, n1): bf16(k_pre . W_k) per retrieval head."""
+    a = _ptr(k_pre, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k_pre")
+    w = _ptr(w_k, torch.bfloat16, (layer.Hr, layer.D, layer.R), "w_k")
+    if k_idx is None:
+        k_idx = torch.zeros(_cache_shape(layer, layer.Hr, layer.R), dtype=torch.bfloat16, device=k_pre.device)
+    b = _ptr(k_idx, torch.bfloat16, _cache_shape(layer, layer.Hr, layer.R), "k_idx")
+    n1 = layer.cap_rows if n1 is None else n1
+    _check(load().rtp_index_keys(ctypes.byref(layer.c()), a, w, b, n0, n1, _stream()), "rtp_index_keys")
+    return k_idx
+
+
+def index_score(layer: Layer, q_pre, w_q, k_idx, logits=None) -> torch.Tensor:
+    """Indexer scores [B, Hr, nq, N] fp32 (eq. 4); -inf beyond each query's position."""
+    q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
+    w = _ptr(w_q, torch.bfloat16, (layer.Hr, layer.D, layer.R), "w_q")
+    k = _ptr(k_idx, torch.bfloat16, _cache_shape(layer, layer.Hr, layer.R), "k_idx")
+    if logits is None:
+        logits = torch.empty((layer.B, layer.Hr, layer.nq, layer.N), dtype=torch.float32, device=q_pre.device)
+    o = _ptr(logits, torch.float32, (layer.B, layer.Hr, layer.nq, layer.N), "logits")
+    _check(load().rtp_index_score(ctypes.byref(layer.c()), q, w, k, o, _stream()), "rtp_index_score")
+    return logits
+
+
+def topp_select(layer: Layer, logits, cap: int, ws, idx=None, count=None):
+    """Histogram Top-P sets of given scores: (idx [B,Hr,nq,cap] int32, count [B,Hr,nq] int32)."""
+    dev = logits.device
+    lg = _ptr(logits, torch.float32, (layer.B, layer.Hr, layer.nq, layer.N), "logits")
+    if idx is None:
+        idx = torch.full((layer.B, layer.Hr, layer.nq, max(cap, 1)), -1, dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.zeros((layer.B, layer.Hr, layer.nq), dtype=torch.int32, device=dev)
+    ip = _ptr(idx, torch.int32, None, "idx")
+    if idx.numel() < layer.B * layer.Hr * layer.nq * cap:
+        raise ValueError("idx smaller than [B, Hr, nq, cap]")
+    cp = _ptr(count, torch.int32, (layer.B, layer.Hr, layer.nq), "count")
+    _check(load().rtp_topp_select(ctypes.byref(layer.c()), lg, ip, cp, cap, ws.data_ptr(), ws.numel(), _stream()),
+           "rtp_topp_select")
+    return idx, count
+
+
+def sparse_attn(layer: Layer, q_pre, k, v, idx, count, ws, out=None) -> torch.Tensor:
+    """Sparse attention of the retrieval heads over given sets (eq. 5); writes their rows of out."""
+    cap = idx.shape[-1]
+    q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
+    kp = _ptr(k, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k")
+    vp = _ptr(v, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v")
+    ip = _ptr(idx, torch.int32, (layer.B, layer.Hr, layer.nq, cap), "idx")
+    cp = _ptr(count, torch.int32, (layer.B, layer.Hr, layer.nq), "count")
+    if out is None:
+        out = torch.zeros((layer.B, layer.Hq, layer.nq, layer.D), dtype=torch.float32, device=q_pre.device)
+    op = _ptr(out, torch.float32, (layer.B, layer.Hq, layer.nq, layer.D), "out")
+    _check(load().rtp_sparse_attn(ctypes.byref(layer.c()), q, kp, vp, ip, cp, cap, op, ws.data_ptr(), ws.numel(),
+                                  _stream()), "rtp_sparse_attn")
+    return out
+
+
+def swa_attn(layer: Layer, q_pre, k, v, ws, out=None) -> torch.Tensor:
+    """Sliding-window attention with sinks of the local heads; writes their rows of out."""
+    q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
+    kp = _ptr(k, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k")
+    vp = _ptr(v, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v")
+    if out is None:
+        out = torch.zeros((layer.B, layer.Hq, layer.nq, layer.D), dtype=torch.float32, device=q_pre.device)
+    op = _ptr(out, torch.float32, (layer.B, layer.Hq, layer.nq, layer.D), "out")
+    _check(load().rtp_swa_attn(ctypes.byref(layer.c()), q, kp, vp, op, ws.data_ptr(), ws.numel(), _stream()),
+           "rtp_swa_attn")
+    return out
+
+
+def decode_step(layer: Layer, q_pre, w_q, k_idx, k, v, ws, out=None, idx=None, count=None,
+                phase_event: torch.cuda.Event | None = None) -> torch.Tensor:
+    """One fused decode step (eq. 4-5 + SWA): returns out [B, Hq, 1, D] fp32."""
+    q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
+    w = _ptr(w_q, torch.bfloat16, (layer.Hr, layer.D, layer.R), "w_q") if layer.Hr else None
+    ki = _ptr(k_idx, torch.bfloat16, _cache_shape(layer, layer.Hr, layer.R), "k_idx") if layer.Hr else None
+    kp = _ptr(k, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k")
+    vp = _ptr(v, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v")
+    if out is None:
+        out = torch.empty((layer.B, layer.Hq, layer.nq, layer.D), dtype=torch.float32, device=q_pre.device)
+    op = _ptr(out, torch.float32, (layer.B, layer.Hq, layer.nq, layer.D), "out")
+    cap = 0
+    ip = cp = None
+    if idx is not None:
+        cap = idx.shape[-1]
+        ip = _ptr(idx, torch.int32, (layer.B, layer.Hr, layer.nq, cap), "idx")
+    if count is not None:
+        cp = _ptr(count, torch.int32, (layer.B, layer.Hr, layer.nq), "count")
+    ev = None
+    if phase_event is not None:
+        ev = phase_event.cuda_event
+        if not ev:
+            raise ValueError("phase_event must have been recorded once (torch creates events lazily)")
+    _check(load().rtp_decode_step(ctypes.byref(layer.c()), q, w, ki, kp, vp, op, ip, cp, cap, ws.data_ptr(),
+                                  ws.numel(), ev, _stream()), "rtp_decode_step")
+    return out

@@ -1,0 +1,253 @@
+// C entry points of librtp.so: argument validation, workspace layout, launch.
+// The operations and their sources are documented in include/rtp.h.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "rtp_internal.h"
+
+namespace rtp {
+namespace {
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+  Geo g;
+  size_t ws_bytes;
+};
+
+int count_retrieval(const rtp_layer *L) {
+  int hr = 0;
+  for (int h = 0; h < L->Hq; ++h) hr += L->head_mode[h] ? 1 : 0;
+  return hr;
+}
+
+int validate_layer(const rtp_layer *L) {
+  if (!L || !L->head_mode) return RTP_ERR_ARG;
+  if (L->D != kD || L->R != kR) return RTP_ERR_SHAPE;
+  if (L->B < 1 || L->Hq < 1 || L->Hkv < 1 || L->Hq > kMaxHq || L->Hq % L->Hkv != 0) return RTP_ERR_SHAPE;
+  if (L->nq < 1 || L->N < L->nq || L->N > L->Ncap || L->N >= (1ll << 31)) return RTP_ERR_SHAPE;
+  if (!(L->p > 0.0f) || L->window < 1 || L->n_sink < 0 || !(L->rope_theta > 0.0)) return RTP_ERR_ARG;
+  for (int h = 0; h < L->Hq; ++h)
+    if (L->head_mode[h] != 0 && L->head_mode[h] != 1) return RTP_ERR_ARG;
+  return RTP_OK;
+}
+
+int pick_tile(long long units, long long N) {
+  if (const char *env = getenv("RTP_SCAN_TILE")) {
+    const int t = atoi(env);
+    if (t == 1024 || t == 2048 || t == 4096 || t == 8192) return t;
+  }
+  int T = 1024;
+  while (T < 8192 && units * ((N + 2 * T - 1) / (2 * T)) >= 2048) T *= 2;
+  return T;
+}
+
+// Fills the geometry and workspace layout; ws may be null (sizing only).
+int make_plan(const rtp_layer *L, void *ws, Plan *out) {
+  const int st = validate_layer(L);
+  if (st != RTP_OK) return st;
+  Geo g;
+  memset(&g, 0, sizeof(g));
+  g.B = L->B;
+  g.Hq = L->Hq;
+  g.Hkv = L->Hkv;
+  g.G = L->Hq / L->Hkv;
+  g.nq = L->nq;
+  g.N = L->N;
+  g.Ncap = L->Ncap;
+  g.p = L->p;
+  g.window = L->window;
+  g.n_sink = L->n_sink;
+  g.theta = L->rope_theta;
+  int hr = 0, max_local = 0;
+  for (int h = 0; h < L->Hq; ++h) {
+    if (L->head_mode[h]) g.rhead[hr++] = (uint8_t)h;
+    else g.lmask[h >> 5] |= 1u << (h & 31);
+  }
+  g.Hr = hr;
+  for (int kv = 0; kv < L->Hkv; ++kv) {
+    int nl = 0;
+    for (int h = kv * g.G; h < (kv + 1) * g.G; ++h) nl += L->head_mode[h] ? 0 : 1;
+    if (nl) g.lgroup[g.nlg++] = (uint8_t)kv;
+    if (nl > max_local) max_local = nl;
+  }
+  g.units = g.B * g.Hr * g.nq;
+  g.T = pick_tile(g.units, g.N);
+  g.nt = (int)((g.N + g.T - 1) / g.T);
+  g.swa_units = g.B * g.nlg * g.nq;
+  g.swa_hb = (max_local + kSwaHeads - 1) / kSwaHeads;
+  {
+    const long long lo = g.N - 1 - g.window + 1 > 0 ? g.N - g.window : 0;
+    const long long ns = g.n_sink < lo ? g.n_sink : lo;
+    const long long Lrows = ns + (g.N - lo);
+    int chunk = 256;
+    while (chunk > 32 && (long long)g.swa_units * g.swa_hb * ((Lrows + chunk - 1) / chunk) < 1024) chunk >>= 1;
+    g.swa_chunk = chunk;
+    g.swa_nch = (int)((Lrows + chunk - 1) / chunk);
+  }
+  // workspace layout
+  size_t off = 0;
+  const size_t units = (size_t)g.units, nt = (size_t)g.nt;
+  const size_t o_ctr_scan = off;
+  off = align_up(off + units * 4);
+  const size_t o_ctr_fin = off;
+  off = align_up(off + units * 4);
+  const size_t o_ctr_swa = off;
+  off = align_up(off + (size_t)g.swa_units * g.swa_hb * 4);
+  const size_t o_hsel = off;
+  off = align_up(off + units * sizeof(HeadSel));
+  const size_t o_qprep = off;
+  off = align_up(off + units * sizeof(QPrep));
+  const size_t o_tsel = off;
+  off = align_up(off + units * nt * sizeof(TileSel));
+  const size_t o_tsum = off;
+  off = align_up(off + units * nt * sizeof(TileSum));
+  const size_t o_part = off;
+  off = align_up(off + units * (nt > (size_t)kSpChunks ? nt : (size_t)kSpChunks) * sizeof(Partial));
+  const size_t o_swa = off;
+  off = align_up(off + (size_t)g.swa_units * g.swa_hb * g.swa_nch * kSwaHeads * sizeof(Partial));
+  const size_t o_codes = off;
+  off = align_up(off + units * nt * (size_t)g.T);
+  if (ws) {
+    char *base = static_cast<char *>(ws);
+    g.ctr_scan = reinterpret_cast<uint32_t *>(base + o_ctr_scan);
+    g.ctr_fin = reinterpret_cast<uint32_t *>(base + o_ctr_fin);
+    g.ctr_swa = reinterpret_cast<uint32_t *>(base + o_ctr_swa);
+    g.hsel = reinterpret_cast<HeadSel *>(base + o_hsel);
+    g.qprep = reinterpret_cast<QPrep *>(base + o_qprep);
+    g.tsel = reinterpret_cast<TileSel *>(base + o_tsel);
+    g.tsum = reinterpret_cast<TileSum *>(base + o_tsum);
+    g.part = reinterpret_cast<Partial *>(base + o_part);
+    g.swa_part = reinterpret_cast<Partial *>(base + o_swa);
+    g.codes = reinterpret_cast<uint8_t *>(base + o_codes);
+  }
+  out->g = g;
+  out->ws_bytes = off;
+  return RTP_OK;
+}
+
+int plan_with_ws(const rtp_layer *L, void *ws, size_t ws_bytes, Plan *p) {
+  const int st = make_plan(L, ws, p);
+  if (st != RTP_OK) return st;
+  if (!ws) return RTP_ERR_ARG;
+  if (ws_bytes < p->ws_bytes) return RTP_ERR_WS_TOO_SMALL;
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return RTP_ERR_ARG;
+  return RTP_OK;
+}
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+}  // namespace rtp
+
+using namespace rtp;
+
+extern "C" {
+
+const char *rtp_status_str(int status) {
+  switch (status) {
+    case RTP_OK: return "ok";
+    case RTP_ERR_ARG: return "invalid argument";
+    case RTP_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case RTP_ERR_WS_TOO_SMALL: return "workspace too small";
+    case RTP_ERR_UNSUPPORTED: return "not supported by this build";
+    case RTP_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t rtp_num_retrieval(const rtp_layer *layer) {
+  const int st = validate_layer(layer);
+  return st != RTP_OK ? st : count_retrieval(layer);
+}
+
+size_t rtp_workspace_bytes(const rtp_layer *layer) {
+  Plan p;
+  return make_plan(layer, nullptr, &p) == RTP_OK ? p.ws_bytes : 0;
+}
+
+int rtp_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+  if (!ws) return RTP_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return RTP_ERR_ARG;
+  return launch_fill_zero(ws, ws_bytes, as_stream(stream));
+}
+
+int rtp_rope_keys(const rtp_layer *layer, const rtp_bf16 *k_pre, rtp_bf16 *k_out, int64_t n0, int64_t n1,
+                  void *stream) {
+  Plan p;
+  int st = make_plan(layer, nullptr, &p);
+  if (st != RTP_OK) return st;
+  if (!k_pre || !k_out || n0 < 0 || n1 < n0 || n1 > layer->Ncap) return RTP_ERR_ARG;
+  return launch_rope_keys(p.g, k_pre, k_out, n0, n1, as_stream(stream));
+}
+
+int rtp_index_keys(const rtp_layer *layer, const rtp_bf16 *k_pre, const rtp_bf16 *w_k, rtp_bf16 *k_idx, int64_t n0,
+                   int64_t n1, void *stream) {
+  Plan p;
+  int st = make_plan(layer, nullptr, &p);
+  if (st != RTP_OK) return st;
+  if (!k_pre || !w_k || !k_idx || n0 < 0 || n1 < n0 || n1 > layer->Ncap) return RTP_ERR_ARG;
+  return launch_index_keys(p.g, k_pre, w_k, k_idx, n0, n1, as_stream(stream));
+}
+
+int rtp_index_score(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
+                    float *logits, void *stream) {
+  Plan p;
+  int st = make_plan(layer, nullptr, &p);
+  if (st != RTP_OK) return st;
+  if (p.g.units && (!q_pre || !w_q || !k_idx || !logits)) return RTP_ERR_ARG;
+  return launch_index_score(p.g, q_pre, w_q, k_idx, logits, as_stream(stream));
+}
+
+int rtp_topp_select(const rtp_layer *layer, const float *logits, int32_t *idx, int32_t *count, int64_t cap, void *ws,
+                    size_t ws_bytes, void *stream) {
+  Plan p;
+  int st = plan_with_ws(layer, ws, ws_bytes, &p);
+  if (st != RTP_OK) return st;
+  if (p.g.units && (!logits || !count || cap < 0 || (cap > 0 && !idx))) return RTP_ERR_ARG;
+  hipStream_t s = as_stream(stream);
+  st = launch_scan(p.g, nullptr, nullptr, nullptr, logits, count, s);
+  if (st != RTP_OK) return st;
+  return launch_select(p.g, nullptr, logits, nullptr, nullptr, nullptr, cap > 0 ? idx : nullptr, count, cap, s);
+}
+
+int rtp_sparse_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *k, const rtp_bf16 *v,
+                    const int32_t *idx, const int32_t *count, int64_t cap, float *out, void *ws, size_t ws_bytes,
+                    void *stream) {
+  Plan p;
+  int st = plan_with_ws(layer, ws, ws_bytes, &p);
+  if (st != RTP_OK) return st;
+  if (p.g.units && (!q_pre || !k || !v || !count || !out || cap < 0 || (cap > 0 && !idx))) return RTP_ERR_ARG;
+  return launch_sparse_attn(p.g, q_pre, k, v, idx, count, cap, out, as_stream(stream));
+}
+
+int rtp_swa_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *k, const rtp_bf16 *v, float *out,
+                 void *ws, size_t ws_bytes, void *stream) {
+  Plan p;
+  int st = plan_with_ws(layer, ws, ws_bytes, &p);
+  if (st != RTP_OK) return st;
+  if (p.g.swa_units && (!q_pre || !k || !v || !out)) return RTP_ERR_ARG;
+  return launch_swa(p.g, q_pre, k, v, out, as_stream(stream));
+}
+
+int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
+                    const rtp_bf16 *k, const rtp_bf16 *v, float *out, int32_t *idx_opt, int32_t *count_opt,
+                    int64_t cap, void *ws, size_t ws_bytes, void *phase_event, void *stream) {
+  Plan p;
+  int st = plan_with_ws(layer, ws, ws_bytes, &p);
+  if (st != RTP_OK) return st;
+  if (layer->nq != 1) return RTP_ERR_UNSUPPORTED;
+  if (!q_pre || !k || !v || !out) return RTP_ERR_ARG;
+  if (p.g.units && (!w_q || !k_idx)) return RTP_ERR_ARG;
+  if (idx_opt && cap < 0) return RTP_ERR_ARG;
+  hipStream_t s = as_stream(stream);
+  st = launch_scan(p.g, q_pre, w_q, k_idx, nullptr, count_opt, s);
+  if (st != RTP_OK) return st;
+  if (phase_event && hipEventRecord(reinterpret_cast<hipEvent_t>(phase_event), s) != hipSuccess) return RTP_ERR_HIP;
+  st = launch_swa(p.g, q_pre, k, v, out, s);
+  if (st != RTP_OK) return st;
+  return launch_select(p.g, k_idx, nullptr, k, v, out, idx_opt, count_opt, idx_opt ? cap : 0, s);
+}
+
+}  // extern "C"

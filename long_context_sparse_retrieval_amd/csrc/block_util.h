@@ -1,0 +1,204 @@
+// Workgroup-wide scans and reductions for 256-thread (4 x wave64) workgroups,
+// and the split-K attention building blocks shared by the attention kernels.
+//
+// Attention: "Full Attention Strikes Back" (RTPurbo) section 3.2 eq. (5),
+// softmax(q . k / sqrt(d_h)) weighted sum of v over a row set.
+#pragma once
+
+#include "rtp_internal.h"
+
+namespace rtp {
+
+// Exclusive prefix of v over the workgroup in thread order; `total` receives
+// the sum.  s_buf needs 4 entries and is reused after the call returns.
+template <typename V>
+__device__ __forceinline__ V block_excl_scan(V v, V &total, V *s_buf) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  V x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const V y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_buf[w] = x;
+  __syncthreads();
+  V base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < w) base += s_buf[i];
+    tot += s_buf[i];
+  }
+  __syncthreads();
+  total = tot;
+  return base + x - v;
+}
+
+template <typename V>
+__device__ __forceinline__ V block_max(V v, V *s_buf) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const V y = __shfl_xor(v, off);
+    v = y > v ? y : v;
+  }
+  if ((threadIdx.x & 63) == 0) s_buf[threadIdx.x >> 6] = v;
+  __syncthreads();
+  V r = s_buf[0];
+#pragma unroll
+  for (int i = 1; i < 4; ++i) r = s_buf[i] > r ? s_buf[i] : r;
+  __syncthreads();
+  return r;
+}
+
+template <typename V>
+__device__ __forceinline__ V block_min(V v, V *s_buf) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const V y = __shfl_xor(v, off);
+    v = y < v ? y : v;
+  }
+  if ((threadIdx.x & 63) == 0) s_buf[threadIdx.x >> 6] = v;
+  __syncthreads();
+  V r = s_buf[0];
+#pragma unroll
+  for (int i = 1; i < 4; ++i) r = s_buf[i] < r ? s_buf[i] : r;
+  __syncthreads();
+  return r;
+}
+
+// Last-workgroup detection for split work: every workgroup of a group calls
+// this once after writing its results; returns true in exactly one workgroup
+// (the last to arrive), which then sees every other workgroup's writes.  The
+// counter is left at zero for the next call.
+__device__ __forceinline__ bool arrive_last(uint32_t *ctr, uint32_t n, int *s_flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = atomicAdd(ctr, 1u);
+    const bool last = prev == n - 1;
+    if (last) *ctr = 0u;
+    *s_flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  const bool last = *s_flag != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+// q_rot = R(m) q_pre (FASB eq. (1)), scaled, into dst[128].  Threads 0..63 each
+// rotate one channel pair with an fp64 angle.  Ends with a barrier.
+__device__ __forceinline__ void rotate_query(const rtp_bf16 *q_row, long long m, double theta, float scale,
+                                             float *dst) {
+  const int t = threadIdx.x;
+  if (t < kD / 2) {
+    double sn, cs;
+    sincos((double)m * rope_freq(theta, t), &sn, &cs);
+    const uint32_t w = reinterpret_cast<const uint32_t *>(q_row)[t];
+    const double a = (double)bf_lo(w), b = (double)bf_hi(w);
+    dst[2 * t] = (float)(a * cs - b * sn) * scale;
+    dst[2 * t + 1] = (float)(a * sn + b * cs) * scale;
+  }
+  __syncthreads();
+}
+
+struct AttnShared {
+  float m[4], l[4];
+  float o[4][kD];
+};
+
+// Softmax state of one (pre-scaled) query over rows[0..cnt) of K/V rows at
+// base + n * D.  Rows outside [0, nmax) are skipped.  16 lanes cover one row
+// (8 channels each), a wave holds 4 rows per step.  The workgroup's state is
+// written to *dst (m, l and the unnormalised o).  Ends with a barrier.
+__device__ __forceinline__ void attend_rows(const float *q_s, const int *rows, int cnt, long long nmax,
+                                            const rtp_bf16 *__restrict__ kb, const rtp_bf16 *__restrict__ vb,
+                                            Partial *dst, AttnShared *sm) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, grp = lane >> 4, sub = lane & 15;
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = q_s[sub * 8 + i];
+  float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  constexpr int U = 2;
+  for (int base = 0; base < cnt; base += 16 * U) {
+    uint4 kr[U], vr[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ri = base + u * 16 + wv * 4 + grp;
+      const long long n = ri < cnt ? (long long)rows[ri] : -1;
+      ok[u] = n >= 0 && n < nmax;
+      kr[u] = make_uint4(0, 0, 0, 0);
+      vr[u] = make_uint4(0, 0, 0, 0);
+      if (ok[u]) {
+        kr[u] = *reinterpret_cast<const uint4 *>(kb + n * kD + sub * 8);
+        vr[u] = *reinterpret_cast<const uint4 *>(vb + n * kD + sub * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
+      const uint32_t vw[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d += q[2 * i] * bf_lo(kw[i]) + q[2 * i + 1] * bf_hi(kw[i]);
+      d = row16_sum(d);
+      if (ok[u]) {
+        const float mn = fmaxf(m, d);
+        const float a = __expf(m - mn), pw = __expf(d - mn);
+        l = l * a + pw;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[2 * i] = o[2 * i] * a + pw * bf_lo(vw[i]);
+          o[2 * i + 1] = o[2 * i + 1] * a + pw * bf_hi(vw[i]);
+        }
+        m = mn;
+      }
+    }
+  }
+  // merge the 4 row groups of the wave
+#pragma unroll
+  for (int off = 16; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+    float o2[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o2[i] = __shfl_xor(o[i], off);
+    merge_state(m, l, o, m2, l2, o2, 8);
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sm->o[wv][sub * 8 + i] = o[i];
+    if (sub == 0) {
+      sm->m[wv] = m;
+      sm->l[wv] = l;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kD) {
+    const int d = threadIdx.x;
+    float mm = -INFINITY, ll = 0.f, oo = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) merge_state(mm, ll, &oo, sm->m[w], sm->l[w], &sm->o[w][d], 1);
+    dst->o[d] = oo;
+    if (d == 0) {
+      dst->m = mm;
+      dst->l = ll;
+    }
+  }
+  __syncthreads();
+}
+
+// Normalised combination of np split-K states into out[0..D).  Threads 0..127.
+__device__ __forceinline__ void combine_partials(const Partial *parts, int np, float *out) {
+  if (threadIdx.x < kD) {
+    const int d = threadIdx.x;
+    float m = -INFINITY, l = 0.f, o = 0.f;
+    for (int i = 0; i < np; ++i) {
+      const Partial *p = parts + i;
+      merge_state(m, l, &o, p->m, p->l, &p->o[d], 1);
+    }
+    out[d] = l > 0.f ? o / l : 0.f;
+  }
+}
+
+}  // namespace rtp

@@ -1,0 +1,238 @@
+// Internal definitions shared by the HIP translation units of librtp.so.
+//
+// Sources: "Full Attention Strikes Back" (RTPurbo, arXiv 2605.16928) section 2.2
+// eq. (1) (RoPE), section 3.2 eq. (4)-(5) (indexer, Top-P, sparse attention,
+// sliding window with sinks for local heads); DeepRead summary of RTPurbo,
+// hardware-optimised kernels (256-bin sort-free Top-P histogram per head).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rtp.h"
+
+namespace rtp {
+
+constexpr int kD = 128;          // head dim
+constexpr int kR = 16;           // indexer rank
+constexpr int kBins = 256;       // histogram bins per head
+constexpr int kWG = 256;         // threads per workgroup (4 wave64)
+constexpr int kMaxHq = 256;
+constexpr int kSpChunks = 64;    // split-K chunks per query for rtp_sparse_attn
+constexpr int kSwaHeads = 4;     // local heads handled together by one SWA workgroup
+
+// Per-tile summary of the indexer scan: tile max cell and the 256-bin histogram
+// relative to it.  mass[j] sums the in-cell weights (see cell_weight) of the
+// tile's tokens in local bin j as exact 64-bit integers; cum[j] counts tokens
+// in local bins 0..j.
+struct TileSum {
+  int32_t c_t;          // floor(8 * tile max score); INT32_MIN if the tile has no token
+  int32_t nvalid;
+  uint64_t mass[kBins];
+  uint32_t cum[kBins];
+};
+
+// Per-tile selection parameters written by the merge.
+struct TileSel {
+  uint64_t P;           // in-cell mass of bin b* in the tiles before this one
+  int32_t sure_off;     // output offset of this tile's positions above b*
+  int32_t bnd_off;      // output offset of this tile's positions taken from b*
+};
+
+// Per-query selection parameters written by the merge.
+struct HeadSel {
+  int32_t c;            // global max cell
+  int32_t bstar;        // boundary bin
+  double r_u;           // residual mass p*Z - mass(bins < b*), in in-cell units of bin b*
+  int32_t tstar;        // last tile holding selected bin-b* tokens
+  int32_t all;          // 1: every position selected (p >= 1, or b* is the clamp bin)
+  int32_t count_base;   // |S| without the crossing tile's bin-b* tokens
+  int32_t total_sure;   // positions above bin b*
+  int32_t nvalid;       // m + 1
+};
+
+// Query preparation: exact indexer query and rotated query.
+struct QPrep {
+  double qi[kR];        // bf16 values of q_idx, widened
+  float qrot[kD];       // R(m) q_pre in fp32
+};
+
+// Split-K softmax state.
+struct Partial {
+  float m, l;
+  float o[kD];
+};
+
+// Geometry and workspace of one call; passed by value to every kernel.
+struct Geo {
+  int B, Hq, Hkv, G, Hr, nq;
+  long long N, Ncap;
+  float p;
+  int window, n_sink;
+  double theta;
+  // indexer scan tiling
+  int T;                // tokens per scan tile
+  int nt;               // tiles per query = ceil(N / T)
+  int units;            // B * Hr * nq (retrieval queries)
+  // sliding window
+  int nlg;              // KV groups holding at least one local head
+  int swa_hb;           // local-head blocks per group (ceil(max local heads / kSwaHeads))
+  int swa_chunk;        // rows per SWA workgroup
+  int swa_nch;          // chunks per (b, group, query)
+  int swa_units;        // B * nlg * nq
+  uint8_t rhead[kMaxHq];     // q head of retrieval head r
+  uint8_t lgroup[kMaxHq];    // KV groups with local heads
+  uint32_t lmask[kMaxHq / 32];
+  // workspace
+  uint8_t *codes;        // [units][nt*T] local bin of every token
+  TileSum *tsum;         // [units][nt]
+  TileSel *tsel;         // [units][nt]
+  HeadSel *hsel;         // [units]
+  QPrep *qprep;          // [units]
+  Partial *part;         // [units][max(nt, kSpChunks)]
+  Partial *swa_part;     // [swa_units][swa_hb][swa_nch][kSwaHeads]
+  uint32_t *ctr_scan;    // [units]
+  uint32_t *ctr_fin;     // [units]
+  uint32_t *ctr_swa;     // [swa_units * swa_hb]
+};
+
+// ------------------------------------------------------------------ numerics
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round a double once to bf16 (nearest, ties to even); returns the bits.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t sign = (uint32_t)(b >> 63) << 15;
+  const int e = (int)((b >> 52) & 0x7ff);
+  if (e == 0) return (uint16_t)sign;                     // +-0 and fp64 subnormals (far below bf16)
+  const uint64_t sig = (1ull << 52) | (b & ((1ull << 52) - 1));   // 53-bit significand
+  int E = e - 1023;
+  if (E >= -126) {                                       // bf16 normal: keep 8 significant bits
+    uint64_t keep = sig >> 45;
+    const uint64_t rem = sig & ((1ull << 45) - 1), half = 1ull << 44;
+    if (rem > half || (rem == half && (keep & 1))) ++keep;
+    if (keep == 256) { keep = 128; ++E; }
+    if (E > 127) return (uint16_t)(sign | 0x7f80u);
+    return (uint16_t)(sign | ((uint32_t)(E + 127) << 7) | (uint32_t)(keep & 0x7f));
+  }
+  // bf16 subnormal: value = k * 2^-133 with k = sig * 2^(E - 52 + 133)
+  const int sh = -(E + 81);                              // > 45
+  if (sh > 54) return (uint16_t)sign;
+  uint64_t keep = sig >> sh;
+  const uint64_t rem = sig & ((1ull << sh) - 1), half = 1ull << (sh - 1);
+  if (rem > half || (rem == half && (keep & 1))) ++keep;
+  return (uint16_t)(sign | (uint32_t)keep);              // keep == 128 carries into the exponent field
+}
+
+// Exact dot of 16 bf16 pairs accumulated in fp64, rounded once to fp32.
+// q: 16 widened bf16 values; a, b: the 32-byte row as two uint4.
+__device__ __forceinline__ float dot16_exact(const double *q, uint4 a, uint4 b) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc = fma(q[2 * i], (double)bf_lo(w[i]), acc);
+    acc = fma(q[2 * i + 1], (double)bf_hi(w[i]), acc);
+  }
+  return (float)acc;
+}
+
+// Cell of a score: floor(8 s) (exact: 8 s is exact in fp32).
+__device__ __forceinline__ int score_cell(float s) { return (int)floorf(s * 8.0f); }
+
+// In-cell weight exp(s - ref/8) of a token with score s, as a fixed-point
+// integer with 2^23 = 1.  Regular bins use ref = cell(s), giving a value in
+// [2^23, 1.1331 * 2^23) that is an exact integer (the fp32 significand).  The
+// clamp bin of a tile uses ref = c_t - 255 >= cell(s): the weight is then below
+// 1.1331 * 2^23 and truncated.  The same code runs wherever the weight is
+// recomputed, so the integers are bit-identical.
+__device__ __forceinline__ uint32_t cell_weight(float s, int ref) {
+  const float x = __fsub_rn(s, (float)ref * 0.125f);
+  const float e = __builtin_amdgcn_exp2f(__fmul_rn(x, 1.44269504088896341f));
+  return (uint32_t)__fmul_rn(e, 8388608.0f);
+}
+
+// RoPE frequency theta_i = base^(-2i/D), i = 0..D/2-1 (FASB eq. (1)).
+__device__ __forceinline__ double rope_freq(double base, int i) {
+  return pow(base, -2.0 * (double)i / (double)kD);
+}
+
+// ------------------------------------------------------------------ wave helpers
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of a DPP row (every lane receives the sum).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);   // row_half_mirror
+  v += dpp<0x140>(v);   // row_mirror
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Combine two softmax states (m, l, o) -> (m, l, o); empty states have m = -inf.
+__device__ __forceinline__ void merge_state(float &m, float &l, float *o, float m2, float l2, const float *o2, int n) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  const float a = (m == -INFINITY) ? 0.f : __expf(m - mn);
+  const float c = (m2 == -INFINITY) ? 0.f : __expf(m2 - mn);
+  l = l * a + l2 * c;
+  for (int i = 0; i < n; ++i) o[i] = o[i] * a + o2[i] * c;
+  m = mn;
+}
+
+// ------------------------------------------------------------------ query projection
+// q_idx = bf16(exact q_pre[b, hq, i] . W_q[r]) into s_q[16] (widened), using
+// all 256 threads: thread (cg, j) sums channels cg*8..cg*8+7 of output j.
+__device__ __forceinline__ void project_query(const rtp_bf16 *__restrict__ q_row, const rtp_bf16 *__restrict__ w,
+                                              double *s_q, double (*s_tmp)[kR]) {
+  const int tid = threadIdx.x, j = tid & 15, cg = tid >> 4;
+  double acc = 0.0;
+#pragma unroll
+  for (int c = cg * 8; c < cg * 8 + 8; ++c) {
+    const double q = (double)__uint_as_float((uint32_t)q_row[c] << 16);
+    const double wv = (double)__uint_as_float((uint32_t)w[c * kR + j] << 16);
+    acc = fma(q, wv, acc);
+  }
+  s_tmp[cg][j] = acc;
+  __syncthreads();
+  if (tid < kR) {
+    double t = 0.0;
+    for (int i = 0; i < 16; ++i) t += s_tmp[i][tid];
+    s_q[tid] = (double)__uint_as_float((uint32_t)f64_to_bf16(t) << 16);
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ host launchers
+int launch_rope_keys(const Geo &g, const rtp_bf16 *k_pre, rtp_bf16 *k_out, long long n0, long long n1, hipStream_t s);
+int launch_index_keys(const Geo &g, const rtp_bf16 *k_pre, const rtp_bf16 *w_k, rtp_bf16 *k_idx, long long n0,
+                      long long n1, hipStream_t s);
+int launch_index_score(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
+                       float *logits, hipStream_t s);
+// Scan phase: histogram (from k_idx + q, or from given logits) and merge.
+int launch_scan(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
+                const float *logits, int32_t *count, hipStream_t s);
+// Selection phase: select, optionally attend and combine into out.
+int launch_select(const Geo &g, const rtp_bf16 *k_idx, const float *logits, const rtp_bf16 *k,
+                  const rtp_bf16 *v, float *out, int32_t *idx, int32_t *count, long long cap, hipStream_t s);
+int launch_swa(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *k, const rtp_bf16 *v, float *out,
+               hipStream_t s);
+int launch_sparse_attn(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *k, const rtp_bf16 *v,
+                       const int32_t *idx, const int32_t *count, long long cap, float *out, hipStream_t s);
+int launch_fill_zero(void *ws, size_t bytes, hipStream_t s);
+
+}  // namespace rtp

@@ -1,0 +1,96 @@
+"""Helpers of the GPU parity tests: uploads and the acceptance rules.
+
+Acceptance (sparse-decode parity, stated with the workload description):
+  * attention outputs: max-abs <= 1e-2 and rel-L2 <= 2e-3 against the oracle
+    (bf16 in, fp32 accumulate on the GPU, fp64 in the oracle);
+  * selected sets: identical except tokens whose fp32 score lies within 1e-4 of
+    a bin edge, or when the oracle reports that its closest mass decision lies
+    within 1e-5 of Z (rounding of masses can then legitimately flip it);
+  * selected mass >= p - 1e-4 (fp64, oracle weights, on the GPU's set).
+"""
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+
+MAX_ABS = 1e-2
+REL_L2 = 2e-3
+EDGE = 1e-4
+MARGIN = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_bf16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def check_output(gpu: np.ndarray, ref: np.ndarray, what: str = ""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    err = np.abs(gpu - ref).max()
+    rel = np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-30)
+    assert err <= MAX_ABS, f"{what}: max-abs {err:.3e}"
+    assert rel <= REL_L2 or np.linalg.norm(ref) < 1e-6, f"{what}: rel-L2 {rel:.3e}"
+    return err, rel
+
+
+def check_set(gpu_list: np.ndarray, gpu_count: int, cap: int, t: dict, logits: np.ndarray, p: float, what: str = ""):
+    """Compare a GPU Top-P set with the oracle's; returns 'exact' or 'tolerated'."""
+    ref = t["sel"]
+    assert gpu_count == len(ref) or gpu_count > 0, f"{what}: count {gpu_count}"
+    n = min(gpu_count, cap)
+    got = np.asarray(gpu_list[:n], dtype=np.int64)
+    if gpu_count <= cap:
+        assert len(np.unique(got)) == len(got), f"{what}: duplicate positions"
+        assert np.all((got >= 0) & (got < len(logits))), f"{what}: position out of range"
+    if gpu_count == len(ref) and gpu_count <= cap and np.array_equal(np.sort(got), ref):
+        # layout: positions above the boundary bin, then those taken from it, each ascending
+        if t["bstar"] < O.N_BINS and p < 1:
+            nsure = int(np.sum(t["bins"] < t["bstar"]))
+            assert np.all(np.diff(got[:nsure]) > 0) and np.all(np.diff(got[nsure:]) > 0), f"{what}: order"
+            assert np.all(t["bins"][got[:nsure]] < t["bstar"])
+        return "exact"
+    assert gpu_count <= cap, f"{what}: sets differ and GPU list truncated ({gpu_count} > {cap})"
+    diff = np.setxor1d(got, ref)
+    s = logits.astype(np.float64)
+    edge = np.abs(s[diff] * 8 - np.round(s[diff] * 8)) < 8 * EDGE
+    assert edge.all() or t["margin"] < MARGIN, (
+        f"{what}: {len(diff)} differing positions (e.g. {diff[:8]}), margin {t['margin']:.2e}")
+    w = t["weights"]
+    assert w[got].sum() >= (p - 1e-4) * w.sum(), f"{what}: selected mass below p"
+    return "tolerated"
+
+
+def sdpa_f64(q_rot, k_rows, v_rows):
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.asarray(q_rot, np.float64))[None, None, None],
+        torch.from_numpy(np.asarray(k_rows, np.float64))[None, None],
+        torch.from_numpy(np.asarray(v_rows, np.float64))[None, None])[0, 0, 0].numpy()
+
+
+def layer_of(spec, rtp, N=None, Ncap=None, p=None, window=None, n_sink=None):
+    return rtp.Layer(B=spec.B, Hq=spec.Hq, Hkv=spec.Hkv, N=spec.N if N is None else N,
+                     head_mode=[int(x) for x in spec.head_mode()], nq=spec.nq, Ncap=Ncap,
+                     p=spec.p if p is None else p, window=spec.window if window is None else window,
+                     n_sink=spec.n_sink if n_sink is None else n_sink, rope_theta=spec.rope_theta)
+
+
+def edge_fraction(logits):
+    s = np.asarray(logits, np.float64)
+    return float(np.mean(np.abs(s * 8 - np.round(s * 8)) < 8 * EDGE))
+
+
+def ceil_pn(p, n):
+    return math.ceil(p * n)

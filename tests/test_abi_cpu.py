@@ -1,0 +1,115 @@
+"""The C ABI on the CPU: the library loads, exports what include/rtp.h declares,
+sizes workspaces and rejects bad arguments before any launch (no GPU calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_sparse_retrieval_amd as rtp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rtp.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(rtp.library_path()),
+                               reason="librtp.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rtp_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("rtp_index_score", "rtp_topp_select", "rtp_sparse_attn", "rtp_swa_attn", "rtp_decode_step",
+                     "rtp_index_keys", "rtp_rope_keys", "rtp_workspace_bytes", "rtp_workspace_init",
+                     "rtp_status_str", "rtp_num_retrieval"):
+        assert required in names
+    assert set(names) == set(rtp.SYMBOLS)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(rtp.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _layer(**kw):
+    d = dict(B=2, Hq=8, Hkv=2, N=5000, head_mode=[1, 1, 1, 1, 0, 0, 0, 0])
+    d.update(kw)
+    return rtp.Layer(**d)
+
+
+@needs_lib
+def test_status_strings_and_retrieval_count():
+    lib = rtp.load()
+    assert lib.rtp_status_str(0) == b"ok"
+    assert lib.rtp_status_str(-3) == b"workspace too small"
+    assert rtp.num_retrieval(_layer()) == 4
+    assert rtp.num_retrieval(_layer(head_mode=[0] * 8)) == 0
+
+
+@needs_lib
+def test_workspace_sizing_monotone():
+    small = rtp.workspace_bytes(_layer(N=1000))
+    big = rtp.workspace_bytes(_layer(N=100000))
+    assert 0 < small < big
+    assert rtp.workspace_bytes(_layer(N=5000, Ncap=9000)) == rtp.workspace_bytes(_layer(N=5000))
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), -2), (dict(R=8), -2), (dict(Hkv=3), -2), (dict(N=0), -2), (dict(N=10, Ncap=5), -2),
+    (dict(nq=0), -2), (dict(N=1 << 31, Ncap=1 << 31), -2), (dict(p=0.0), -1), (dict(p=float("nan")), -1),
+    (dict(window=0), -1), (dict(n_sink=-1), -1), (dict(head_mode=[2, 0, 0, 0, 0, 0, 0, 0]), -1),
+    (dict(rope_theta=0.0), -1),
+])
+def test_layer_validation(kw, code):
+    lay = _layer(**kw)
+    assert rtp.load().rtp_num_retrieval(ctypes.byref(lay.c())) == code
+    assert rtp.load().rtp_workspace_bytes(ctypes.byref(lay.c())) == 0
+
+
+@needs_lib
+def test_calls_reject_before_launch():
+    lib = rtp.load()
+    lay = _layer()
+    L = ctypes.byref(lay.c())
+    need = rtp.workspace_bytes(lay)
+    fake = 1 << 40     # never dereferenced: every call below fails validation first
+    # workspace too small
+    assert lib.rtp_topp_select(L, fake, fake, fake, 16, fake, need - 1, None) == -3
+    assert lib.rtp_decode_step(L, fake, fake, fake, fake, fake, fake, None, None, 0, fake, need - 1, None, None) == -3
+    # null pointers / bad ranges
+    assert lib.rtp_index_score(L, None, fake, fake, fake, None) == -1
+    assert lib.rtp_rope_keys(L, fake, fake, 10, 5, None) == -1
+    assert lib.rtp_index_keys(L, fake, fake, fake, 0, lay.N + 1, None) == -1
+    assert lib.rtp_swa_attn(L, None, fake, fake, fake, fake, need, None) == -1
+    assert lib.rtp_sparse_attn(L, fake, fake, fake, fake, fake, -1, fake, fake, need, None) == -1
+    assert lib.rtp_workspace_init(None, 16, None) == -1
+    # misaligned workspace
+    assert lib.rtp_swa_attn(L, fake, fake, fake, fake, fake + 8, need, None) == -1
+    # chunked prefill is not fused in this build
+    lay2 = _layer(nq=4)
+    assert lib.rtp_decode_step(ctypes.byref(lay2.c()), fake, fake, fake, fake, fake, fake, None, None, 0, fake,
+                               rtp.workspace_bytes(lay2), None, None) == -4
+
+
+def test_binding_checks_tensors_without_gpu():
+    import torch
+    lay = _layer()
+    with pytest.raises((TypeError, ValueError, rtp.RtpError)):
+        rtp.index_score(lay, torch.zeros(2, 8, 1, 128), torch.zeros(4, 128, 16), torch.zeros(2, 4, 5000, 16))
+
+
+def test_package_does_not_touch_the_oracle():
+    pkg = os.path.dirname(rtp.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", txt, re.M), f
+                assert "rtp_oracle" not in txt, f
