@@ -1,0 +1,289 @@
+"""Benchmark of one sparse-attention decode step (RTPurbo) on one MI355X.
+
+Metric: decode attention microseconds per step and achieved HBM GB/s at 1M
+context (Qwen3-32B-shaped layer, the headline line) and at 128K context
+(Qwen3-8B-shaped layer, batch 4, reported beside it).  A step is one
+rtp_decode_step: every head of the layer and every sequence of the batch,
+from query preparation to the attention output.  Inputs are seeded synthetic
+caches already resident in HBM; several replicas of the caches are rotated so
+that successive steps do not hit the 256 MB Infinity Cache.
+
+GB/s counts algorithmic bytes (what the method must move): 32 B of indexer
+key per cached token per retrieval head, 512 B per K/V row of the union of
+the selected sets of each KV group, 512 B per window-plus-sink row of each
+local KV group.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gen  # noqa: E402
+import long_context_sparse_retrieval_amd as rtp  # noqa: E402
+
+METRIC = "decode attn µs/step + achieved HBM GB/s at 128K and 1M ctx, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+CSRC = os.path.join(ROOT, "long_context_sparse_retrieval_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def up(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+class Case:
+    """One benchmark workload resident on the GPU, with rotating cache replicas."""
+
+    def __init__(self, cfg: int, replicas: int):
+        self.cfg = cfg
+        self.spec = spec = gen.spec_for(cfg)
+        t0 = time.time()
+        self.wl = wl = gen.make_workload(spec, gen.workload.default_seed(cfg))
+        log(f"[bench] cfg{cfg} {spec.name}: drew inputs in {time.time() - t0:.1f}s")
+        self.layer = rtp.Layer(B=spec.B, Hq=spec.Hq, Hkv=spec.Hkv, N=spec.N,
+                               head_mode=[int(h) for h in spec.head_mode()], p=spec.p, window=spec.window,
+                               n_sink=spec.n_sink, rope_theta=spec.rope_theta)
+        t0 = time.time()
+        self.q = up(wl.q_pre)
+        self.w_q = up(wl.w_q)
+        k_pre = up(wl.k_pre)
+        # caches written by the library's own cache writers (RoPE keys, indexer keys)
+        k = rtp.rope_keys(self.layer, k_pre)
+        k_idx = rtp.index_keys(self.layer, k_pre, up(wl.w_k))
+        del k_pre
+        v = up(wl.v)
+        torch.cuda.synchronize()
+        self.reps = [(k_idx, k, v)]
+        for _ in range(replicas - 1):
+            self.reps.append((k_idx.clone(), k.clone(), v.clone()))
+        torch.cuda.synchronize()
+        log(f"[bench] cfg{cfg}: caches + {replicas} replicas on GPU in {time.time() - t0:.1f}s")
+        self.ws = rtp.workspace(self.layer)
+        self.out = torch.empty((spec.B, spec.Hq, 1, spec.D), dtype=torch.float32, device="cuda")
+        self._sets()
+
+    def _sets(self):
+        spec = self.spec
+        Hr = spec.Hr
+        idx = torch.full((spec.B, Hr, 1, spec.N), -1, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros((spec.B, Hr, 1), dtype=torch.int32, device="cuda")
+        k_idx, k, v = self.reps[0]
+        rtp.decode_step(self.layer, self.q, self.w_q, k_idx, k, v, self.ws, self.out, idx=idx, count=cnt)
+        torch.cuda.synchronize()
+        idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+        self.counts = cnt[:, :, 0]
+        rheads = spec.retrieval_heads()
+        union = total = 0
+        for b in range(spec.B):
+            for g in spec.ret_groups:
+                rs = [r for r, h in enumerate(rheads) if h // spec.G == g]
+                sets = [idx[b, r, 0, :cnt[b, r, 0]] for r in rs]
+                union += len(np.unique(np.concatenate(sets)))
+                total += sum(len(s) for s in sets)
+        self.gather_rows_union, self.gather_rows_sum = union, total
+        # algorithmic bytes of one step
+        n_scan = spec.B * Hr * spec.N
+        lo = max(0, spec.N - spec.window)
+        swa_rows = min(spec.n_sink, lo) + (spec.N - lo)
+        n_local_groups = spec.Hkv - len(spec.ret_groups)
+        self.bytes_scan = 32 * n_scan
+        self.bytes_swa = 512 * swa_rows * spec.B * n_local_groups
+        self.bytes_gather = 512 * union
+        self.bytes_total = self.bytes_scan + self.bytes_swa + self.bytes_gather
+
+    def run(self, steps: int, warmup: int):
+        """Warm up, then time exactly `steps` steps; returns (ms/step, ms of the scan kernel per step)."""
+        R = len(self.reps)
+        for s in range(warmup):
+            k_idx, k, v = self.reps[s % R]
+            rtp.decode_step(self.layer, self.q, self.w_q, k_idx, k, v, self.ws, self.out)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for e in mids:
+            e.record()          # materialise the underlying hipEvent
+        t_begin = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_begin.record()
+        for s in range(steps):
+            k_idx, k, v = self.reps[s % R]
+            starts[s].record()
+            rtp.decode_step(self.layer, self.q, self.w_q, k_idx, k, v, self.ws, self.out, phase_event=mids[s])
+        t_end.record()
+        torch.cuda.synchronize()
+        ms_step = t_begin.elapsed_time(t_end) / steps
+        ms_scan = float(np.mean([starts[s].elapsed_time(mids[s]) for s in range(steps)]))
+        return ms_step, ms_scan
+
+
+def copy_ceiling_gbps() -> float:
+    """Plain device copy of 2 GiB (read + write bytes / time), the box's practical streaming rate."""
+    n = 1 << 29
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    del a, b
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def traffic_per_launch():
+    """rocprof-measured HBM bytes per scan launch, if taken on the current kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(case: Case) -> dict:
+    """The oracle, single-threaded, on a bounded sample of the 1M workload."""
+    import threadpoolctl
+
+    import oracle as O
+
+    spec, wl = case.spec, case.wl
+    r_sample = [0, 1]                       # one needle-class and one diffuse-class retrieval query
+    rheads = spec.retrieval_heads()
+    g_loc = [g for g in range(spec.Hkv) if g not in spec.ret_groups][0]
+    loc_heads = list(range(g_loc * spec.G, (g_loc + 1) * spec.G))
+    with threadpoolctl.threadpool_limits(1):
+        kc, ki = O.build_caches(wl, groups=[rheads[r] // spec.G for r in r_sample] + [g_loc], heads=r_sample)
+        t0 = time.perf_counter()
+        O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
+                      n_sink=spec.n_sink, rope_base=spec.rope_theta, heads=[rheads[r] for r in r_sample])
+        t_ret = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
+                      n_sink=spec.n_sink, rope_base=spec.rope_theta, heads=loc_heads)
+        t_loc = time.perf_counter() - t0
+    sel = int(case.counts[0, r_sample[0]] + case.counts[0, r_sample[1]])
+    lo = max(0, spec.N - spec.window)
+    swa_rows = min(spec.n_sink, lo) + (spec.N - lo)
+    sample_bytes = 32 * spec.N * len(r_sample) + 512 * sel + 512 * swa_rows
+    return {"value": round(sample_bytes / (t_ret + t_loc) / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{spec.name}: 2 of {spec.Hr} retrieval queries (1 needle-class, 1 diffuse) + the "
+                       f"{spec.G} local heads of one KV group; {t_ret + t_loc:.1f}s single-threaded "
+                       f"(host cpu_count {os.cpu_count()})")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", type=int, default=0, help="run only this config (3 or 4)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    rtp.load()
+    copy_gbps = copy_ceiling_gbps()
+    log(f"[bench] device copy ceiling {copy_gbps:.0f} GB/s")
+
+    cfgs = [args.only] if args.only else [4, 3]
+    summ, cpu = {}, None
+    for cfg in cfgs:
+        case = Case(cfg, args.replicas)
+        ms, ms_scan = case.run(args.steps, args.warmup)
+        gbps = case.bytes_total / (ms * 1e-3) / 1e9
+        summ[cfg] = dict(ms=ms, us=ms * 1e3, gbps=gbps, frac=gbps / HBM_PEAK_GBPS, scan_us=ms_scan * 1e3,
+                         scan_gbps=case.bytes_scan / (ms_scan * 1e-3) / 1e9, scan_bytes=case.bytes_scan,
+                         bytes=case.bytes_total, spec=case.spec, counts=case.counts,
+                         union=case.gather_rows_union, rsum=case.gather_rows_sum)
+        log(f"[bench] cfg{cfg}: {ms * 1e3:.1f} us/step, scan kernel {ms_scan * 1e3:.1f} us, {gbps:.0f} GB/s "
+            f"algorithmic; |S| {case.counts.ravel().tolist()}")
+        if cfg == 4 and not args.no_cpu_baseline:
+            t0 = time.time()
+            cpu = cpu_baseline(case)
+            log(f"[bench] cpu baseline {cpu['value']} GB/s ({time.time() - t0:.1f}s incl. cache build)")
+        del case
+        torch.cuda.empty_cache()
+
+    main_cfg = cfgs[0]
+    s = summ[main_cfg]
+    spec = s["spec"]
+    out = {
+        "metric": METRIC,
+        "value": round(s["gbps"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(s["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{spec.name}: one decode step of a {spec.Hq}-q/{spec.Hkv}-kv-head layer, "
+                               f"batch {spec.B}, context {spec.N}, {spec.Hr} retrieval q heads "
+                               f"(indexer rank 16, p={spec.p}), other heads SWA {spec.window}+{spec.n_sink} sinks",
+                   "context": spec.N, "batch": spec.B, "q_heads": spec.Hq, "kv_heads": spec.Hkv,
+                   "retrieval_q_heads": spec.Hr, "p": spec.p, "window": spec.window, "sinks": spec.n_sink,
+                   "cache_replicas": args.replicas},
+        "us_per_step": round(s["us"], 2),
+        "hbm_frac": round(s["frac"], 4),
+        "algorithmic_bytes_per_step": s["bytes"],
+        "selected_tokens": {"per_query": s["counts"].ravel().tolist(), "kv_rows_union": s["union"],
+                            "kv_rows_sum": s["rsum"]},
+        "roofline": {"bound": "hbm", "kernel": "scan_kernel (indexer scores + tile histograms + merge)",
+                     "achieved": round(s["scan_gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(s["scan_gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel_us": round(s["scan_us"], 2), "algorithmic_bytes_per_launch": s["scan_bytes"]},
+        "copy_ceiling_GBps": round(copy_gbps, 1),
+    }
+    if main_cfg == 4:
+        out["roofline"]["traffic"] = traffic_per_launch()
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    if 3 in summ and main_cfg != 3:
+        s3 = summ[3]
+        out["ctx_128k"] = {"workload": s3["spec"].name, "us_per_step": round(s3["us"], 2),
+                           "GBps": round(s3["gbps"], 1), "hbm_frac": round(s3["frac"], 4),
+                           "algorithmic_bytes_per_step": s3["bytes"], "scan_kernel_us": round(s3["scan_us"], 2),
+                           "scan_GBps": round(s3["scan_gbps"], 1),
+                           "selected_tokens": s3["counts"].ravel().tolist()}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

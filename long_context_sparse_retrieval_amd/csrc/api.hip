@@ -81,14 +81,21 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
     const long long lo = g.N - 1 - g.window + 1 > 0 ? g.N - g.window : 0;
     const long long ns = g.n_sink < lo ? g.n_sink : lo;
     const long long Lrows = ns + (g.N - lo);
-    int chunk = 256;
-    while (chunk > 32 && (long long)g.swa_units * g.swa_hb * ((Lrows + chunk - 1) / chunk) < 1024) chunk >>= 1;
-    g.swa_chunk = chunk;
+    long long chunk = (Lrows + 15) / 16;
+    chunk = (chunk + 31) / 32 * 32;
+    if (chunk < 64) chunk = 64;
+    g.swa_chunk = (int)chunk;
     g.swa_nch = (int)((Lrows + chunk - 1) / chunk);
   }
   // workspace layout
   size_t off = 0;
   const size_t units = (size_t)g.units, nt = (size_t)g.nt;
+  const size_t o_ring = off;
+  off = align_up(off + units * kRing * 8);
+  const size_t o_cmax = off;
+  off = align_up(off + units * 4);
+  const size_t o_cmin = off;
+  off = align_up(off + units * 4);
   const size_t o_ctr_scan = off;
   off = align_up(off + units * 4);
   const size_t o_ctr_fin = off;
@@ -111,6 +118,9 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
   off = align_up(off + units * nt * (size_t)g.T);
   if (ws) {
     char *base = static_cast<char *>(ws);
+    g.ring = reinterpret_cast<uint64_t *>(base + o_ring);
+    g.cmax = reinterpret_cast<uint32_t *>(base + o_cmax);
+    g.cmin = reinterpret_cast<uint32_t *>(base + o_cmin);
     g.ctr_scan = reinterpret_cast<uint32_t *>(base + o_ctr_scan);
     g.ctr_fin = reinterpret_cast<uint32_t *>(base + o_ctr_fin);
     g.ctr_swa = reinterpret_cast<uint32_t *>(base + o_ctr_swa);

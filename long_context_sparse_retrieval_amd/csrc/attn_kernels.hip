@@ -25,8 +25,10 @@ struct SwaShared {
   float q[kSwaHeads][kD];
   float m[4][kSwaHeads], l[4][kSwaHeads];
   float o[4][kSwaHeads][kD];
+  double2 rope[kD / 2];
   int heads[kSwaHeads];
   int flag;
+  CombineShared cb;
 };
 
 // Position of window row ri for a query at m: sinks first, then the window.
@@ -64,11 +66,11 @@ __global__ __launch_bounds__(kWG) void swa_kernel(Geo g, const rtp_bf16 *__restr
     }
     for (int c = cnt; c < kSwaHeads; ++c) sm.heads[c] = -1;
   }
-  __syncthreads();
+  rope_table(m, g.theta, sm.rope);       // ends with a barrier (also publishes sm.heads)
   for (int hh = 0; hh < kSwaHeads; ++hh) {
     const int h = sm.heads[hh];
     if (h >= 0) {
-      rotate_query(q_pre + (((size_t)b * g.Hq + h) * g.nq + i) * kD, m, g.theta, kScale, sm.q[hh]);
+      rotate_query(q_pre + (((size_t)b * g.Hq + h) * g.nq + i) * kD, sm.rope, kScale, sm.q[hh]);
     } else {
       if (tid < kD) sm.q[hh][tid] = 0.f;
       __syncthreads();
@@ -156,30 +158,26 @@ __global__ __launch_bounds__(kWG) void swa_kernel(Geo g, const rtp_bf16 *__restr
     }
   }
   __syncthreads();
-  Partial *parts = g.swa_part + ((size_t)(unit * g.swa_hb + hb) * g.swa_nch) * kSwaHeads;
+  // partials laid out [unit][head block][head][chunk]
+  Partial *parts = g.swa_part + ((size_t)(unit * g.swa_hb + hb) * kSwaHeads) * g.swa_nch;
   for (int x2 = tid; x2 < kSwaHeads * kD; x2 += kWG) {
     const int hh = x2 / kD, d = x2 % kD;
     float m_ = -INFINITY, l_ = 0.f, o_ = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) merge_state(m_, l_, &o_, sm.m[w][hh], sm.l[w][hh], &sm.o[w][hh][d], 1);
-    Partial *p = parts + (size_t)ch * kSwaHeads + hh;
-    p->o[d] = o_;
+    Partial *p = parts + (size_t)hh * g.swa_nch + ch;
+    st_coherent(&p->o[d], o_);
     if (d == 0) {
-      p->m = m_;
-      p->l = l_;
+      st_coherent(&p->m, m_);
+      st_coherent(&p->l, l_);
     }
   }
   if (!arrive_last(g.ctr_swa + unit * g.swa_hb + hb, (uint32_t)g.swa_nch, &sm.flag)) return;
-  for (int x2 = tid; x2 < kSwaHeads * kD; x2 += kWG) {
-    const int hh = x2 / kD, d = x2 % kD;
+  for (int hh = 0; hh < kSwaHeads; ++hh) {
     const int h = sm.heads[hh];
     if (h < 0) continue;
-    float m_ = -INFINITY, l_ = 0.f, o_ = 0.f;
-    for (int c = 0; c < g.swa_nch; ++c) {
-      const Partial *p = parts + (size_t)c * kSwaHeads + hh;
-      merge_state(m_, l_, &o_, p->m, p->l, &p->o[d], 1);
-    }
-    out[(((size_t)b * g.Hq + h) * g.nq + i) * kD + d] = l_ > 0.f ? o_ / l_ : 0.f;
+    combine_partials(parts + (size_t)hh * g.swa_nch, g.swa_nch, out + (((size_t)b * g.Hq + h) * g.nq + i) * kD,
+                     &sm.cb);
   }
 }
 
@@ -189,6 +187,8 @@ struct SpShared {
   int flag;
   Partial extra;
   AttnShared at;
+  double2 rope[kD / 2];
+  CombineShared cb;
 };
 
 // Sparse attention over a given index list: one workgroup per (query, chunk).
@@ -204,7 +204,8 @@ __global__ __launch_bounds__(kWG) void sparse_attn_kernel(Geo g, const rtp_bf16 
   const int i = unit % g.nq, br = unit / g.nq, r = br % g.Hr, b = br / g.Hr;
   const int hq = g.rhead[r], kvg = hq / g.G;
   const long long m = g.N - g.nq + i;
-  rotate_query(q_pre + (((size_t)b * g.Hq + hq) * g.nq + i) * kD, m, g.theta, kScale, sm.q);
+  rope_table(m, g.theta, sm.rope);
+  rotate_query(q_pre + (((size_t)b * g.Hq + hq) * g.nq + i) * kD, sm.rope, kScale, sm.q);
   long long cnt = count[unit];
   if (cnt > cap) cnt = cap;
   if (cnt < 0) cnt = 0;
@@ -224,14 +225,15 @@ __global__ __launch_bounds__(kWG) void sparse_attn_kernel(Geo g, const rtp_bf16 
   }
   Partial *dst = g.part + (size_t)unit * kSpChunks + ch;
   if (tid < kD) {
-    dst->o[tid] = run_o;
+    st_coherent(&dst->o[tid], run_o);
     if (tid == 0) {
-      dst->m = run_m;
-      dst->l = run_l;
+      st_coherent(&dst->m, run_m);
+      st_coherent(&dst->l, run_l);
     }
   }
   if (!arrive_last(g.ctr_fin + unit, (uint32_t)kSpChunks, &sm.flag)) return;
-  combine_partials(g.part + (size_t)unit * kSpChunks, kSpChunks, out + (((size_t)b * g.Hq + hq) * g.nq + i) * kD);
+  combine_partials(g.part + (size_t)unit * kSpChunks, kSpChunks, out + (((size_t)b * g.Hq + hq) * g.nq + i) * kD,
+                   &sm.cb);
 }
 
 }  // namespace

@@ -65,35 +65,65 @@ __device__ __forceinline__ V block_min(V v, V *s_buf) {
   return r;
 }
 
-// Last-workgroup detection for split work: every workgroup of a group calls
-// this once after writing its results; returns true in exactly one workgroup
-// (the last to arrive), which then sees every other workgroup's writes.  The
-// counter is left at zero for the next call.
+// Handoff between the workgroups of one kernel without agent-scope release
+// fences: such a fence writes back the whole L2 of the XCD, and those
+// writebacks serialise across the GPU (about 0.2 us each).  Instead, every
+// result that another workgroup of the same kernel reads is published with a
+// coherent store (agent-scope relaxed atomic: written through the L2), each
+// thread waits for its stores to complete, and the workgroup then counts in
+// with a relaxed atomic.  Only the last workgroup to arrive performs an
+// agent-scope acquire (an L2 invalidate) before reading the others' results.
+template <typename V>
+__device__ __forceinline__ void st_coherent(V *p, V v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Returns true in exactly one workgroup of a group of n (the last to arrive),
+// which may then read every result the others published with st_coherent.
+// The counter is left at zero for the next call.
 __device__ __forceinline__ bool arrive_last(uint32_t *ctr, uint32_t n, int *s_flag) {
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);          // this thread's coherent stores have completed
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(ctr, 1u);
+    const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = prev == n - 1;
-    if (last) *ctr = 0u;
+    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *s_flag = last ? 1 : 0;
   }
   __syncthreads();
   const bool last = *s_flag != 0;
-  if (last) __threadfence();
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return last;
 }
 
-// q_rot = R(m) q_pre (FASB eq. (1)), scaled, into dst[128].  Threads 0..63 each
-// rotate one channel pair with an fp64 angle.  Ends with a barrier.
-__device__ __forceinline__ void rotate_query(const rtp_bf16 *q_row, long long m, double theta, float scale,
-                                             float *dst) {
+// Copies a softmax state from LDS to global memory with coherent stores.
+__device__ __forceinline__ void publish_partial(Partial *dst, const Partial *src) {
+  const int t = threadIdx.x;
+  if (t < kD) st_coherent(&dst->o[t], src->o[t]);
+  if (t == kD) st_coherent(&dst->m, src->m);
+  if (t == kD + 1) st_coherent(&dst->l, src->l);
+}
+
+// cos/sin of m * theta_i (FASB eq. (1)) in fp64 for the 64 channel pairs,
+// into tab[64] (x = cos, y = sin).  Threads 0..63; ends with a barrier.
+__device__ __forceinline__ void rope_table(long long m, double theta, double2 *tab) {
   const int t = threadIdx.x;
   if (t < kD / 2) {
     double sn, cs;
     sincos((double)m * rope_freq(theta, t), &sn, &cs);
+    tab[t] = make_double2(cs, sn);
+  }
+  __syncthreads();
+}
+
+// q_rot = R(m) q_pre with a table from rope_table, scaled, into dst[128].
+// Threads 0..63 rotate one channel pair each; ends with a barrier.
+__device__ __forceinline__ void rotate_query(const rtp_bf16 *q_row, const double2 *tab, float scale, float *dst) {
+  const int t = threadIdx.x;
+  if (t < kD / 2) {
     const uint32_t w = reinterpret_cast<const uint32_t *>(q_row)[t];
     const double a = (double)bf_lo(w), b = (double)bf_hi(w);
+    const double cs = tab[t].x, sn = tab[t].y;
     dst[2 * t] = (float)(a * cs - b * sn) * scale;
     dst[2 * t + 1] = (float)(a * sn + b * cs) * scale;
   }
@@ -188,17 +218,61 @@ __device__ __forceinline__ void attend_rows(const float *q_s, const int *rows, i
   __syncthreads();
 }
 
-// Normalised combination of np split-K states into out[0..D).  Threads 0..127.
-__device__ __forceinline__ void combine_partials(const Partial *parts, int np, float *out) {
-  if (threadIdx.x < kD) {
-    const int d = threadIdx.x;
-    float m = -INFINITY, l = 0.f, o = 0.f;
-    for (int i = 0; i < np; ++i) {
-      const Partial *p = parts + i;
-      merge_state(m, l, &o, p->m, p->l, &p->o[d], 1);
+struct CombineShared {
+  float scale[256];
+  float red[8][kD];
+  float lred[8];
+  float m_red[4];
+  float gmax;
+};
+
+// Normalised combination of np split-K states into out[0..D) by the whole
+// workgroup.  The max of every state is loaded in one parallel round, then the
+// scaled o vectors are summed with independent float4 loads (8 groups of 32
+// threads, one float4 of channels each).
+__device__ __forceinline__ void combine_partials(const Partial *parts, int np, float *out, CombineShared *sm) {
+  const int tid = threadIdx.x, d4 = tid & 31, grp = tid >> 5;
+  float gm = -INFINITY;
+  for (int t = tid; t < np; t += kWG) gm = fmaxf(gm, parts[t].m);
+  gm = block_max<float>(gm, sm->m_red);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float lacc = 0.f;
+  for (int t0 = 0; t0 < np; t0 += kWG) {
+    const int t = t0 + tid;
+    if (t < np) {
+      const float m = parts[t].m;
+      sm->scale[tid] = (m == -INFINITY || gm == -INFINITY) ? 0.f : __expf(m - gm);
     }
-    out[d] = l > 0.f ? o / l : 0.f;
+    __syncthreads();
+    const int nn = np - t0 < kWG ? np - t0 : kWG;
+#pragma unroll 8
+    for (int x = grp; x < nn; x += 8) {
+      const float sc = sm->scale[x];
+      const float4 o = reinterpret_cast<const float4 *>(parts[t0 + x].o)[d4];
+      acc.x += o.x * sc;
+      acc.y += o.y * sc;
+      acc.z += o.z * sc;
+      acc.w += o.w * sc;
+      if (d4 == 0) lacc += parts[t0 + x].l * sc;
+    }
+    __syncthreads();
   }
+  sm->red[grp][4 * d4 + 0] = acc.x;
+  sm->red[grp][4 * d4 + 1] = acc.y;
+  sm->red[grp][4 * d4 + 2] = acc.z;
+  sm->red[grp][4 * d4 + 3] = acc.w;
+  if (d4 == 0) sm->lred[grp] = lacc;
+  __syncthreads();
+  if (tid < kD) {
+    float o = 0.f, l = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      o += sm->red[x][tid];
+      l += sm->lred[x];
+    }
+    out[tid] = l > 0.f ? o / l : 0.f;
+  }
+  __syncthreads();
 }
 
 }  // namespace rtp

@@ -20,6 +20,7 @@ constexpr int kWG = 256;         // threads per workgroup (4 wave64)
 constexpr int kMaxHq = 256;
 constexpr int kSpChunks = 64;    // split-K chunks per query for rtp_sparse_attn
 constexpr int kSwaHeads = 4;     // local heads handled together by one SWA workgroup
+constexpr int kRing = 4096;      // absolute score cells tracked per query (512 logit units)
 
 // Per-tile summary of the indexer scan: tile max cell and the 256-bin histogram
 // relative to it.  mass[j] sums the in-cell weights (see cell_weight) of the
@@ -57,9 +58,9 @@ struct QPrep {
   float qrot[kD];       // R(m) q_pre in fp32
 };
 
-// Split-K softmax state.
-struct Partial {
-  float m, l;
+// Split-K softmax state (o is 16-byte aligned for vector loads).
+struct alignas(16) Partial {
+  float m, l, pad0, pad1;
   float o[kD];
 };
 
@@ -91,6 +92,9 @@ struct Geo {
   QPrep *qprep;          // [units]
   Partial *part;         // [units][max(nt, kSpChunks)]
   Partial *swa_part;     // [swa_units][swa_hb][swa_nch][kSwaHeads]
+  uint64_t *ring;        // [units][kRing] exact in-cell mass per absolute cell (cell mod kRing)
+  uint32_t *cmax;        // [units] encoded max cell (0 = none)
+  uint32_t *cmin;        // [units] encoded min base cell (0 = none)
   uint32_t *ctr_scan;    // [units]
   uint32_t *ctr_fin;     // [units]
   uint32_t *ctr_swa;     // [swa_units * swa_hb]

@@ -40,48 +40,76 @@ struct ScanShared {
   int flag;
   // merge
   double wcum[kBins];
+  double2 rope[kD / 2];
 };
 
 template <int T>
 __device__ __forceinline__ int lg_slot(int nl) { return nl + nl / ScanShared<T>::TPT; }
 
-// Merge the tile histograms of one query into its selection parameters.
+// Encodings of the per-query max cell and min base cell for unsigned atomicMax
+// on a zero-initialised word (0 means "no tile yet").
+__device__ __forceinline__ uint32_t enc_max(int c) { return (uint32_t)c + 0x80000000u; }
+__device__ __forceinline__ int dec_max(uint32_t e) { return (int)(e - 0x80000000u); }
+__device__ __forceinline__ uint32_t enc_min(int c) { return 0x7fffffffu - (uint32_t)c; }
+__device__ __forceinline__ int dec_min(uint32_t e) { return (int)(0x7fffffffu - e); }
+
+// Merge the histograms of one query into its selection parameters (run by the
+// last workgroup of the query).  Every tile has added its bins into the
+// query's ring of absolute cells (exact 64-bit integer sums), so the global
+// histogram is 256 ring reads.  Cells spread over more than kRing would alias
+// in the ring; that case falls back to shifting every tile histogram.
 template <int T>
 __device__ void merge_query(const Geo &g, int unit, long long m, const rtp_bf16 *q_pre, int32_t *count_out,
                             ScanShared<T> &sm) {
   const int tid = threadIdx.x;
   const TileSum *ts = g.tsum + (size_t)unit * g.nt;
-  // global max cell
-  int c = INT32_MIN;
-  for (int t = tid; t < g.nt; t += kWG) c = max(c, ts[t].c_t);
-  c = block_max<int>(c, sm.red_i);
-  // regular bins (exact integer sums) and the clamp bin (fp64)
+  uint64_t *ring = g.ring + (size_t)unit * kRing;
+  const int c = dec_max(__hip_atomic_load(g.cmax + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const int base_min = dec_min(__hip_atomic_load(g.cmin + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const long long span = (long long)c - base_min;
   const int j = tid;
   unsigned long long H = 0;
   double w255 = 0.0;
-  for (int t = 0; t < g.nt; ++t) {
-    const int ct = ts[t].c_t;
-    if (ct == INT32_MIN) continue;
-    const long long d = (long long)c - ct;
-    if (j <= kBnd && j - d >= 0) H += ts[t].mass[j - d];
-    if (j + d >= kBins - 1) {
-      const unsigned long long mj = ts[t].mass[j];
-      if (mj) w255 += (double)mj * exp(-(double)(j + d) * 0.125);
+  if (span < kRing) {
+    if (j <= kBnd) H = ring[(c - j) & (kRing - 1)];
+    for (long long cell = (long long)c - (kBins - 1) - j; cell >= base_min; cell -= kWG) {
+      const unsigned long long mj = ring[cell & (kRing - 1)];
+      if (mj) w255 += (double)mj * exp((double)(cell - c) * 0.125);
     }
+    __syncthreads();
+    for (long long cell = (long long)base_min + j; cell <= c; cell += kWG) ring[cell & (kRing - 1)] = 0ull;
+  } else {
+    // slow path: shift every tile histogram
+    for (int t = 0; t < g.nt; ++t) {
+      const int ct = ts[t].c_t;
+      if (ct == INT32_MIN) continue;
+      const long long d = (long long)c - ct;
+      if (j <= kBnd && j - d >= 0) H += ts[t].mass[j - d];
+      if (j + d >= kBins - 1) {
+        const unsigned long long mj = ts[t].mass[j];
+        if (mj) w255 += (double)mj * exp(-(double)(j + d) * 0.125);
+      }
+    }
+    __syncthreads();
+    for (int x = j; x < kRing; x += kWG) ring[x] = 0ull;
+  }
+  if (tid == 0) {
+    g.cmax[unit] = 0u;
+    g.cmin[unit] = 0u;
   }
   // clamp-bin mass: fixed-order sum over threads
   sm.wcum[j] = w255;
   __syncthreads();
   if (tid == 0) {
     double s = 0.0;
-    for (int i = 0; i < kBins; ++i) s += sm.wcum[i];
+    for (int x = 0; x < kBins; ++x) s += sm.wcum[x];
     sm.red_d[0] = s;
   }
   __syncthreads();
   const double W255 = sm.red_d[0] * 0x1p-23;
   __syncthreads();
   const double Wj = j <= kBnd ? (double)H * 0x1p-23 * exp(-(double)j * 0.125) : W255;
-  // inclusive scan of bin masses from the top bin down (fixed order)
+  // cumulative bin masses from the top bin down (fixed order)
   double tot;
   const double excl = block_excl_scan<double>(Wj, tot, sm.red_d);
   const double incl = excl + Wj;
@@ -104,11 +132,13 @@ __device__ void merge_query(const Geo &g, int unit, long long m, const rtp_bf16 
     const int t = t0 + tid;
     unsigned long long bm = 0;
     int sure = 0, bc = 0;
-    if (t < g.nt && ts[t].c_t != INT32_MIN) {
-      const long long bl = (long long)bstar - ((long long)c - ts[t].c_t);
+    const int ct = t < g.nt ? ts[t].c_t : INT32_MIN;
+    if (ct != INT32_MIN) {
+      const long long bl = (long long)bstar - ((long long)c - ct);
       if (bl >= 1) sure = (int)ts[t].cum[(bl < kBins - 1 ? (int)bl : kBins - 1) - 1];
       if (bl >= 0 && bl <= kBnd) {
-        bc = (int)(ts[t].cum[bl] - (bl ? ts[t].cum[bl - 1] : 0u));
+        const uint32_t hi = ts[t].cum[bl];
+        bc = (int)(hi - (bl ? ts[t].cum[bl - 1] : 0u));
         bm = ts[t].mass[bl];
       }
     }
@@ -152,7 +182,8 @@ __device__ void merge_query(const Geo &g, int unit, long long m, const rtp_bf16 
   if (q_pre) {
     const int i = unit % g.nq, br = unit / g.nq, r = br % g.Hr, b = br / g.Hr;
     const rtp_bf16 *q_row = q_pre + (((size_t)b * g.Hq + g.rhead[r]) * g.nq + i) * kD;
-    rotate_query(q_row, m, g.theta, 0.08838834764831845f, qp->qrot);
+    rope_table(m, g.theta, sm.rope);
+    rotate_query(q_row, sm.rope, 0.08838834764831845f, qp->qrot);
   }
 }
 
@@ -198,7 +229,7 @@ __global__ __launch_bounds__(kWG) void scan_kernel(Geo g, const rtp_bf16 *__rest
 #pragma unroll
     for (int x = 0; x < kR; ++x) q[x] = sm.q[x];
     const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hr + r) * g.Ncap * kR);
-#pragma unroll 4
+#pragma unroll 8
     for (int k = 0; k < TPT; ++k) {
       const int nl = k * kWG + tid;
       const long long n = n0 + nl;
@@ -268,14 +299,22 @@ __global__ __launch_bounds__(kWG) void scan_kernel(Geo g, const rtp_bf16 *__rest
     const unsigned int cn = sm.cnt[0][j] + sm.cnt[1][j] + sm.cnt[2][j] + sm.cnt[3][j];
     unsigned int tot;
     const unsigned int ex = block_excl_scan<unsigned int>(cn, tot, reinterpret_cast<unsigned int *>(sm.red_i));
-    tsum->mass[j] = ms;
-    tsum->cum[j] = ex + cn;
+    st_coherent(&tsum->mass[j], (uint64_t)ms);
+    st_coherent(&tsum->cum[j], (uint32_t)(ex + cn));
     int nvt;
     (void)block_excl_scan<int>(nv, nvt, sm.red_i);
     if (tid == 0) {
-      tsum->c_t = c_t;
-      tsum->nvalid = nvt;
+      st_coherent(&tsum->c_t, (int32_t)c_t);
+      st_coherent(&tsum->nvalid, (int32_t)nvt);
     }
+  }
+  if (c_t != INT32_MIN) {
+    if (tid == 0) {
+      atomicMax(g.cmax + unit, enc_max(c_t));
+      atomicMax(g.cmin + unit, enc_min(c_t - (kBins - 1)));
+    }
+    const unsigned long long ms = sm.mass[0][tid] + sm.mass[1][tid] + sm.mass[2][tid] + sm.mass[3][tid];
+    if (ms) atomicAdd((unsigned long long *)(g.ring + (size_t)unit * kRing + ((c_t - tid) & (kRing - 1))), ms);
   }
   if (!arrive_last(g.ctr_scan + unit, (uint32_t)g.nt, &sm.flag)) return;
   merge_query<T>(g, unit, m, FROM_LOGITS ? nullptr : q_pre, count_out, sm);
@@ -289,6 +328,8 @@ struct SelShared {
   int red_i[4];
   int flag;
   AttnShared at;
+  CombineShared cb;
+  Partial res;
 };
 
 // Selection kernel: one workgroup per (query unit, tile); optionally attends.
@@ -409,9 +450,10 @@ __global__ __launch_bounds__(kWG) void select_kernel(Geo g, const rtp_bf16 *__re
   const int hq = g.rhead[r];
   const int kvg = hq / g.G;
   const size_t cbase = ((size_t)b * g.Hkv + kvg) * g.Ncap * kD;
-  attend_rows(sm.q, sm.list, tot_s + tot_b, g.N, kc + cbase, vc + cbase, g.part + (size_t)unit * g.nt + t, &sm.at);
+  attend_rows(sm.q, sm.list, tot_s + tot_b, g.N, kc + cbase, vc + cbase, &sm.res, &sm.at);
+  publish_partial(g.part + (size_t)unit * g.nt + t, &sm.res);
   if (!arrive_last(g.ctr_fin + unit, (uint32_t)g.nt, &sm.flag)) return;
-  combine_partials(g.part + (size_t)unit * g.nt, g.nt, out + (((size_t)b * g.Hq + hq) * g.nq + i) * kD);
+  combine_partials(g.part + (size_t)unit * g.nt, g.nt, out + (((size_t)b * g.Hq + hq) * g.nq + i) * kD, &sm.cb);
 }
 
 template <int T>

@@ -97,6 +97,10 @@ def _logit_case(kind, rng, n):
         return (np.round(rng.standard_normal(n) * 8) / 8).astype(np.float32)
     if kind == "wide":      # spans far more than the 32 logits of the histogram: clamp bin in use
         return (rng.standard_normal(n) * 30.0).astype(np.float32)
+    if kind == "huge":      # spans more than the 512 logits the merge ring holds: exact fallback merge
+        s = (rng.standard_normal(n) * 300.0).astype(np.float32)
+        s[0] = -2000.0
+        return s
     if kind == "needles":
         s = (rng.standard_normal(n) * 2.0).astype(np.float32)
         s[rng.choice(n, min(n, 20), replace=False)] += 9.0
@@ -105,7 +109,7 @@ def _logit_case(kind, rng, n):
 
 
 @pytest.mark.parametrize("N", [1, 5, 1000, 4097, 33000])
-@pytest.mark.parametrize("kind", ["gauss1", "gauss4", "uniform", "dominant", "ties", "wide", "needles"])
+@pytest.mark.parametrize("kind", ["gauss1", "gauss4", "uniform", "dominant", "ties", "wide", "huge", "needles"])
 @pytest.mark.parametrize("p", [0.9, 0.5, 1.0])
 def test_topp_select_matches_oracle(N, kind, p):
     say(f"topp_select N={N} kind={kind} p={p}")
