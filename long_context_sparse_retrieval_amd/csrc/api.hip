@@ -75,6 +75,14 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
   g.units = g.B * g.Hr * g.nq;
   g.T = pick_tile(g.units, g.N);
   g.nt = (int)((g.N + g.T - 1) / g.T);
+  {
+    // about 512 finishing workgroups, each over at most 32K positions (staged in LDS)
+    long long per = (long long)g.units * g.N / 512;
+    int tpw = 1;
+    while (tpw * 2 <= 32768 / g.T && tpw * 2 <= 32 && (long long)tpw * 2 * g.T <= per) tpw *= 2;
+    g.fin_tpw = tpw;
+    g.fin_nwg = (g.nt + tpw - 1) / tpw;
+  }
   g.swa_units = g.B * g.nlg * g.nq;
   g.swa_hb = (max_local + kSwaHeads - 1) / kSwaHeads;
   {
@@ -96,8 +104,6 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
   off = align_up(off + units * 4);
   const size_t o_cmin = off;
   off = align_up(off + units * 4);
-  const size_t o_ctr_scan = off;
-  off = align_up(off + units * 4);
   const size_t o_ctr_fin = off;
   off = align_up(off + units * 4);
   const size_t o_ctr_swa = off;
@@ -111,7 +117,7 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
   const size_t o_tsum = off;
   off = align_up(off + units * nt * sizeof(TileSum));
   const size_t o_part = off;
-  off = align_up(off + units * (nt > (size_t)kSpChunks ? nt : (size_t)kSpChunks) * sizeof(Partial));
+  off = align_up(off + units * (nt > (size_t)kSpChunks ? nt : (size_t)kSpChunks) * sizeof(Partial));  // >= fin_nwg
   const size_t o_swa = off;
   off = align_up(off + (size_t)g.swa_units * g.swa_hb * g.swa_nch * kSwaHeads * sizeof(Partial));
   const size_t o_codes = off;
@@ -121,13 +127,12 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
     g.ring = reinterpret_cast<uint64_t *>(base + o_ring);
     g.cmax = reinterpret_cast<uint32_t *>(base + o_cmax);
     g.cmin = reinterpret_cast<uint32_t *>(base + o_cmin);
-    g.ctr_scan = reinterpret_cast<uint32_t *>(base + o_ctr_scan);
     g.ctr_fin = reinterpret_cast<uint32_t *>(base + o_ctr_fin);
     g.ctr_swa = reinterpret_cast<uint32_t *>(base + o_ctr_swa);
+    g.tsum = reinterpret_cast<TileSum *>(base + o_tsum);
     g.hsel = reinterpret_cast<HeadSel *>(base + o_hsel);
     g.qprep = reinterpret_cast<QPrep *>(base + o_qprep);
     g.tsel = reinterpret_cast<TileSel *>(base + o_tsel);
-    g.tsum = reinterpret_cast<TileSum *>(base + o_tsum);
     g.part = reinterpret_cast<Partial *>(base + o_part);
     g.swa_part = reinterpret_cast<Partial *>(base + o_swa);
     g.codes = reinterpret_cast<uint8_t *>(base + o_codes);
@@ -146,7 +151,12 @@ int plan_with_ws(const rtp_layer *L, void *ws, size_t ws_bytes, Plan *p) {
   return RTP_OK;
 }
 
-hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+// The launch wrappers report failures through hipGetLastError(); clear an
+// error left by earlier, unrelated runtime calls so it is not taken for ours.
+hipStream_t as_stream(void *s) {
+  (void)hipGetLastError();
+  return reinterpret_cast<hipStream_t>(s);
+}
 
 }  // namespace
 }  // namespace rtp
@@ -217,9 +227,10 @@ int rtp_topp_select(const rtp_layer *layer, const float *logits, int32_t *idx, i
   if (st != RTP_OK) return st;
   if (p.g.units && (!logits || !count || cap < 0 || (cap > 0 && !idx))) return RTP_ERR_ARG;
   hipStream_t s = as_stream(stream);
-  st = launch_scan(p.g, nullptr, nullptr, nullptr, logits, count, s);
+  st = launch_phase_a(p.g, nullptr, nullptr, nullptr, logits, nullptr, nullptr, nullptr, true, false, s);
   if (st != RTP_OK) return st;
-  return launch_select(p.g, nullptr, logits, nullptr, nullptr, nullptr, cap > 0 ? idx : nullptr, count, cap, s);
+  return launch_finish(p.g, nullptr, nullptr, nullptr, logits, nullptr, nullptr, nullptr, cap > 0 ? idx : nullptr,
+                       count, cap, s);
 }
 
 int rtp_sparse_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *k, const rtp_bf16 *v,
@@ -238,7 +249,7 @@ int rtp_swa_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *
   int st = plan_with_ws(layer, ws, ws_bytes, &p);
   if (st != RTP_OK) return st;
   if (p.g.swa_units && (!q_pre || !k || !v || !out)) return RTP_ERR_ARG;
-  return launch_swa(p.g, q_pre, k, v, out, as_stream(stream));
+  return launch_phase_a(p.g, q_pre, nullptr, nullptr, nullptr, k, v, out, false, true, as_stream(stream));
 }
 
 int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
@@ -252,12 +263,10 @@ int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf1
   if (p.g.units && (!w_q || !k_idx)) return RTP_ERR_ARG;
   if (idx_opt && cap < 0) return RTP_ERR_ARG;
   hipStream_t s = as_stream(stream);
-  st = launch_scan(p.g, q_pre, w_q, k_idx, nullptr, count_opt, s);
+  st = launch_phase_a(p.g, q_pre, w_q, k_idx, nullptr, k, v, out, true, true, s);
   if (st != RTP_OK) return st;
   if (phase_event && hipEventRecord(reinterpret_cast<hipEvent_t>(phase_event), s) != hipSuccess) return RTP_ERR_HIP;
-  st = launch_swa(p.g, q_pre, k, v, out, s);
-  if (st != RTP_OK) return st;
-  return launch_select(p.g, k_idx, nullptr, k, v, out, idx_opt, count_opt, idx_opt ? cap : 0, s);
+  return launch_finish(p.g, q_pre, w_q, k_idx, nullptr, k, v, out, idx_opt, count_opt, idx_opt ? cap : 0, s);
 }
 
 }  // extern "C"

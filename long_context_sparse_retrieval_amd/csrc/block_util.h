@@ -109,8 +109,15 @@ __device__ __forceinline__ void publish_partial(Partial *dst, const Partial *src
 __device__ __forceinline__ void rope_table(long long m, double theta, double2 *tab) {
   const int t = threadIdx.x;
   if (t < kD / 2) {
+    // reduce the fp64 angle by 2 pi (three-part constant, fused multiply-adds)
+    // so that sin/cos take their short-argument path at any position
+    const double x = (double)m * rope_freq(theta, t);
+    const double k = rint(x * 0.15915494309189535);
+    double y = fma(-k, 6.283185307179586232, x);
+    y = fma(-k, 2.4492935982947064e-16, y);
+    y = fma(-k, -5.9895396194366793e-33, y);
     double sn, cs;
-    sincos((double)m * rope_freq(theta, t), &sn, &cs);
+    sincos(y, &sn, &cs);
     tab[t] = make_double2(cs, sn);
   }
   __syncthreads();

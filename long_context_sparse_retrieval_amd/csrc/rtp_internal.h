@@ -33,29 +33,30 @@ struct TileSum {
   uint32_t cum[kBins];
 };
 
-// Per-tile selection parameters written by the merge.
+// Per-tile selection parameters written by the threshold kernel.
 struct TileSel {
   uint64_t P;           // in-cell mass of bin b* in the tiles before this one
   int32_t sure_off;     // output offset of this tile's positions above b*
   int32_t bnd_off;      // output offset of this tile's positions taken from b*
 };
 
-// Per-query selection parameters written by the merge.
+// Per-query selection parameters written by the threshold kernel.
 struct HeadSel {
+  double r_u;           // residual mass p*Z - mass(bins < b*), in in-cell units of bin b*
   int32_t c;            // global max cell
   int32_t bstar;        // boundary bin
-  double r_u;           // residual mass p*Z - mass(bins < b*), in in-cell units of bin b*
   int32_t tstar;        // last tile holding selected bin-b* tokens
   int32_t all;          // 1: every position selected (p >= 1, or b* is the clamp bin)
   int32_t count_base;   // |S| without the crossing tile's bin-b* tokens
   int32_t total_sure;   // positions above bin b*
-  int32_t nvalid;       // m + 1
+  int32_t base_min;     // lowest ring cell in use
+  int32_t pad;
 };
 
 // Query preparation: exact indexer query and rotated query.
 struct QPrep {
   double qi[kR];        // bf16 values of q_idx, widened
-  float qrot[kD];       // R(m) q_pre in fp32
+  float qrot[kD];       // R(m) q_pre / sqrt(D) in fp32
 };
 
 // Split-K softmax state (o is 16-byte aligned for vector loads).
@@ -75,6 +76,8 @@ struct Geo {
   int T;                // tokens per scan tile
   int nt;               // tiles per query = ceil(N / T)
   int units;            // B * Hr * nq (retrieval queries)
+  int fin_tpw;          // scan tiles per finishing workgroup
+  int fin_nwg;          // finishing workgroups per query = ceil(nt / fin_tpw)
   // sliding window
   int nlg;              // KV groups holding at least one local head
   int swa_hb;           // local-head blocks per group (ceil(max local heads / kSwaHeads))
@@ -95,7 +98,6 @@ struct Geo {
   uint64_t *ring;        // [units][kRing] exact in-cell mass per absolute cell (cell mod kRing)
   uint32_t *cmax;        // [units] encoded max cell (0 = none)
   uint32_t *cmin;        // [units] encoded min base cell (0 = none)
-  uint32_t *ctr_scan;    // [units]
   uint32_t *ctr_fin;     // [units]
   uint32_t *ctr_swa;     // [swa_units * swa_hb]
 };
@@ -227,14 +229,15 @@ int launch_index_keys(const Geo &g, const rtp_bf16 *k_pre, const rtp_bf16 *w_k, 
                       long long n1, hipStream_t s);
 int launch_index_score(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
                        float *logits, hipStream_t s);
-// Scan phase: histogram (from k_idx + q, or from given logits) and merge.
-int launch_scan(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
-                const float *logits, int32_t *count, hipStream_t s);
-// Selection phase: select, optionally attend and combine into out.
-int launch_select(const Geo &g, const rtp_bf16 *k_idx, const float *logits, const rtp_bf16 *k,
-                  const rtp_bf16 *v, float *out, int32_t *idx, int32_t *count, long long cap, hipStream_t s);
-int launch_swa(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *k, const rtp_bf16 *v, float *out,
-               hipStream_t s);
+// Phase A: SWA workgroups of the local heads and/or scan tiles of the
+// retrieval queries (scores from k_idx + q, or from given logits).
+int launch_phase_a(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
+                   const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, bool with_scan,
+                   bool with_swa, hipStream_t s);
+// Finish phase: global threshold, selection, optional attention + combine.
+int launch_finish(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
+                  const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, int32_t *idx,
+                  int32_t *count, long long cap, hipStream_t s);
 int launch_sparse_attn(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *k, const rtp_bf16 *v,
                        const int32_t *idx, const int32_t *count, long long cap, float *out, hipStream_t s);
 int launch_fill_zero(void *ws, size_t bytes, hipStream_t s);

@@ -1,0 +1,199 @@
+// Sliding-window attention with attention sinks for the local heads, as
+// workgroups that run inside the scan launch (their latency hides under the
+// indexer stream) or on their own.
+//
+// "Full Attention Strikes Back" (RTPurbo) section 3.2: local heads attend, in
+// prefill and decode alike, to a sliding window plus attention sinks; the
+// attention itself is eq. (5)'s softmax(q . k / sqrt(d_h)) over those rows.
+//
+// A workgroup serves up to four local q heads of one KV group over one chunk
+// of window rows, so a K/V row is read once for all of them (GQA).  16 lanes
+// cover one 256-byte row (16 bytes each, coalesced); every lane group keeps
+// four rows in flight, so a 64-row chunk is requested in one round.  Chunk
+// states are combined by the last workgroup of each (sequence, group, query).
+#pragma once
+
+#include "block_util.h"
+
+namespace rtp {
+
+constexpr float kInvSqrtD = 0.08838834764831845f;   // 1 / sqrt(128)
+
+struct SwaShared {
+  float q[kSwaHeads][kD];
+  float m[4][kSwaHeads], l[4][kSwaHeads];
+  float o[4][kSwaHeads][kD];
+  double2 rope[kD / 2];
+  int heads[kSwaHeads];
+  int flag;
+  CombineShared cb;
+};
+
+// Position of window row ri for a query at m: the sinks first, then the window.
+__device__ __forceinline__ long long swa_row(long long ri, long long lo, long long ns) {
+  return ri < ns ? ri : lo + (ri - ns);
+}
+
+// Number of SWA workgroups of a launch (a multiple of 8 for the XCD mapping).
+__host__ __device__ __forceinline__ long long swa_blocks(const Geo &g) {
+  const long long chunks = (long long)g.swa_units * g.swa_nch;
+  return (chunks + 7) / 8 * 8 * g.swa_hb;
+}
+
+// One SWA workgroup; x = its index among the SWA workgroups of the launch.
+__device__ __forceinline__ void swa_block(const Geo &g, long long x, const rtp_bf16 *__restrict__ q_pre,
+                                          const rtp_bf16 *__restrict__ kc, const rtp_bf16 *__restrict__ vc,
+                                          float *__restrict__ out, SwaShared &sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, sub = lane & 15;
+  // XCD-aware mapping: blocks x and x + 8 hold the head blocks of one chunk (same XCD)
+  const long long xcd = x & 7, y = x >> 3;
+  const int hb = (int)(y % g.swa_hb);
+  const long long chunk_id = (y / g.swa_hb) * 8 + xcd;     // over (unit, chunk)
+  if (chunk_id >= (long long)g.swa_units * g.swa_nch) return;
+  const int unit = (int)(chunk_id / g.swa_nch), ch = (int)(chunk_id % g.swa_nch);
+  const int i = unit % g.nq, bl = unit / g.nq, lgi = bl % g.nlg, b = bl / g.nlg;
+  const int kvg = g.lgroup[lgi];
+  const long long m = g.N - g.nq + i;
+  const long long lo = m - g.window + 1 > 0 ? m - g.window + 1 : 0;
+  const long long ns = g.n_sink < lo ? g.n_sink : lo;
+  const long long L = ns + (m - lo + 1);
+  const long long r0 = (long long)ch * g.swa_chunk;
+  const long long r1 = r0 + g.swa_chunk < L ? r0 + g.swa_chunk : L;
+  const size_t cbase = ((size_t)b * g.Hkv + kvg) * g.Ncap * kD;
+  const rtp_bf16 *kb = kc + cbase, *vb = vc + cbase;
+
+  // request the first rows before preparing the queries
+  constexpr int U = 4;
+  uint4 kr[U], vr[U];
+  bool ok[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const long long ri = r0 + u * 16 + wv * 4 + grp;
+    ok[u] = ri < r1;
+    kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
+    if (ok[u]) {
+      const long long n = swa_row(ri, lo, ns);
+      kr[u] = *reinterpret_cast<const uint4 *>(kb + n * kD + sub * 8);
+      vr[u] = *reinterpret_cast<const uint4 *>(vb + n * kD + sub * 8);
+    }
+  }
+  if (tid == 0) {
+    int cnt = 0, seen = 0;
+    for (int h = kvg * g.G; h < (kvg + 1) * g.G; ++h) {
+      if (!((g.lmask[h >> 5] >> (h & 31)) & 1u)) continue;
+      if (seen >= hb * kSwaHeads && cnt < kSwaHeads) sm.heads[cnt++] = h;
+      ++seen;
+    }
+    for (int c = cnt; c < kSwaHeads; ++c) sm.heads[c] = -1;
+  }
+  rope_table(m, g.theta, sm.rope);       // ends with a barrier (also publishes sm.heads)
+  for (int hh = 0; hh < kSwaHeads; ++hh) {
+    const int h = sm.heads[hh];
+    if (h >= 0) {
+      rotate_query(q_pre + (((size_t)b * g.Hq + h) * g.nq + i) * kD, sm.rope, kInvSqrtD, sm.q[hh]);
+    } else {
+      if (tid < kD) sm.q[hh][tid] = 0.f;
+      __syncthreads();
+    }
+  }
+  float q[kSwaHeads][8];
+#pragma unroll
+  for (int hh = 0; hh < kSwaHeads; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[hh][e] = sm.q[hh][sub * 8 + e];
+  float mm[kSwaHeads], ll[kSwaHeads], oo[kSwaHeads][8];
+#pragma unroll
+  for (int hh = 0; hh < kSwaHeads; ++hh) {
+    mm[hh] = -INFINITY;
+    ll[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oo[hh][e] = 0.f;
+  }
+  for (long long base = r0;;) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
+      const uint32_t vw[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+      float kf[8], vf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf[2 * e] = bf_lo(kw[e]);
+        kf[2 * e + 1] = bf_hi(kw[e]);
+        vf[2 * e] = bf_lo(vw[e]);
+        vf[2 * e + 1] = bf_hi(vw[e]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < kSwaHeads; ++hh) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d += q[hh][e] * kf[e];
+        d = row16_sum(d);
+        if (ok[u]) {
+          const float mn = fmaxf(mm[hh], d);
+          const float a = __expf(mm[hh] - mn), pw = __expf(d - mn);
+          ll[hh] = ll[hh] * a + pw;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) oo[hh][e] = oo[hh][e] * a + pw * vf[e];
+          mm[hh] = mn;
+        }
+      }
+    }
+    base += 16 * U;
+    if (base >= r1) break;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long ri = base + u * 16 + wv * 4 + grp;
+      ok[u] = ri < r1;
+      kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
+      if (ok[u]) {
+        const long long n = swa_row(ri, lo, ns);
+        kr[u] = *reinterpret_cast<const uint4 *>(kb + n * kD + sub * 8);
+        vr[u] = *reinterpret_cast<const uint4 *>(vb + n * kD + sub * 8);
+      }
+    }
+  }
+  // merge the row groups of each wave, then the waves through LDS
+#pragma unroll
+  for (int hh = 0; hh < kSwaHeads; ++hh) {
+#pragma unroll
+    for (int off = 16; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(mm[hh], off), l2 = __shfl_xor(ll[hh], off);
+      float o2[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(oo[hh][e], off);
+      merge_state(mm[hh], ll[hh], oo[hh], m2, l2, o2, 8);
+    }
+    if (grp == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm.o[wv][hh][sub * 8 + e] = oo[hh][e];
+      if (sub == 0) {
+        sm.m[wv][hh] = mm[hh];
+        sm.l[wv][hh] = ll[hh];
+      }
+    }
+  }
+  __syncthreads();
+  // partials laid out [unit][head block][head][chunk]
+  Partial *parts = g.swa_part + ((size_t)(unit * g.swa_hb + hb) * kSwaHeads) * g.swa_nch;
+  for (int x2 = tid; x2 < kSwaHeads * kD; x2 += kWG) {
+    const int hh = x2 / kD, d = x2 % kD;
+    float m_ = -INFINITY, l_ = 0.f, o_ = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) merge_state(m_, l_, &o_, sm.m[w][hh], sm.l[w][hh], &sm.o[w][hh][d], 1);
+    Partial *p = parts + (size_t)hh * g.swa_nch + ch;
+    st_coherent(&p->o[d], o_);
+    if (d == 0) {
+      st_coherent(&p->m, m_);
+      st_coherent(&p->l, l_);
+    }
+  }
+  if (!arrive_last(g.ctr_swa + unit * g.swa_hb + hb, (uint32_t)g.swa_nch, &sm.flag)) return;
+  for (int hh = 0; hh < kSwaHeads; ++hh) {
+    const int h = sm.heads[hh];
+    if (h < 0) continue;
+    combine_partials(parts + (size_t)hh * g.swa_nch, g.swa_nch, out + (((size_t)b * g.Hq + h) * g.nq + i) * kD,
+                     &sm.cb);
+  }
+}
+
+}  // namespace rtp

@@ -13,12 +13,17 @@
 // in LDS with integer atomics.  Bins are 1/8 logit wide on a fixed grid, so
 // tile histograms merge exactly by an integer shift; masses are summed as
 // exact 64-bit integers of in-cell weights (deterministic in any order).  The
-// last workgroup of a query merges all tiles (boundary bin b*, per-tile prefix
-// of bin-b* mass and output offsets).  A second kernel re-reads one code byte
-// per token, takes every token above b* and the ordered prefix of bin b*
-// (recomputing only those tokens' scores), gathers their K/V rows and writes a
-// split-K softmax state; the last workgroup of a query combines them.
+// second kernel re-reads one code byte per token; each of its workgroups first
+// rebuilds the query's global histogram from an exact absolute-cell ring the
+// scan tiles filled with integer atomics (boundary bin b*, residual mass,
+// per-tile prefix of bin-b* mass), then takes every token of its tile above
+// b* and the ordered prefix of bin b* (recomputing only those tokens' scores),
+// gathers their K/V rows and writes a split-K softmax state; the last
+// workgroup of a query combines them.  The sliding-window workgroups of the
+// local heads run inside the scan launch, so their latency hides under the
+// indexer stream.
 #include "block_util.h"
+#include "swa.h"
 
 namespace rtp {
 
@@ -26,25 +31,27 @@ namespace {
 
 constexpr int kBnd = 254;   // highest regular bin; bin 255 is the clamp bin
 
+constexpr int kCells = 512;      // absolute score cells tracked per tile while streaming (64 logit units)
+
+// A histogram entry packs the token count (bits 40..63) above the summed
+// in-cell masses (bits 0..39; at most 8192 tokens of < 1.14 * 2^23 each).
+constexpr int kCountShift = 40;
+constexpr unsigned long long kMassMask = (1ull << kCountShift) - 1;
+
 template <int T>
 struct ScanShared {
   static constexpr int TPT = T / kWG;
-  float lg[T + kWG];                       // scores by tile position, one pad slot per TPT
-  unsigned long long mass[4][kBins];       // per-wave histograms
-  unsigned int cnt[4][kBins];
+  uint8_t codes[T];                        // local bin of every position of the tile
+  unsigned long long hist[4][kCells];      // per-wave histograms by absolute cell mod kCells:
+                                           // count << 40 | exact in-cell mass
   double q[kR];
   double qtmp[16][kR];
-  double red_d[4];
-  unsigned long long red_u[4];
+  float red_f[4];
   int red_i[4];
-  int flag;
-  // merge
-  double wcum[kBins];
-  double2 rope[kD / 2];
+  unsigned int red_u32[4];
+  unsigned long long red_u[4];
+  double red_d[4];
 };
-
-template <int T>
-__device__ __forceinline__ int lg_slot(int nl) { return nl + nl / ScanShared<T>::TPT; }
 
 // Encodings of the per-query max cell and min base cell for unsigned atomicMax
 // on a zero-initialised word (0 means "no tile yet").
@@ -53,21 +60,222 @@ __device__ __forceinline__ int dec_max(uint32_t e) { return (int)(e - 0x80000000
 __device__ __forceinline__ uint32_t enc_min(int c) { return 0x7fffffffu - (uint32_t)c; }
 __device__ __forceinline__ int dec_min(uint32_t e) { return (int)(0x7fffffffu - e); }
 
-// Merge the histograms of one query into its selection parameters (run by the
-// last workgroup of the query).  Every tile has added its bins into the
-// query's ring of absolute cells (exact 64-bit integer sums), so the global
-// histogram is 256 ring reads.  Cells spread over more than kRing would alias
-// in the ring; that case falls back to shifting every tile histogram.
+
+// One scan workgroup: tile t of query unit (blk = unit * nt + t).
+template <int T, bool FROM_LOGITS>
+__device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rtp_bf16 *__restrict__ q_pre,
+                                           const rtp_bf16 *__restrict__ w_q, const rtp_bf16 *__restrict__ k_idx,
+                                           const float *__restrict__ logits, ScanShared<T> &sm) {
+  constexpr int TPT = T / kWG;
+  constexpr int BATCH = TPT < 8 ? TPT : 8;
+  const int tid = threadIdx.x, wv = tid >> 6;
+  const int unit = (int)(blk / g.nt), t = (int)(blk % g.nt);
+  const int i = unit % g.nq, br = unit / g.nq, r = br % g.Hr, b = br / g.Hr;
+  const long long m = g.N - g.nq + i;
+  const long long n0 = (long long)t * T;
+
+  // pass 1: scores in registers; consecutive threads take consecutive positions.
+  // Each score is binned at once by its absolute cell (no tile max needed), so
+  // the histogram work overlaps the stream.  The first batch of key rows is
+  // requested before the query projection.
+  float lg[TPT];
+  float mx = -INFINITY;
+  int cmin = INT32_MAX;
+  for (int x = tid; x < 4 * kCells; x += kWG) (&sm.hist[0][0])[x] = 0ull;
+  auto bin_abs = [&](float sc) {
+    if (sc != -INFINITY) {
+      const int cell = score_cell(sc);
+      atomicAdd(&sm.hist[wv][cell & (kCells - 1)], (unsigned long long)cell_weight(sc, cell) | (1ull << kCountShift));
+      mx = fmaxf(mx, sc);
+      cmin = min(cmin, cell);
+    }
+  };
+  if (FROM_LOGITS) {
+    __syncthreads();
+    const float *row = logits + (size_t)unit * g.N;
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) {
+      const long long n = n0 + k * kWG + tid;
+      lg[k] = (n <= m) ? row[n] : -INFINITY;
+      bin_abs(lg[k]);
+    }
+  } else {
+    const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hr + r) * g.Ncap * kR);
+    uint4 ra[BATCH], rb[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const long long n = n0 + u * kWG + tid;
+      ra[u] = rb[u] = make_uint4(0, 0, 0, 0);
+      if (n <= m) {
+        ra[u] = rows[2 * n];
+        rb[u] = rows[2 * n + 1];
+      }
+    }
+    project_query(q_pre + (((size_t)b * g.Hq + g.rhead[r]) * g.nq + i) * kD, w_q + (size_t)r * kD * kR, sm.q,
+                  sm.qtmp);
+    double q[kR];
+#pragma unroll
+    for (int x = 0; x < kR; ++x) {
+      const unsigned long long v = (unsigned long long)__double_as_longlong(sm.q[x]);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+      q[x] = __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const long long n = n0 + u * kWG + tid;
+      lg[u] = (n <= m) ? dot16_exact(q, ra[u], rb[u]) : -INFINITY;
+      bin_abs(lg[u]);
+    }
+#pragma unroll
+    for (int k = BATCH; k < TPT; ++k) {
+      const long long n = n0 + k * kWG + tid;
+      lg[k] = (n <= m) ? dot16_exact(q, rows[2 * n], rows[2 * n + 1]) : -INFINITY;
+      bin_abs(lg[k]);
+    }
+  }
+  mx = block_max<float>(mx, sm.red_f);
+  cmin = block_min<int>(cmin, sm.red_i);
+  const int c_t = (mx == -INFINITY) ? INT32_MIN : score_cell(mx);
+
+  // local bins j = c_t - cell; cells 255 or more below c_t form the clamp bin 255,
+  // weighted relative to its base cell c_t - 255
+  unsigned long long packed = 0;
+  // (a span of at most kCells - 2 keeps every cell unique mod kCells and the clamp
+  // cells c_t - 255 .. cmin within the 256 threads below)
+  if (c_t != INT32_MIN && (long long)c_t - cmin <= kCells - 2) {
+    const int j = tid;
+    if (j < kBins - 1) {
+      const int cell = c_t - j;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) packed += sm.hist[w][cell & (kCells - 1)];
+    }
+    // clamp bin: cells c_t - 255 - x for x = 0..(c_t - 255 - cmin)
+    const long long cell = (long long)c_t - (kBins - 1) - tid;
+    double cm = 0.0;
+    unsigned long long cc = 0;
+    if (cell >= cmin) {
+      unsigned long long e = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) e += sm.hist[w][cell & (kCells - 1)];
+      cm = (double)(e & kMassMask) * exp(-(double)tid * 0.125);
+      cc = e >> kCountShift;
+    }
+    double tm;
+    (void)block_excl_scan<double>(cm, tm, sm.red_d);
+    unsigned long long tc;
+    (void)block_excl_scan<unsigned long long>(cc, tc, sm.red_u);
+    if (j == kBins - 1) packed = (unsigned long long)tm | (tc << kCountShift);
+  } else {
+    // cells of this tile span kCells or more: rebin relative to c_t from the scores in registers
+    __syncthreads();
+    for (int x = tid; x < 4 * kBins; x += kWG) sm.hist[x / kBins][x % kBins] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) {
+      const float sc = lg[k];
+      if (sc == -INFINITY) continue;
+      const int cell = score_cell(sc);
+      const int jb = c_t - cell >= kBins - 1 ? kBins - 1 : c_t - cell;
+      const uint32_t u = jb == kBins - 1 ? cell_weight(sc, c_t - (kBins - 1)) : cell_weight(sc, cell);
+      atomicAdd(&sm.hist[wv][jb], (unsigned long long)u | (1ull << kCountShift));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) packed += sm.hist[w][tid];
+  }
+
+  // codes (local bins) from the scores in registers
+#pragma unroll
+  for (int k = 0; k < TPT; ++k) {
+    const float sc = lg[k];
+    uint8_t code = 255;
+    if (sc != -INFINITY) {
+      const int jb = c_t - score_cell(sc);
+      code = (uint8_t)(jb >= kBins - 1 ? kBins - 1 : jb);
+    }
+    sm.codes[k * kWG + tid] = code;
+  }
+  __syncthreads();
+  {
+    uint8_t *dst = g.codes + (size_t)unit * g.nt * T + (size_t)t * T + (size_t)tid * TPT;
+    const uint8_t *src = sm.codes + tid * TPT;
+    if constexpr (TPT % 16 == 0) {
+#pragma unroll
+      for (int k = 0; k < TPT; k += 16)
+        *reinterpret_cast<uint4 *>(dst + k) = *reinterpret_cast<const uint4 *>(src + k);
+    } else {
+#pragma unroll
+      for (int k = 0; k < TPT; k += 4)
+        *reinterpret_cast<uint32_t *>(dst + k) = *reinterpret_cast<const uint32_t *>(src + k);
+    }
+  }
+
+  // tile summary, read by the merge kernel
+  TileSum *tsum = g.tsum + (size_t)unit * g.nt + t;
+  const unsigned long long ms = packed & kMassMask;
+  const unsigned int cn = (unsigned int)(packed >> kCountShift);
+  unsigned int tot;
+  const unsigned int ex = block_excl_scan<unsigned int>(cn, tot, sm.red_u32);
+  tsum->mass[tid] = ms;
+  tsum->cum[tid] = ex + cn;
+  if (tid == 0) {
+    tsum->c_t = c_t;
+    tsum->nvalid = (int32_t)tot;
+  }
+  // absolute-cell histogram of the query: exact integer sums in any order
+  if (c_t != INT32_MIN) {
+    if (tid == 0) {
+      atomicMax(g.cmax + unit, enc_max(c_t));
+      atomicMax(g.cmin + unit, enc_min(c_t - (kBins - 1)));
+    }
+    if (ms) atomicAdd((unsigned long long *)(g.ring + (size_t)unit * kRing + ((c_t - tid) & (kRing - 1))), ms);
+  }
+}
+
 template <int T>
-__device__ void merge_query(const Geo &g, int unit, long long m, const rtp_bf16 *q_pre, int32_t *count_out,
-                            ScanShared<T> &sm) {
-  const int tid = threadIdx.x;
+union PhaseAShared {
+  ScanShared<T> scan;
+  SwaShared swa;
+};
+
+// Phase A: the local heads' sliding-window workgroups (first) and the
+// retrieval heads' scan tiles in one launch.
+template <int T, bool FROM_LOGITS>
+__global__ __launch_bounds__(kWG) void phase_a_kernel(Geo g, const rtp_bf16 *__restrict__ q_pre,
+                                                      const rtp_bf16 *__restrict__ w_q,
+                                                      const rtp_bf16 *__restrict__ k_idx,
+                                                      const float *__restrict__ logits,
+                                                      const rtp_bf16 *__restrict__ kc,
+                                                      const rtp_bf16 *__restrict__ vc, float *__restrict__ out,
+                                                      long long n_swa) {
+  __shared__ PhaseAShared<T> sm;
+  const long long x = blockIdx.x;
+  if (x < n_swa)
+    swa_block(g, x, q_pre, kc, vc, out, sm.swa);
+  else
+    scan_block<T, FROM_LOGITS>(g, x - n_swa, q_pre, w_q, k_idx, logits, sm.scan);
+}
+
+struct ThrShared {
+  double qi[kR];
+  double qtmp[16][kR];
+  double2 rope[kD / 2];
+  double wcum[kBins];
+  double red_d[4];
+  unsigned long long red_u[4];
+  int red_i[4];
+};
+
+// The query's global histogram from the ring (or, when its cells span more
+// than the ring holds, from every tile histogram): boundary bin, residual
+// mass in in-cell units of bin b*, and whether every position is taken.
+__device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, int base_min, ThrShared &sm,
+                                                 int &bstar_out, double &r_u_out, int &all_out) {
+  const int tid = threadIdx.x, j = tid;
   const TileSum *ts = g.tsum + (size_t)unit * g.nt;
-  uint64_t *ring = g.ring + (size_t)unit * kRing;
-  const int c = dec_max(__hip_atomic_load(g.cmax + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  const int base_min = dec_min(__hip_atomic_load(g.cmin + unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const uint64_t *ring = g.ring + (size_t)unit * kRing;
   const long long span = (long long)c - base_min;
-  const int j = tid;
   unsigned long long H = 0;
   double w255 = 0.0;
   if (span < kRing) {
@@ -76,10 +284,7 @@ __device__ void merge_query(const Geo &g, int unit, long long m, const rtp_bf16 
       const unsigned long long mj = ring[cell & (kRing - 1)];
       if (mj) w255 += (double)mj * exp((double)(cell - c) * 0.125);
     }
-    __syncthreads();
-    for (long long cell = (long long)base_min + j; cell <= c; cell += kWG) ring[cell & (kRing - 1)] = 0ull;
   } else {
-    // slow path: shift every tile histogram
     for (int t = 0; t < g.nt; ++t) {
       const int ct = ts[t].c_t;
       if (ct == INT32_MIN) continue;
@@ -90,12 +295,6 @@ __device__ void merge_query(const Geo &g, int unit, long long m, const rtp_bf16 
         if (mj) w255 += (double)mj * exp(-(double)(j + d) * 0.125);
       }
     }
-    __syncthreads();
-    for (int x = j; x < kRing; x += kWG) ring[x] = 0ull;
-  }
-  if (tid == 0) {
-    g.cmax[unit] = 0u;
-    g.cmin[unit] = 0u;
   }
   // clamp-bin mass: fixed-order sum over threads
   sm.wcum[j] = w255;
@@ -109,37 +308,63 @@ __device__ void merge_query(const Geo &g, int unit, long long m, const rtp_bf16 
   const double W255 = sm.red_d[0] * 0x1p-23;
   __syncthreads();
   const double Wj = j <= kBnd ? (double)H * 0x1p-23 * exp(-(double)j * 0.125) : W255;
-  // cumulative bin masses from the top bin down (fixed order)
-  double tot;
-  const double excl = block_excl_scan<double>(Wj, tot, sm.red_d);
-  const double incl = excl + Wj;
-  const double Z = tot;
+  double Z;
+  const double excl = block_excl_scan<double>(Wj, Z, sm.red_d);
   const double need = (double)g.p * Z;
-  const int cand = (incl >= need) ? j : kBins;
-  int bstar = block_min<int>(cand, sm.red_i);
+  int bstar = block_min<int>(excl + Wj >= need ? j : kBins, sm.red_i);
   if (bstar >= kBins) bstar = kBins - 1;
   sm.wcum[j] = excl;                      // mass above bin j
   __syncthreads();
   const double before = sm.wcum[bstar];
   __syncthreads();
-  const int all = (g.p >= 1.0f || bstar >= kBins - 1) ? 1 : 0;
-  const double r_u = (need - before) * 0x1p23 * exp((double)bstar * 0.125);
+  all_out = (g.p >= 1.0f || bstar >= kBins - 1) ? 1 : 0;
+  r_u_out = (need - before) * 0x1p23 * exp((double)bstar * 0.125);
+  bstar_out = bstar;
+}
 
-  // per tile: bin-b* prefix mass, sure / boundary counts and offsets
+// Threshold kernel: one workgroup per query.  Global threshold, per-tile
+// prefix of bin-b* mass and output offsets, and the prepared queries.
+__global__ __launch_bounds__(kWG) void threshold_kernel(Geo g, const rtp_bf16 *__restrict__ q_pre,
+                                                        const rtp_bf16 *__restrict__ w_q, int32_t *count) {
+  __shared__ ThrShared sm;
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int i = unit % g.nq, br = unit / g.nq, r = br % g.Hr, b = br / g.Hr;
+  const long long m = g.N - g.nq + i;
+  const TileSum *ts = g.tsum + (size_t)unit * g.nt;
+  const int c = dec_max(g.cmax[unit]);
+  const int base_min = dec_min(g.cmin[unit]);
+  const int ct0 = tid < g.nt ? ts[tid].c_t : INT32_MIN;     // first chunk of tile maxima, early
+  QPrep *qp = g.qprep + unit;
+  if (q_pre) {
+    const rtp_bf16 *q_row = q_pre + (((size_t)b * g.Hq + g.rhead[r]) * g.nq + i) * kD;
+    if (w_q) {
+      project_query(q_row, w_q + (size_t)r * kD * kR, sm.qi, sm.qtmp);
+      if (tid < kR) qp->qi[tid] = sm.qi[tid];
+    }
+    rope_table(m, g.theta, sm.rope);
+    rotate_query(q_row, sm.rope, kInvSqrtD, qp->qrot);
+  }
+  int bstar, all;
+  double r_u;
+  global_threshold(g, unit, c, base_min, sm, bstar, r_u, all);
+  // per tile: bin-b* prefix mass, counts above b* and in b*, output offsets; the
+  // crossing tile is the last one whose bin-b* tokens start below the residual,
+  // and every bin-b* token of the tiles before it is taken
   unsigned long long carryP = 0;
   int carryS = 0, carryB = 0, tstar = -1, bo_star = -1;
   for (int t0 = 0; t0 < g.nt; t0 += kWG) {
-    const int t = t0 + tid;
+    const int tt = t0 + tid;
     unsigned long long bm = 0;
     int sure = 0, bc = 0;
-    const int ct = t < g.nt ? ts[t].c_t : INT32_MIN;
-    if (ct != INT32_MIN) {
-      const long long bl = (long long)bstar - ((long long)c - ct);
-      if (bl >= 1) sure = (int)ts[t].cum[(bl < kBins - 1 ? (int)bl : kBins - 1) - 1];
+    const int ctt = t0 == 0 ? ct0 : (tt < g.nt ? ts[tt].c_t : INT32_MIN);
+    if (ctt != INT32_MIN && !all) {
+      const long long bl = (long long)bstar - ((long long)c - ctt);
+      if (bl >= 1) sure = (int)ts[tt].cum[(bl < kBins - 1 ? (int)bl : kBins - 1) - 1];
       if (bl >= 0 && bl <= kBnd) {
-        const uint32_t hi = ts[t].cum[bl];
-        bc = (int)(hi - (bl ? ts[t].cum[bl - 1] : 0u));
-        bm = ts[t].mass[bl];
+        const uint32_t hi = ts[tt].cum[bl];
+        bc = (int)(hi - (bl ? ts[tt].cum[bl - 1] : 0u));
+        bm = ts[tt].mass[bl];
       }
     }
     unsigned long long totP;
@@ -147,181 +372,40 @@ __device__ void merge_query(const Geo &g, int unit, long long m, const rtp_bf16 
     const unsigned long long P = carryP + block_excl_scan<unsigned long long>(bm, totP, sm.red_u);
     const int so = carryS + block_excl_scan<int>(sure, totS, sm.red_i);
     const int bo = carryB + block_excl_scan<int>(bc, totB, sm.red_i);
-    if (t < g.nt) {
-      TileSel *tl = g.tsel + (size_t)unit * g.nt + t;
+    if (tt < g.nt) {
+      TileSel *tl = g.tsel + (size_t)unit * g.nt + tt;
       tl->P = P;
       tl->sure_off = so;
       tl->bnd_off = bo;
     }
-    // the crossing tile is the last one whose bin-b* tokens start below the residual;
-    // every bin-b* token of the tiles before it is taken
-    const bool crossing = t < g.nt && bc > 0 && (double)P < r_u;
-    tstar = max(tstar, block_max<int>(crossing ? t : -1, sm.red_i));
+    const bool crossing = tt < g.nt && bc > 0 && (double)P < r_u;
+    tstar = max(tstar, block_max<int>(crossing ? tt : -1, sm.red_i));
     bo_star = max(bo_star, block_max<int>(crossing ? bo : -1, sm.red_i));
     carryP += totP;
     carryS += totS;
     carryB += totB;
   }
-  const int total_sure = carryS;
-  const int count_base = total_sure + (tstar >= 0 ? bo_star : 0);
   if (tid == 0) {
     HeadSel *hs = g.hsel + unit;
+    hs->r_u = r_u;
     hs->c = c;
     hs->bstar = bstar;
-    hs->r_u = r_u;
     hs->tstar = tstar;
     hs->all = all;
-    hs->count_base = count_base;
-    hs->total_sure = total_sure;
-    hs->nvalid = (int)(m + 1);
-    if (all && count_out) count_out[unit] = (int)(m + 1);
-  }
-  // query preparation for the selection kernel
-  QPrep *qp = g.qprep + unit;
-  if (tid < kR) qp->qi[tid] = sm.q[tid];
-  if (q_pre) {
-    const int i = unit % g.nq, br = unit / g.nq, r = br % g.Hr, b = br / g.Hr;
-    const rtp_bf16 *q_row = q_pre + (((size_t)b * g.Hq + g.rhead[r]) * g.nq + i) * kD;
-    rope_table(m, g.theta, sm.rope);
-    rotate_query(q_row, sm.rope, 0.08838834764831845f, qp->qrot);
+    hs->total_sure = carryS;
+    hs->count_base = carryS + (tstar >= 0 ? bo_star : 0);
+    hs->base_min = base_min;
+    if (all && count) count[unit] = (int)(m + 1);
   }
 }
 
-// Scan kernel: one workgroup per (query unit, tile of T positions).
-template <int T, bool FROM_LOGITS>
-__global__ __launch_bounds__(kWG) void scan_kernel(Geo g, const rtp_bf16 *__restrict__ q_pre,
-                                                   const rtp_bf16 *__restrict__ w_q,
-                                                   const rtp_bf16 *__restrict__ k_idx,
-                                                   const float *__restrict__ logits, int32_t *count_out) {
-  constexpr int TPT = T / kWG;
-  __shared__ ScanShared<T> sm;
-  const int tid = threadIdx.x, wv = tid >> 6;
-  const int unit = blockIdx.x / g.nt, t = blockIdx.x % g.nt;
-  const int i = unit % g.nq, br = unit / g.nq, r = br % g.Hr, b = br / g.Hr;
-  const long long m = g.N - g.nq + i;
-  const long long n0 = (long long)t * T;
-
-  for (int x = tid; x < 4 * kBins; x += kWG) {
-    (&sm.mass[0][0])[x] = 0ull;
-    (&sm.cnt[0][0])[x] = 0u;
-  }
-  if (!FROM_LOGITS) {
-    project_query(q_pre + (((size_t)b * g.Hq + g.rhead[r]) * g.nq + i) * kD, w_q + (size_t)r * kD * kR, sm.q,
-                  sm.qtmp);
-  } else {
-    __syncthreads();
-  }
-
-  // pass 1: scores (coalesced: consecutive threads take consecutive positions)
-  float mx = -INFINITY;
-  if (FROM_LOGITS) {
-    const float *row = logits + (size_t)unit * g.N;
-#pragma unroll 4
-    for (int k = 0; k < TPT; ++k) {
-      const int nl = k * kWG + tid;
-      const long long n = n0 + nl;
-      const float s = (n <= m) ? row[n] : -INFINITY;
-      sm.lg[lg_slot<T>(nl)] = s;
-      mx = fmaxf(mx, s);
-    }
-  } else {
-    double q[kR];
-#pragma unroll
-    for (int x = 0; x < kR; ++x) q[x] = sm.q[x];
-    const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hr + r) * g.Ncap * kR);
-#pragma unroll 8
-    for (int k = 0; k < TPT; ++k) {
-      const int nl = k * kWG + tid;
-      const long long n = n0 + nl;
-      float s = -INFINITY;
-      if (n <= m) s = dot16_exact(q, rows[2 * n], rows[2 * n + 1]);
-      sm.lg[lg_slot<T>(nl)] = s;
-      mx = fmaxf(mx, s);
-    }
-  }
-  mx = block_max<float>(mx, reinterpret_cast<float *>(sm.red_d));
-  const int c_t = (mx == -INFINITY) ? INT32_MIN : score_cell(mx);
-
-  // pass 2: histogram and codes (each thread owns TPT consecutive positions)
-  uint8_t code[TPT];
-  int nv = 0;
-#pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    const int nl = tid * TPT + k;
-    const float s = sm.lg[lg_slot<T>(nl)];
-    code[k] = 255;
-    if (s != -INFINITY) {
-      const int cell = score_cell(s);
-      int jb = c_t - cell;
-      uint32_t u;
-      if (jb >= kBins - 1) {
-        jb = kBins - 1;
-        u = cell_weight(s, c_t - (kBins - 1));
-      } else {
-        u = cell_weight(s, cell);
-      }
-      atomicAdd(&sm.mass[wv][jb], (unsigned long long)u);
-      atomicAdd(&sm.cnt[wv][jb], 1u);
-      code[k] = (uint8_t)jb;
-      ++nv;
-    }
-  }
-  {
-    uint8_t *dst = g.codes + (size_t)unit * g.nt * T + (size_t)t * T + (size_t)tid * TPT;
-    if constexpr (TPT % 16 == 0) {
-#pragma unroll
-      for (int k = 0; k < TPT; k += 16) {
-        uint4 v;
-        uint32_t w[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-          w[x] = (uint32_t)code[k + 4 * x] | ((uint32_t)code[k + 4 * x + 1] << 8) |
-                 ((uint32_t)code[k + 4 * x + 2] << 16) | ((uint32_t)code[k + 4 * x + 3] << 24);
-        v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
-        *reinterpret_cast<uint4 *>(dst + k) = v;
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < TPT; k += 4) {
-        const uint32_t w0 = (uint32_t)code[k] | ((uint32_t)code[k + 1] << 8) | ((uint32_t)code[k + 2] << 16) |
-                            ((uint32_t)code[k + 3] << 24);
-        *reinterpret_cast<uint32_t *>(dst + k) = w0;
-      }
-    }
-  }
-  __syncthreads();
-
-  // tile summary
-  TileSum *tsum = g.tsum + (size_t)unit * g.nt + t;
-  {
-    const int j = tid;
-    const unsigned long long ms = sm.mass[0][j] + sm.mass[1][j] + sm.mass[2][j] + sm.mass[3][j];
-    const unsigned int cn = sm.cnt[0][j] + sm.cnt[1][j] + sm.cnt[2][j] + sm.cnt[3][j];
-    unsigned int tot;
-    const unsigned int ex = block_excl_scan<unsigned int>(cn, tot, reinterpret_cast<unsigned int *>(sm.red_i));
-    st_coherent(&tsum->mass[j], (uint64_t)ms);
-    st_coherent(&tsum->cum[j], (uint32_t)(ex + cn));
-    int nvt;
-    (void)block_excl_scan<int>(nv, nvt, sm.red_i);
-    if (tid == 0) {
-      st_coherent(&tsum->c_t, (int32_t)c_t);
-      st_coherent(&tsum->nvalid, (int32_t)nvt);
-    }
-  }
-  if (c_t != INT32_MIN) {
-    if (tid == 0) {
-      atomicMax(g.cmax + unit, enc_max(c_t));
-      atomicMax(g.cmin + unit, enc_min(c_t - (kBins - 1)));
-    }
-    const unsigned long long ms = sm.mass[0][tid] + sm.mass[1][tid] + sm.mass[2][tid] + sm.mass[3][tid];
-    if (ms) atomicAdd((unsigned long long *)(g.ring + (size_t)unit * kRing + ((c_t - tid) & (kRing - 1))), ms);
-  }
-  if (!arrive_last(g.ctr_scan + unit, (uint32_t)g.nt, &sm.flag)) return;
-  merge_query<T>(g, unit, m, FROM_LOGITS ? nullptr : q_pre, count_out, sm);
-}
-
-struct SelShared {
-  int list[8192];
+struct FinShared {
+  static constexpr int kList = 2048;
+  static constexpr int kCodes = 32768;
+  uint8_t codes[kCodes];                   // codes of this workgroup's tiles
+  int list[kList];                         // positions pending attention
+  TileSel tsel[32];
+  int ct[32];
   float q[kD];
   double qi[kR];
   unsigned long long red_u[4];
@@ -332,185 +416,270 @@ struct SelShared {
   Partial res;
 };
 
-// Selection kernel: one workgroup per (query unit, tile); optionally attends.
+// Finish kernel: one workgroup per (query unit, run of fin_tpw tiles).  Tiles
+// before the crossing tile take their whole bin b*, tiles after it none; only
+// the crossing tile recomputes the scores of its bin-b* tokens for the ordered
+// fill.  Selected positions are written (optional) and attended (optional);
+// the last workgroup of the query combines the states and resets the ring.
 template <int T, bool FROM_LOGITS, bool ATTEND>
-__global__ __launch_bounds__(kWG) void select_kernel(Geo g, const rtp_bf16 *__restrict__ k_idx,
+__global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__restrict__ k_idx,
                                                      const float *__restrict__ logits,
                                                      const rtp_bf16 *__restrict__ kc,
                                                      const rtp_bf16 *__restrict__ vc, float *__restrict__ out,
                                                      int32_t *__restrict__ idx, int32_t *__restrict__ count,
                                                      long long cap) {
-  constexpr int TPT = T / kWG;
-  static_assert(T <= 8192, "selection list sized for T <= 8192");
-  __shared__ SelShared sm;
+  constexpr int TPT = T / kWG;             // positions per thread per tile (consecutive)
+  static_assert(T <= FinShared::kCodes, "tile larger than the code staging area");
+  __shared__ FinShared sm;
   const int tid = threadIdx.x;
-  const int unit = blockIdx.x / g.nt, t = blockIdx.x % g.nt;
+  const int unit = blockIdx.x / g.fin_nwg, w = blockIdx.x % g.fin_nwg;
   const int i = unit % g.nq, br = unit / g.nq, r = br % g.Hr, b = br / g.Hr;
+  const int hq = g.rhead[r];
   const long long m = g.N - g.nq + i;
-  const long long n0 = (long long)t * T;
+  const int t_begin = w * g.fin_tpw;
+  const int t_end = t_begin + g.fin_tpw < g.nt ? t_begin + g.fin_tpw : g.nt;
+  const int kvg = hq / g.G;
+  const size_t cbase = ((size_t)b * g.Hkv + kvg) * g.Ncap * kD;
+
+  // one round of independent loads: all codes of the run, tile parameters, query
+  {
+    constexpr int kPer = FinShared::kCodes / 16 / kWG;
+    const uint4 *src = reinterpret_cast<const uint4 *>(g.codes + (size_t)unit * g.nt * T + (size_t)t_begin * T);
+    const int n16 = (t_end - t_begin) * T / 16;
+    uint4 cv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int x = tid + u * kWG;
+      if (x < n16) cv[u] = src[x];
+    }
+    if (tid < t_end - t_begin) {
+      sm.tsel[tid] = g.tsel[(size_t)unit * g.nt + t_begin + tid];
+      sm.ct[tid] = g.tsum[(size_t)unit * g.nt + t_begin + tid].c_t;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int x = tid + u * kWG;
+      if (x < n16) reinterpret_cast<uint4 *>(sm.codes)[x] = cv[u];
+    }
+  }
   const HeadSel hs = g.hsel[unit];
-  const TileSum *ts = g.tsum + (size_t)unit * g.nt + t;
-  const TileSel tl = g.tsel[(size_t)unit * g.nt + t];
-  const int ct = ts->c_t;
-  if (tid < kR) sm.qi[tid] = g.qprep[unit].qi[tid];
+  if (!FROM_LOGITS && tid < kR) sm.qi[tid] = g.qprep[unit].qi[tid];
   if (ATTEND && tid < kD) sm.q[tid] = g.qprep[unit].qrot[tid];
   __syncthreads();
 
-  // classify this thread's TPT consecutive positions
-  uint8_t code[TPT];
-  {
-    const uint8_t *src = g.codes + (size_t)unit * g.nt * T + (size_t)t * T + (size_t)tid * TPT;
-    if constexpr (TPT % 16 == 0) {
-#pragma unroll
-      for (int k = 0; k < TPT; k += 16) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(src + k);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int x = 0; x < 16; ++x) code[k + x] = (uint8_t)(w[x >> 2] >> (8 * (x & 3)));
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < TPT; k += 4) {
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(src + k);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) code[k + x] = (uint8_t)(w >> (8 * x));
-      }
+  float run_m = -INFINITY, run_l = 0.f, run_o = 0.f;    // thread d < 128 holds channel d
+  int nlist = 0;                                        // block-uniform
+  int emitted_b = 0;                                    // bin-b* positions taken in the crossing tile
+  for (int t = t_begin; t < t_end; ++t) {
+    const TileSel tl = sm.tsel[t - t_begin];
+    const int ct = sm.ct[t - t_begin];
+    const long long n0 = (long long)t * T;
+    const bool any = ct != INT32_MIN;
+    int bl = -1;
+    if (any && !hs.all) {
+      const long long blv = (long long)hs.bstar - ((long long)hs.c - ct);
+      bl = blv < -1 ? -1 : (int)blv;
     }
-  }
-  const long long nbase = n0 + (long long)tid * TPT;
-  int bl = -1;                  // local index of bin b*
-  bool any = ct != INT32_MIN;
-  if (any && !hs.all) {
-    const long long d = (long long)hs.c - ct;
-    const long long blv = (long long)hs.bstar - d;
-    bl = blv < -1 ? -1 : (int)blv;
-  }
-  const bool bnd_on = any && !hs.all && bl >= 0 && bl <= kBnd && t <= hs.tstar;
-  unsigned sure_m = 0, bnd_m = 0;     // bit k: position k of this thread
-  unsigned long long bmass = 0;
-  uint32_t bu[TPT];
-#pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    const long long n = nbase + k;
-    bu[k] = 0;
-    if (!any || n > m) continue;
-    if (hs.all || (int)code[k] < bl) {
-      sure_m |= 1u << k;
-    } else if (bnd_on && (int)code[k] == bl) {
-      float s;
-      if (FROM_LOGITS) {
-        s = logits[(size_t)unit * g.N + n];
-      } else {
-        const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hr + r) * g.Ncap * kR);
-        s = dot16_exact(sm.qi, rows[2 * n], rows[2 * n + 1]);
-      }
-      bu[k] = cell_weight(s, score_cell(s));
-      bmass += bu[k];
-      bnd_m |= 1u << k;
-    }
-  }
-  // ordered fill of bin b*: a token is taken while the mass before it is below the residual
-  unsigned long long tot_u;
-  unsigned long long pre = tl.P + block_excl_scan<unsigned long long>(bmass, tot_u, sm.red_u);
-  unsigned take_m = 0;
-#pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    if (bnd_m & (1u << k)) {
-      if ((double)pre < hs.r_u) take_m |= 1u << k;
-      pre += bu[k];
-    }
-  }
-  const int ns = __popc(sure_m), nb = __popc(take_m);
-  int tot_s, tot_b;
-  const int rs = block_excl_scan<int>(ns, tot_s, sm.red_i);
-  const int rb = block_excl_scan<int>(nb, tot_b, sm.red_i);
-  // outputs: positions above b* first, then the taken bin-b* positions
-  const long long so = hs.all ? n0 : (long long)tl.sure_off;
-  const long long bo = (long long)hs.total_sure + tl.bnd_off;
-  {
-    int a = rs, c2 = rb;
+    const bool bnd_ok = any && !hs.all && bl >= 0 && bl <= kBnd;
+    const bool crossing = bnd_ok && t == hs.tstar;
+    const bool take_all_bnd = bnd_ok && t < hs.tstar;
+    const long long nbase = n0 + (long long)tid * TPT;
+    const uint8_t *cd = sm.codes + (t - t_begin) * T + tid * TPT;
+    unsigned sure_m = 0, bnd_m = 0;
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
-      const int n = (int)(nbase + k);
-      if (sure_m & (1u << k)) {
-        if (idx && so + a < cap) idx[(size_t)unit * cap + so + a] = n;
-        if (ATTEND) sm.list[a] = n;
-        ++a;
+      const int code = cd[k];
+      if (!any || nbase + k > m) continue;
+      if (hs.all || code < bl) sure_m |= 1u << k;
+      else if (code == bl && (take_all_bnd || crossing)) bnd_m |= 1u << k;
+    }
+    unsigned take_m = take_all_bnd ? bnd_m : 0u;
+    if (crossing) {
+      // ordered fill: a bin-b* token is taken while the mass before it is below the residual
+      auto weight = [&](long long n) -> uint32_t {
+        float sc;
+        if (FROM_LOGITS) {
+          sc = logits[(size_t)unit * g.N + n];
+        } else {
+          const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hr + r) * g.Ncap * kR);
+          sc = dot16_exact(sm.qi, rows[2 * n], rows[2 * n + 1]);
+        }
+        return cell_weight(sc, score_cell(sc));
+      };
+      unsigned long long bmass = 0;
+#pragma unroll
+      for (int k = 0; k < TPT; ++k)
+        if (bnd_m & (1u << k)) bmass += weight(nbase + k);
+      unsigned long long tot_u;
+      unsigned long long pre = tl.P + block_excl_scan<unsigned long long>(bmass, tot_u, sm.red_u);
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) {
+        if (bnd_m & (1u << k)) {
+          if ((double)pre < hs.r_u) take_m |= 1u << k;
+          pre += weight(nbase + k);
+        }
       }
-      if (take_m & (1u << k)) {
-        if (idx && bo + c2 < cap) idx[(size_t)unit * cap + bo + c2] = n;
-        if (ATTEND) sm.list[tot_s + c2] = n;
-        ++c2;
+    }
+    int ts_, tb_;
+    const int rs = block_excl_scan<int>(__popc(sure_m), ts_, sm.red_i);
+    const int rb = block_excl_scan<int>(__popc(take_m), tb_, sm.red_i);
+    if (crossing) emitted_b = tb_;
+    if (idx) {   // positions above b* first, then the taken bin-b* positions, each ascending
+      const long long so = hs.all ? n0 : (long long)tl.sure_off;
+      const long long bo = (long long)hs.total_sure + tl.bnd_off;
+      int a = rs, c2 = rb;
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) {
+        const int n = (int)(nbase + k);
+        if (sure_m & (1u << k)) {
+          if (so + a < cap) idx[(size_t)unit * cap + so + a] = n;
+          ++a;
+        }
+        if (take_m & (1u << k)) {
+          if (bo + c2 < cap) idx[(size_t)unit * cap + bo + c2] = n;
+          ++c2;
+        }
+      }
+    }
+    if (ATTEND) {
+      const int add = ts_ + tb_;
+      if (nlist + add > FinShared::kList && nlist > 0) {   // flush the pending list
+        attend_rows(sm.q, sm.list, nlist, g.N, kc + cbase, vc + cbase, &sm.res, &sm.at);
+        if (tid < kD) merge_state(run_m, run_l, &run_o, sm.res.m, sm.res.l, &sm.res.o[tid], 1);
+        nlist = 0;
+      }
+      if (add <= FinShared::kList) {
+        int a = nlist + rs, c2 = nlist + ts_ + rb;
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+          const int n = (int)(nbase + k);
+          if (sure_m & (1u << k)) sm.list[a++] = n;
+          if (take_m & (1u << k)) sm.list[c2++] = n;
+        }
+        nlist += add;
+        __syncthreads();
+      } else {
+        // a tile with more selected positions than the list: attend it in pieces
+        for (int l0 = 0; l0 < add; l0 += FinShared::kList) {
+          __syncthreads();
+          int a = rs, c2 = ts_ + rb;
+#pragma unroll
+          for (int k = 0; k < TPT; ++k) {
+            const int n = (int)(nbase + k);
+            if (sure_m & (1u << k)) {
+              if (a >= l0 && a < l0 + FinShared::kList) sm.list[a - l0] = n;
+              ++a;
+            }
+            if (take_m & (1u << k)) {
+              if (c2 >= l0 && c2 < l0 + FinShared::kList) sm.list[c2 - l0] = n;
+              ++c2;
+            }
+          }
+          __syncthreads();
+          const int cnt = add - l0 < FinShared::kList ? add - l0 : FinShared::kList;
+          attend_rows(sm.q, sm.list, cnt, g.N, kc + cbase, vc + cbase, &sm.res, &sm.at);
+          if (tid < kD) merge_state(run_m, run_l, &run_o, sm.res.m, sm.res.l, &sm.res.o[tid], 1);
+        }
       }
     }
   }
-  if (count && !hs.all && t == hs.tstar && tid == 0) count[unit] = hs.count_base + tot_b;
-  if (!ATTEND) return;
-  __syncthreads();
-  const int hq = g.rhead[r];
-  const int kvg = hq / g.G;
-  const size_t cbase = ((size_t)b * g.Hkv + kvg) * g.Ncap * kD;
-  attend_rows(sm.q, sm.list, tot_s + tot_b, g.N, kc + cbase, vc + cbase, &sm.res, &sm.at);
-  publish_partial(g.part + (size_t)unit * g.nt + t, &sm.res);
-  if (!arrive_last(g.ctr_fin + unit, (uint32_t)g.nt, &sm.flag)) return;
-  combine_partials(g.part + (size_t)unit * g.nt, g.nt, out + (((size_t)b * g.Hq + hq) * g.nq + i) * kD, &sm.cb);
+  if (count && !hs.all && tid == 0 && hs.tstar >= t_begin && hs.tstar < t_end) count[unit] = hs.count_base + emitted_b;
+  if (ATTEND) {
+    if (nlist > 0) {
+      attend_rows(sm.q, sm.list, nlist, g.N, kc + cbase, vc + cbase, &sm.res, &sm.at);
+      if (tid < kD) merge_state(run_m, run_l, &run_o, sm.res.m, sm.res.l, &sm.res.o[tid], 1);
+    }
+    Partial *dst = g.part + (size_t)unit * g.fin_nwg + w;
+    if (tid < kD) {
+      st_coherent(&dst->o[tid], run_o);
+      if (tid == 0) {
+        st_coherent(&dst->m, run_m);
+        st_coherent(&dst->l, run_l);
+      }
+    }
+  }
+  if (!arrive_last(g.ctr_fin + unit, (uint32_t)g.fin_nwg, &sm.flag)) return;
+  // last workgroup of the query: reset its ring for the next call, combine the states
+  {
+    uint64_t *ring = g.ring + (size_t)unit * kRing;
+    if ((long long)hs.c - hs.base_min < kRing) {
+      for (long long cell = (long long)hs.base_min + tid; cell <= hs.c; cell += kWG) ring[cell & (kRing - 1)] = 0ull;
+    } else {
+      for (int x = tid; x < kRing; x += kWG) ring[x] = 0ull;
+    }
+    if (tid == 0) {
+      g.cmax[unit] = 0u;
+      g.cmin[unit] = 0u;
+    }
+  }
+  if (ATTEND)
+    combine_partials(g.part + (size_t)unit * g.fin_nwg, g.fin_nwg,
+                     out + (((size_t)b * g.Hq + hq) * g.nq + i) * kD, &sm.cb);
 }
 
 template <int T>
-int launch_scan_t(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
-                  const float *logits, int32_t *count, hipStream_t s) {
-  const unsigned grid = (unsigned)((long long)g.units * g.nt);
+int launch_phase_a_t(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
+                     const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, bool with_swa,
+                     hipStream_t s) {
+  const long long n_swa = with_swa ? swa_blocks(g) : 0;
+  const long long grid = n_swa + (long long)g.units * g.nt;
+  if (grid == 0) return RTP_OK;
   if (logits)
-    hipLaunchKernelGGL((scan_kernel<T, true>), dim3(grid), dim3(kWG), 0, s, g, q_pre, w_q, k_idx, logits, count);
+    hipLaunchKernelGGL((phase_a_kernel<T, true>), dim3((unsigned)grid), dim3(kWG), 0, s, g, q_pre, w_q, k_idx, logits,
+                       k, v, out, n_swa);
   else
-    hipLaunchKernelGGL((scan_kernel<T, false>), dim3(grid), dim3(kWG), 0, s, g, q_pre, w_q, k_idx, logits, count);
+    hipLaunchKernelGGL((phase_a_kernel<T, false>), dim3((unsigned)grid), dim3(kWG), 0, s, g, q_pre, w_q, k_idx,
+                       logits, k, v, out, n_swa);
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ERR_HIP;
 }
 
 template <int T>
-int launch_select_t(const Geo &g, const rtp_bf16 *k_idx, const float *logits, const rtp_bf16 *k, const rtp_bf16 *v,
-                    float *out, int32_t *idx, int32_t *count, long long cap, hipStream_t s) {
-  const unsigned grid = (unsigned)((long long)g.units * g.nt);
-  if (out) {
-    if (logits)
-      hipLaunchKernelGGL((select_kernel<T, true, true>), dim3(grid), dim3(kWG), 0, s, g, k_idx, logits, k, v, out,
-                         idx, count, cap);
-    else
-      hipLaunchKernelGGL((select_kernel<T, false, true>), dim3(grid), dim3(kWG), 0, s, g, k_idx, logits, k, v, out,
-                         idx, count, cap);
+int launch_finish_t(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
+                    const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, int32_t *idx,
+                    int32_t *count, long long cap, hipStream_t s) {
+  const unsigned grid = (unsigned)((long long)g.units * g.fin_nwg);
+  if (grid == 0) return RTP_OK;
+  hipLaunchKernelGGL(threshold_kernel, dim3((unsigned)g.units), dim3(kWG), 0, s, g, out ? q_pre : nullptr,
+                     logits ? nullptr : w_q, count);
+  if (hipGetLastError() != hipSuccess) return RTP_ERR_HIP;
+#define RTP_FIN(FL, AT)                                                                                         \
+  hipLaunchKernelGGL((finish_kernel<T, FL, AT>), dim3(grid), dim3(kWG), 0, s, g, k_idx, logits, k, v, out, idx, \
+                     count, cap)
+  if (logits) {
+    if (out) RTP_FIN(true, true); else RTP_FIN(true, false);
   } else {
-    if (logits)
-      hipLaunchKernelGGL((select_kernel<T, true, false>), dim3(grid), dim3(kWG), 0, s, g, k_idx, logits, k, v, out,
-                         idx, count, cap);
-    else
-      hipLaunchKernelGGL((select_kernel<T, false, false>), dim3(grid), dim3(kWG), 0, s, g, k_idx, logits, k, v, out,
-                         idx, count, cap);
+    if (out) RTP_FIN(false, true); else RTP_FIN(false, false);
   }
+#undef RTP_FIN
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ERR_HIP;
 }
 
 }  // namespace
 
-int launch_scan(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx, const float *logits,
-                int32_t *count, hipStream_t s) {
-  if (g.units == 0) return RTP_OK;
-  switch (g.T) {
-    case 1024: return launch_scan_t<1024>(g, q_pre, w_q, k_idx, logits, count, s);
-    case 2048: return launch_scan_t<2048>(g, q_pre, w_q, k_idx, logits, count, s);
-    case 4096: return launch_scan_t<4096>(g, q_pre, w_q, k_idx, logits, count, s);
-    case 8192: return launch_scan_t<8192>(g, q_pre, w_q, k_idx, logits, count, s);
+int launch_phase_a(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
+                   const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, bool with_scan,
+                   bool with_swa, hipStream_t s) {
+  Geo gg = g;
+  if (!with_scan) gg.units = 0;
+  if (!with_swa && gg.units == 0) return RTP_OK;
+  switch (gg.T) {
+    case 1024: return launch_phase_a_t<1024>(gg, q_pre, w_q, k_idx, logits, k, v, out, with_swa, s);
+    case 2048: return launch_phase_a_t<2048>(gg, q_pre, w_q, k_idx, logits, k, v, out, with_swa, s);
+    case 4096: return launch_phase_a_t<4096>(gg, q_pre, w_q, k_idx, logits, k, v, out, with_swa, s);
+    case 8192: return launch_phase_a_t<8192>(gg, q_pre, w_q, k_idx, logits, k, v, out, with_swa, s);
     default: return RTP_ERR_UNSUPPORTED;
   }
 }
 
-int launch_select(const Geo &g, const rtp_bf16 *k_idx, const float *logits, const rtp_bf16 *k, const rtp_bf16 *v,
-                  float *out, int32_t *idx, int32_t *count, long long cap, hipStream_t s) {
+int launch_finish(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
+                  const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, int32_t *idx,
+                  int32_t *count, long long cap, hipStream_t s) {
   if (g.units == 0) return RTP_OK;
   switch (g.T) {
-    case 1024: return launch_select_t<1024>(g, k_idx, logits, k, v, out, idx, count, cap, s);
-    case 2048: return launch_select_t<2048>(g, k_idx, logits, k, v, out, idx, count, cap, s);
-    case 4096: return launch_select_t<4096>(g, k_idx, logits, k, v, out, idx, count, cap, s);
-    case 8192: return launch_select_t<8192>(g, k_idx, logits, k, v, out, idx, count, cap, s);
+    case 1024: return launch_finish_t<1024>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, s);
+    case 2048: return launch_finish_t<2048>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, s);
+    case 4096: return launch_finish_t<4096>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, s);
+    case 8192: return launch_finish_t<8192>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, s);
     default: return RTP_ERR_UNSUPPORTED;
   }
 }
