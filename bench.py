@@ -36,7 +36,8 @@ import long_context_sparse_retrieval_amd as rtp  # noqa: E402
 METRIC = "decode attn µs/step + achieved HBM GB/s at 128K and 1M ctx, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 CSRC = os.path.join(ROOT, "long_context_sparse_retrieval_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "phase_a_kernel.qwen3-32b-layer-1m-b1.traffic.json")
+CPU_SAMPLE_SECONDS = 12.0
 
 
 def log(*a):
@@ -116,7 +117,7 @@ class Case:
         self.bytes_total = self.bytes_scan + self.bytes_swa + self.bytes_gather
 
     def run(self, steps: int, warmup: int):
-        """Warm up, then time exactly `steps` steps; returns (ms/step, ms of the scan kernel per step)."""
+        """Warm up, then time exactly `steps` steps; returns (ms/step, ms of the phase-A kernel per step)."""
         R = len(self.reps)
         for s in range(warmup):
             k_idx, k, v = self.reps[s % R]
@@ -136,8 +137,8 @@ class Case:
         t_end.record()
         torch.cuda.synchronize()
         ms_step = t_begin.elapsed_time(t_end) / steps
-        ms_scan = float(np.mean([starts[s].elapsed_time(mids[s]) for s in range(steps)]))
-        return ms_step, ms_scan
+        ms_pa = float(np.mean([starts[s].elapsed_time(mids[s]) for s in range(steps)]))
+        return ms_step, ms_pa
 
 
 def copy_ceiling_gbps() -> float:
@@ -159,46 +160,68 @@ def copy_ceiling_gbps() -> float:
     return 2 * n * 4 / (ms * 1e-3) / 1e9
 
 
-def traffic_per_launch():
-    """rocprof-measured HBM bytes per scan launch, if taken on the current kernel sources."""
+def calibration_copy(n_bytes: int = 1 << 30, reps: int = 3) -> None:
+    """A plain streaming copy of known size (negation: read n_bytes, write n_bytes).
+
+    Run under rocprofv3 --pmc, its FETCH_SIZE / WRITE_SIZE readings give the
+    scale from those counters to bytes moved on this device.
+    """
+    a = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def traffic_per_launch(workload: str):
+    """rocprof-measured HBM bytes per phase-A launch, if taken on the current kernel sources."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
 
 
 def cpu_baseline(case: Case) -> dict:
-    """The oracle, single-threaded, on a bounded sample of the 1M workload."""
+    """The oracle, single-threaded, on a bounded sample of the 1M workload.
+
+    Sample: two retrieval queries of KV group 0 (one needle-class, one diffuse)
+    over the whole context, plus the local heads of one local KV group; the
+    pass is repeated until about CPU_SAMPLE_SECONDS of oracle time is spent.
+    Cache writing (RoPE and indexer keys) happens before the clock starts, as
+    on the GPU side.
+    """
     import threadpoolctl
 
     import oracle as O
 
     spec, wl = case.spec, case.wl
-    r_sample = [0, 1]                       # one needle-class and one diffuse-class retrieval query
+    r_sample = [0, 1]
     rheads = spec.retrieval_heads()
     g_loc = [g for g in range(spec.Hkv) if g not in spec.ret_groups][0]
     loc_heads = list(range(g_loc * spec.G, (g_loc + 1) * spec.G))
     with threadpoolctl.threadpool_limits(1):
         kc, ki = O.build_caches(wl, groups=[rheads[r] // spec.G for r in r_sample] + [g_loc], heads=r_sample)
-        t0 = time.perf_counter()
-        O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
-                      n_sink=spec.n_sink, rope_base=spec.rope_theta, heads=[rheads[r] for r in r_sample])
-        t_ret = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
-                      n_sink=spec.n_sink, rope_base=spec.rope_theta, heads=loc_heads)
-        t_loc = time.perf_counter() - t0
+        passes, spent = 0, 0.0
+        while spent < CPU_SAMPLE_SECONDS or passes < 2:
+            t0 = time.perf_counter()
+            O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
+                          n_sink=spec.n_sink, rope_base=spec.rope_theta, heads=[rheads[r] for r in r_sample])
+            O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
+                          n_sink=spec.n_sink, rope_base=spec.rope_theta, heads=loc_heads)
+            spent += time.perf_counter() - t0
+            passes += 1
     sel = int(case.counts[0, r_sample[0]] + case.counts[0, r_sample[1]])
     lo = max(0, spec.N - spec.window)
     swa_rows = min(spec.n_sink, lo) + (spec.N - lo)
     sample_bytes = 32 * spec.N * len(r_sample) + 512 * sel + 512 * swa_rows
-    return {"value": round(sample_bytes / (t_ret + t_loc) / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{spec.name}: 2 of {spec.Hr} retrieval queries (1 needle-class, 1 diffuse) + the "
-                       f"{spec.G} local heads of one KV group; {t_ret + t_loc:.1f}s single-threaded "
-                       f"(host cpu_count {os.cpu_count()})")}
+    return {"value": round(sample_bytes * passes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{spec.name}: 2 of {spec.Hr} retrieval queries (1 needle-class, 1 diffuse, whole "
+                       f"{spec.N}-token context) + the {spec.G} local heads of one KV group, "
+                       f"{passes} passes in {spent:.1f}s, single-threaded (host cpu_count {os.cpu_count()})")}
 
 
 def main():
@@ -209,6 +232,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", type=int, default=0, help="run only this config (3 or 4)")
+    ap.add_argument("--calib", action="store_true", help="run the known-size copy used to scale HBM counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -216,6 +240,8 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     rtp.load()
+    if args.calib:
+        calibration_copy()
     copy_gbps = copy_ceiling_gbps()
     log(f"[bench] device copy ceiling {copy_gbps:.0f} GB/s")
 
@@ -223,13 +249,14 @@ def main():
     summ, cpu = {}, None
     for cfg in cfgs:
         case = Case(cfg, args.replicas)
-        ms, ms_scan = case.run(args.steps, args.warmup)
+        ms, ms_pa = case.run(args.steps, args.warmup)
         gbps = case.bytes_total / (ms * 1e-3) / 1e9
-        summ[cfg] = dict(ms=ms, us=ms * 1e3, gbps=gbps, frac=gbps / HBM_PEAK_GBPS, scan_us=ms_scan * 1e3,
-                         scan_gbps=case.bytes_scan / (ms_scan * 1e-3) / 1e9, scan_bytes=case.bytes_scan,
+        pa_bytes = case.bytes_scan + case.bytes_swa
+        summ[cfg] = dict(ms=ms, us=ms * 1e3, gbps=gbps, frac=gbps / HBM_PEAK_GBPS, pa_us=ms_pa * 1e3,
+                         pa_gbps=pa_bytes / (ms_pa * 1e-3) / 1e9, pa_bytes=pa_bytes,
                          bytes=case.bytes_total, spec=case.spec, counts=case.counts,
                          union=case.gather_rows_union, rsum=case.gather_rows_sum)
-        log(f"[bench] cfg{cfg}: {ms * 1e3:.1f} us/step, scan kernel {ms_scan * 1e3:.1f} us, {gbps:.0f} GB/s "
+        log(f"[bench] cfg{cfg}: {ms * 1e3:.1f} us/step, phase-A kernel {ms_pa * 1e3:.1f} us, {gbps:.0f} GB/s "
             f"algorithmic; |S| {case.counts.ravel().tolist()}")
         if cfg == 4 and not args.no_cpu_baseline:
             t0 = time.time()
@@ -252,7 +279,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32/f64",
         "data": "synthetic",
         "config": {"workload": f"{spec.name}: one decode step of a {spec.Hq}-q/{spec.Hkv}-kv-head layer, "
                                f"batch {spec.B}, context {spec.N}, {spec.Hr} retrieval q heads "
@@ -265,22 +292,23 @@ def main():
         "algorithmic_bytes_per_step": s["bytes"],
         "selected_tokens": {"per_query": s["counts"].ravel().tolist(), "kv_rows_union": s["union"],
                             "kv_rows_sum": s["rsum"]},
-        "roofline": {"bound": "hbm", "kernel": "scan_kernel (indexer scores + tile histograms + merge)",
-                     "achieved": round(s["scan_gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(s["scan_gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel_us": round(s["scan_us"], 2), "algorithmic_bytes_per_launch": s["scan_bytes"]},
+        "roofline": {"bound": "hbm",
+                     "kernel": "phase_a_kernel (indexer scores, codes, tile histograms; local-head SWA)",
+                     "achieved": round(s["pa_gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(s["pa_gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel_us": round(s["pa_us"], 2), "algorithmic_bytes_per_launch": s["pa_bytes"]},
         "copy_ceiling_GBps": round(copy_gbps, 1),
     }
     if main_cfg == 4:
-        out["roofline"]["traffic"] = traffic_per_launch()
+        out["roofline"]["traffic"] = traffic_per_launch(spec.name)
     if cpu is not None:
         out["cpu_baseline"] = cpu
     if 3 in summ and main_cfg != 3:
         s3 = summ[3]
         out["ctx_128k"] = {"workload": s3["spec"].name, "us_per_step": round(s3["us"], 2),
                            "GBps": round(s3["gbps"], 1), "hbm_frac": round(s3["frac"], 4),
-                           "algorithmic_bytes_per_step": s3["bytes"], "scan_kernel_us": round(s3["scan_us"], 2),
-                           "scan_GBps": round(s3["scan_gbps"], 1),
+                           "algorithmic_bytes_per_step": s3["bytes"], "phase_a_kernel_us": round(s3["pa_us"], 2),
+                           "phase_a_GBps": round(s3["pa_gbps"], 1),
                            "selected_tokens": s3["counts"].ravel().tolist()}
     print(json.dumps(out), flush=True)
 

@@ -1,0 +1,137 @@
+"""Summaries of rocprofv3 runs of bench.py, written under profiles/.
+
+  python prof_summary.py stats DIR OUT.txt --cmd "..."
+      per-kernel dispatch counts and durations from a --kernel-trace run
+  python prof_summary.py traffic FETCH_DIR WRITE_DIR OUT.json --workload NAME --cmd "..."
+      HBM bytes per phase-A launch from two --pmc runs (FETCH_SIZE, then WRITE_SIZE),
+      each scaled by what the same counter reads for bench.py's known-size copy
+
+DIR holds the rocpd SQLite database(s) rocprofv3 wrote (-d DIR).
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import json
+import os
+import re
+import sqlite3
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PHASE_A = "phase_a_kernel"
+CALIB = "neg"                     # bench.calibration_copy: torch.neg over 1 GiB of float32
+CALIB_BYTES = 1 << 30
+
+
+def short(name: str) -> str:
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "").replace("rtp::", "")
+    return re.sub(r"\(.*", "", n)
+
+
+def dbs(d: str):
+    out = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
+    if not out:
+        sys.exit(f"no rocpd database under {d}")
+    return out
+
+
+def kernel_rows(d: str):
+    rows = []
+    for db in dbs(d):
+        con = sqlite3.connect(db)
+        rows += con.execute("select name, grid_x / workgroup_x, duration from kernels").fetchall()
+    return rows
+
+
+def counter_rows(d: str, counter: str):
+    """(kernel name, value in KiB) per dispatch, summed over the device's instances."""
+    per = defaultdict(float)
+    names = {}
+    for db in dbs(d):
+        con = sqlite3.connect(db)
+        q = ("select k.dispatch_id, k.name, c.value from counters_collection c "
+             "join kernels k on c.dispatch_id = k.dispatch_id where c.counter_name = ?")
+        for did, name, v in con.execute(q, (counter,)).fetchall():
+            per[(db, did)] += v
+            names[(db, did)] = name
+    return [(names[k], v) for k, v in per.items()]
+
+
+def cmd_stats(a):
+    rows = kernel_rows(a.dir)
+    agg = defaultdict(list)
+    for name, grid, dur in rows:
+        agg[(short(name), grid)].append(dur)
+    total = sum(sum(v) for v in agg.values())
+    lines = [f"# rocprofv3 kernel trace: {a.title}", "", "command:", f"    {a.cmd}", "",
+             f"{'kernel':60s} {'grid':>8s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for (n, g), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{n[:60]:60s} {g:8d} {len(v):6d} {sum(v) / len(v) / 1e3:9.2f} {min(v) / 1e3:9.2f} "
+                     f"{max(v) / 1e3:9.2f} {100 * sum(v) / total:6.2f}")
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def mean_kib(rows, pred):
+    v = [x for n, x in rows if pred(short(n))]
+    if not v:
+        return None, 0
+    return sum(v) / len(v), len(v)
+
+
+def cmd_traffic(a):
+    sys.path.insert(0, ROOT)
+    from bench import kernel_source_hash
+
+    fetch = counter_rows(a.fetch_dir, "FETCH_SIZE")
+    write = counter_rows(a.write_dir, "WRITE_SIZE")
+    is_pa = lambda n: n.startswith(PHASE_A)
+    is_cal = lambda n: "elementwise" in n and CALIB in n and "FillFunctor" not in n
+    f_pa, nf = mean_kib(fetch, is_pa)
+    w_pa, nw = mean_kib(write, is_pa)
+    f_cal, ncf = mean_kib(fetch, is_cal)
+    w_cal, ncw = mean_kib(write, is_cal)
+    if None in (f_pa, w_pa, f_cal, w_cal):
+        sys.exit(f"missing dispatches: phase A {nf}/{nw}, calibration copy {ncf}/{ncw}")
+    s_fetch = CALIB_BYTES / (f_cal * 1024)
+    s_write = CALIB_BYTES / (w_cal * 1024)
+    rd = f_pa * 1024 * s_fetch
+    wr = w_pa * 1024 * s_write
+    out = {"kernel": PHASE_A, "workload": a.workload, "kernel_source_hash": kernel_source_hash(),
+           "fetch_kib_per_launch": round(f_pa, 1), "write_kib_per_launch": round(w_pa, 1),
+           "launches": [nf, nw],
+           "calibration": {"kernel": "torch.neg over 1 GiB float32 (reads 1 GiB, writes 1 GiB)",
+                           "fetch_kib": round(f_cal, 1), "write_kib": round(w_cal, 1),
+                           "fetch_scale": round(s_fetch, 4), "write_scale": round(s_write, 4)},
+           "read_bytes_per_launch": int(rd), "write_bytes_per_launch": int(wr),
+           "bytes_per_launch": int(rd + wr), "commands": a.cmd}
+    with open(a.out, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sp = ap.add_subparsers(dest="what", required=True)
+    s = sp.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("out")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--title", default="")
+    t = sp.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("out")
+    t.add_argument("--workload", required=True)
+    t.add_argument("--cmd", action="append", required=True)
+    a = ap.parse_args()
+    cmd_stats(a) if a.what == "stats" else cmd_traffic(a)
+
+
+if __name__ == "__main__":
+    main()
