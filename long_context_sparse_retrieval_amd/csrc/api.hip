@@ -108,12 +108,8 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
   off = align_up(off + units * 4);
   const size_t o_ctr_swa = off;
   off = align_up(off + (size_t)g.swa_units * g.swa_hb * 4);
-  const size_t o_hsel = off;
-  off = align_up(off + units * sizeof(HeadSel));
   const size_t o_qprep = off;
   off = align_up(off + units * sizeof(QPrep));
-  const size_t o_tsel = off;
-  off = align_up(off + units * nt * sizeof(TileSel));
   const size_t o_tsum = off;
   off = align_up(off + units * nt * sizeof(TileSum));
   const size_t o_part = off;
@@ -130,9 +126,7 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
     g.ctr_fin = reinterpret_cast<uint32_t *>(base + o_ctr_fin);
     g.ctr_swa = reinterpret_cast<uint32_t *>(base + o_ctr_swa);
     g.tsum = reinterpret_cast<TileSum *>(base + o_tsum);
-    g.hsel = reinterpret_cast<HeadSel *>(base + o_hsel);
     g.qprep = reinterpret_cast<QPrep *>(base + o_qprep);
-    g.tsel = reinterpret_cast<TileSel *>(base + o_tsel);
     g.part = reinterpret_cast<Partial *>(base + o_part);
     g.swa_part = reinterpret_cast<Partial *>(base + o_swa);
     g.codes = reinterpret_cast<uint8_t *>(base + o_codes);

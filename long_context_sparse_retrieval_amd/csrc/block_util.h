@@ -156,7 +156,7 @@ __device__ __forceinline__ void attend_rows(const float *q_s, const int *rows, i
   float m = -INFINITY, l = 0.f, o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
-  constexpr int U = 2;
+  constexpr int U = 4;
   for (int base = 0; base < cnt; base += 16 * U) {
     uint4 kr[U], vr[U];
     bool ok[U];
@@ -226,58 +226,46 @@ __device__ __forceinline__ void attend_rows(const float *q_s, const int *rows, i
 }
 
 struct CombineShared {
-  float scale[256];
   float red[8][kD];
-  float lred[8];
-  float m_red[4];
-  float gmax;
+  float m8[8], l8[8];
 };
 
 // Normalised combination of np split-K states into out[0..D) by the whole
-// workgroup.  The max of every state is loaded in one parallel round, then the
-// scaled o vectors are summed with independent float4 loads (8 groups of 32
-// threads, one float4 of channels each).
+// workgroup, in one round of loads: 8 groups of 32 threads, group x merging
+// states x, x + 8, ... (a float4 of channels per thread, four states in
+// flight), then the 8 group states merged in a fixed order.
 __device__ __forceinline__ void combine_partials(const Partial *parts, int np, float *out, CombineShared *sm) {
   const int tid = threadIdx.x, d4 = tid & 31, grp = tid >> 5;
-  float gm = -INFINITY;
-  for (int t = tid; t < np; t += kWG) gm = fmaxf(gm, parts[t].m);
-  gm = block_max<float>(gm, sm->m_red);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float lacc = 0.f;
-  for (int t0 = 0; t0 < np; t0 += kWG) {
-    const int t = t0 + tid;
-    if (t < np) {
-      const float m = parts[t].m;
-      sm->scale[tid] = (m == -INFINITY || gm == -INFINITY) ? 0.f : __expf(m - gm);
+  float m = -INFINITY, l = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int x0 = grp; x0 < np; x0 += 32) {
+    float pm[4], pl[4];
+    float4 po[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {          // clamped, unconditional loads
+      const int x = x0 + 8 * u < np ? x0 + 8 * u : np - 1;
+      pm[u] = parts[x].m;
+      pl[u] = parts[x].l;
+      po[u] = reinterpret_cast<const float4 *>(parts[x].o)[d4];
     }
-    __syncthreads();
-    const int nn = np - t0 < kWG ? np - t0 : kWG;
-#pragma unroll 8
-    for (int x = grp; x < nn; x += 8) {
-      const float sc = sm->scale[x];
-      const float4 o = reinterpret_cast<const float4 *>(parts[t0 + x].o)[d4];
-      acc.x += o.x * sc;
-      acc.y += o.y * sc;
-      acc.z += o.z * sc;
-      acc.w += o.w * sc;
-      if (d4 == 0) lacc += parts[t0 + x].l * sc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (x0 + 8 * u >= np) break;
+      const float o2[4] = {po[u].x, po[u].y, po[u].z, po[u].w};
+      merge_state(m, l, o, pm[u], pl[u], o2, 4);
     }
-    __syncthreads();
   }
-  sm->red[grp][4 * d4 + 0] = acc.x;
-  sm->red[grp][4 * d4 + 1] = acc.y;
-  sm->red[grp][4 * d4 + 2] = acc.z;
-  sm->red[grp][4 * d4 + 3] = acc.w;
-  if (d4 == 0) sm->lred[grp] = lacc;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) sm->red[grp][4 * d4 + c] = o[c];
+  if (d4 == 0) {
+    sm->m8[grp] = m;
+    sm->l8[grp] = l;
+  }
   __syncthreads();
   if (tid < kD) {
-    float o = 0.f, l = 0.f;
+    float mm = -INFINITY, ll = 0.f, oo = 0.f;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      o += sm->red[x][tid];
-      l += sm->lred[x];
-    }
-    out[tid] = l > 0.f ? o / l : 0.f;
+    for (int x = 0; x < 8; ++x) merge_state(mm, ll, &oo, sm->m8[x], sm->l8[x], &sm->red[x][tid], 1);
+    out[tid] = ll > 0.f ? oo / ll : 0.f;
   }
   __syncthreads();
 }

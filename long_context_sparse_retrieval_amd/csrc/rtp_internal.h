@@ -33,24 +33,13 @@ struct TileSum {
   uint32_t cum[kBins];
 };
 
-// Per-tile selection parameters written by the threshold kernel.
+// Per-tile selection parameters, derived by each finishing workgroup.
 struct TileSel {
   uint64_t P;           // in-cell mass of bin b* in the tiles before this one
   int32_t sure_off;     // output offset of this tile's positions above b*
   int32_t bnd_off;      // output offset of this tile's positions taken from b*
-};
-
-// Per-query selection parameters written by the threshold kernel.
-struct HeadSel {
-  double r_u;           // residual mass p*Z - mass(bins < b*), in in-cell units of bin b*
-  int32_t c;            // global max cell
-  int32_t bstar;        // boundary bin
-  int32_t tstar;        // last tile holding selected bin-b* tokens
-  int32_t all;          // 1: every position selected (p >= 1, or b* is the clamp bin)
-  int32_t count_base;   // |S| without the crossing tile's bin-b* tokens
-  int32_t total_sure;   // positions above bin b*
-  int32_t base_min;     // lowest ring cell in use
-  int32_t pad;
+  int32_t n_sure;       // positions of this tile above b*
+  int32_t n_bnd;        // positions of this tile in b*
 };
 
 // Query preparation: exact indexer query and rotated query.
@@ -90,8 +79,6 @@ struct Geo {
   // workspace
   uint8_t *codes;        // [units][nt*T] local bin of every token
   TileSum *tsum;         // [units][nt]
-  TileSel *tsel;         // [units][nt]
-  HeadSel *hsel;         // [units]
   QPrep *qprep;          // [units]
   Partial *part;         // [units][max(nt, kSpChunks)]
   Partial *swa_part;     // [swa_units][swa_hb][swa_nch][kSwaHeads]

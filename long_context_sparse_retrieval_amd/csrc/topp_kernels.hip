@@ -46,6 +46,7 @@ struct ScanShared {
                                            // count << 40 | exact in-cell mass
   double q[kR];
   double qtmp[16][kR];
+  double2 rope[kD / 2];
   float red_f[4];
   int red_i[4];
   unsigned int red_u32[4];
@@ -82,13 +83,16 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
   float mx = -INFINITY;
   int cmin = INT32_MAX;
   for (int x = tid; x < 4 * kCells; x += kWG) (&sm.hist[0][0])[x] = 0ull;
+  // branchless, so a whole batch of rows stays one basic block and its loads
+  // can be issued together; absent positions (-inf) add nothing
   auto bin_abs = [&](float sc) {
-    if (sc != -INFINITY) {
-      const int cell = score_cell(sc);
-      atomicAdd(&sm.hist[wv][cell & (kCells - 1)], (unsigned long long)cell_weight(sc, cell) | (1ull << kCountShift));
-      mx = fmaxf(mx, sc);
-      cmin = min(cmin, cell);
-    }
+    const bool ok = sc != -INFINITY;
+    const float s = ok ? sc : 0.f;
+    const int cell = score_cell(s);
+    const unsigned long long add = ok ? ((unsigned long long)cell_weight(s, cell) | (1ull << kCountShift)) : 0ull;
+    atomicAdd(&sm.hist[wv][cell & (kCells - 1)], add);
+    mx = fmaxf(mx, sc);
+    cmin = min(cmin, ok ? cell : INT32_MAX);
   };
   if (FROM_LOGITS) {
     __syncthreads();
@@ -96,20 +100,22 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
       const long long n = n0 + k * kWG + tid;
-      lg[k] = (n <= m) ? row[n] : -INFINITY;
+      const float sc = row[n <= m ? n : m];            // clamped, unconditional load
+      lg[k] = n <= m ? sc : -INFINITY;
       bin_abs(lg[k]);
     }
   } else {
+    // rolling window of BATCH rows per thread: slot u is refilled with the row
+    // BATCH positions ahead as soon as it is consumed, so about BATCH rows per
+    // thread stay in flight; loads are clamped to a valid row and unconditional
     const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hr + r) * g.Ncap * kR);
     uint4 ra[BATCH], rb[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const long long n = n0 + u * kWG + tid;
-      ra[u] = rb[u] = make_uint4(0, 0, 0, 0);
-      if (n <= m) {
-        ra[u] = rows[2 * n];
-        rb[u] = rows[2 * n + 1];
-      }
+      const long long nc = n <= m ? n : m;
+      ra[u] = rows[2 * nc];
+      rb[u] = rows[2 * nc + 1];
     }
     project_query(q_pre + (((size_t)b * g.Hq + g.rhead[r]) * g.nq + i) * kD, w_q + (size_t)r * kD * kR, sm.q,
                   sm.qtmp);
@@ -122,16 +128,21 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
       q[x] = __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
     }
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const long long n = n0 + u * kWG + tid;
-      lg[u] = (n <= m) ? dot16_exact(q, ra[u], rb[u]) : -INFINITY;
-      bin_abs(lg[u]);
-    }
+    for (int kb = 0; kb < TPT; kb += BATCH) {
 #pragma unroll
-    for (int k = BATCH; k < TPT; ++k) {
-      const long long n = n0 + k * kWG + tid;
-      lg[k] = (n <= m) ? dot16_exact(q, rows[2 * n], rows[2 * n + 1]) : -INFINITY;
-      bin_abs(lg[k]);
+      for (int u = 0; u < BATCH; ++u) {
+        const int k = kb + u;
+        const long long n = n0 + k * kWG + tid;
+        const float sc = dot16_exact(q, ra[u], rb[u]);
+        lg[k] = n <= m ? sc : -INFINITY;
+        bin_abs(lg[k]);
+        if (kb + BATCH < TPT) {
+          const long long nn = n + BATCH * kWG;
+          const long long nc = nn <= m ? nn : m;
+          ra[u] = rows[2 * nc];
+          rb[u] = rows[2 * nc + 1];
+        }
+      }
     }
   }
   mx = block_max<float>(mx, sm.red_f);
@@ -231,6 +242,14 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
     }
     if (ms) atomicAdd((unsigned long long *)(g.ring + (size_t)unit * kRing + ((c_t - tid) & (kRing - 1))), ms);
   }
+  // the query's prepared forms for the finishing workgroups: the indexer query
+  // and the rotated, scaled attention query
+  if (!FROM_LOGITS && t == 0) {
+    QPrep *qp = g.qprep + unit;
+    if (tid < kR) qp->qi[tid] = sm.q[tid];
+    rope_table(m, g.theta, sm.rope);
+    rotate_query(q_pre + (((size_t)b * g.Hq + g.rhead[r]) * g.nq + i) * kD, sm.rope, kInvSqrtD, qp->qrot);
+  }
 }
 
 template <int T>
@@ -257,10 +276,8 @@ __global__ __launch_bounds__(kWG) void phase_a_kernel(Geo g, const rtp_bf16 *__r
     scan_block<T, FROM_LOGITS>(g, x - n_swa, q_pre, w_q, k_idx, logits, sm.scan);
 }
 
-struct ThrShared {
-  double qi[kR];
-  double qtmp[16][kR];
-  double2 rope[kD / 2];
+// Per-workgroup scratch of the global threshold.
+struct ThrScratch {
   double wcum[kBins];
   double red_d[4];
   unsigned long long red_u[4];
@@ -268,10 +285,14 @@ struct ThrShared {
 };
 
 // The query's global histogram from the ring (or, when its cells span more
-// than the ring holds, from every tile histogram): boundary bin, residual
+// than the ring holds, from every tile histogram): boundary bin b*, residual
 // mass in in-cell units of bin b*, and whether every position is taken.
-__device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, int base_min, ThrShared &sm,
-                                                 int &bstar_out, double &r_u_out, int &all_out) {
+// H_ring is this thread's ring entry for bin j = tid (cell c - j), loaded by
+// the caller.  Every workgroup of a query computes identical values: the
+// integer bins are exact and every floating-point sum has a fixed order.
+__device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, int base_min,
+                                                 unsigned long long H_ring, ThrScratch &sm, int &bstar_out,
+                                                 double &r_u_out, int &all_out) {
   const int tid = threadIdx.x, j = tid;
   const TileSum *ts = g.tsum + (size_t)unit * g.nt;
   const uint64_t *ring = g.ring + (size_t)unit * kRing;
@@ -279,7 +300,7 @@ __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, 
   unsigned long long H = 0;
   double w255 = 0.0;
   if (span < kRing) {
-    if (j <= kBnd) H = ring[(c - j) & (kRing - 1)];
+    H = j <= kBnd ? H_ring : 0ull;
     for (long long cell = (long long)c - (kBins - 1) - j; cell >= base_min; cell -= kWG) {
       const unsigned long long mj = ring[cell & (kRing - 1)];
       if (mj) w255 += (double)mj * exp((double)(cell - c) * 0.125);
@@ -296,16 +317,15 @@ __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, 
       }
     }
   }
-  // clamp-bin mass: fixed-order sum over threads
+  // clamp-bin mass: fixed pairwise tree over the threads
   sm.wcum[j] = w255;
   __syncthreads();
-  if (tid == 0) {
-    double s = 0.0;
-    for (int x = 0; x < kBins; ++x) s += sm.wcum[x];
-    sm.red_d[0] = s;
+#pragma unroll
+  for (int s = kWG / 2; s > 0; s >>= 1) {
+    if (j < s) sm.wcum[j] += sm.wcum[j + s];
+    __syncthreads();
   }
-  __syncthreads();
-  const double W255 = sm.red_d[0] * 0x1p-23;
+  const double W255 = sm.wcum[0] * 0x1p-23;
   __syncthreads();
   const double Wj = j <= kBnd ? (double)H * 0x1p-23 * exp(-(double)j * 0.125) : W255;
   double Z;
@@ -322,105 +342,34 @@ __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, 
   bstar_out = bstar;
 }
 
-// Threshold kernel: one workgroup per query.  Global threshold, per-tile
-// prefix of bin-b* mass and output offsets, and the prepared queries.
-__global__ __launch_bounds__(kWG) void threshold_kernel(Geo g, const rtp_bf16 *__restrict__ q_pre,
-                                                        const rtp_bf16 *__restrict__ w_q, int32_t *count) {
-  __shared__ ThrShared sm;
-  const int tid = threadIdx.x;
-  const int unit = blockIdx.x;
-  const int i = unit % g.nq, br = unit / g.nq, r = br % g.Hr, b = br / g.Hr;
-  const long long m = g.N - g.nq + i;
-  const TileSum *ts = g.tsum + (size_t)unit * g.nt;
-  const int c = dec_max(g.cmax[unit]);
-  const int base_min = dec_min(g.cmin[unit]);
-  const int ct0 = tid < g.nt ? ts[tid].c_t : INT32_MIN;     // first chunk of tile maxima, early
-  QPrep *qp = g.qprep + unit;
-  if (q_pre) {
-    const rtp_bf16 *q_row = q_pre + (((size_t)b * g.Hq + g.rhead[r]) * g.nq + i) * kD;
-    if (w_q) {
-      project_query(q_row, w_q + (size_t)r * kD * kR, sm.qi, sm.qtmp);
-      if (tid < kR) qp->qi[tid] = sm.qi[tid];
-    }
-    rope_table(m, g.theta, sm.rope);
-    rotate_query(q_row, sm.rope, kInvSqrtD, qp->qrot);
-  }
-  int bstar, all;
-  double r_u;
-  global_threshold(g, unit, c, base_min, sm, bstar, r_u, all);
-  // per tile: bin-b* prefix mass, counts above b* and in b*, output offsets; the
-  // crossing tile is the last one whose bin-b* tokens start below the residual,
-  // and every bin-b* token of the tiles before it is taken
-  unsigned long long carryP = 0;
-  int carryS = 0, carryB = 0, tstar = -1, bo_star = -1;
-  for (int t0 = 0; t0 < g.nt; t0 += kWG) {
-    const int tt = t0 + tid;
-    unsigned long long bm = 0;
-    int sure = 0, bc = 0;
-    const int ctt = t0 == 0 ? ct0 : (tt < g.nt ? ts[tt].c_t : INT32_MIN);
-    if (ctt != INT32_MIN && !all) {
-      const long long bl = (long long)bstar - ((long long)c - ctt);
-      if (bl >= 1) sure = (int)ts[tt].cum[(bl < kBins - 1 ? (int)bl : kBins - 1) - 1];
-      if (bl >= 0 && bl <= kBnd) {
-        const uint32_t hi = ts[tt].cum[bl];
-        bc = (int)(hi - (bl ? ts[tt].cum[bl - 1] : 0u));
-        bm = ts[tt].mass[bl];
-      }
-    }
-    unsigned long long totP;
-    int totS, totB;
-    const unsigned long long P = carryP + block_excl_scan<unsigned long long>(bm, totP, sm.red_u);
-    const int so = carryS + block_excl_scan<int>(sure, totS, sm.red_i);
-    const int bo = carryB + block_excl_scan<int>(bc, totB, sm.red_i);
-    if (tt < g.nt) {
-      TileSel *tl = g.tsel + (size_t)unit * g.nt + tt;
-      tl->P = P;
-      tl->sure_off = so;
-      tl->bnd_off = bo;
-    }
-    const bool crossing = tt < g.nt && bc > 0 && (double)P < r_u;
-    tstar = max(tstar, block_max<int>(crossing ? tt : -1, sm.red_i));
-    bo_star = max(bo_star, block_max<int>(crossing ? bo : -1, sm.red_i));
-    carryP += totP;
-    carryS += totS;
-    carryB += totB;
-  }
-  if (tid == 0) {
-    HeadSel *hs = g.hsel + unit;
-    hs->r_u = r_u;
-    hs->c = c;
-    hs->bstar = bstar;
-    hs->tstar = tstar;
-    hs->all = all;
-    hs->total_sure = carryS;
-    hs->count_base = carryS + (tstar >= 0 ? bo_star : 0);
-    hs->base_min = base_min;
-    if (all && count) count[unit] = (int)(m + 1);
-  }
-}
-
 struct FinShared {
   static constexpr int kList = 2048;
   static constexpr int kCodes = 32768;
   uint8_t codes[kCodes];                   // codes of this workgroup's tiles
   int list[kList];                         // positions pending attention
-  TileSel tsel[32];
+  int blist[kWG];                          // bin-b* positions of the crossing tile, one round
+  TileSel tsel[32];                        // selection parameters of this workgroup's tiles
   int ct[32];
   float q[kD];
   double qi[kR];
-  unsigned long long red_u[4];
-  int red_i[4];
   int flag;
-  AttnShared at;
-  CombineShared cb;
+  union {
+    ThrScratch thr;
+    AttnShared at;
+    CombineShared cb;
+  };
   Partial res;
 };
 
-// Finish kernel: one workgroup per (query unit, run of fin_tpw tiles).  Tiles
-// before the crossing tile take their whole bin b*, tiles after it none; only
-// the crossing tile recomputes the scores of its bin-b* tokens for the ordered
-// fill.  Selected positions are written (optional) and attended (optional);
-// the last workgroup of the query combines the states and resets the ring.
+// Finish kernel: one workgroup per (query unit, run of fin_tpw tiles).
+// Each workgroup first derives the query's threshold from the ring and the
+// per-tile prefix of bin-b* mass over all tiles (identical in every workgroup
+// of the query).  Tiles before the crossing tile take their whole bin b*,
+// tiles after it none; the crossing tile takes the ordered prefix of its
+// bin-b* tokens whose preceding mass is below the residual (their scores are
+// recomputed in parallel).  Selected positions are written (optional) and
+// attended (optional); the last workgroup of the query combines the states
+// and resets the ring.
 template <int T, bool FROM_LOGITS, bool ATTEND>
 __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__restrict__ k_idx,
                                                      const float *__restrict__ logits,
@@ -440,106 +389,190 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
   const int t_end = t_begin + g.fin_tpw < g.nt ? t_begin + g.fin_tpw : g.nt;
   const int kvg = hq / g.G;
   const size_t cbase = ((size_t)b * g.Hkv + kvg) * g.Ncap * kD;
+  const TileSum *ts = g.tsum + (size_t)unit * g.nt;
 
-  // one round of independent loads: all codes of the run, tile parameters, query
-  {
-    constexpr int kPer = FinShared::kCodes / 16 / kWG;
-    const uint4 *src = reinterpret_cast<const uint4 *>(g.codes + (size_t)unit * g.nt * T + (size_t)t_begin * T);
-    const int n16 = (t_end - t_begin) * T / 16;
-    uint4 cv[kPer];
+  // independent loads first: the query's cell range, the first tile maxima,
+  // every code of this run, the prepared query
+  const int c = dec_max(g.cmax[unit]);
+  const int base_min = dec_min(g.cmin[unit]);
+  const int ct0 = tid < g.nt ? ts[tid].c_t : INT32_MIN;
+  constexpr int kPer = FinShared::kCodes / 16 / kWG;
+  const uint4 *src = reinterpret_cast<const uint4 *>(g.codes + (size_t)unit * g.nt * T + (size_t)t_begin * T);
+  const int n16 = (t_end - t_begin) * T / 16;
+  uint4 cv[kPer];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int x = tid + u * kWG;
-      if (x < n16) cv[u] = src[x];
-    }
-    if (tid < t_end - t_begin) {
-      sm.tsel[tid] = g.tsel[(size_t)unit * g.nt + t_begin + tid];
-      sm.ct[tid] = g.tsum[(size_t)unit * g.nt + t_begin + tid].c_t;
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int x = tid + u * kWG;
-      if (x < n16) reinterpret_cast<uint4 *>(sm.codes)[x] = cv[u];
-    }
+  for (int u = 0; u < kPer; ++u) {         // clamped, unconditional: the loads stay in flight together
+    const int x = tid + u * kWG;
+    cv[u] = src[x < n16 ? x : n16 - 1];
   }
-  const HeadSel hs = g.hsel[unit];
   if (!FROM_LOGITS && tid < kR) sm.qi[tid] = g.qprep[unit].qi[tid];
   if (ATTEND && tid < kD) sm.q[tid] = g.qprep[unit].qrot[tid];
+  const unsigned long long H_ring = g.ring[(size_t)unit * kRing + ((c - tid) & (kRing - 1))];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int x = tid + u * kWG;
+    if (x < n16) reinterpret_cast<uint4 *>(sm.codes)[x] = cv[u];
+  }
+
+  int bstar, all;
+  double r_u;
+  global_threshold(g, unit, c, base_min, H_ring, sm.thr, bstar, r_u, all);
+
+  // per tile of the query: bin-b* prefix mass, counts above b* and in b*,
+  // output offsets; the crossing tile is the last one whose bin-b* tokens
+  // start below the residual, and every bin-b* token before it is taken
+  unsigned long long carryP = 0;
+  int carryS = 0, carryB = 0, tstar = -1, bo_star = -1;
+  for (int t0 = 0; t0 < g.nt; t0 += kWG) {
+    const int tt = t0 + tid;
+    unsigned long long bm = 0;
+    int sure = 0, bc = 0;
+    const int ctt = t0 == 0 ? ct0 : (tt < g.nt ? ts[tt].c_t : INT32_MIN);
+    if (ctt != INT32_MIN && !all) {
+      const long long bl = (long long)bstar - ((long long)c - ctt);
+      if (bl >= 1) sure = (int)ts[tt].cum[(bl < kBins - 1 ? (int)bl : kBins - 1) - 1];
+      if (bl >= 0 && bl <= kBnd) {
+        const uint32_t hi = ts[tt].cum[bl];
+        bc = (int)(hi - (bl ? ts[tt].cum[bl - 1] : 0u));
+        bm = ts[tt].mass[bl];
+      }
+    }
+    unsigned long long totP, totSB;
+    const unsigned long long P = carryP + block_excl_scan<unsigned long long>(bm, totP, sm.thr.red_u);
+    const unsigned long long sb =
+        block_excl_scan<unsigned long long>(((unsigned long long)sure << 32) | (unsigned)bc, totSB, sm.thr.red_u);
+    const int so = carryS + (int)(sb >> 32), bo = carryB + (int)(sb & 0xffffffffu);
+    if (tt >= t_begin && tt < t_end) {
+      TileSel &tl = sm.tsel[tt - t_begin];
+      tl.P = P;
+      tl.sure_off = so;
+      tl.bnd_off = bo;
+      tl.n_sure = sure;
+      tl.n_bnd = bc;
+      sm.ct[tt - t_begin] = ctt;
+    }
+    const bool crossing = tt < g.nt && bc > 0 && (double)P < r_u;
+    tstar = max(tstar, block_max<int>(crossing ? tt : -1, sm.thr.red_i));
+    bo_star = max(bo_star, block_max<int>(crossing ? bo : -1, sm.thr.red_i));
+    carryP += totP;
+    carryS += (int)(totSB >> 32);
+    carryB += (int)(totSB & 0xffffffffu);
+  }
+  const int total_sure = carryS;
+  const int count_base = carryS + (tstar >= 0 ? bo_star : 0);
+  if (count && tid == 0 && w == 0) {
+    if (all) count[unit] = (int)(m + 1);
+    else if (tstar < 0) count[unit] = count_base;
+  }
   __syncthreads();
 
   float run_m = -INFINITY, run_l = 0.f, run_o = 0.f;    // thread d < 128 holds channel d
   int nlist = 0;                                        // block-uniform
-  int emitted_b = 0;                                    // bin-b* positions taken in the crossing tile
   for (int t = t_begin; t < t_end; ++t) {
     const TileSel tl = sm.tsel[t - t_begin];
     const int ct = sm.ct[t - t_begin];
-    const long long n0 = (long long)t * T;
-    const bool any = ct != INT32_MIN;
+    if (ct == INT32_MIN) continue;                      // no position in the tile
     int bl = -1;
-    if (any && !hs.all) {
-      const long long blv = (long long)hs.bstar - ((long long)hs.c - ct);
+    if (!all) {
+      const long long blv = (long long)bstar - ((long long)c - ct);
       bl = blv < -1 ? -1 : (int)blv;
     }
-    const bool bnd_ok = any && !hs.all && bl >= 0 && bl <= kBnd;
-    const bool crossing = bnd_ok && t == hs.tstar;
-    const bool take_all_bnd = bnd_ok && t < hs.tstar;
+    const bool bnd_ok = !all && bl >= 0 && bl <= kBnd;
+    const bool crossing = bnd_ok && t == tstar;
+    const bool take_all_bnd = bnd_ok && t < tstar;
+    // block-uniform skip of a tile that contributes nothing
+    if (!all && tl.n_sure == 0 && !((take_all_bnd || crossing) && tl.n_bnd > 0)) continue;
+    const long long n0 = (long long)t * T;
     const long long nbase = n0 + (long long)tid * TPT;
-    const uint8_t *cd = sm.codes + (t - t_begin) * T + tid * TPT;
-    unsigned sure_m = 0, bnd_m = 0;
+    // this thread's TPT consecutive codes, read as words
+    uint32_t cw[TPT / 4];
+    {
+      const uint8_t *cd = sm.codes + (t - t_begin) * T + tid * TPT;
+      if constexpr (TPT >= 16) {
 #pragma unroll
-    for (int k = 0; k < TPT; ++k) {
-      const int code = cd[k];
-      if (!any || nbase + k > m) continue;
-      if (hs.all || code < bl) sure_m |= 1u << k;
-      else if (code == bl && (take_all_bnd || crossing)) bnd_m |= 1u << k;
+        for (int v = 0; v < TPT / 16; ++v) {
+          const uint4 x4 = reinterpret_cast<const uint4 *>(cd)[v];
+          cw[4 * v] = x4.x;
+          cw[4 * v + 1] = x4.y;
+          cw[4 * v + 2] = x4.z;
+          cw[4 * v + 3] = x4.w;
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < TPT / 4; ++v) cw[v] = reinterpret_cast<const uint32_t *>(cd)[v];
+      }
+    }
+    const long long lim = m - nbase;                    // positions beyond the query are never taken
+    const unsigned valid_m = lim >= TPT - 1 ? (TPT == 32 ? 0xffffffffu : ((1u << TPT) - 1u))
+                                            : (lim < 0 ? 0u : ((1u << (lim + 1)) - 1u));
+    unsigned sure_m = 0, bnd_m = 0;
+    if (all) {
+      sure_m = valid_m;
+    } else {
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) {
+        const int code = (int)((cw[k >> 2] >> (8 * (k & 3))) & 0xffu);
+        sure_m |= (code < bl ? 1u : 0u) << k;
+        bnd_m |= (code == bl ? 1u : 0u) << k;
+      }
+      sure_m &= valid_m;
+      bnd_m = (take_all_bnd || crossing) ? (bnd_m & valid_m) : 0u;
     }
     unsigned take_m = take_all_bnd ? bnd_m : 0u;
+    int emitted_b = 0;
     if (crossing) {
-      // ordered fill: a bin-b* token is taken while the mass before it is below the residual
-      auto weight = [&](long long n) -> uint32_t {
-        float sc;
-        if (FROM_LOGITS) {
-          sc = logits[(size_t)unit * g.N + n];
-        } else {
-          const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hr + r) * g.Ncap * kR);
-          sc = dot16_exact(sm.qi, rows[2 * n], rows[2 * n + 1]);
+      // ordered fill of bin b*: the tile's bin-b* tokens in position order, a
+      // round of 256 at a time, each weighed by one thread; a token is taken
+      // while the mass before it is below the residual, so the taken tokens
+      // are a prefix of that order
+      int nbt;
+      const int boff = block_excl_scan<int>(__popc(bnd_m), nbt, sm.thr.red_i);
+      unsigned long long pre = tl.P;
+      int ntake = 0;
+      for (int r0 = 0; r0 < nbt; r0 += kWG) {
+        int jx = boff;
+        for (unsigned mm = bnd_m; mm; mm &= mm - 1, ++jx)
+          if (jx >= r0 && jx < r0 + kWG) sm.blist[jx - r0] = (int)(nbase + __builtin_ctz(mm));
+        __syncthreads();
+        const int cnt = nbt - r0 < kWG ? nbt - r0 : kWG;
+        unsigned long long wt = 0;
+        if (tid < cnt) {
+          const long long n = sm.blist[tid];
+          float sc;
+          if (FROM_LOGITS) {
+            sc = logits[(size_t)unit * g.N + n];
+          } else {
+            const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hr + r) * g.Ncap * kR);
+            sc = dot16_exact(sm.qi, rows[2 * n], rows[2 * n + 1]);
+          }
+          wt = cell_weight(sc, score_cell(sc));
         }
-        return cell_weight(sc, score_cell(sc));
-      };
-      unsigned long long bmass = 0;
-#pragma unroll
-      for (int k = 0; k < TPT; ++k)
-        if (bnd_m & (1u << k)) bmass += weight(nbase + k);
-      unsigned long long tot_u;
-      unsigned long long pre = tl.P + block_excl_scan<unsigned long long>(bmass, tot_u, sm.red_u);
-#pragma unroll
-      for (int k = 0; k < TPT; ++k) {
-        if (bnd_m & (1u << k)) {
-          if ((double)pre < hs.r_u) take_m |= 1u << k;
-          pre += weight(nbase + k);
-        }
+        unsigned long long tot_w;
+        const unsigned long long ex = block_excl_scan<unsigned long long>(wt, tot_w, sm.thr.red_u);
+        int ntk;
+        (void)block_excl_scan<int>(tid < cnt && (double)(pre + ex) < r_u ? 1 : 0, ntk, sm.thr.red_i);
+        ntake += ntk;
+        pre += tot_w;
+        if (ntk < cnt) break;                           // block-uniform
       }
+      int jx = boff;
+      for (unsigned mm = bnd_m; mm; mm &= mm - 1, ++jx)
+        if (jx < ntake) take_m |= 1u << __builtin_ctz(mm);
+      emitted_b = ntake;
     }
-    int ts_, tb_;
-    const int rs = block_excl_scan<int>(__popc(sure_m), ts_, sm.red_i);
-    const int rb = block_excl_scan<int>(__popc(take_m), tb_, sm.red_i);
-    if (crossing) emitted_b = tb_;
+    // one scan for both ranks: positions above b* in the low half, bin-b* in the high half
+    int tot;
+    const int ex = block_excl_scan<int>(__popc(sure_m) | (__popc(take_m) << 16), tot, sm.thr.red_i);
+    const int rs = ex & 0xffff, rb = ex >> 16, ts_ = tot & 0xffff, tb_ = tot >> 16;
+    if (crossing && count && tid == 0) count[unit] = count_base + emitted_b;
     if (idx) {   // positions above b* first, then the taken bin-b* positions, each ascending
-      const long long so = hs.all ? n0 : (long long)tl.sure_off;
-      const long long bo = (long long)hs.total_sure + tl.bnd_off;
-      int a = rs, c2 = rb;
-#pragma unroll
-      for (int k = 0; k < TPT; ++k) {
-        const int n = (int)(nbase + k);
-        if (sure_m & (1u << k)) {
-          if (so + a < cap) idx[(size_t)unit * cap + so + a] = n;
-          ++a;
-        }
-        if (take_m & (1u << k)) {
-          if (bo + c2 < cap) idx[(size_t)unit * cap + bo + c2] = n;
-          ++c2;
-        }
-      }
+      int32_t *dst = idx + (size_t)unit * cap;
+      long long a = (all ? n0 : (long long)tl.sure_off) + rs;
+      for (unsigned mm = sure_m; mm; mm &= mm - 1, ++a)
+        if (a < cap) dst[a] = (int)(nbase + __builtin_ctz(mm));
+      long long c2 = (long long)total_sure + tl.bnd_off + rb;
+      for (unsigned mm = take_m; mm; mm &= mm - 1, ++c2)
+        if (c2 < cap) dst[c2] = (int)(nbase + __builtin_ctz(mm));
     }
     if (ATTEND) {
       const int add = ts_ + tb_;
@@ -549,32 +582,22 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
         nlist = 0;
       }
       if (add <= FinShared::kList) {
-        int a = nlist + rs, c2 = nlist + ts_ + rb;
-#pragma unroll
-        for (int k = 0; k < TPT; ++k) {
-          const int n = (int)(nbase + k);
-          if (sure_m & (1u << k)) sm.list[a++] = n;
-          if (take_m & (1u << k)) sm.list[c2++] = n;
-        }
+        int a = nlist + rs;
+        for (unsigned mm = sure_m; mm; mm &= mm - 1) sm.list[a++] = (int)(nbase + __builtin_ctz(mm));
+        a = nlist + ts_ + rb;
+        for (unsigned mm = take_m; mm; mm &= mm - 1) sm.list[a++] = (int)(nbase + __builtin_ctz(mm));
         nlist += add;
         __syncthreads();
       } else {
         // a tile with more selected positions than the list: attend it in pieces
         for (int l0 = 0; l0 < add; l0 += FinShared::kList) {
           __syncthreads();
-          int a = rs, c2 = ts_ + rb;
-#pragma unroll
-          for (int k = 0; k < TPT; ++k) {
-            const int n = (int)(nbase + k);
-            if (sure_m & (1u << k)) {
-              if (a >= l0 && a < l0 + FinShared::kList) sm.list[a - l0] = n;
-              ++a;
-            }
-            if (take_m & (1u << k)) {
-              if (c2 >= l0 && c2 < l0 + FinShared::kList) sm.list[c2 - l0] = n;
-              ++c2;
-            }
-          }
+          int a = rs;
+          for (unsigned mm = sure_m; mm; mm &= mm - 1, ++a)
+            if (a >= l0 && a < l0 + FinShared::kList) sm.list[a - l0] = (int)(nbase + __builtin_ctz(mm));
+          a = ts_ + rb;
+          for (unsigned mm = take_m; mm; mm &= mm - 1, ++a)
+            if (a >= l0 && a < l0 + FinShared::kList) sm.list[a - l0] = (int)(nbase + __builtin_ctz(mm));
           __syncthreads();
           const int cnt = add - l0 < FinShared::kList ? add - l0 : FinShared::kList;
           attend_rows(sm.q, sm.list, cnt, g.N, kc + cbase, vc + cbase, &sm.res, &sm.at);
@@ -583,7 +606,6 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
       }
     }
   }
-  if (count && !hs.all && tid == 0 && hs.tstar >= t_begin && hs.tstar < t_end) count[unit] = hs.count_base + emitted_b;
   if (ATTEND) {
     if (nlist > 0) {
       attend_rows(sm.q, sm.list, nlist, g.N, kc + cbase, vc + cbase, &sm.res, &sm.at);
@@ -599,11 +621,12 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
     }
   }
   if (!arrive_last(g.ctr_fin + unit, (uint32_t)g.fin_nwg, &sm.flag)) return;
-  // last workgroup of the query: reset its ring for the next call, combine the states
+  // last workgroup of the query (every workgroup has read the ring): reset the
+  // ring and the cell range for the next call, combine the states
   {
     uint64_t *ring = g.ring + (size_t)unit * kRing;
-    if ((long long)hs.c - hs.base_min < kRing) {
-      for (long long cell = (long long)hs.base_min + tid; cell <= hs.c; cell += kWG) ring[cell & (kRing - 1)] = 0ull;
+    if ((long long)c - base_min < kRing) {
+      for (long long cell = (long long)base_min + tid; cell <= c; cell += kWG) ring[cell & (kRing - 1)] = 0ull;
     } else {
       for (int x = tid; x < kRing; x += kWG) ring[x] = 0ull;
     }
@@ -639,9 +662,6 @@ int launch_finish_t(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, co
                     int32_t *count, long long cap, hipStream_t s) {
   const unsigned grid = (unsigned)((long long)g.units * g.fin_nwg);
   if (grid == 0) return RTP_OK;
-  hipLaunchKernelGGL(threshold_kernel, dim3((unsigned)g.units), dim3(kWG), 0, s, g, out ? q_pre : nullptr,
-                     logits ? nullptr : w_q, count);
-  if (hipGetLastError() != hipSuccess) return RTP_ERR_HIP;
 #define RTP_FIN(FL, AT)                                                                                         \
   hipLaunchKernelGGL((finish_kernel<T, FL, AT>), dim3(grid), dim3(kWG), 0, s, g, k_idx, logits, k, v, out, idx, \
                      count, cap)
