@@ -76,7 +76,8 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
   g.T = pick_tile(g.units, g.N);
   g.nt = (int)((g.N + g.T - 1) / g.T);
   {
-    // about 512 finishing workgroups, each over at most 32K positions (staged in LDS)
+    // about 512 finishing workgroups, each over at most 32K positions (their
+    // codes are staged in LDS); more workgroups only add contention
     long long per = (long long)g.units * g.N / 512;
     int tpw = 1;
     while (tpw * 2 <= 32768 / g.T && tpw * 2 <= 32 && (long long)tpw * 2 * g.T <= per) tpw *= 2;
@@ -92,6 +93,10 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
     long long chunk = (Lrows + 15) / 16;
     chunk = (chunk + 31) / 32 * 32;
     if (chunk < 64) chunk = 64;
+    if (const char *env = getenv("RTP_SWA_CHUNK")) {
+      const long long c = atoll(env);
+      if (c >= 64 && c % 64 == 0) chunk = c;
+    }
     g.swa_chunk = (int)chunk;
     g.swa_nch = (int)((Lrows + chunk - 1) / chunk);
   }

@@ -5,6 +5,8 @@
 // softmax(q . k / sqrt(d_h)) weighted sum of v over a row set.
 #pragma once
 
+#include <type_traits>
+
 #include "rtp_internal.h"
 
 namespace rtp {
@@ -15,10 +17,14 @@ template <typename V>
 __device__ __forceinline__ V block_excl_scan(V v, V &total, V *s_buf) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   V x = v;
+  if constexpr (sizeof(V) == 4 && std::is_integral<V>::value) {
+    x = (V)wave_incl_scan_u32((uint32_t)v);
+  } else {
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const V y = __shfl_up(x, off);
-    if (lane >= off) x += y;
+    for (int off = 1; off < 64; off <<= 1) {
+      const V y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
   }
   if (lane == 63) s_buf[w] = x;
   __syncthreads();

@@ -165,6 +165,23 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, 32-bit integers: sums of
+// four within each row of 16 (row shifts 1-3), then of 8 and 16 (row shifts 4
+// and 8 on the upper banks), then row 0's total into rows 1 and 3 and lane
+// 31's running total into rows 2 and 3 (row broadcasts 15 and 31).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+  const int xi = (int)x;
+  int v = xi;
+  v += __builtin_amdgcn_update_dpp(0, xi, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, xi, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, xi, 0x113, 0xF, 0xF, true);   // row_shr:3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xE, true);    // row_shr:4, banks 1-3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xC, true);    // row_shr:8, banks 2-3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, true);    // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, true);    // row_bcast:31 into rows 2, 3
+  return (uint32_t)v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

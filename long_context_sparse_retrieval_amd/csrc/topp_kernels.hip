@@ -68,7 +68,7 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
                                            const rtp_bf16 *__restrict__ w_q, const rtp_bf16 *__restrict__ k_idx,
                                            const float *__restrict__ logits, ScanShared<T> &sm) {
   constexpr int TPT = T / kWG;
-  constexpr int BATCH = TPT < 8 ? TPT : 8;
+  constexpr int BATCH = TPT < 5 ? TPT : 5;
   const int tid = threadIdx.x, wv = tid >> 6;
   const int unit = (int)(blk / g.nt), t = (int)(blk % g.nt);
   const int i = unit % g.nq, br = unit / g.nq, r = br % g.Hr, b = br / g.Hr;
@@ -128,20 +128,17 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
       q[x] = __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
     }
 #pragma unroll
-    for (int kb = 0; kb < TPT; kb += BATCH) {
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int k = kb + u;
-        const long long n = n0 + k * kWG + tid;
-        const float sc = dot16_exact(q, ra[u], rb[u]);
-        lg[k] = n <= m ? sc : -INFINITY;
-        bin_abs(lg[k]);
-        if (kb + BATCH < TPT) {
-          const long long nn = n + BATCH * kWG;
-          const long long nc = nn <= m ? nn : m;
-          ra[u] = rows[2 * nc];
-          rb[u] = rows[2 * nc + 1];
-        }
+    for (int k = 0; k < TPT; ++k) {
+      const int u = k % BATCH;
+      const long long n = n0 + k * kWG + tid;
+      const float sc = dot16_exact(q, ra[u], rb[u]);
+      lg[k] = n <= m ? sc : -INFINITY;
+      bin_abs(lg[k]);
+      if (k + BATCH < TPT) {
+        const long long nn = n + BATCH * kWG;
+        const long long nc = nn <= m ? nn : m;
+        ra[u] = rows[2 * nc];
+        rb[u] = rows[2 * nc + 1];
       }
     }
   }
@@ -261,7 +258,7 @@ union PhaseAShared {
 // Phase A: the local heads' sliding-window workgroups (first) and the
 // retrieval heads' scan tiles in one launch.
 template <int T, bool FROM_LOGITS>
-__global__ __launch_bounds__(kWG) void phase_a_kernel(Geo g, const rtp_bf16 *__restrict__ q_pre,
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4, 8))) void phase_a_kernel(Geo g, const rtp_bf16 *__restrict__ q_pre,
                                                       const rtp_bf16 *__restrict__ w_q,
                                                       const rtp_bf16 *__restrict__ k_idx,
                                                       const float *__restrict__ logits,
@@ -281,6 +278,7 @@ struct ThrScratch {
   double wcum[kBins];
   double red_d[4];
   unsigned long long red_u[4];
+  uint32_t red_u32[4];
   int red_i[4];
 };
 
@@ -291,8 +289,8 @@ struct ThrScratch {
 // the caller.  Every workgroup of a query computes identical values: the
 // integer bins are exact and every floating-point sum has a fixed order.
 __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, int base_min,
-                                                 unsigned long long H_ring, ThrScratch &sm, int &bstar_out,
-                                                 double &r_u_out, int &all_out) {
+                                                 unsigned long long H_ring, unsigned long long R1,
+                                                 ThrScratch &sm, int &bstar_out, double &r_u_out, int &all_out) {
   const int tid = threadIdx.x, j = tid;
   const TileSum *ts = g.tsum + (size_t)unit * g.nt;
   const uint64_t *ring = g.ring + (size_t)unit * kRing;
@@ -300,8 +298,11 @@ __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, 
   unsigned long long H = 0;
   double w255 = 0.0;
   if (span < kRing) {
+    // clamp cells c - 255 - j - 256 x, x = 0, 1, ...: the first one (R1) was loaded by the caller
     H = j <= kBnd ? H_ring : 0ull;
-    for (long long cell = (long long)c - (kBins - 1) - j; cell >= base_min; cell -= kWG) {
+    const long long cell1 = (long long)c - (kBins - 1) - j;
+    if (R1) w255 += (double)R1 * exp((double)(cell1 - c) * 0.125);
+    for (long long cell = cell1 - kWG; cell >= base_min; cell -= kWG) {
       const unsigned long long mj = ring[cell & (kRing - 1)];
       if (mj) w255 += (double)mj * exp((double)(cell - c) * 0.125);
     }
@@ -391,32 +392,42 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
   const size_t cbase = ((size_t)b * g.Hkv + kvg) * g.Ncap * kD;
   const TileSum *ts = g.tsum + (size_t)unit * g.nt;
 
-  // independent loads first: the query's cell range, the first tile maxima,
-  // every code of this run, the prepared query
+  // Loads are counted in issue order (vmcnt), so everything the threshold
+  // needs is requested before the bulk of codes: the cell range, the first
+  // tile maxima and the prepared query, then the ring cells, then the codes.
   const int c = dec_max(g.cmax[unit]);
   const int base_min = dec_min(g.cmin[unit]);
   const int ct0 = tid < g.nt ? ts[tid].c_t : INT32_MIN;
-  constexpr int kPer = FinShared::kCodes / 16 / kWG;
-  const uint4 *src = reinterpret_cast<const uint4 *>(g.codes + (size_t)unit * g.nt * T + (size_t)t_begin * T);
-  const int n16 = (t_end - t_begin) * T / 16;
-  uint4 cv[kPer];
+  double qi_v = 0.0;
+  float qrot_v = 0.f;
+  if (!FROM_LOGITS && tid < kR) qi_v = g.qprep[unit].qi[tid];
+  if (ATTEND && tid < kD) qrot_v = g.qprep[unit].qrot[tid];
+  const uint64_t *ring = g.ring + (size_t)unit * kRing;
+  const unsigned long long H_ring = ring[(c - tid) & (kRing - 1)];
+  const long long cell1 = (long long)c - (kBins - 1) - tid;
+  const unsigned long long R1 = ((long long)c - base_min < kRing && cell1 >= base_min) ? ring[cell1 & (kRing - 1)] : 0ull;
+  {
+    // every code of this run goes straight from memory to LDS (gfx950 LDS-DMA
+    // loads: lane l of a wave lands at the wave's base + 16 l), so nothing is
+    // held in registers while the threshold is worked out
+    constexpr int kPer = FinShared::kCodes / 16 / kWG;
+    const uint4 *src = reinterpret_cast<const uint4 *>(g.codes + (size_t)unit * g.nt * T + (size_t)t_begin * T);
+    const int n16 = (t_end - t_begin) * T / 16;            // a multiple of 64
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {         // clamped, unconditional: the loads stay in flight together
-    const int x = tid + u * kWG;
-    cv[u] = src[x < n16 ? x : n16 - 1];
+    for (int u = 0; u < kPer; ++u) {
+      const int x0 = u * kWG + (tid & ~63);                 // the wave's first 16-byte slot
+      if (x0 < n16)
+        __builtin_amdgcn_global_load_lds(src + x0 + (tid & 63),
+                                         (__attribute__((address_space(3))) void *)(sm.codes + (size_t)x0 * 16),
+                                         16, 0, 0);
+    }
   }
-  if (!FROM_LOGITS && tid < kR) sm.qi[tid] = g.qprep[unit].qi[tid];
-  if (ATTEND && tid < kD) sm.q[tid] = g.qprep[unit].qrot[tid];
-  const unsigned long long H_ring = g.ring[(size_t)unit * kRing + ((c - tid) & (kRing - 1))];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int x = tid + u * kWG;
-    if (x < n16) reinterpret_cast<uint4 *>(sm.codes)[x] = cv[u];
-  }
+  if (!FROM_LOGITS && tid < kR) sm.qi[tid] = qi_v;
+  if (ATTEND && tid < kD) sm.q[tid] = qrot_v;
 
   int bstar, all;
   double r_u;
-  global_threshold(g, unit, c, base_min, H_ring, sm.thr, bstar, r_u, all);
+  global_threshold(g, unit, c, base_min, H_ring, R1, sm.thr, bstar, r_u, all);
 
   // per tile of the query: bin-b* prefix mass, counts above b* and in b*,
   // output offsets; the crossing tile is the last one whose bin-b* tokens
@@ -464,6 +475,7 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
     if (all) count[unit] = (int)(m + 1);
     else if (tstar < 0) count[unit] = count_base;
   }
+  __builtin_amdgcn_s_waitcnt(0);                        // this wave's code loads have landed in LDS
   __syncthreads();
 
   float run_m = -INFINITY, run_l = 0.f, run_o = 0.f;    // thread d < 128 holds channel d
@@ -527,6 +539,7 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
       // are a prefix of that order
       int nbt;
       const int boff = block_excl_scan<int>(__popc(bnd_m), nbt, sm.thr.red_i);
+      nbt = nbt < T ? nbt : T;
       unsigned long long pre = tl.P;
       int ntake = 0;
       for (int r0 = 0; r0 < nbt; r0 += kWG) {
@@ -535,9 +548,10 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
           if (jx >= r0 && jx < r0 + kWG) sm.blist[jx - r0] = (int)(nbase + __builtin_ctz(mm));
         __syncthreads();
         const int cnt = nbt - r0 < kWG ? nbt - r0 : kWG;
-        unsigned long long wt = 0;
+        uint32_t wt = 0;                                  // < 1.14 * 2^23 each, < 2^32 per round
         if (tid < cnt) {
-          const long long n = sm.blist[tid];
+          long long n = sm.blist[tid];
+          n = n < 0 ? 0 : (n > m ? m : n);
           float sc;
           if (FROM_LOGITS) {
             sc = logits[(size_t)unit * g.N + n];
@@ -547,8 +561,8 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
           }
           wt = cell_weight(sc, score_cell(sc));
         }
-        unsigned long long tot_w;
-        const unsigned long long ex = block_excl_scan<unsigned long long>(wt, tot_w, sm.thr.red_u);
+        uint32_t tot_w;
+        const uint32_t ex = block_excl_scan<uint32_t>(wt, tot_w, sm.thr.red_u32);
         int ntk;
         (void)block_excl_scan<int>(tid < cnt && (double)(pre + ex) < r_u ? 1 : 0, ntk, sm.thr.red_i);
         ntake += ntk;
@@ -563,16 +577,17 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
     // one scan for both ranks: positions above b* in the low half, bin-b* in the high half
     int tot;
     const int ex = block_excl_scan<int>(__popc(sure_m) | (__popc(take_m) << 16), tot, sm.thr.red_i);
-    const int rs = ex & 0xffff, rb = ex >> 16, ts_ = tot & 0xffff, tb_ = tot >> 16;
+    const int rs = ex & 0xffff, rb = ex >> 16;
+    const int ts_ = min(tot & 0xffff, T), tb_ = min(tot >> 16, T);
     if (crossing && count && tid == 0) count[unit] = count_base + emitted_b;
     if (idx) {   // positions above b* first, then the taken bin-b* positions, each ascending
       int32_t *dst = idx + (size_t)unit * cap;
       long long a = (all ? n0 : (long long)tl.sure_off) + rs;
       for (unsigned mm = sure_m; mm; mm &= mm - 1, ++a)
-        if (a < cap) dst[a] = (int)(nbase + __builtin_ctz(mm));
+        if ((unsigned long long)a < (unsigned long long)cap) dst[a] = (int)(nbase + __builtin_ctz(mm));
       long long c2 = (long long)total_sure + tl.bnd_off + rb;
       for (unsigned mm = take_m; mm; mm &= mm - 1, ++c2)
-        if (c2 < cap) dst[c2] = (int)(nbase + __builtin_ctz(mm));
+        if ((unsigned long long)c2 < (unsigned long long)cap) dst[c2] = (int)(nbase + __builtin_ctz(mm));
     }
     if (ATTEND) {
       const int add = ts_ + tb_;
