@@ -1,0 +1,86 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark times.
+
+The GPU runs one whole decode step of the 128K (batch 4) and 1M layers: every
+head, caches written by the library's own cache writers, the same tile and
+workgroup plan as the benchmark.  The oracle, which cannot redo the whole step
+in seconds, builds its own caches for a sample and recomputes, one by one:
+one concentrated and one diffuse retrieval query of sequence 0 (whole
+context), and the local heads of one KV group.  Every other query is checked
+through properties that hold at any size (positions unique, in range, count
+within [1, m + 1]).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import long_context_sparse_retrieval_amd as rtp
+import oracle as O
+from parity import check_output, check_set, dev_bf16, layer_of, say
+
+pytestmark = pytest.mark.gpu
+
+# config -> sampled retrieval heads r of sequence 0 (r = 0 concentrated, r = 1 diffuse)
+FULL = {"128k-b4": (3, [0, 1]), "1m-b1": (4, [0, 1])}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    rtp.load()
+    torch.cuda.init()
+
+
+@pytest.mark.parametrize("case", list(FULL))
+def test_decode_step_full_size_sampled(case):
+    cfg, r_sample = FULL[case]
+    spec = gen.spec_for(cfg)
+    say(f"full-size decode {case}: {spec.name} N={spec.N} B={spec.B} Hr={spec.Hr}")
+    wl = gen.make_workload(spec, gen.workload.default_seed(cfg))
+    lay = layer_of(spec, rtp)
+
+    # GPU: the benchmark's configuration
+    k_pre = dev_bf16(wl.k_pre)
+    k = rtp.rope_keys(lay, k_pre)
+    k_idx = rtp.index_keys(lay, k_pre, dev_bf16(wl.w_k))
+    del k_pre
+    v = dev_bf16(wl.v)
+    ws = rtp.workspace(lay)
+    cap = spec.N
+    idx = torch.full((spec.B, spec.Hr, 1, cap), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((spec.B, spec.Hr, 1), dtype=torch.int32, device="cuda")
+    out = rtp.decode_step(lay, dev_bf16(wl.q_pre), dev_bf16(wl.w_q), k_idx, k, v, ws, idx=idx, count=cnt)
+    torch.cuda.synchronize()
+    out, idx, cnt = out.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+    del k, v, k_idx
+    torch.cuda.empty_cache()
+    say(f"{case}: GPU step done; |S| = {cnt.ravel().tolist()}")
+
+    # properties of every query's set
+    m = spec.N - 1
+    for b in range(spec.B):
+        for r in range(spec.Hr):
+            c = int(cnt[b, r, 0])
+            assert 1 <= c <= m + 1, f"b{b} r{r}: count {c}"
+            got = idx[b, r, 0, :c]
+            assert np.all((got >= 0) & (got <= m)), f"b{b} r{r}: position out of range"
+            assert len(np.unique(got)) == c, f"b{b} r{r}: duplicate positions"
+    assert np.all(np.isfinite(out)), "non-finite output"
+
+    # the oracle on the sample, from its own caches
+    rheads = spec.retrieval_heads()
+    g_loc = [g for g in range(spec.Hkv) if g not in spec.ret_groups][0]
+    loc_heads = list(range(g_loc * spec.G, (g_loc + 1) * spec.G))
+    groups = sorted({rheads[r] // spec.G for r in r_sample} | {g_loc})
+    kc, ki = O.build_caches(wl, groups=groups, heads=r_sample)
+    say(f"{case}: oracle caches built for groups {groups}, retrieval heads {r_sample}")
+    res = O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
+                        n_sink=spec.n_sink, rope_base=spec.rope_theta, heads=[rheads[r] for r in r_sample] + loc_heads,
+                        batches=[0], want_logits=True)
+    verdicts = []
+    for (b, h, i), ref in res["out"].items():
+        check_output(out[b, h, i], ref, f"{case} b{b} h{h}")
+    for (b, r, i), t in res["topp"].items():
+        verdicts.append(check_set(idx[b, r, i], int(cnt[b, r, i]), cap, t, res["logits"][(b, r, i)], spec.p,
+                                  f"{case} b{b} r{r}"))
+    say(f"{case}: sampled sets {verdicts.count('exact')} exact, {verdicts.count('tolerated')} tolerated; "
+        f"{len(res['out'])} head outputs checked")
