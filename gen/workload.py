@@ -16,11 +16,17 @@ test and are not computed here.
 Draw order for ``make_workload`` (one ``numpy.random.default_rng(seed)``):
   1. W_q for every retrieval q head r (ascending), each (D, R) ~ N(0, 1/D);
      then W_k the same way unless the spec shares one draw (W_k = W_q).
-  2. u = the unscaled pre-RoPE queries, (B, Hq, nq, D) ~ N(0, 1).
+  2. u = the unscaled pre-RoPE queries, (B, Hq, nq, D) ~ N(0, 1).  In
+     "topics" mode (chunked prefill) these are the per-query perturbations xi,
+     followed by one draw of two topic directions per head, (B, Hq, 2, D);
+     query i of head h takes topic i % 2 and the direction
+     normalize(t_topic + mix * xi_i).
   3. For b, then KV group g: the group's pre-RoPE keys.  Retrieval groups get
      (N, D) ~ N(0, 1) followed by one draw of all needle positions of the
      group's retrieval heads (without replacement, split in head order);
-     a needle key is alpha * sqrt(D) * u_hat + its background draw.  Local
+     a needle key is alpha * sqrt(D) * u_hat + its background draw (in
+     "topics" mode every head plants both topics, topic 0 then topic 1, with
+     u_hat the topic direction).  Local
      groups get draws only on the rows a local head reads (window + sinks).
   4. For b, then g: values, on the same rows as the keys.
 """
@@ -66,13 +72,16 @@ class WorkloadSpec:
     n_sink: int = 4
     rope_theta: float = 1.0e6
     # needle recipe: "fixed" -> every retrieval query plants n_needles at alpha;
-    # "classes" -> class (b*Hr + r) % 2: 0 concentrated, 1 diffuse
+    # "classes" -> class (b*Hr + r) % 2: 0 concentrated, 1 diffuse;
+    # "topics" -> every retrieval head plants a concentrated topic (0) and a
+    # diffuse topic (1); query i uses topic i % 2 (chunked prefill)
     needle_mode: str = "fixed"
     n_needles: int = 32
     alpha: float = 3.0
     conc: tuple = (16, 4.0)
     diffuse: tuple = (8192, 0.5)
     budget_targets: tuple = (500, 2500)
+    topic_mix: float = 0.3
     # "unit": q = u; "table": q = s_(b,r) * u with s from the calibration table
     query_scale: str = "unit"
     shared_w: bool = True
@@ -121,6 +130,8 @@ CONFIGS = {
                     needle_mode="classes", query_scale="table"),
     4: WorkloadSpec("qwen3-32b-layer-1m-b1", B=1, Hq=64, Hkv=8, N=1048576, ret_groups=(0, 1),
                     needle_mode="classes", query_scale="table"),
+    5: WorkloadSpec("prefill-128k-4096q-4h", B=1, Hq=4, Hkv=1, N=131072, nq=4096, ret_groups=(0,),
+                    needle_mode="topics", query_scale="table"),
 }
 
 
@@ -154,12 +165,21 @@ class Workload:
     u: np.ndarray = None         # float32 [B, Hq, nq, D] unscaled query draws
     needles: dict = field(default_factory=dict)   # (b, r) -> int64 positions
     classes: dict = field(default_factory=dict)   # (b, r) -> 0 concentrated / 1 diffuse
-    scales: dict = field(default_factory=dict)    # (b, r) -> query scale
+    scales: dict = field(default_factory=dict)    # (b, r) -> query scale ((b, r, topic) in topics mode)
+    topics: np.ndarray = None    # float32 [B, Hq, 2, D] topic directions (topics mode)
 
     @property
     def positions(self) -> np.ndarray:
         """Query positions m of the nq queries (the last nq cache rows)."""
         return np.arange(self.spec.N - self.spec.nq, self.spec.N, dtype=np.int64)
+
+
+def query_directions(xi: np.ndarray, topics: np.ndarray, mix: float) -> np.ndarray:
+    """Unit query directions of topics mode: normalize(t_(i % 2) + mix * xi_i), float64."""
+    B, Hq, nq, D = xi.shape
+    tsel = topics[:, :, np.arange(nq) % 2].astype(np.float64)
+    d = tsel + mix * xi.astype(np.float64)
+    return d / np.linalg.norm(d, axis=-1, keepdims=True)
 
 
 def load_scale_table() -> dict:
@@ -197,21 +217,33 @@ def make_workload(spec: WorkloadSpec, seed: int, scales: dict | None = None) -> 
         for r in range(Hr):
             w_k[r] = f32_to_bf16_bits(rng.standard_normal((D, R), dtype=np.float32) * np.float32(inv_sqrt_d))
 
-    # 2. unscaled queries
+    # 2. unscaled queries (topics mode: perturbations, then the topic directions)
     u = rng.standard_normal((B, Hq, nq, D), dtype=np.float32)
+    topics = None
+    if spec.needle_mode == "topics":
+        topics = rng.standard_normal((B, Hq, 2, D), dtype=np.float32)
 
-    # query scales
+    # query scales: (b, r) -> s, or (b, r, topic) -> s in topics mode
     if scales is None:
         scales = {}
         if spec.query_scale == "table":
             tab = load_scale_table().get(scale_key(spec, seed))
             if tab is None:
                 raise KeyError(f"no calibrated query scales for {scale_key(spec, seed)} in {_SCALES_FILE}")
-            for b, r, s, *_ in tab:
-                scales[(int(b), int(r))] = float(s)
-    q = u.astype(np.float64)
-    for (b, r), s in scales.items():
-        q[b, rheads[r]] *= s
+            for e in tab:
+                if spec.needle_mode == "topics":
+                    scales[(int(e[0]), int(e[1]), int(e[2]))] = float(e[3])
+                else:
+                    scales[(int(e[0]), int(e[1]))] = float(e[2])
+    if topics is None:
+        q = u.astype(np.float64)
+        for (b, r), s in scales.items():
+            q[b, rheads[r]] *= s
+    else:
+        q = query_directions(u, topics, spec.topic_mix)
+        for key, s in scales.items():
+            b, r, tpc = key
+            q[b, rheads[r], tpc::2] *= s
     q_pre = f32_to_bf16_bits(q.astype(np.float32))
 
     # 3. keys (+ needles), 4. values
@@ -225,18 +257,22 @@ def make_workload(spec: WorkloadSpec, seed: int, scales: dict | None = None) -> 
             if g in spec.ret_groups:
                 kg = rng.standard_normal((N, D), dtype=np.float32)
                 rs = [r for r in range(Hr) if rheads[r] // G == g]
-                recipes = [spec.needle_recipe(b, r) for r in rs]
-                total = sum(c for c, _, _ in recipes)
+                if topics is None:
+                    plants = [((b, r), spec.needle_recipe(b, r), u[b, rheads[r], 0]) for r in rs]
+                else:
+                    plants = [((b, r, tpc), (*(spec.conc if tpc == 0 else spec.diffuse), tpc), topics[b, rheads[r], tpc])
+                              for r in rs for tpc in (0, 1)]
+                total = sum(rec[0] for _, rec, _ in plants)
                 pos_all = rng.choice(n_avail, size=total, replace=False).astype(np.int64)
                 off = 0
-                for r, (cnt, alpha, cls) in zip(rs, recipes):
+                for key, (cnt, alpha, cls), dvec in plants:
                     pos = np.sort(pos_all[off:off + cnt])
                     off += cnt
-                    direction = u[b, rheads[r], 0].astype(np.float64)
+                    direction = dvec.astype(np.float64)
                     direction /= np.linalg.norm(direction)
                     kg[pos] += (alpha * math.sqrt(D) * direction).astype(np.float32)
-                    needles[(b, r)] = pos
-                    classes[(b, r)] = cls
+                    needles[key] = pos
+                    classes[key] = cls
                 k_pre[b, g] = f32_to_bf16_bits(kg)
                 del kg
             else:
@@ -250,4 +286,4 @@ def make_workload(spec: WorkloadSpec, seed: int, scales: dict | None = None) -> 
 
     return Workload(spec=spec, seed=seed, q_pre=q_pre, w_q=w_q, w_k=w_k, k_pre=k_pre, v=v,
                     head_mode=spec.head_mode(), u=u, needles=needles, classes=classes,
-                    scales={k: float(s) for k, s in scales.items()})
+                    scales={k: float(s) for k, s in scales.items()}, topics=topics)

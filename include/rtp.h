@@ -152,8 +152,14 @@ int rtp_swa_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *
  * rtp_sparse_attn + rtp_swa_attn without materialising the scores.
  * idx_opt/count_opt (may be NULL) receive the selected sets as rtp_topp_select
  * writes them.  phase_event (may be NULL) is a hipEvent_t recorded on `stream`
- * between the scan phase and the selection/attention phase (for profiling).
- * This build implements nq == 1 only (RTP_ERR_UNSUPPORTED otherwise). */
+ * between the scan phase and the selection/attention phase (nq == 1), or after
+ * the query preparation (nq > 1), for profiling.
+ * nq > 1 (chunked prefill, causal: query i at position N-nq+i sees 0..N-nq+i)
+ * runs the indexer as a matrix-core GEMM, Top-P per query and attention over
+ * each query's set, in chunks of queries whose positions fit the workspace.
+ * Its scores are the exact products of the bf16 inputs summed by the matrix
+ * core (order of the 16-term fp32 sum not specified), so a position within one
+ * rounding of a bin edge may fall on either side. */
 int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *w_q,
                     const rtp_bf16 *k_idx, const rtp_bf16 *k, const rtp_bf16 *v, float *out,
                     int32_t *idx_opt, int32_t *count_opt, int64_t cap,

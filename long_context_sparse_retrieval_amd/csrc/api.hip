@@ -121,8 +121,30 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
   off = align_up(off + units * (nt > (size_t)kSpChunks ? nt : (size_t)kSpChunks) * sizeof(Partial));  // >= fin_nwg
   const size_t o_swa = off;
   off = align_up(off + (size_t)g.swa_units * g.swa_hb * g.swa_nch * kSwaHeads * sizeof(Partial));
+  // the codes of the decode path and, for nq > 1, the chunked prefill's
+  // selected positions (never used by the same call) share one region
+  g.pf_qch = 0;
+  size_t pf_idx_bytes = 0, pf_cnt_bytes = 0;
+  if (g.nq > 1 && g.units > 0) {
+    const long long per_q = (long long)g.B * g.Hr * g.N * 4;      // bytes of positions per query index
+    long long qch = (1ll << 30) / per_q;                            // about 1 GiB of positions per chunk
+    qch = qch / 16 * 16;
+    if (const char *env = getenv("RTP_PF_QCH")) {          // tuning / test override
+      const long long v = atoll(env);
+      if (v >= 16 && v % 16 == 0) qch = v;
+    }
+    if (qch < 16) qch = 16;
+    if (qch > g.nq) qch = g.nq;
+    g.pf_qch = (int)qch;
+    pf_idx_bytes = align_up((size_t)qch * per_q);
+    pf_cnt_bytes = align_up((size_t)g.B * g.Hr * qch * 4);
+  }
   const size_t o_codes = off;
-  off = align_up(off + units * nt * (size_t)g.T);
+  {
+    const size_t codes_bytes = units * nt * (size_t)g.T;
+    const size_t pf_bytes = pf_idx_bytes + pf_cnt_bytes;
+    off = align_up(off + (codes_bytes > pf_bytes ? codes_bytes : pf_bytes));
+  }
   if (ws) {
     char *base = static_cast<char *>(ws);
     g.ring = reinterpret_cast<uint64_t *>(base + o_ring);
@@ -135,6 +157,8 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
     g.part = reinterpret_cast<Partial *>(base + o_part);
     g.swa_part = reinterpret_cast<Partial *>(base + o_swa);
     g.codes = reinterpret_cast<uint8_t *>(base + o_codes);
+    g.pf_idx = reinterpret_cast<int32_t *>(base + o_codes);
+    g.pf_cnt = reinterpret_cast<int32_t *>(base + o_codes + pf_idx_bytes);
   }
   out->g = g;
   out->ws_bytes = off;
@@ -257,11 +281,25 @@ int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf1
   Plan p;
   int st = plan_with_ws(layer, ws, ws_bytes, &p);
   if (st != RTP_OK) return st;
-  if (layer->nq != 1) return RTP_ERR_UNSUPPORTED;
   if (!q_pre || !k || !v || !out) return RTP_ERR_ARG;
   if (p.g.units && (!w_q || !k_idx)) return RTP_ERR_ARG;
   if (idx_opt && cap < 0) return RTP_ERR_ARG;
   hipStream_t s = as_stream(stream);
+  if (layer->nq > 1) {
+    // chunked prefill: matrix-core selection and attention per chunk of queries
+    st = launch_pf_qprep(p.g, q_pre, w_q, s);
+    if (st != RTP_OK) return st;
+    if (phase_event && hipEventRecord(reinterpret_cast<hipEvent_t>(phase_event), s) != hipSuccess) return RTP_ERR_HIP;
+    for (int i0 = 0; p.g.units && i0 < p.g.nq; i0 += p.g.pf_qch) {
+      const int nqc = p.g.nq - i0 < p.g.pf_qch ? p.g.nq - i0 : p.g.pf_qch;
+      st = launch_pf_select(p.g, k_idx, i0, nqc, p.g.pf_idx, p.g.N, p.g.pf_cnt, idx_opt, count_opt,
+                            idx_opt ? cap : 0, s);
+      if (st != RTP_OK) return st;
+      st = launch_pf_attn(p.g, i0, nqc, k, v, p.g.pf_idx, p.g.N, p.g.pf_cnt, out, s);
+      if (st != RTP_OK) return st;
+    }
+    return launch_phase_a(p.g, q_pre, nullptr, nullptr, nullptr, k, v, out, false, true, s);
+  }
   st = launch_phase_a(p.g, q_pre, w_q, k_idx, nullptr, k, v, out, true, true, s);
   if (st != RTP_OK) return st;
   if (phase_event && hipEventRecord(reinterpret_cast<hipEvent_t>(phase_event), s) != hipSuccess) return RTP_ERR_HIP;

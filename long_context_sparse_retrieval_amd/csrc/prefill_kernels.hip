@@ -1,0 +1,556 @@
+// Chunked prefill (nq > 1 causal queries per head): the indexer as a GEMM on
+// the matrix cores, exact per-query 256-bin Top-P, and attention over the
+// selected rows.
+//
+// "Full Attention Strikes Back" (RTPurbo) section 3.2: eq. (4) scores every
+// earlier position of each query with the rank-16 indexer, eq. (5) keeps the
+// Top-P set and attends over it.  Query i of a chunk of nq sits at position
+// m_i = N - nq + i and sees positions 0..m_i.
+//
+// Design for gfx950.  One selection workgroup owns 16 queries of one head and
+// their whole prefixes, so each query's histogram lives in LDS and never has
+// to be merged across workgroups.  The K = 16 contraction is one
+// v_mfma_f32_16x16x16_bf16 per 16 keys (16 queries x 16 keys per wave); the
+// products of two bf16 values are exact in fp32, only the order of the 16-term
+// sum is the matrix core's.  The logits are never stored: four passes
+// recompute them from the indexer keys (4 MiB per head at 128K, resident in
+// the Infinity Cache) -- per-query maximum, exact integer histogram, per-chunk
+// counts and bin-b* mass, then the ordered selection.  Keys are split into
+// chunks, each processed in position order by one wave, so the selected
+// positions come out in ascending order with offsets from a per-chunk prefix.
+#include "block_util.h"
+
+namespace rtp {
+
+namespace {
+
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kQB = 16;         // queries per selection workgroup (the matrix-core M dimension)
+constexpr int kMaxCh = 128;     // key chunks per query
+constexpr int kUnroll = 8;      // 16-key blocks whose loads are issued together
+
+// ------------------------------------------------------------------ row (16-lane) helpers
+template <int CTRL, int RMASK = 0xF, int BMASK = 0xF>
+__device__ __forceinline__ int dppi(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, RMASK, BMASK, true);
+}
+// sum over the 16 lanes of a row, every lane receives it
+__device__ __forceinline__ int row_sum_i(int v) {
+  v += dppi<0xB1>(v);
+  v += dppi<0x4E>(v);
+  v += dppi<0x141>(v);
+  v += dppi<0x140>(v);
+  return v;
+}
+__device__ __forceinline__ float row_max_f(float v) {
+  v = fmaxf(v, __int_as_float(dppi<0xB1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dppi<0x4E>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dppi<0x141>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dppi<0x140>(__float_as_int(v))));
+  return v;
+}
+// inclusive prefix over the lanes of a row (row shifts 1-3, then 4 and 8 on the upper banks)
+__device__ __forceinline__ uint32_t row_incl_scan_u32(uint32_t x) {
+  const int xi = (int)x;
+  int v = xi;
+  v += dppi<0x111>(xi);
+  v += dppi<0x112>(xi);
+  v += dppi<0x113>(xi);
+  v += dppi<0x114, 0xF, 0xE>(v);
+  v += dppi<0x118, 0xF, 0xC>(v);
+  return (uint32_t)v;
+}
+__device__ __forceinline__ unsigned long long row_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Per query of a selection workgroup.
+struct PfSel {
+  double r_u;     // residual of p*Z in in-cell units of bin b*
+  int c;          // max cell
+  int bstar;      // boundary bin; 256 when every position is taken
+  int all;
+  int cstar;      // crossing chunk (-1: none)
+  int n_sure;     // positions above b*
+  int valid;
+};
+
+struct PfShared {
+  union {
+    struct {
+      unsigned long long mass[kQB][kBins];
+      uint32_t cnt[kQB][kBins];
+    } h;
+    struct {
+      unsigned long long bm[kQB][kMaxCh];   // bin-b* mass per chunk, then its exclusive prefix
+      int ns[kQB][kMaxCh];                  // positions above b* per chunk, then exclusive prefix
+      int nb[kQB][kMaxCh];                  // bin-b* positions per chunk, then exclusive prefix
+    } c;
+  };
+  PfSel sel[kQB];
+  float wmax[4][kQB];
+};
+
+// Selection: one workgroup per (b, r, block of 16 queries of the chunk [i0, i0 + nqc)).
+// Writes the selected positions of each query to idx_ws[unit_local][capw] (and,
+// optionally, to idx[unit][cap], truncated) and its count to cnt_ws / count.
+__global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *__restrict__ k_idx, int i0, int nqc,
+                                                        int kc, int32_t *__restrict__ idx_ws, long long capw,
+                                                        int32_t *__restrict__ cnt_ws, int32_t *__restrict__ idx,
+                                                        int32_t *__restrict__ count, long long cap) {
+  __shared__ PfShared sm;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, row = lane >> 4, col = lane & 15;
+  const int nblk = (nqc + kQB - 1) / kQB;
+  const int br = blockIdx.x / nblk, qb = blockIdx.x % nblk;
+  const int r = br % g.Hr, b = br / g.Hr;
+  const int qi0 = i0 + qb * kQB;                         // first query index (0..nq) of the block
+  const int nvalid = min(kQB, i0 + nqc - qi0);
+  const long long mpos0 = g.N - g.nq;                    // position of query index 0
+  const long long m_last = mpos0 + qi0 + nvalid - 1;
+  const uint2 *keys = reinterpret_cast<const uint2 *>(k_idx + ((size_t)b * g.Hr + r) * g.Ncap * kR);
+
+  // A operand: lane holds q_idx[query col][dims 4 row .. 4 row + 3] as bf16
+  bf16x4_t a;
+  {
+    const int q = col;
+    const bool ok = q < nvalid;
+    const QPrep *qp = g.qprep + ((size_t)br * g.nq + qi0 + (ok ? q : 0));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float f = ok ? (float)qp->qi[4 * row + j] : 0.f;
+      a[j] = (short)(__float_as_uint(f) >> 16);         // the values are bf16, so exact
+    }
+  }
+  // this lane's four queries (rows of the MFMA result) and their positions
+  long long mq[4];
+  bool qv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = 4 * row + i;
+    qv[i] = q < nvalid;
+    mq[i] = mpos0 + qi0 + q;
+  }
+  const int nch = (int)((m_last + 1 + kc - 1) / kc);
+
+  // Runs body(n0, d) for every 16-key block of the chunks this wave owns, in
+  // position order within a chunk; chunk_end(ch) after each chunk.
+  auto sweep = [&](auto &&body, auto &&chunk_begin, auto &&chunk_end) {
+    for (int ch = wv; ch < nch; ch += 4) {
+      chunk_begin(ch);
+      const long long k0 = (long long)ch * kc;
+      const long long k1 = k0 + kc < m_last + 1 ? k0 + kc : m_last + 1;
+      for (long long n0 = k0; n0 < k1; n0 += 16 * kUnroll) {
+        uint2 kv[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {              // clamped, unconditional loads
+          long long nr = n0 + 16 * u + col;
+          nr = nr < g.N ? nr : g.N - 1;
+          kv[u] = keys[nr * 4 + row];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          if (n0 + 16 * u >= k1) break;                   // wave-uniform
+          bf16x4_t bv;
+          bv[0] = (short)(kv[u].x & 0xffffu);
+          bv[1] = (short)(kv[u].x >> 16);
+          bv[2] = (short)(kv[u].y & 0xffffu);
+          bv[3] = (short)(kv[u].y >> 16);
+          const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+          const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bv, zero, 0, 0, 0);
+          body(n0 + 16 * u, d);
+        }
+      }
+      chunk_end(ch);
+    }
+  };
+  auto nop = [](int) {};
+
+  // ---- pass 1: per-query maximum
+  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  sweep([&](long long n0, const f32x4_t &d) {
+          const long long n = n0 + col;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (qv[i] && n <= mq[i]) mx[i] = fmaxf(mx[i], d[i]);
+        },
+        nop, nop);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float v = row_max_f(mx[i]);
+    if (col == 0) sm.wmax[wv][4 * row + i] = v;
+  }
+  for (int x = tid; x < kQB * kBins; x += kWG) {
+    (&sm.h.mass[0][0])[x] = 0ull;
+    (&sm.h.cnt[0][0])[x] = 0u;
+  }
+  __syncthreads();
+  if (tid < kQB) {
+    const float v = fmaxf(fmaxf(sm.wmax[0][tid], sm.wmax[1][tid]), fmaxf(sm.wmax[2][tid], sm.wmax[3][tid]));
+    sm.sel[tid].c = tid < nvalid ? score_cell(v) : 0;
+    sm.sel[tid].valid = tid < nvalid ? 1 : 0;
+  }
+  __syncthreads();
+  int cq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cq[i] = sm.sel[4 * row + i].c;
+
+  // ---- pass 2: exact 256-bin histogram per query (bins relative to the query's max cell)
+  sweep([&](long long n0, const f32x4_t &d) {
+          const long long n = n0 + col;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (!(qv[i] && n <= mq[i])) continue;
+            const float s = d[i];
+            const int cell = score_cell(s);
+            int j = cq[i] - cell;
+            uint32_t w;
+            if (j >= kBins - 1) {
+              j = kBins - 1;
+              w = cell_weight(s, cq[i] - (kBins - 1));
+            } else {
+              w = cell_weight(s, cell);
+            }
+            atomicAdd(&sm.h.mass[4 * row + i][j], (unsigned long long)w);
+            atomicAdd(&sm.h.cnt[4 * row + i][j], 1u);
+          }
+        },
+        nop, nop);
+  __syncthreads();
+
+  // ---- threshold per query: wave w takes queries w, w + 4, ...; lane holds bins 4 lane .. 4 lane + 3
+  for (int q = wv; q < kQB; q += 4) {
+    if (q >= nvalid) continue;                            // wave-uniform
+    double W[4];
+    double loc = 0.0;
+    int cnt_lt = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int j = 4 * lane + k;
+      W[k] = (double)sm.h.mass[q][j] * 0x1p-23 * exp(-(double)j * 0.125);
+      loc += W[k];
+    }
+    // wave exclusive scan of the lane sums (fixed order)
+    double incl = loc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const double Z = __shfl(incl, 63);
+    double e = incl - loc;
+    const double need = (double)g.p * Z;
+    int cand = kBins;
+    double before_c = 0.0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (cand == kBins && e + W[k] >= need) {
+        cand = 4 * lane + k;
+        before_c = e;
+      }
+      e += W[k];
+    }
+    int bstar = cand;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) bstar = min(bstar, __shfl_xor(bstar, off));
+    if (bstar >= kBins) bstar = kBins - 1;
+    const double before = __shfl(before_c, bstar / 4);
+    const int all = (g.p >= 1.0f || bstar >= kBins - 1) ? 1 : 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cnt_lt += (4 * lane + k < bstar) ? (int)sm.h.cnt[q][4 * lane + k] : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) cnt_lt += __shfl_xor(cnt_lt, off);
+    if (lane == 0) {
+      PfSel &ps = sm.sel[q];
+      ps.all = all;
+      ps.bstar = all ? kBins : bstar;
+      ps.r_u = (need - before) * 0x1p23 * exp((double)bstar * 0.125);
+      ps.n_sure = all ? (int)(mpos0 + qi0 + q + 1) : cnt_lt;
+    }
+  }
+  __syncthreads();                                        // the histogram is dead from here on
+  for (int x = tid; x < kQB * kMaxCh; x += kWG) {
+    (&sm.c.bm[0][0])[x] = 0ull;
+    (&sm.c.ns[0][0])[x] = 0;
+    (&sm.c.nb[0][0])[x] = 0;
+  }
+  int bs[4], allq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bs[i] = sm.sel[4 * row + i].bstar;
+    allq[i] = sm.sel[4 * row + i].all;
+  }
+  __syncthreads();
+
+  // ---- pass 3: per chunk, positions above b*, positions in b* and their mass
+  {
+    int ns[4], nb[4];
+    unsigned long long bm[4];
+    sweep([&](long long n0, const f32x4_t &d) {
+            const long long n = n0 + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (!(qv[i] && n <= mq[i])) continue;
+              const float s = d[i];
+              const int cell = score_cell(s);
+              const int j = min(cq[i] - cell, kBins - 1);
+              if (j < bs[i]) {
+                ++ns[i];
+              } else if (!allq[i] && j == bs[i]) {
+                ++nb[i];
+                bm[i] += cell_weight(s, cell);
+              }
+            }
+          },
+          [&](int) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              ns[i] = nb[i] = 0;
+              bm[i] = 0ull;
+            }
+          },
+          [&](int ch) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int a1 = row_sum_i(ns[i]), a2 = row_sum_i(nb[i]);
+              const unsigned long long a3 = row_sum_u64(bm[i]);
+              if (col == 0) {
+                sm.c.ns[4 * row + i][ch] = a1;
+                sm.c.nb[4 * row + i][ch] = a2;
+                sm.c.bm[4 * row + i][ch] = a3;
+              }
+            }
+          });
+  }
+  __syncthreads();
+
+  // ---- per query: exclusive prefixes over chunks (position order) and the crossing chunk
+  for (int q = wv; q < kQB; q += 4) {
+    if (q >= nvalid) continue;
+    const PfSel ps = sm.sel[q];
+    // lane holds chunks 2 lane, 2 lane + 1
+    unsigned long long m0 = 0, m1 = 0;
+    int s0 = 0, s1 = 0, b0 = 0, b1 = 0;
+    if (2 * lane < nch) { m0 = sm.c.bm[q][2 * lane]; s0 = sm.c.ns[q][2 * lane]; b0 = sm.c.nb[q][2 * lane]; }
+    if (2 * lane + 1 < nch) { m1 = sm.c.bm[q][2 * lane + 1]; s1 = sm.c.ns[q][2 * lane + 1]; b1 = sm.c.nb[q][2 * lane + 1]; }
+    unsigned long long mi = m0 + m1;
+    int si = s0 + s1, bi = b0 + b1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned long long ym = __shfl_up(mi, off);
+      const int ys = __shfl_up(si, off), yb = __shfl_up(bi, off);
+      if (lane >= off) {
+        mi += ym;
+        si += ys;
+        bi += yb;
+      }
+    }
+    const unsigned long long Pm0 = mi - m0 - m1, Pm1 = Pm0 + m0;
+    const int Ps0 = si - s0 - s1, Ps1 = Ps0 + s0, Pb0 = bi - b0 - b1, Pb1 = Pb0 + b0;
+    int cross = -1;
+    if (!ps.all) {
+      if (2 * lane < nch && b0 > 0 && (double)Pm0 < ps.r_u) cross = 2 * lane;
+      if (2 * lane + 1 < nch && b1 > 0 && (double)Pm1 < ps.r_u) cross = 2 * lane + 1;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) cross = max(cross, __shfl_xor(cross, off));
+    if (2 * lane < nch) { sm.c.bm[q][2 * lane] = Pm0; sm.c.ns[q][2 * lane] = Ps0; sm.c.nb[q][2 * lane] = Pb0; }
+    if (2 * lane + 1 < nch) { sm.c.bm[q][2 * lane + 1] = Pm1; sm.c.ns[q][2 * lane + 1] = Ps1; sm.c.nb[q][2 * lane + 1] = Pb1; }
+    if (lane == 0) sm.sel[q].cstar = cross;
+  }
+  __syncthreads();
+
+  // ---- pass 4: ordered selection; positions above b* at [0, n_sure), taken bin-b* positions after them
+  {
+    int cs[4], nsure[4];
+    double ru[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      cs[i] = sm.sel[4 * row + i].cstar;
+      nsure[i] = sm.sel[4 * row + i].n_sure;
+      ru[i] = sm.sel[4 * row + i].r_u;
+    }
+    int rs[4], rb[4];
+    unsigned long long rm[4];
+    int cur = 0;
+    const unsigned below = (1u << col) - 1u;
+    sweep([&](long long n0, const f32x4_t &d) {
+            const long long n = n0 + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int q = 4 * row + i;
+              const bool ok = qv[i] && n <= mq[i];
+              const float s = d[i];
+              const int cell = score_cell(s);
+              const int j = min(cq[i] - cell, kBins - 1);
+              const bool sure = ok && j < bs[i];
+              const bool bnd = ok && !allq[i] && j == bs[i];
+              bool take = bnd && cur < cs[i];
+              if (cur == cs[i]) {                           // row-uniform: the crossing chunk of query q
+                const uint32_t w = bnd ? cell_weight(s, cell) : 0u;
+                const uint32_t inc = row_incl_scan_u32(w);
+                const unsigned long long pre = (unsigned long long)sm.c.bm[q][cur] + rm[i] + (inc - w);
+                take = bnd && (double)pre < ru[i];
+                rm[i] += __shfl(inc, (lane & ~15) + 15);
+              }
+              const unsigned long long bsure = __ballot(sure), btake = __ballot(take);
+              const unsigned rsure = (unsigned)(bsure >> (16 * row)) & 0xffffu;
+              const unsigned rtake = (unsigned)(btake >> (16 * row)) & 0xffffu;
+              const size_t ul = (size_t)br * nqc + (qi0 - i0) + q;         // chunk-local unit
+              const size_t ug = (size_t)br * g.nq + qi0 + q;                // global unit
+              if (sure) {
+                const long long at = (long long)sm.c.ns[q][cur] + rs[i] + __popc(rsure & below);
+                idx_ws[ul * capw + at] = (int)n;
+                if (idx && at < cap) idx[ug * cap + at] = (int)n;
+              }
+              if (take) {
+                const long long at = (long long)nsure[i] + sm.c.nb[q][cur] + rb[i] + __popc(rtake & below);
+                if (at < capw) idx_ws[ul * capw + at] = (int)n;
+                if (idx && at < cap) idx[ug * cap + at] = (int)n;
+              }
+              rs[i] += __popc(rsure);
+              rb[i] += __popc(rtake);
+            }
+          },
+          [&](int ch) {
+            cur = ch;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              rs[i] = rb[i] = 0;
+              rm[i] = 0ull;
+            }
+          },
+          [&](int ch) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int q = 4 * row + i;
+              if (qv[i] && ch == cs[i] && col == 0) {
+                const int c_ = nsure[i] + sm.c.nb[q][ch] + rb[i];
+                cnt_ws[(size_t)br * nqc + (qi0 - i0) + q] = c_;
+                if (count) count[(size_t)br * g.nq + qi0 + q] = c_;
+              }
+            }
+          });
+  }
+  // queries without a crossing chunk: every position (p >= 1 or b* the clamp
+  // bin) -- the residual is positive otherwise, so the first chunk holding a
+  // bin-b* position always crosses
+  if (tid < nvalid && sm.sel[tid].cstar < 0) {
+    const int c_ = sm.sel[tid].n_sure;
+    cnt_ws[(size_t)br * nqc + (qi0 - i0) + tid] = c_;
+    if (count) count[(size_t)br * g.nq + qi0 + tid] = c_;
+  }
+}
+
+// Query preparation for every (b, r, i) of the chunk: exact indexer query and
+// the rotated, 1/sqrt(D)-scaled attention query (fp64 angles).
+struct PrepShared {
+  double q[kR];
+  double qtmp[16][kR];
+  double2 rope[kD / 2];
+};
+
+__global__ __launch_bounds__(kWG) void pf_qprep_kernel(Geo g, const rtp_bf16 *__restrict__ q_pre,
+                                                       const rtp_bf16 *__restrict__ w_q) {
+  __shared__ PrepShared sm;
+  const int unit = blockIdx.x;
+  const int i = unit % g.nq, br = unit / g.nq, r = br % g.Hr, b = br / g.Hr;
+  const long long m = g.N - g.nq + i;
+  const rtp_bf16 *q_row = q_pre + (((size_t)b * g.Hq + g.rhead[r]) * g.nq + i) * kD;
+  QPrep *qp = g.qprep + unit;
+  project_query(q_row, w_q + (size_t)r * kD * kR, sm.q, sm.qtmp);
+  if (threadIdx.x < kR) qp->qi[threadIdx.x] = sm.q[threadIdx.x];
+  rope_table(m, g.theta, sm.rope);
+  rotate_query(q_row, sm.rope, 0.08838834764831845f, qp->qrot);
+}
+
+constexpr int kPfSplit = 8;     // split-K workgroups per query in the prefill attention
+
+struct PfAttnShared {
+  float q[kD];
+  int list[1024];
+  int flag;
+  Partial extra;
+  AttnShared at;
+  CombineShared cb;
+};
+
+// Attention of the chunk's retrieval queries over their selected rows:
+// kPfSplit workgroups per query, split-K states combined by the last one.
+__global__ __launch_bounds__(kWG) void pf_attn_kernel(Geo g, int i0, int nqc, const rtp_bf16 *__restrict__ kc,
+                                                      const rtp_bf16 *__restrict__ vc,
+                                                      const int32_t *__restrict__ idx_ws, long long capw,
+                                                      const int32_t *__restrict__ cnt_ws, float *__restrict__ out) {
+  __shared__ PfAttnShared sm;
+  const int tid = threadIdx.x;
+  const int ul = blockIdx.x / kPfSplit, sp = blockIdx.x % kPfSplit;
+  const int ii = ul % nqc, br = ul / nqc, r = br % g.Hr, b = br / g.Hr;
+  const int i = i0 + ii;
+  const int hq = g.rhead[r], kvg = hq / g.G;
+  const size_t ug = (size_t)br * g.nq + i;
+  if (tid < kD) sm.q[tid] = g.qprep[ug].qrot[tid];
+  long long cnt = cnt_ws[ul];
+  cnt = cnt < 0 ? 0 : (cnt > capw ? capw : cnt);
+  const long long per = (cnt + kPfSplit - 1) / kPfSplit;
+  const long long a0 = (long long)sp * per;
+  const long long a1 = a0 + per < cnt ? a0 + per : cnt;
+  const size_t cbase = ((size_t)b * g.Hkv + kvg) * g.Ncap * kD;
+  const int32_t *list = idx_ws + (size_t)ul * capw;
+  float run_m = -INFINITY, run_l = 0.f, run_o = 0.f;
+  for (long long s0 = a0; s0 < a1; s0 += 1024) {
+    const int n = (int)(a1 - s0 < 1024 ? a1 - s0 : 1024);
+    __syncthreads();
+    for (int x = tid; x < n; x += kWG) sm.list[x] = list[s0 + x];
+    __syncthreads();
+    attend_rows(sm.q, sm.list, n, g.N - g.nq + i + 1, kc + cbase, vc + cbase, &sm.extra, &sm.at);
+    if (tid < kD) merge_state(run_m, run_l, &run_o, sm.extra.m, sm.extra.l, &sm.extra.o[tid], 1);
+  }
+  Partial *dst = g.part + (size_t)ul * kPfSplit + sp;
+  if (tid < kD) {
+    st_coherent(&dst->o[tid], run_o);
+    if (tid == 0) {
+      st_coherent(&dst->m, run_m);
+      st_coherent(&dst->l, run_l);
+    }
+  }
+  if (!arrive_last(g.ctr_fin + ul, (uint32_t)kPfSplit, &sm.flag)) return;
+  combine_partials(g.part + (size_t)ul * kPfSplit, kPfSplit, out + (((size_t)b * g.Hq + hq) * g.nq + i) * kD, &sm.cb);
+}
+
+}  // namespace
+
+int pf_split() { return kPfSplit; }
+
+int launch_pf_qprep(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, hipStream_t s) {
+  if (g.units == 0) return RTP_OK;
+  hipLaunchKernelGGL(pf_qprep_kernel, dim3((unsigned)g.units), dim3(kWG), 0, s, g, q_pre, w_q);
+  return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ERR_HIP;
+}
+
+int launch_pf_select(const Geo &g, const rtp_bf16 *k_idx, int i0, int nqc, int32_t *idx_ws, long long capw,
+                     int32_t *cnt_ws, int32_t *idx, int32_t *count, long long cap, hipStream_t s) {
+  if (g.units == 0 || nqc <= 0) return RTP_OK;
+  const long long span = g.N;                            // longest prefix
+  long long kc = (span + kMaxCh - 1) / kMaxCh;
+  kc = (kc + 16 * kUnroll - 1) / (16 * kUnroll) * (16 * kUnroll);
+  if (kc < 1024) kc = 1024;
+  const int nblk = (nqc + kQB - 1) / kQB;
+  const long long grid = (long long)g.B * g.Hr * nblk;
+  hipLaunchKernelGGL(pf_select_kernel, dim3((unsigned)grid), dim3(kWG), 0, s, g, k_idx, i0, nqc, (int)kc, idx_ws, capw,
+                     cnt_ws, idx, count, cap);
+  return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ERR_HIP;
+}
+
+int launch_pf_attn(const Geo &g, int i0, int nqc, const rtp_bf16 *k, const rtp_bf16 *v, const int32_t *idx_ws,
+                   long long capw, const int32_t *cnt_ws, float *out, hipStream_t s) {
+  if (g.units == 0 || nqc <= 0) return RTP_OK;
+  const long long grid = (long long)g.B * g.Hr * nqc * kPfSplit;
+  hipLaunchKernelGGL(pf_attn_kernel, dim3((unsigned)grid), dim3(kWG), 0, s, g, i0, nqc, k, v, idx_ws, capw, cnt_ws,
+                     out);
+  return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ERR_HIP;
+}
+
+}  // namespace rtp

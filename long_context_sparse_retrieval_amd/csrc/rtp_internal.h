@@ -86,6 +86,9 @@ struct Geo {
   uint32_t *cmax;        // [units] encoded max cell (0 = none)
   uint32_t *cmin;        // [units] encoded min base cell (0 = none)
   uint32_t *ctr_fin;     // [units]
+  int pf_qch;            // chunked prefill: queries per selection chunk
+  int32_t *pf_idx;       // [B * Hr * pf_qch][N] selected positions of one chunk (shares the codes' space)
+  int32_t *pf_cnt;       // [B * Hr * pf_qch]
   uint32_t *ctr_swa;     // [swa_units * swa_hb]
 };
 
@@ -245,5 +248,14 @@ int launch_finish(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, cons
 int launch_sparse_attn(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *k, const rtp_bf16 *v,
                        const int32_t *idx, const int32_t *count, long long cap, float *out, hipStream_t s);
 int launch_fill_zero(void *ws, size_t bytes, hipStream_t s);
+// Chunked prefill (nq > 1): query preparation for every retrieval query; the
+// matrix-core selection of the queries [i0, i0 + nqc) into idx_ws / cnt_ws
+// (and optionally idx / count); attention of those queries over idx_ws.
+int launch_pf_qprep(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, hipStream_t s);
+int launch_pf_select(const Geo &g, const rtp_bf16 *k_idx, int i0, int nqc, int32_t *idx_ws, long long capw,
+                     int32_t *cnt_ws, int32_t *idx, int32_t *count, long long cap, hipStream_t s);
+int launch_pf_attn(const Geo &g, int i0, int nqc, const rtp_bf16 *k, const rtp_bf16 *v, const int32_t *idx_ws,
+                   long long capw, const int32_t *cnt_ws, float *out, hipStream_t s);
+int pf_split();
 
 }  // namespace rtp

@@ -1,4 +1,4 @@
-"""Write gen/query_scales.json: per-query scales of the 128K and 1M decode workloads.
+"""Write gen/query_scales.json: query scales of the 128K / 1M decode and the chunked-prefill workloads.
 
 TEST INFRASTRUCTURE (calls only the oracle and the input generator).
 
@@ -11,7 +11,11 @@ about 500 tokens (concentrated class) or 2500 tokens (diffuse class).  The
 scale is found by bisection on log s; the set size is non-increasing in s up
 to bf16 rounding of q.
 
-Usage:  python oracle/calibrate_queries.py [cfg ...]     (default: 3 4)
+The chunked-prefill workload (config 5) plants a concentrated and a diffuse
+topic per head; all its queries of one topic share a scale, found the same
+way on the last query of that topic (the longest prefix).
+
+Usage:  python oracle/calibrate_queries.py [cfg ...]     (default: 3 4 5)
 """
 import json
 import math
@@ -29,7 +33,58 @@ from gen.workload import _SCALES_FILE, default_seed, f32_to_bf16_bits, scale_key
 import oracle as O  # noqa: E402
 
 
+def bisect_scale(count, target, iters):
+    """Scale s with count(s) closest to target; count is non-increasing in s."""
+    lo, hi = math.log(1e-3), math.log(1e2)
+    best = None
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        c = count(math.exp(mid))
+        if best is None or abs(c - target) < abs(best[1] - target):
+            best = (math.exp(mid), c)
+        if c > target:
+            lo = mid
+        else:
+            hi = mid
+        if c == target:
+            break
+    s = float(f"{best[0]:.9g}")
+    return s, count(s)
+
+
+def calibrate_topics(cfg: int, iters: int = 34):
+    spec = gen.spec_for(cfg)
+    seed = default_seed(cfg)
+    wl = gen.make_workload(spec, seed, scales={})
+    rheads = spec.retrieval_heads()
+    dirs = gen.workload.query_directions(wl.u, wl.topics, spec.topic_mix)
+    entries = []
+    for b in range(spec.B):
+        for r, h in enumerate(rheads):
+            g = h // spec.G
+            kidx = O.index_project(wl.k_pre[b, g], wl.w_k[r])
+            for tpc in (0, 1):
+                t0 = time.time()
+                i = spec.nq - 1 if (spec.nq - 1) % 2 == tpc else spec.nq - 2
+                m = spec.N - spec.nq + i
+                d = dirs[b, h, i]
+
+                def count(s):
+                    q = f32_to_bf16_bits((d * s).astype(np.float32))
+                    s_idx = O.indexer_logits(O.index_project(q, wl.w_q[r]), kidx[:m + 1])
+                    return len(O.topp_select(s_idx, spec.p)["sel"])
+
+                target = spec.budget_targets[tpc]
+                s, c = bisect_scale(count, target, iters)
+                entries.append([b, r, tpc, s, int(c)])
+                print(f"cfg{cfg} b={b} r={r} topic={tpc} target={target} scale={s:.5g} count={c} "
+                      f"({time.time() - t0:.1f}s)", flush=True)
+    return scale_key(spec, seed), entries
+
+
 def calibrate(cfg: int, iters: int = 34):
+    if gen.spec_for(cfg).needle_mode == "topics":
+        return calibrate_topics(cfg, iters)
     spec = gen.spec_for(cfg)
     seed = default_seed(cfg)
     wl = gen.make_workload(spec, seed, scales={})
@@ -83,4 +138,4 @@ def main(cfgs):
 
 
 if __name__ == "__main__":
-    main([int(a) for a in sys.argv[1:]] or [3, 4])
+    main([int(a) for a in sys.argv[1:]] or [3, 4, 5])

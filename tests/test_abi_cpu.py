@@ -92,10 +92,12 @@ def test_calls_reject_before_launch():
     assert lib.rtp_workspace_init(None, 16, None) == -1
     # misaligned workspace
     assert lib.rtp_swa_attn(L, fake, fake, fake, fake, fake + 8, need, None) == -1
-    # chunked prefill is not fused in this build
+    # chunked prefill (nq > 1) is validated the same way before any launch
     lay2 = _layer(nq=4)
-    assert lib.rtp_decode_step(ctypes.byref(lay2.c()), fake, fake, fake, fake, fake, fake, None, None, 0, fake,
-                               rtp.workspace_bytes(lay2), None, None) == -4
+    L2 = ctypes.byref(lay2.c())
+    need2 = rtp.workspace_bytes(lay2)
+    assert lib.rtp_decode_step(L2, fake, fake, fake, fake, fake, fake, None, None, 0, fake, need2 - 1, None, None) == -3
+    assert lib.rtp_decode_step(L2, fake, None, fake, fake, fake, fake, None, None, 0, fake, need2, None, None) == -1
 
 
 def test_binding_checks_tensors_without_gpu():

@@ -84,3 +84,52 @@ def test_decode_step_full_size_sampled(case):
                                   f"{case} b{b} r{r}"))
     say(f"{case}: sampled sets {verdicts.count('exact')} exact, {verdicts.count('tolerated')} tolerated; "
         f"{len(res['out'])} head outputs checked")
+
+
+def test_prefill_full_size_sampled():
+    """4096 causal queries x 4 heads against a 128K cache (the chunked-prefill workload)."""
+    spec = gen.spec_for(5)
+    say(f"full-size prefill: {spec.name} N={spec.N} nq={spec.nq} Hr={spec.Hr}")
+    wl = gen.make_workload(spec, gen.workload.default_seed(5))
+    lay = layer_of(spec, rtp)
+    k_pre = dev_bf16(wl.k_pre)
+    k = rtp.rope_keys(lay, k_pre)
+    k_idx = rtp.index_keys(lay, k_pre, dev_bf16(wl.w_k))
+    del k_pre
+    v = dev_bf16(wl.v)
+    ws = rtp.workspace(lay)
+    cap = 8192
+    idx = torch.full((spec.B, spec.Hr, spec.nq, cap), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((spec.B, spec.Hr, spec.nq), dtype=torch.int32, device="cuda")
+    q, wq = dev_bf16(wl.q_pre), dev_bf16(wl.w_q)
+    rtp.decode_step(lay, q, wq, k_idx, k, v, ws, idx=idx, count=cnt)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    out = rtp.decode_step(lay, q, wq, k_idx, k, v, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    out, idx, cnt = out.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+    c = cnt.ravel()
+    say(f"full-size prefill: step {e0.elapsed_time(e1):.2f} ms; |S| min {c.min()} median {int(np.median(c))} "
+        f"max {c.max()}")
+    for r in range(spec.Hr):
+        for i in range(spec.nq):
+            m = spec.N - spec.nq + i
+            ci = int(cnt[0, r, i])
+            assert 1 <= ci <= m + 1, f"r{r} i{i}: count {ci}"
+            if ci <= cap:
+                got = idx[0, r, i, :ci]
+                assert np.all((got >= 0) & (got <= m)), f"r{r} i{i}: position out of range"
+    assert np.all(np.isfinite(out)), "non-finite output"
+    del k, v, k_idx
+    torch.cuda.empty_cache()
+
+    queries = [0, 1, spec.nq // 2, spec.nq // 2 + 1, spec.nq - 2, spec.nq - 1]
+    kc, ki = O.build_caches(wl)
+    res = O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
+                        n_sink=spec.n_sink, rope_base=spec.rope_theta, queries=queries, want_logits=True)
+    for (b, h, i), ref in res["out"].items():
+        check_output(out[b, h, i], ref, f"prefill b{b} h{h} i{i}")
+    verdicts = [check_set(idx[b, r, i], int(cnt[b, r, i]), cap, t, res["logits"][(b, r, i)], spec.p,
+                          f"prefill b{b} r{r} i{i}") for (b, r, i), t in res["topp"].items()]
+    say(f"full-size prefill: sampled sets {verdicts.count('exact')} exact, {verdicts.count('tolerated')} tolerated")

@@ -259,3 +259,50 @@ def test_decode_step_matches_oracle(case):
                                   f"{case} b{b} r{r}"))
     say(f"{case}: sets {verdicts.count('exact')} exact, {verdicts.count('tolerated')} tolerated; "
         f"|S| = {sorted(int(c) for c in cnt.ravel())}")
+
+
+# ----------------------------------------------------------------------------- chunked prefill (nq > 1)
+# name -> (config, spec overrides, query scales (None: 3 / 4.5 per topic), RTP_PF_QCH override)
+PREFILL_CASES = {
+    "pf-3k-64q": (5, dict(N=3000, nq=64, diffuse=(200, 0.5)), None, None),
+    "pf-ragged-37q": (5, dict(N=2500, nq=37, diffuse=(150, 0.5)), None, None),
+    "pf-p1": (5, dict(N=1200, nq=20, p=1.0, diffuse=(100, 0.5)), None, None),
+    "pf-every-position": (5, dict(N=48, nq=48, conc=(0, 4.0), diffuse=(0, 0.5)), None, None),
+    "pf-query-chunks": (5, dict(N=5000, nq=80, diffuse=(300, 0.5)), None, "16"),
+    "pf-layer-with-local-heads": (2, dict(B=2, N=3000, nq=24, n_needles=16, window=512), {}, None),
+}
+
+
+def _prefill_scales(spec, given):
+    if given is not None:
+        return given
+    return {(b, r, t): (3.0 if t == 0 else 4.5) for b in range(spec.B) for r in range(spec.Hr) for t in (0, 1)}
+
+
+@pytest.mark.parametrize("case", list(PREFILL_CASES))
+def test_prefill_step_matches_oracle(case, monkeypatch):
+    cfg, over, scales, qch = PREFILL_CASES[case]
+    spec = gen.spec_for(cfg, query_scale="unit", **over)
+    say(f"prefill {case}: {spec}")
+    if qch is not None:
+        monkeypatch.setenv("RTP_PF_QCH", qch)
+    wl = gen.make_workload(spec, 300 + cfg, scales=_prefill_scales(spec, scales))
+    kc, ki = O.build_caches(wl)
+    lay = layer_of(spec, rtp)
+    ws = rtp.workspace(lay)
+    cap = spec.N
+    idx = torch.full((spec.B, spec.Hr, spec.nq, cap), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((spec.B, spec.Hr, spec.nq), dtype=torch.int32, device="cuda")
+    args = (dev_bf16(wl.q_pre), dev_bf16(wl.w_q), dev_bf16(ki), dev_bf16(kc), dev_bf16(wl.v))
+    out = rtp.decode_step(lay, *args, ws, idx=idx, count=cnt).cpu().numpy()
+    out2 = rtp.decode_step(lay, *args, ws).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.array_equal(out, out2), "two runs differ (non-deterministic)"
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    res = O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
+                        n_sink=spec.n_sink, rope_base=spec.rope_theta, want_logits=True)
+    for (b, h, i), ref in res["out"].items():
+        check_output(out[b, h, i], ref, f"{case} b{b} h{h} i{i}")
+    verdicts = [check_set(idx[b, r, i], int(cnt[b, r, i]), cap, t, res["logits"][(b, r, i)], spec.p,
+                          f"{case} b{b} r{r} i{i}") for (b, r, i), t in res["topp"].items()]
+    say(f"{case}: sets {verdicts.count('exact')} exact, {verdicts.count('tolerated')} tolerated")
