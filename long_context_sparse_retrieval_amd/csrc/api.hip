@@ -127,7 +127,7 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
   size_t pf_idx_bytes = 0, pf_cnt_bytes = 0;
   if (g.nq > 1 && g.units > 0) {
     const long long per_q = (long long)g.B * g.Hr * g.N * 4;      // bytes of positions per query index
-    long long qch = (1ll << 30) / per_q;                            // about 1 GiB of positions per chunk
+    long long qch = (8ll << 30) / per_q;                            // up to 8 GiB of positions per chunk
     qch = qch / 16 * 16;
     if (const char *env = getenv("RTP_PF_QCH")) {          // tuning / test override
       const long long v = atoll(env);

@@ -10,7 +10,9 @@
 // Design for gfx950.  One selection workgroup owns 16 queries of one head and
 // their whole prefixes, so each query's histogram lives in LDS and never has
 // to be merged across workgroups.  The K = 16 contraction is one
-// v_mfma_f32_16x16x16_bf16 per 16 keys (16 queries x 16 keys per wave); the
+// v_mfma_f32_16x16x16_bf16 per 16 keys (16 keys x 16 queries per wave; each
+// lane gets four keys of one query, so a row of 16 lanes updates 16 different
+// query histograms and LDS atomics rarely collide); the
 // products of two bf16 values are exact in fp32, only the order of the 16-term
 // sum is the matrix core's.  The logits are never stored: four passes
 // recompute them from the indexer keys (4 MiB per head at 128K, resident in
@@ -30,43 +32,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kQB = 16;         // queries per selection workgroup (the matrix-core M dimension)
 constexpr int kMaxCh = 128;     // key chunks per query
 constexpr int kUnroll = 8;      // 16-key blocks whose loads are issued together
-
-// ------------------------------------------------------------------ row (16-lane) helpers
-template <int CTRL, int RMASK = 0xF, int BMASK = 0xF>
-__device__ __forceinline__ int dppi(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, RMASK, BMASK, true);
-}
-// sum over the 16 lanes of a row, every lane receives it
-__device__ __forceinline__ int row_sum_i(int v) {
-  v += dppi<0xB1>(v);
-  v += dppi<0x4E>(v);
-  v += dppi<0x141>(v);
-  v += dppi<0x140>(v);
-  return v;
-}
-__device__ __forceinline__ float row_max_f(float v) {
-  v = fmaxf(v, __int_as_float(dppi<0xB1>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dppi<0x4E>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dppi<0x141>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dppi<0x140>(__float_as_int(v))));
-  return v;
-}
-// inclusive prefix over the lanes of a row (row shifts 1-3, then 4 and 8 on the upper banks)
-__device__ __forceinline__ uint32_t row_incl_scan_u32(uint32_t x) {
-  const int xi = (int)x;
-  int v = xi;
-  v += dppi<0x111>(xi);
-  v += dppi<0x112>(xi);
-  v += dppi<0x113>(xi);
-  v += dppi<0x114, 0xF, 0xE>(v);
-  v += dppi<0x118, 0xF, 0xC>(v);
-  return (uint32_t)v;
-}
-__device__ __forceinline__ unsigned long long row_sum_u64(unsigned long long v) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
-  return v;
-}
 
 // Per query of a selection workgroup.
 struct PfSel {
@@ -113,31 +78,26 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
   const long long m_last = mpos0 + qi0 + nvalid - 1;
   const uint2 *keys = reinterpret_cast<const uint2 *>(k_idx + ((size_t)b * g.Hr + r) * g.Ncap * kR);
 
-  // A operand: lane holds q_idx[query col][dims 4 row .. 4 row + 3] as bf16
-  bf16x4_t a;
+  // Matrix-core operands: A = 16 keys x 16 dims (lane: key col, dims 4 row ..
+  // 4 row + 3), B = 16 dims x 16 queries (lane: query col, the same dims), so
+  // lane (row, col) receives the scores of query col against keys 4 row .. 4 row
+  // + 3 of the block: the 16 lanes of a row serve 16 different queries.
+  bf16x4_t bq;
+  const int qc = col;                                    // this lane's query
+  const bool qv = qc < nvalid;
   {
-    const int q = col;
-    const bool ok = q < nvalid;
-    const QPrep *qp = g.qprep + ((size_t)br * g.nq + qi0 + (ok ? q : 0));
+    const QPrep *qp = g.qprep + ((size_t)br * g.nq + qi0 + (qv ? qc : 0));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float f = ok ? (float)qp->qi[4 * row + j] : 0.f;
-      a[j] = (short)(__float_as_uint(f) >> 16);         // the values are bf16, so exact
+      const float f = qv ? (float)qp->qi[4 * row + j] : 0.f;
+      bq[j] = (short)(__float_as_uint(f) >> 16);        // the values are bf16, so exact
     }
   }
-  // this lane's four queries (rows of the MFMA result) and their positions
-  long long mq[4];
-  bool qv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = 4 * row + i;
-    qv[i] = q < nvalid;
-    mq[i] = mpos0 + qi0 + q;
-  }
+  const long long mq = mpos0 + qi0 + qc;                 // position of this lane's query
   const int nch = (int)((m_last + 1 + kc - 1) / kc);
 
   // Runs body(n0, d) for every 16-key block of the chunks this wave owns, in
-  // position order within a chunk; chunk_end(ch) after each chunk.
+  // position order within a chunk; d[i] = score of key n0 + 4 row + i.
   auto sweep = [&](auto &&body, auto &&chunk_begin, auto &&chunk_end) {
     for (int ch = wv; ch < nch; ch += 4) {
       chunk_begin(ch);
@@ -154,35 +114,48 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
           if (n0 + 16 * u >= k1) break;                   // wave-uniform
-          bf16x4_t bv;
-          bv[0] = (short)(kv[u].x & 0xffffu);
-          bv[1] = (short)(kv[u].x >> 16);
-          bv[2] = (short)(kv[u].y & 0xffffu);
-          bv[3] = (short)(kv[u].y >> 16);
+          bf16x4_t ak;
+          ak[0] = (short)(kv[u].x & 0xffffu);
+          ak[1] = (short)(kv[u].x >> 16);
+          ak[2] = (short)(kv[u].y & 0xffffu);
+          ak[3] = (short)(kv[u].y >> 16);
           const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-          const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bv, zero, 0, 0, 0);
-          body(n0 + 16 * u, d);
+          const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, bq, zero, 0, 0, 0);
+          body(n0 + 16 * u + 4 * row, d);
         }
       }
       chunk_end(ch);
     }
   };
   auto nop = [](int) {};
+  // sum over the four lanes of a column (the same query)
+  auto col_sum_i = [](int v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+  };
+  // exclusive prefix over the rows of a column, and the column total
+  auto col_scan = [&](unsigned long long v, unsigned long long &total) {
+    unsigned long long x = v;
+    const unsigned long long t1 = __shfl_up(x, 16);
+    if (row >= 1) x += t1;
+    const unsigned long long t2 = __shfl_up(x, 32);
+    if (row >= 2) x += t2;
+    total = __shfl(x, 48 + col);
+    return x - v;
+  };
 
   // ---- pass 1: per-query maximum
-  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  sweep([&](long long n0, const f32x4_t &d) {
-          const long long n = n0 + col;
+  float mx = -INFINITY;
+  sweep([&](long long nb0, const f32x4_t &d) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (qv[i] && n <= mq[i]) mx[i] = fmaxf(mx[i], d[i]);
+            if (qv && nb0 + i <= mq) mx = fmaxf(mx, d[i]);
         },
         nop, nop);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float v = row_max_f(mx[i]);
-    if (col == 0) sm.wmax[wv][4 * row + i] = v;
-  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (row == 0) sm.wmax[wv][qc] = mx;
   for (int x = tid; x < kQB * kBins; x += kWG) {
     (&sm.h.mass[0][0])[x] = 0ull;
     (&sm.h.cnt[0][0])[x] = 0u;
@@ -194,28 +167,25 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
     sm.sel[tid].valid = tid < nvalid ? 1 : 0;
   }
   __syncthreads();
-  int cq[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) cq[i] = sm.sel[4 * row + i].c;
+  const int cq = sm.sel[qc].c;
 
   // ---- pass 2: exact 256-bin histogram per query (bins relative to the query's max cell)
-  sweep([&](long long n0, const f32x4_t &d) {
-          const long long n = n0 + col;
+  sweep([&](long long nb0, const f32x4_t &d) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            if (!(qv[i] && n <= mq[i])) continue;
+            if (!(qv && nb0 + i <= mq)) continue;
             const float s = d[i];
             const int cell = score_cell(s);
-            int j = cq[i] - cell;
+            int j = cq - cell;
             uint32_t w;
             if (j >= kBins - 1) {
               j = kBins - 1;
-              w = cell_weight(s, cq[i] - (kBins - 1));
+              w = cell_weight(s, cq - (kBins - 1));
             } else {
               w = cell_weight(s, cell);
             }
-            atomicAdd(&sm.h.mass[4 * row + i][j], (unsigned long long)w);
-            atomicAdd(&sm.h.cnt[4 * row + i][j], 1u);
+            atomicAdd(&sm.h.mass[qc][j], (unsigned long long)w);
+            atomicAdd(&sm.h.cnt[qc][j], 1u);
           }
         },
         nop, nop);
@@ -233,8 +203,7 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
       W[k] = (double)sm.h.mass[q][j] * 0x1p-23 * exp(-(double)j * 0.125);
       loc += W[k];
     }
-    // wave exclusive scan of the lane sums (fixed order)
-    double incl = loc;
+    double incl = loc;                                    // wave inclusive scan (fixed order)
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const double y = __shfl_up(incl, off);
@@ -277,51 +246,40 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
     (&sm.c.ns[0][0])[x] = 0;
     (&sm.c.nb[0][0])[x] = 0;
   }
-  int bs[4], allq[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bs[i] = sm.sel[4 * row + i].bstar;
-    allq[i] = sm.sel[4 * row + i].all;
-  }
+  const int bs = sm.sel[qc].bstar, allq = sm.sel[qc].all;
   __syncthreads();
 
   // ---- pass 3: per chunk, positions above b*, positions in b* and their mass
   {
-    int ns[4], nb[4];
-    unsigned long long bm[4];
-    sweep([&](long long n0, const f32x4_t &d) {
-            const long long n = n0 + col;
+    int ns = 0, nbb = 0;
+    unsigned long long bm = 0;
+    sweep([&](long long nb0, const f32x4_t &d) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              if (!(qv[i] && n <= mq[i])) continue;
+              if (!(qv && nb0 + i <= mq)) continue;
               const float s = d[i];
               const int cell = score_cell(s);
-              const int j = min(cq[i] - cell, kBins - 1);
-              if (j < bs[i]) {
-                ++ns[i];
-              } else if (!allq[i] && j == bs[i]) {
-                ++nb[i];
-                bm[i] += cell_weight(s, cell);
+              const int j = min(cq - cell, kBins - 1);
+              if (j < bs) {
+                ++ns;
+              } else if (!allq && j == bs) {
+                ++nbb;
+                bm += cell_weight(s, cell);
               }
             }
           },
           [&](int) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              ns[i] = nb[i] = 0;
-              bm[i] = 0ull;
-            }
+            ns = nbb = 0;
+            bm = 0ull;
           },
           [&](int ch) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int a1 = row_sum_i(ns[i]), a2 = row_sum_i(nb[i]);
-              const unsigned long long a3 = row_sum_u64(bm[i]);
-              if (col == 0) {
-                sm.c.ns[4 * row + i][ch] = a1;
-                sm.c.nb[4 * row + i][ch] = a2;
-                sm.c.bm[4 * row + i][ch] = a3;
-              }
+            const int a1 = col_sum_i(ns), a2 = col_sum_i(nbb);
+            unsigned long long a3 = bm + __shfl_xor(bm, 16);
+            a3 += __shfl_xor(a3, 32);
+            if (row == 0) {
+              sm.c.ns[qc][ch] = a1;
+              sm.c.nb[qc][ch] = a2;
+              sm.c.bm[qc][ch] = a3;
             }
           });
   }
@@ -365,73 +323,73 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
 
   // ---- pass 4: ordered selection; positions above b* at [0, n_sure), taken bin-b* positions after them
   {
-    int cs[4], nsure[4];
-    double ru[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      cs[i] = sm.sel[4 * row + i].cstar;
-      nsure[i] = sm.sel[4 * row + i].n_sure;
-      ru[i] = sm.sel[4 * row + i].r_u;
-    }
-    int rs[4], rb[4];
-    unsigned long long rm[4];
-    int cur = 0;
-    const unsigned below = (1u << col) - 1u;
-    sweep([&](long long n0, const f32x4_t &d) {
-            const long long n = n0 + col;
+    const int cs = sm.sel[qc].cstar, nsure = sm.sel[qc].n_sure;
+    const double ru = sm.sel[qc].r_u;
+    const size_t ul = (size_t)br * nqc + (qi0 - i0) + qc;    // chunk-local unit of this lane's query
+    const size_t ug = (size_t)br * g.nq + qi0 + qc;           // global unit
+    int rs = 0, rb = 0, cur = 0;
+    unsigned long long rm = 0;
+    sweep([&](long long nb0, const f32x4_t &d) {
+            bool sure[4], bnd[4];
+            uint32_t w[4];
+            int ls = 0, lt = 0;
+            uint32_t lw = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int q = 4 * row + i;
-              const bool ok = qv[i] && n <= mq[i];
+              const bool ok = qv && nb0 + i <= mq;
               const float s = d[i];
               const int cell = score_cell(s);
-              const int j = min(cq[i] - cell, kBins - 1);
-              const bool sure = ok && j < bs[i];
-              const bool bnd = ok && !allq[i] && j == bs[i];
-              bool take = bnd && cur < cs[i];
-              if (cur == cs[i]) {                           // row-uniform: the crossing chunk of query q
-                const uint32_t w = bnd ? cell_weight(s, cell) : 0u;
-                const uint32_t inc = row_incl_scan_u32(w);
-                const unsigned long long pre = (unsigned long long)sm.c.bm[q][cur] + rm[i] + (inc - w);
-                take = bnd && (double)pre < ru[i];
-                rm[i] += __shfl(inc, (lane & ~15) + 15);
-              }
-              const unsigned long long bsure = __ballot(sure), btake = __ballot(take);
-              const unsigned rsure = (unsigned)(bsure >> (16 * row)) & 0xffffu;
-              const unsigned rtake = (unsigned)(btake >> (16 * row)) & 0xffffu;
-              const size_t ul = (size_t)br * nqc + (qi0 - i0) + q;         // chunk-local unit
-              const size_t ug = (size_t)br * g.nq + qi0 + q;                // global unit
-              if (sure) {
-                const long long at = (long long)sm.c.ns[q][cur] + rs[i] + __popc(rsure & below);
-                idx_ws[ul * capw + at] = (int)n;
-                if (idx && at < cap) idx[ug * cap + at] = (int)n;
-              }
-              if (take) {
-                const long long at = (long long)nsure[i] + sm.c.nb[q][cur] + rb[i] + __popc(rtake & below);
-                if (at < capw) idx_ws[ul * capw + at] = (int)n;
-                if (idx && at < cap) idx[ug * cap + at] = (int)n;
-              }
-              rs[i] += __popc(rsure);
-              rb[i] += __popc(rtake);
+              const int j = min(cq - cell, kBins - 1);
+              sure[i] = ok && j < bs;
+              bnd[i] = ok && !allq && j == bs;
+              w[i] = (bnd[i] && cur == cs) ? cell_weight(s, cell) : 0u;
+              ls += sure[i] ? 1 : 0;
+              lw += w[i];
             }
+            // ordered fill inside the crossing chunk: mass of the earlier bin-b* keys of the block
+            unsigned long long wtot;
+            const unsigned long long wpre = col_scan(lw, wtot);
+            unsigned long long acc = (unsigned long long)sm.c.bm[qc][cur] + rm + wpre;
+            bool take[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              take[i] = bnd[i] && (cur < cs || (cur == cs && (double)acc < ru));
+              acc += w[i];
+              lt += take[i] ? 1 : 0;
+            }
+            rm += wtot;
+            unsigned long long stot, ttot;
+            const unsigned long long spre = col_scan((unsigned long long)ls, stot);
+            const unsigned long long tpre = col_scan((unsigned long long)lt, ttot);
+            long long as = (long long)sm.c.ns[qc][cur] + rs + (long long)spre;
+            long long at = (long long)nsure + sm.c.nb[qc][cur] + rb + (long long)tpre;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int n = (int)(nb0 + i);
+              if (sure[i]) {
+                idx_ws[ul * capw + as] = n;
+                if (idx && as < cap) idx[ug * cap + as] = n;
+                ++as;
+              }
+              if (take[i]) {
+                if (at < capw) idx_ws[ul * capw + at] = n;
+                if (idx && at < cap) idx[ug * cap + at] = n;
+                ++at;
+              }
+            }
+            rs += (int)stot;
+            rb += (int)ttot;
           },
           [&](int ch) {
             cur = ch;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              rs[i] = rb[i] = 0;
-              rm[i] = 0ull;
-            }
+            rs = rb = 0;
+            rm = 0ull;
           },
           [&](int ch) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int q = 4 * row + i;
-              if (qv[i] && ch == cs[i] && col == 0) {
-                const int c_ = nsure[i] + sm.c.nb[q][ch] + rb[i];
-                cnt_ws[(size_t)br * nqc + (qi0 - i0) + q] = c_;
-                if (count) count[(size_t)br * g.nq + qi0 + q] = c_;
-              }
+            if (qv && ch == cs && row == 0) {
+              const int c_ = nsure + sm.c.nb[qc][ch] + rb;
+              cnt_ws[ul] = c_;
+              if (count) count[ug] = c_;
             }
           });
   }
