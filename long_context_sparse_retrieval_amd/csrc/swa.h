@@ -10,7 +10,8 @@
 // of window rows, so a K/V row is read once for all of them (GQA).  16 lanes
 // cover one 256-byte row (16 bytes each, coalesced); every lane group keeps
 // four rows in flight, so a 64-row chunk is requested in one round.  Chunk
-// states are combined by the last workgroup of each (sequence, group, query).
+// states are combined by the last workgroup of each (sequence, group, query),
+// one wave per head.
 #pragma once
 
 #include "block_util.h"
@@ -26,8 +27,18 @@ struct SwaShared {
   double2 rope[kD / 2];
   int heads[kSwaHeads];
   int flag;
-  CombineShared cb;
 };
+
+// The k-th local q head of KV group kvg (ascending head index), or -1.
+__device__ __forceinline__ int local_head(const Geo &g, int kvg, int k) {
+  int seen = 0;
+  for (int h = kvg * g.G; h < (kvg + 1) * g.G; ++h) {
+    if (!((g.lmask[h >> 5] >> (h & 31)) & 1u)) continue;
+    if (seen == k) return h;
+    ++seen;
+  }
+  return -1;
+}
 
 // Position of window row ri for a query at m: the sinks first, then the window.
 __device__ __forceinline__ long long swa_row(long long ri, long long lo, long long ns) {
@@ -77,25 +88,23 @@ __device__ __forceinline__ void swa_block(const Geo &g, long long x, const rtp_b
       vr[u] = *reinterpret_cast<const uint4 *>(vb + n * kD + sub * 8);
     }
   }
-  if (tid == 0) {
-    int cnt = 0, seen = 0;
-    for (int h = kvg * g.G; h < (kvg + 1) * g.G; ++h) {
-      if (!((g.lmask[h >> 5] >> (h & 31)) & 1u)) continue;
-      if (seen >= hb * kSwaHeads && cnt < kSwaHeads) sm.heads[cnt++] = h;
-      ++seen;
-    }
-    for (int c = cnt; c < kSwaHeads; ++c) sm.heads[c] = -1;
+  // every head's query in one round: thread (hh, t) loads and rotates channel
+  // pair t of the hh-th local head of this head block (threads 0..63 also
+  // build the RoPE table of position m)
+  const int hh_mine = tid >> 6, pt = tid & 63;
+  const int h_mine = local_head(g, kvg, hb * kSwaHeads + hh_mine);
+  uint32_t qw = 0;
+  if (h_mine >= 0)
+    qw = reinterpret_cast<const uint32_t *>(q_pre + (((size_t)b * g.Hq + h_mine) * g.nq + i) * kD)[pt];
+  rope_table(m, g.theta, sm.rope);       // ends with a barrier
+  {
+    const double a = (double)bf_lo(qw), c2 = (double)bf_hi(qw);
+    const double cs = sm.rope[pt].x, sn = sm.rope[pt].y;
+    sm.q[hh_mine][2 * pt] = h_mine >= 0 ? (float)(a * cs - c2 * sn) * kInvSqrtD : 0.f;
+    sm.q[hh_mine][2 * pt + 1] = h_mine >= 0 ? (float)(a * sn + c2 * cs) * kInvSqrtD : 0.f;
+    if (pt == 0) sm.heads[hh_mine] = h_mine;
   }
-  rope_table(m, g.theta, sm.rope);       // ends with a barrier (also publishes sm.heads)
-  for (int hh = 0; hh < kSwaHeads; ++hh) {
-    const int h = sm.heads[hh];
-    if (h >= 0) {
-      rotate_query(q_pre + (((size_t)b * g.Hq + h) * g.nq + i) * kD, sm.rope, kInvSqrtD, sm.q[hh]);
-    } else {
-      if (tid < kD) sm.q[hh][tid] = 0.f;
-      __syncthreads();
-    }
-  }
+  __syncthreads();
   float q[kSwaHeads][8];
 #pragma unroll
   for (int hh = 0; hh < kSwaHeads; ++hh)
@@ -188,12 +197,10 @@ __device__ __forceinline__ void swa_block(const Geo &g, long long x, const rtp_b
     }
   }
   if (!arrive_last(g.ctr_swa + unit * g.swa_hb + hb, (uint32_t)g.swa_nch, &sm.flag)) return;
-  for (int hh = 0; hh < kSwaHeads; ++hh) {
-    const int h = sm.heads[hh];
-    if (h < 0) continue;
-    combine_partials(parts + (size_t)hh * g.swa_nch, g.swa_nch, out + (((size_t)b * g.Hq + h) * g.nq + i) * kD,
-                     &sm.cb);
-  }
+  // wave hh combines head hh's chunk states (all heads in one round of loads)
+  const int h = sm.heads[wv];
+  if (h >= 0)
+    wave_combine(parts + (size_t)wv * g.swa_nch, g.swa_nch, out + (((size_t)b * g.Hq + h) * g.nq + i) * kD);
 }
 
 }  // namespace rtp
