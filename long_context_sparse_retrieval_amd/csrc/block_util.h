@@ -39,13 +39,31 @@ __device__ __forceinline__ V block_excl_scan(V v, V &total, V *s_buf) {
   return base + x - v;
 }
 
+// Wave-wide reduction of a 32-bit value with DPP: within each row of 16
+// (quad swaps, half-row and row mirrors), then row 0 into row 1 and row 2 into
+// row 3 (row broadcast 15), then rows 0-1 into rows 2-3 (row broadcast 31);
+// lane 63 ends with the result.  Lanes whose source is absent keep their value.
+template <int CTRL, int RMASK, typename V>
+__device__ __forceinline__ V dpp_keep(V x) {
+  const int xi = __builtin_bit_cast(int, x);
+  return __builtin_bit_cast(V, __builtin_amdgcn_update_dpp(xi, xi, CTRL, RMASK, 0xF, false));
+}
+
+template <typename V, typename Op>
+__device__ __forceinline__ V wave_reduce(V v, Op op) {
+  v = op(v, dpp_keep<0xB1, 0xF>(v));
+  v = op(v, dpp_keep<0x4E, 0xF>(v));
+  v = op(v, dpp_keep<0x141, 0xF>(v));
+  v = op(v, dpp_keep<0x140, 0xF>(v));
+  v = op(v, dpp_keep<0x142, 0xA>(v));
+  v = op(v, dpp_keep<0x143, 0xC>(v));
+  return __builtin_bit_cast(V, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 template <typename V>
 __device__ __forceinline__ V block_max(V v, V *s_buf) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const V y = __shfl_xor(v, off);
-    v = y > v ? y : v;
-  }
+  static_assert(sizeof(V) == 4, "32-bit values");
+  v = wave_reduce(v, [](V a, V b) { return b > a ? b : a; });
   if ((threadIdx.x & 63) == 0) s_buf[threadIdx.x >> 6] = v;
   __syncthreads();
   V r = s_buf[0];
@@ -57,11 +75,8 @@ __device__ __forceinline__ V block_max(V v, V *s_buf) {
 
 template <typename V>
 __device__ __forceinline__ V block_min(V v, V *s_buf) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const V y = __shfl_xor(v, off);
-    v = y < v ? y : v;
-  }
+  static_assert(sizeof(V) == 4, "32-bit values");
+  v = wave_reduce(v, [](V a, V b) { return b < a ? b : a; });
   if ((threadIdx.x & 63) == 0) s_buf[threadIdx.x >> 6] = v;
   __syncthreads();
   V r = s_buf[0];
@@ -69,6 +84,20 @@ __device__ __forceinline__ V block_min(V v, V *s_buf) {
   for (int i = 1; i < 4; ++i) r = s_buf[i] < r ? s_buf[i] : r;
   __syncthreads();
   return r;
+}
+
+// Maximum of a and minimum of b over the workgroup with one pair of barriers.
+__device__ __forceinline__ void block_max_min(float &a, int &b, float *s_f, int *s_i) {
+  a = wave_reduce(a, [](float x, float y) { return fmaxf(x, y); });
+  b = wave_reduce(b, [](int x, int y) { return y < x ? y : x; });
+  if ((threadIdx.x & 63) == 0) {
+    s_f[threadIdx.x >> 6] = a;
+    s_i[threadIdx.x >> 6] = b;
+  }
+  __syncthreads();
+  a = fmaxf(fmaxf(s_f[0], s_f[1]), fmaxf(s_f[2], s_f[3]));
+  b = min(min(s_i[0], s_i[1]), min(s_i[2], s_i[3]));
+  __syncthreads();
 }
 
 // Handoff between the workgroups of one kernel without agent-scope release

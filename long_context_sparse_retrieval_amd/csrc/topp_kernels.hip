@@ -142,8 +142,7 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
       }
     }
   }
-  mx = block_max<float>(mx, sm.red_f);
-  cmin = block_min<int>(cmin, sm.red_i);
+  block_max_min(mx, cmin, sm.red_f, sm.red_i);
   const int c_t = (mx == -INFINITY) ? INT32_MIN : score_cell(mx);
 
   // local bins j = c_t - cell; cells 255 or more below c_t form the clamp bin 255,
@@ -158,22 +157,24 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
 #pragma unroll
       for (int w = 0; w < 4; ++w) packed += sm.hist[w][cell & (kCells - 1)];
     }
-    // clamp bin: cells c_t - 255 - x for x = 0..(c_t - 255 - cmin)
-    const long long cell = (long long)c_t - (kBins - 1) - tid;
-    double cm = 0.0;
-    unsigned long long cc = 0;
-    if (cell >= cmin) {
-      unsigned long long e = 0;
+    // clamp bin: cells c_t - 255 - x for x = 0..(c_t - 255 - cmin), if any
+    if ((long long)cmin <= (long long)c_t - (kBins - 1)) {            // block-uniform
+      const long long cell = (long long)c_t - (kBins - 1) - tid;
+      double cm = 0.0;
+      unsigned long long cc = 0;
+      if (cell >= cmin) {
+        unsigned long long e = 0;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) e += sm.hist[w][cell & (kCells - 1)];
-      cm = (double)(e & kMassMask) * exp(-(double)tid * 0.125);
-      cc = e >> kCountShift;
+        for (int w = 0; w < 4; ++w) e += sm.hist[w][cell & (kCells - 1)];
+        cm = (double)(e & kMassMask) * exp(-(double)tid * 0.125);
+        cc = e >> kCountShift;
+      }
+      double tm;
+      (void)block_excl_scan<double>(cm, tm, sm.red_d);
+      unsigned long long tc;
+      (void)block_excl_scan<unsigned long long>(cc, tc, sm.red_u);
+      if (j == kBins - 1) packed = (unsigned long long)tm | (tc << kCountShift);
     }
-    double tm;
-    (void)block_excl_scan<double>(cm, tm, sm.red_d);
-    unsigned long long tc;
-    (void)block_excl_scan<unsigned long long>(cc, tc, sm.red_u);
-    if (j == kBins - 1) packed = (unsigned long long)tm | (tc << kCountShift);
   } else {
     // cells of this tile span kCells or more: rebin relative to c_t from the scores in registers
     __syncthreads();
