@@ -141,6 +141,23 @@ class Case:
         return ms_step, ms_pa
 
 
+    def run_dense(self, steps: int, warmup: int) -> float:
+        """ms per call of the dense comparator (every head over every cached position) on the same caches."""
+        R = len(self.reps)
+        for s in range(warmup):
+            _, k, v = self.reps[s % R]
+            rtp.dense_attn(self.layer, self.q, k, v, self.ws, out=self.out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for s in range(steps):
+            _, k, v = self.reps[s % R]
+            rtp.dense_attn(self.layer, self.q, k, v, self.ws, out=self.out)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+
 def copy_ceiling_gbps() -> float:
     """Plain device copy of 2 GiB (read + write bytes / time), the box's practical streaming rate."""
     n = 1 << 29
@@ -251,13 +268,17 @@ def main():
         case = Case(cfg, args.replicas)
         ms, ms_pa = case.run(args.steps, args.warmup)
         gbps = case.bytes_total / (ms * 1e-3) / 1e9
+        ms_dense = case.run_dense(max(5, args.steps // 10), 3)
+        dense_bytes = 512 * case.spec.B * case.spec.Hkv * case.spec.N
         pa_bytes = case.bytes_scan + case.bytes_swa
         summ[cfg] = dict(ms=ms, us=ms * 1e3, gbps=gbps, frac=gbps / HBM_PEAK_GBPS, pa_us=ms_pa * 1e3,
                          pa_gbps=pa_bytes / (ms_pa * 1e-3) / 1e9, pa_bytes=pa_bytes,
                          bytes=case.bytes_total, spec=case.spec, counts=case.counts,
-                         union=case.gather_rows_union, rsum=case.gather_rows_sum)
+                         union=case.gather_rows_union, rsum=case.gather_rows_sum,
+                         dense_us=ms_dense * 1e3, dense_gbps=dense_bytes / (ms_dense * 1e-3) / 1e9)
         log(f"[bench] cfg{cfg}: {ms * 1e3:.1f} us/step, phase-A kernel {ms_pa * 1e3:.1f} us, {gbps:.0f} GB/s "
-            f"algorithmic; |S| {case.counts.ravel().tolist()}")
+            f"algorithmic; |S| {case.counts.ravel().tolist()}; dense comparator {ms_dense * 1e3:.1f} us "
+            f"({dense_bytes / (ms_dense * 1e-3) / 1e9:.0f} GB/s), sparse step {ms_dense / ms:.2f}x faster")
         if cfg == 4 and not args.no_cpu_baseline:
             t0 = time.time()
             cpu = cpu_baseline(case)
@@ -298,6 +319,12 @@ def main():
                      "frac": round(s["pa_gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel_us": round(s["pa_us"], 2), "algorithmic_bytes_per_launch": s["pa_bytes"]},
         "copy_ceiling_GBps": round(copy_gbps, 1),
+        "dense_comparator": {"what": "rtp_dense_attn: every head over every cached position, same caches",
+                             "us_per_step": round(s["dense_us"], 2), "GBps": round(s["dense_gbps"], 1),
+                             "sparse_speedup": round(s["dense_us"] / s["us"], 3),
+                             "dense_at_hbm_peak_us": round(512 * spec.B * spec.Hkv * spec.N / HBM_PEAK_GBPS / 1e3, 2),
+                             "sparse_speedup_vs_dense_at_peak":
+                                 round(512 * spec.B * spec.Hkv * spec.N / HBM_PEAK_GBPS / 1e3 / s["us"], 3)},
     }
     if main_cfg == 4:
         out["roofline"]["traffic"] = traffic_per_launch(spec.name)
@@ -309,6 +336,8 @@ def main():
                            "GBps": round(s3["gbps"], 1), "hbm_frac": round(s3["frac"], 4),
                            "algorithmic_bytes_per_step": s3["bytes"], "phase_a_kernel_us": round(s3["pa_us"], 2),
                            "phase_a_GBps": round(s3["pa_gbps"], 1),
+                           "dense_comparator_us": round(s3["dense_us"], 2),
+                           "sparse_speedup_vs_dense": round(s3["dense_us"] / s3["us"], 3),
                            "selected_tokens": s3["counts"].ravel().tolist()}
     print(json.dumps(out), flush=True)
 

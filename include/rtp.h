@@ -146,6 +146,18 @@ int rtp_sparse_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf1
 int rtp_swa_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *k,
                  const rtp_bf16 *v, float *out, void *ws, size_t ws_bytes, void *stream);
 
+/* Dense attention, the comparator of the sparse step: every q head (retrieval
+ * and local alike) attends over every cached position 0..m_i with the same
+ * RoPE'd query, softmax(q_rot . K[n] / sqrt(D)) V[n] (eq. (5) with the full
+ * set, i.e. plain causal decode attention as in FASB section 2).  The pages
+ * measure their kernels against a dense FlashAttention-2 decode (DeepRead
+ * summary, "Key Results"); this call is that baseline built the same way as
+ * the rest of this library (GQA: one K/V row read serves the group's heads,
+ * split-K over the cache).  Layouts as rtp_swa_attn; writes every row of out.
+ * The workspace of rtp_workspace_bytes(layer) covers this call. */
+int rtp_dense_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *k,
+                   const rtp_bf16 *v, float *out, void *ws, size_t ws_bytes, void *stream);
+
 /* One whole step (FASB eq. (4)-(5) and section 3.2): indexer scan, histogram
  * Top-P, sparse attention for retrieval heads and SWA for local heads; writes
  * every row of out [B,Hq,nq,D] fp32.  Equals rtp_index_score + rtp_topp_select +

@@ -16,8 +16,8 @@ import torch
 
 __all__ = [
     "Layer", "RtpError", "library_path", "load", "num_retrieval", "workspace_bytes", "workspace",
-    "rope_keys", "index_keys", "index_score", "topp_select", "sparse_attn", "swa_attn", "decode_step",
-    "SYMBOLS",
+    "rope_keys", "index_keys", "index_score", "topp_select", "sparse_attn", "swa_attn", "dense_attn",
+    "decode_step", "SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -26,7 +26,7 @@ _lib = None
 
 SYMBOLS = ("rtp_num_retrieval", "rtp_workspace_bytes", "rtp_workspace_init", "rtp_status_str", "rtp_rope_keys",
            "rtp_index_keys", "rtp_index_score", "rtp_topp_select", "rtp_sparse_attn", "rtp_swa_attn",
-           "rtp_decode_step")
+           "rtp_dense_attn", "rtp_decode_step")
 
 
 class RtpError(RuntimeError):
@@ -67,6 +67,7 @@ def load():
         "rtp_topp_select": (ctypes.c_int, [L, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]),
         "rtp_sparse_attn": (ctypes.c_int, [L, vp, vp, vp, vp, vp, i64, vp, vp, ctypes.c_size_t, vp]),
         "rtp_swa_attn": (ctypes.c_int, [L, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+        "rtp_dense_attn": (ctypes.c_int, [L, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "rtp_decode_step": (ctypes.c_int, [L, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -244,6 +245,19 @@ def swa_attn(layer: Layer, q_pre, k, v, ws, out=None) -> torch.Tensor:
     op = _ptr(out, torch.float32, (layer.B, layer.Hq, layer.nq, layer.D), "out")
     _check(load().rtp_swa_attn(ctypes.byref(layer.c()), q, kp, vp, op, ws.data_ptr(), ws.numel(), _stream()),
            "rtp_swa_attn")
+    return out
+
+
+def dense_attn(layer: Layer, q_pre, k, v, ws, out=None) -> torch.Tensor:
+    """Dense attention of every head over every cached position (the comparator); writes every row of out."""
+    q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
+    kp = _ptr(k, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k")
+    vp = _ptr(v, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v")
+    if out is None:
+        out = torch.empty((layer.B, layer.Hq, layer.nq, layer.D), dtype=torch.float32, device=q_pre.device)
+    op = _ptr(out, torch.float32, (layer.B, layer.Hq, layer.nq, layer.D), "out")
+    _check(load().rtp_dense_attn(ctypes.byref(layer.c()), q, kp, vp, op, ws.data_ptr(), ws.numel(), _stream()),
+           "rtp_dense_attn")
     return out
 
 

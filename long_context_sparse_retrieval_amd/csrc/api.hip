@@ -44,9 +44,22 @@ int pick_tile(long long units, long long N) {
 }
 
 // Fills the geometry and workspace layout; ws may be null (sizing only).
-int make_plan(const rtp_layer *L, void *ws, Plan *out) {
+// dense: the comparator's plan -- every head attends like a local head over a
+// window covering the whole cache with no sinks, in chunks of about 2048
+// workgroups in total.
+int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
   const int st = validate_layer(L);
   if (st != RTP_OK) return st;
+  int8_t all_local[kMaxHq];
+  rtp_layer LD;
+  if (dense) {
+    memset(all_local, 0, sizeof(all_local));
+    LD = *L;
+    LD.head_mode = all_local;
+    LD.window = (int32_t)(L->N < 0x7fffffff ? L->N : 0x7fffffff);
+    LD.n_sink = 0;
+    L = &LD;
+  }
   Geo g;
   memset(&g, 0, sizeof(g));
   g.B = L->B;
@@ -93,6 +106,10 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
     long long chunk = (Lrows + 15) / 16;
     chunk = (chunk + 31) / 32 * 32;
     if (chunk < 64) chunk = 64;
+    if (dense) {
+      const long long per = (long long)g.swa_units * g.swa_hb * Lrows / 2048;
+      chunk = per < 1024 ? 1024 : (per + 63) / 64 * 64;
+    }
     if (const char *env = getenv("RTP_SWA_CHUNK")) {
       const long long c = atoll(env);
       if (c >= 64 && c % 64 == 0) chunk = c;
@@ -165,8 +182,8 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out) {
   return RTP_OK;
 }
 
-int plan_with_ws(const rtp_layer *L, void *ws, size_t ws_bytes, Plan *p) {
-  const int st = make_plan(L, ws, p);
+int plan_with_ws(const rtp_layer *L, void *ws, size_t ws_bytes, Plan *p, bool dense = false) {
+  const int st = make_plan(L, ws, p, dense);
   if (st != RTP_OK) return st;
   if (!ws) return RTP_ERR_ARG;
   if (ws_bytes < p->ws_bytes) return RTP_ERR_WS_TOO_SMALL;
@@ -206,8 +223,9 @@ int32_t rtp_num_retrieval(const rtp_layer *layer) {
 }
 
 size_t rtp_workspace_bytes(const rtp_layer *layer) {
-  Plan p;
-  return make_plan(layer, nullptr, &p) == RTP_OK ? p.ws_bytes : 0;
+  Plan p, pd;
+  if (make_plan(layer, nullptr, &p) != RTP_OK || make_plan(layer, nullptr, &pd, true) != RTP_OK) return 0;
+  return p.ws_bytes > pd.ws_bytes ? p.ws_bytes : pd.ws_bytes;
 }
 
 int rtp_workspace_init(void *ws, size_t ws_bytes, void *stream) {
@@ -272,6 +290,15 @@ int rtp_swa_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *
   int st = plan_with_ws(layer, ws, ws_bytes, &p);
   if (st != RTP_OK) return st;
   if (p.g.swa_units && (!q_pre || !k || !v || !out)) return RTP_ERR_ARG;
+  return launch_phase_a(p.g, q_pre, nullptr, nullptr, nullptr, k, v, out, false, true, as_stream(stream));
+}
+
+int rtp_dense_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *k, const rtp_bf16 *v, float *out,
+                   void *ws, size_t ws_bytes, void *stream) {
+  Plan p;
+  int st = plan_with_ws(layer, ws, ws_bytes, &p, true);
+  if (st != RTP_OK) return st;
+  if (!q_pre || !k || !v || !out) return RTP_ERR_ARG;
   return launch_phase_a(p.g, q_pre, nullptr, nullptr, nullptr, k, v, out, false, true, as_stream(stream));
 }
 

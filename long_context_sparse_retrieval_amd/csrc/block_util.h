@@ -306,23 +306,23 @@ __device__ __forceinline__ void combine_partials(const Partial *parts, int np, f
 }
 
 // Normalised combination of np split-K states into out[0..D) by one wave:
-// lane l holds channels 2l and 2l + 1; eight states are loaded per round and
+// lane l holds channels 2l and 2l + 1; sixteen states are loaded per round and
 // merged in index order.
 __device__ __forceinline__ void wave_combine(const Partial *parts, int np, float *out) {
   const int lane = threadIdx.x & 63;
   float m = -INFINITY, l = 0.f, o[2] = {0.f, 0.f};
-  for (int x0 = 0; x0 < np; x0 += 8) {
-    float pm[8], pl[8];
-    float2 po[8];
+  for (int x0 = 0; x0 < np; x0 += 16) {
+    float pm[16], pl[16];
+    float2 po[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {          // clamped, unconditional loads
+    for (int u = 0; u < 16; ++u) {         // clamped, unconditional loads
       const int x = x0 + u < np ? x0 + u : np - 1;
       pm[u] = parts[x].m;
       pl[u] = parts[x].l;
       po[u] = reinterpret_cast<const float2 *>(parts[x].o)[lane];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 16; ++u) {
       if (x0 + u >= np) break;
       const float o2[2] = {po[u].x, po[u].y};
       merge_state(m, l, o, pm[u], pl[u], o2, 2);

@@ -306,3 +306,28 @@ def test_prefill_step_matches_oracle(case, monkeypatch):
     verdicts = [check_set(idx[b, r, i], int(cnt[b, r, i]), cap, t, res["logits"][(b, r, i)], spec.p,
                           f"{case} b{b} r{r} i{i}") for (b, r, i), t in res["topp"].items()]
     say(f"{case}: sets {verdicts.count('exact')} exact, {verdicts.count('tolerated')} tolerated")
+
+
+# ----------------------------------------------------------------------------- dense comparator
+@pytest.mark.parametrize("N,nq,Hq,Hkv", [(1, 1, 4, 1), (5, 1, 4, 2), (300, 3, 8, 2), (5000, 1, 8, 1),
+                                          (70000, 1, 16, 2), (9000, 2, 32, 8)])
+def test_dense_attn_matches_oracle(N, nq, Hq, Hkv):
+    say(f"dense N={N} nq={nq} Hq={Hq} Hkv={Hkv}")
+    rng = np.random.default_rng(N + 7 * nq + Hq)
+    B = 1
+    q = _rand_bf16(rng, (B, Hq, nq, 128), 1.5)
+    k = _rand_bf16(rng, (B, Hkv, N, 128), 1.0)
+    v = _rand_bf16(rng, (B, Hkv, N, 128), 1.0)
+    hm = [0] * Hq
+    lay = rtp.Layer(B=B, Hq=Hq, Hkv=Hkv, N=N, nq=nq, head_mode=hm)
+    ws = rtp.workspace(lay)
+    out = rtp.dense_attn(lay, dev_bf16(q), dev_bf16(k), dev_bf16(v), ws)
+    out2 = rtp.dense_attn(lay, dev_bf16(q), dev_bf16(k), dev_bf16(v), ws)
+    torch.cuda.synchronize()
+    out, out2 = out.cpu().numpy(), out2.cpu().numpy()
+    assert np.array_equal(out, out2), "two runs differ (non-deterministic)"
+    dummy_w = np.zeros((0, 128, 16), np.uint16)
+    res = O.decode_step(q, dummy_w, None, k, v, np.zeros(Hq, np.int8), N=N, p=0.9, window=N, n_sink=0,
+                        rope_base=1e6)
+    for (b, h, i), ref in res["out"].items():
+        check_output(out[b, h, i], ref, f"dense b{b} h{h} i{i}")
