@@ -15,7 +15,9 @@ test and are not computed here.
 
 Draw order for ``make_workload`` (one ``numpy.random.default_rng(seed)``):
   1. W_q for every retrieval q head r (ascending), each (D, R) ~ N(0, 1/D);
-     then W_k the same way unless the spec shares one draw (W_k = W_q).
+     then W_k the same way unless the spec shares one draw (W_k = W_q).  With
+     shared indexer keys (idx_group > 1): W_k for every indexer-key head first,
+     then W_q per retrieval head, or W_q[r] = W_k[r // idx_group] when shared.
   2. u = the unscaled pre-RoPE queries, (B, Hq, nq, D) ~ N(0, 1).  In
      "topics" mode (chunked prefill) these are the per-query perturbations xi,
      followed by one draw of two topic directions per head, (B, Hq, 2, D);
@@ -82,6 +84,8 @@ class WorkloadSpec:
     diffuse: tuple = (8192, 0.5)
     budget_targets: tuple = (500, 2500)
     topic_mix: float = 0.3
+    # retrieval heads sharing one indexer-key head (1: one per head; G: one per KV group)
+    idx_group: int = 1
     # "unit": q = u; "table": q = s_(b,r) * u with s from the calibration table
     query_scale: str = "unit"
     shared_w: bool = True
@@ -103,6 +107,11 @@ class WorkloadSpec:
     @property
     def Hr(self) -> int:
         return len(self.ret_groups) * self.G
+
+    @property
+    def Hi(self) -> int:
+        """Indexer-key heads (rows of W_k and of the indexer-key cache)."""
+        return self.Hr // self.idx_group
 
     def needle_recipe(self, b: int, r: int) -> tuple:
         """(count, alpha, class) of the needles planted for retrieval head r of batch b."""
@@ -158,7 +167,7 @@ class Workload:
     seed: int
     q_pre: np.ndarray            # uint16 bf16 bits [B, Hq, nq, D]
     w_q: np.ndarray              # uint16 [Hr, D, R]
-    w_k: np.ndarray              # uint16 [Hr, D, R]
+    w_k: np.ndarray              # uint16 [Hi, D, R] (Hi = Hr / idx_group)
     k_pre: np.ndarray            # uint16 [B, Hkv, N, D] pre-RoPE keys (zero rows never read)
     v: np.ndarray                # uint16 [B, Hkv, N, D]
     head_mode: np.ndarray        # int8 [Hq]
@@ -207,15 +216,30 @@ def make_workload(spec: WorkloadSpec, seed: int, scales: dict | None = None) -> 
     inv_sqrt_d = 1.0 / math.sqrt(D)
 
     # 1. projections
-    w_q = np.empty((Hr, D, R), dtype=np.uint16)
-    for r in range(Hr):
-        w_q[r] = f32_to_bf16_bits(rng.standard_normal((D, R), dtype=np.float32) * np.float32(inv_sqrt_d))
-    if spec.shared_w:
-        w_k = w_q.copy()
-    else:
-        w_k = np.empty_like(w_q)
+    ig = spec.idx_group
+    draw_w = lambda: f32_to_bf16_bits(rng.standard_normal((D, R), dtype=np.float32) * np.float32(inv_sqrt_d))
+    if ig == 1:
+        w_q = np.empty((Hr, D, R), dtype=np.uint16)
         for r in range(Hr):
-            w_k[r] = f32_to_bf16_bits(rng.standard_normal((D, R), dtype=np.float32) * np.float32(inv_sqrt_d))
+            w_q[r] = draw_w()
+        if spec.shared_w:
+            w_k = w_q.copy()
+        else:
+            w_k = np.empty_like(w_q)
+            for r in range(Hr):
+                w_k[r] = draw_w()
+    else:
+        # shared indexer keys: one W_k per indexer-key head; with shared_w every
+        # retrieval head of the group projects its query with that same matrix
+        w_k = np.empty((Hr // ig, D, R), dtype=np.uint16)
+        for i in range(Hr // ig):
+            w_k[i] = draw_w()
+        if spec.shared_w:
+            w_q = np.repeat(w_k, ig, axis=0)
+        else:
+            w_q = np.empty((Hr, D, R), dtype=np.uint16)
+            for r in range(Hr):
+                w_q[r] = draw_w()
 
     # 2. unscaled queries (topics mode: perturbations, then the topic directions)
     u = rng.standard_normal((B, Hq, nq, D), dtype=np.float32)

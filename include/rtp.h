@@ -80,6 +80,11 @@ typedef struct rtp_layer {
   int32_t window;             /* local heads: window W >= 1 (positions m-W+1..m) */
   int32_t n_sink;             /* local heads: sink positions 0..n_sink-1, >= 0 */
   double rope_theta;          /* RoPE base of eq. (1), > 0 */
+  int32_t idx_group;          /* retrieval q heads sharing one indexer-key head: 0 or 1 = one per
+                                 retrieval head (eq. (4) writes W_k per head), Hq/Hkv = one per KV
+                                 group (then retrieval heads come in whole groups).  The indexer-key
+                                 heads Hi = Hr / idx_group are numbered in retrieval-head order:
+                                 k_idx is [B,Hi,Ncap,R], w_k is [Hi,D,R]; w_q stays [Hr,D,R] */
 } rtp_layer;
 
 /* Number of retrieval heads Hr implied by layer->head_mode (or a negative status). */

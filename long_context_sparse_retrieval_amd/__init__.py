@@ -38,7 +38,7 @@ class _CLayer(ctypes.Structure):
         ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
         ("R", ctypes.c_int32), ("nq", ctypes.c_int32), ("N", ctypes.c_int64), ("Ncap", ctypes.c_int64),
         ("head_mode", ctypes.POINTER(ctypes.c_int8)), ("p", ctypes.c_float), ("window", ctypes.c_int32),
-        ("n_sink", ctypes.c_int32), ("rope_theta", ctypes.c_double),
+        ("n_sink", ctypes.c_int32), ("rope_theta", ctypes.c_double), ("idx_group", ctypes.c_int32),
     ]
 
 
@@ -95,6 +95,7 @@ class Layer:
     rope_theta: float = 1.0e6
     D: int = 128
     R: int = 16
+    idx_group: int = 1        # retrieval heads sharing one indexer-key head (1 or Hq // Hkv)
     _keep: list = field(default_factory=list, repr=False, compare=False)
 
     @property
@@ -105,12 +106,17 @@ class Layer:
     def Hr(self) -> int:
         return int(sum(1 for h in self.head_mode if h))
 
+    @property
+    def Hi(self) -> int:
+        """Indexer-key heads (rows of k_idx / w_k)."""
+        return self.Hr // max(1, self.idx_group)
+
     def c(self) -> _CLayer:
         hm = (ctypes.c_int8 * len(self.head_mode))(*[int(h) for h in self.head_mode])
         self._keep = [hm]
         return _CLayer(self.B, self.Hq, self.Hkv, self.D, self.R, self.nq, self.N, self.cap_rows,
                        ctypes.cast(hm, ctypes.POINTER(ctypes.c_int8)), self.p, self.window, self.n_sink,
-                       self.rope_theta)
+                       self.rope_theta, self.idx_group)
 
 
 def _check(status: int, what: str):
@@ -181,10 +187,10 @@ def index_keys(layer: Layer, k_pre: torch.Tensor, w_k: torch.Tensor, k_idx: torc
                n0: int = 0, n1: int | None = None) -> torch.Tensor:
     """Indexer-key cache rows [n0, n1): bf16(k_pre . W_k) per retrieval head."""
     a = _ptr(k_pre, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k_pre")
-    w = _ptr(w_k, torch.bfloat16, (layer.Hr, layer.D, layer.R), "w_k")
+    w = _ptr(w_k, torch.bfloat16, (layer.Hi, layer.D, layer.R), "w_k")
     if k_idx is None:
-        k_idx = torch.zeros(_cache_shape(layer, layer.Hr, layer.R), dtype=torch.bfloat16, device=k_pre.device)
-    b = _ptr(k_idx, torch.bfloat16, _cache_shape(layer, layer.Hr, layer.R), "k_idx")
+        k_idx = torch.zeros(_cache_shape(layer, layer.Hi, layer.R), dtype=torch.bfloat16, device=k_pre.device)
+    b = _ptr(k_idx, torch.bfloat16, _cache_shape(layer, layer.Hi, layer.R), "k_idx")
     n1 = layer.cap_rows if n1 is None else n1
     _check(load().rtp_index_keys(ctypes.byref(layer.c()), a, w, b, n0, n1, _stream()), "rtp_index_keys")
     return k_idx
@@ -194,7 +200,7 @@ def index_score(layer: Layer, q_pre, w_q, k_idx, logits=None) -> torch.Tensor:
     """Indexer scores [B, Hr, nq, N] fp32 (eq. 4); -inf beyond each query's position."""
     q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
     w = _ptr(w_q, torch.bfloat16, (layer.Hr, layer.D, layer.R), "w_q")
-    k = _ptr(k_idx, torch.bfloat16, _cache_shape(layer, layer.Hr, layer.R), "k_idx")
+    k = _ptr(k_idx, torch.bfloat16, _cache_shape(layer, layer.Hi, layer.R), "k_idx")
     if logits is None:
         logits = torch.empty((layer.B, layer.Hr, layer.nq, layer.N), dtype=torch.float32, device=q_pre.device)
     o = _ptr(logits, torch.float32, (layer.B, layer.Hr, layer.nq, layer.N), "logits")
@@ -266,7 +272,7 @@ def decode_step(layer: Layer, q_pre, w_q, k_idx, k, v, ws, out=None, idx=None, c
     """One fused decode step (eq. 4-5 + SWA): returns out [B, Hq, 1, D] fp32."""
     q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
     w = _ptr(w_q, torch.bfloat16, (layer.Hr, layer.D, layer.R), "w_q") if layer.Hr else None
-    ki = _ptr(k_idx, torch.bfloat16, _cache_shape(layer, layer.Hr, layer.R), "k_idx") if layer.Hr else None
+    ki = _ptr(k_idx, torch.bfloat16, _cache_shape(layer, layer.Hi, layer.R), "k_idx") if layer.Hr else None
     kp = _ptr(k, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k")
     vp = _ptr(v, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v")
     if out is None:

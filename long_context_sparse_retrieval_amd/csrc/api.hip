@@ -30,6 +30,12 @@ int validate_layer(const rtp_layer *L) {
   if (!(L->p > 0.0f) || L->window < 1 || L->n_sink < 0 || !(L->rope_theta > 0.0)) return RTP_ERR_ARG;
   for (int h = 0; h < L->Hq; ++h)
     if (L->head_mode[h] != 0 && L->head_mode[h] != 1) return RTP_ERR_ARG;
+  const int G = L->Hq / L->Hkv;
+  if (L->idx_group < 0 || (L->idx_group > 1 && L->idx_group != G)) return RTP_ERR_ARG;
+  if (L->idx_group > 1)        // shared indexer keys: retrieval heads come in whole KV groups
+    for (int kv = 0; kv < L->Hkv; ++kv)
+      for (int h = kv * G + 1; h < (kv + 1) * G; ++h)
+        if (L->head_mode[h] != L->head_mode[kv * G]) return RTP_ERR_ARG;
   return RTP_OK;
 }
 
@@ -58,6 +64,7 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
     LD.head_mode = all_local;
     LD.window = (int32_t)(L->N < 0x7fffffff ? L->N : 0x7fffffff);
     LD.n_sink = 0;
+    LD.idx_group = 1;
     L = &LD;
   }
   Geo g;
@@ -79,6 +86,8 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
     else g.lmask[h >> 5] |= 1u << (h & 31);
   }
   g.Hr = hr;
+  g.ig = L->idx_group > 1 ? L->idx_group : 1;
+  g.Hi = hr / g.ig;
   for (int kv = 0; kv < L->Hkv; ++kv) {
     int nl = 0;
     for (int h = kv * g.G; h < (kv + 1) * g.G; ++h) nl += L->head_mode[h] ? 0 : 1;

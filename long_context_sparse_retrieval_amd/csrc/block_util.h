@@ -323,9 +323,8 @@ __device__ __forceinline__ void wave_combine(const Partial *parts, int np, float
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      if (x0 + u >= np) break;
       const float o2[2] = {po[u].x, po[u].y};
-      merge_state(m, l, o, pm[u], pl[u], o2, 2);
+      if (x0 + u < np) merge_state(m, l, o, pm[u], pl[u], o2, 2);
     }
   }
   out[2 * lane] = l > 0.f ? o[0] / l : 0.f;

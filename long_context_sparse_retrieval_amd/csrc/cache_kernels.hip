@@ -50,8 +50,8 @@ __global__ __launch_bounds__(kWG) void index_keys_kernel(Geo g, const rtp_bf16 *
   __shared__ double s_x[16][kD + 1];
   const int tid = threadIdx.x;
   const int br = blockIdx.x / blocks_per, blk = blockIdx.x % blocks_per;
-  const int b = br / g.Hr, r = br % g.Hr;
-  const int kvg = g.rhead[r] / g.G;
+  const int b = br / g.Hi, r = br % g.Hi;                // r: indexer-key head
+  const int kvg = g.rhead[r * g.ig] / g.G;
   const long long nb = n0 + (long long)blk * 16;
   const int nrows = (int)min<long long>(16, per - (long long)blk * 16);
   for (int i = tid; i < kD * kR; i += kWG) {
@@ -73,15 +73,15 @@ __global__ __launch_bounds__(kWG) void index_keys_kernel(Geo g, const rtp_bf16 *
   double acc = 0.0;
 #pragma unroll 8
   for (int c = 0; c < kD; ++c) acc = fma(s_x[rr][c], s_w[c][j], acc);
-  k_idx[(((size_t)b * g.Hr + r) * g.Ncap + nb + rr) * kR + j] = f64_to_bf16(acc);
+  k_idx[(((size_t)b * g.Hi + r) * g.Ncap + nb + rr) * kR + j] = f64_to_bf16(acc);
 }
 
 int launch_index_keys(const Geo &g, const rtp_bf16 *k_pre, const rtp_bf16 *w_k, rtp_bf16 *k_idx, long long n0,
                       long long n1, hipStream_t s) {
   const long long per = n1 - n0;
-  if (per == 0 || g.Hr == 0) return RTP_OK;
+  if (per == 0 || g.Hi == 0) return RTP_OK;
   const int blocks_per = (int)((per + 15) / 16);
-  hipLaunchKernelGGL(index_keys_kernel, dim3((unsigned)((long long)blocks_per * g.B * g.Hr)), dim3(kWG), 0, s, g,
+  hipLaunchKernelGGL(index_keys_kernel, dim3((unsigned)((long long)blocks_per * g.B * g.Hi)), dim3(kWG), 0, s, g,
                      k_pre, w_k, k_idx, n0, per, blocks_per);
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ERR_HIP;
 }
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kWG) void index_score_kernel(Geo g, const rtp_bf16 
 #pragma unroll
   for (int j = 0; j < kR; ++j) q[j] = s_q[j];
   const long long m = g.N - g.nq + i;
-  const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hr + r) * g.Ncap * kR);
+  const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hi + r / g.ig) * g.Ncap * kR);
   float *out = logits + (size_t)unit * g.N;
   for (int k = 0; k < 4; ++k) {
     const long long n = (long long)blk * 1024 + k * kWG + threadIdx.x;

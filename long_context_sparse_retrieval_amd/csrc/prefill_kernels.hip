@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
   const int nvalid = min(kQB, i0 + nqc - qi0);
   const long long mpos0 = g.N - g.nq;                    // position of query index 0
   const long long m_last = mpos0 + qi0 + nvalid - 1;
-  const uint2 *keys = reinterpret_cast<const uint2 *>(k_idx + ((size_t)b * g.Hr + r) * g.Ncap * kR);
+  const uint2 *keys = reinterpret_cast<const uint2 *>(k_idx + ((size_t)b * g.Hi + r / g.ig) * g.Ncap * kR);
 
   // Matrix-core operands: A = 16 keys x 16 dims (lane: key col, dims 4 row ..
   // 4 row + 3), B = 16 dims x 16 queries (lane: query col, the same dims), so

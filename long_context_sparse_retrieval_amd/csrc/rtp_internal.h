@@ -57,6 +57,8 @@ struct alignas(16) Partial {
 // Geometry and workspace of one call; passed by value to every kernel.
 struct Geo {
   int B, Hq, Hkv, G, Hr, nq;
+  int ig;               // retrieval heads per indexer-key head (1 or G)
+  int Hi;               // indexer-key heads = Hr / ig
   long long N, Ncap;
   float p;
   int window, n_sink;

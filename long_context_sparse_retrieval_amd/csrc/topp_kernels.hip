@@ -62,7 +62,38 @@ __device__ __forceinline__ uint32_t enc_min(int c) { return 0x7fffffffu - (uint3
 __device__ __forceinline__ int dec_min(uint32_t e) { return (int)(0x7fffffffu - e); }
 
 
-// One scan workgroup: tile t of query unit (blk = unit * nt + t).
+// Scan workgroups of a launch: units * nt, or with shared indexer keys one
+// per (retrieval head, tile) in the order below, padded.
+__host__ __device__ __forceinline__ long long scan_blocks(const Geo &g) {
+  if (g.ig == 1) return (long long)g.units * g.nt;
+  const long long slots = (long long)g.B * g.Hi * g.nq * g.nt;
+  return (slots + 7) / 8 * 8 * g.ig;
+}
+
+// Query unit and tile of scan workgroup blk; false for padding.  With shared
+// indexer keys the ig heads that read the same key rows get workgroups 8
+// apart (the same XCD, dispatched together), so the rows come from its L2
+// for all but the first.
+__device__ __forceinline__ bool scan_unit_tile(const Geo &g, long long blk, int &unit, int &t) {
+  if (g.ig == 1) {
+    unit = (int)(blk / g.nt);
+    t = (int)(blk % g.nt);
+    return true;
+  }
+  const long long xcd = blk & 7, y = blk >> 3;
+  const int h = (int)(y % g.ig);
+  long long s = (y / g.ig) * 8 + xcd;                    // over (b, indexer head, query, tile)
+  t = (int)(s % g.nt);
+  s /= g.nt;
+  const int i = (int)(s % g.nq);
+  s /= g.nq;
+  const int ih = (int)(s % g.Hi), b = (int)(s / g.Hi);
+  if (b >= g.B) return false;
+  unit = ((b * g.Hr) + ih * g.ig + h) * g.nq + i;
+  return true;
+}
+
+// One scan workgroup: tile t of query unit (scan_unit_tile).
 template <int T, bool FROM_LOGITS>
 __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rtp_bf16 *__restrict__ q_pre,
                                            const rtp_bf16 *__restrict__ w_q, const rtp_bf16 *__restrict__ k_idx,
@@ -70,7 +101,8 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
   constexpr int TPT = T / kWG;
   constexpr int BATCH = TPT < 5 ? TPT : 5;
   const int tid = threadIdx.x, wv = tid >> 6;
-  const int unit = (int)(blk / g.nt), t = (int)(blk % g.nt);
+  int unit, t;
+  if (!scan_unit_tile(g, blk, unit, t)) return;
   const int i = unit % g.nq, br = unit / g.nq, r = br % g.Hr, b = br / g.Hr;
   const long long m = g.N - g.nq + i;
   const long long n0 = (long long)t * T;
@@ -108,7 +140,7 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
     // rolling window of BATCH rows per thread: slot u is refilled with the row
     // BATCH positions ahead as soon as it is consumed, so about BATCH rows per
     // thread stay in flight; loads are clamped to a valid row and unconditional
-    const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hr + r) * g.Ncap * kR);
+    const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hi + r / g.ig) * g.Ncap * kR);
     uint4 ra[BATCH], rb[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
@@ -557,7 +589,7 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
           if (FROM_LOGITS) {
             sc = logits[(size_t)unit * g.N + n];
           } else {
-            const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hr + r) * g.Ncap * kR);
+            const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hi + r / g.ig) * g.Ncap * kR);
             sc = dot16_exact(sm.qi, rows[2 * n], rows[2 * n + 1]);
           }
           wt = cell_weight(sc, score_cell(sc));
@@ -661,7 +693,7 @@ int launch_phase_a_t(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, c
                      const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, bool with_swa,
                      hipStream_t s) {
   const long long n_swa = with_swa ? swa_blocks(g) : 0;
-  const long long grid = n_swa + (long long)g.units * g.nt;
+  const long long grid = n_swa + (g.units ? scan_blocks(g) : 0);
   if (grid == 0) return RTP_OK;
   if (logits)
     hipLaunchKernelGGL((phase_a_kernel<T, true>), dim3((unsigned)grid), dim3(kWG), 0, s, g, q_pre, w_q, k_idx, logits,

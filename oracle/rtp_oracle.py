@@ -286,11 +286,12 @@ def query_positions(N: int, nq: int) -> np.ndarray:
 
 
 def decode_step(q_pre, w_q, k_idx, k_cache, v_cache, head_mode, *, N, p, window, n_sink,
-                rope_base, heads=None, batches=None, queries=None, want_logits=False) -> dict:
+                rope_base, heads=None, batches=None, queries=None, want_logits=False, idx_group=1) -> dict:
     """One decode (nq = 1) or chunked-prefill (nq > 1) step of the layer.
 
-    q_pre [B, Hq, nq, D] bf16; w_q [Hr, D, R] bf16; k_idx [B, Hr, >=N, R] bf16
-    (indexer keys of retrieval head r); k_cache / v_cache [B, Hkv, >=N, D] bf16
+    q_pre [B, Hq, nq, D] bf16; w_q [Hr, D, R] bf16; k_idx [B, Hi, >=N, R] bf16
+    (indexer keys; retrieval head r reads head r // idx_group);
+    k_cache / v_cache [B, Hkv, >=N, D] bf16
     (post-RoPE keys, values); head_mode [Hq] (1 retrieval, 0 local).
     Retrieval heads: eq. (4) scores, Top-P, eq. (5) over the selected set.
     Local heads: eq. (5) over the sliding window plus sinks.
@@ -314,7 +315,7 @@ def decode_step(q_pre, w_q, k_idx, k_cache, v_cache, head_mode, *, N, p, window,
                 if hm[h]:
                     r = rindex[h]
                     q_idx = index_project(q_pre[b, h, i], w_q[r])
-                    s = indexer_logits(q_idx, k_idx[b, r, :m + 1])
+                    s = indexer_logits(q_idx, k_idx[b, r // idx_group, :m + 1])
                     t = topp_select(s, p)
                     rows = t["sel"]
                     sel[(b, r, i)] = rows
@@ -334,24 +335,27 @@ def decode_step(q_pre, w_q, k_idx, k_cache, v_cache, head_mode, *, N, p, window,
 def build_caches(wl, groups=None, heads=None):
     """Post-RoPE key cache and indexer-key cache of a generated workload (oracle's own arithmetic).
 
-    Returns (k_cache [B,Hkv,N,D] bf16, k_idx [B,Hr,N,R] bf16).  ``groups`` /
-    ``heads`` restrict which KV groups / retrieval heads are filled (others
-    stay zero).
+    Returns (k_cache [B,Hkv,N,D] bf16, k_idx [B,Hi,N,R] bf16).  Indexer-key
+    head i serves retrieval heads i*ig .. i*ig+ig-1 (ig = spec.idx_group) and
+    projects the keys of their KV group with W_k[i] (FASB eq. (4); ig > 1 is
+    the shared-per-group variant).  ``groups`` / ``heads`` restrict which KV
+    groups / retrieval heads are filled (others stay zero).
     """
     spec = wl.spec
     B, Hkv, N, D = wl.k_pre.shape
     G = spec.Hq // Hkv
+    ig = getattr(spec, "idx_group", 1)
     rheads = [int(h) for h in np.nonzero(wl.head_mode)[0]]
     k_cache = np.zeros_like(wl.k_pre)
-    k_idx = np.zeros((B, len(rheads), N, spec.R), dtype=np.uint16)
+    k_idx = np.zeros((B, len(rheads) // ig, N, spec.R), dtype=np.uint16)
     pos = np.arange(N, dtype=np.int64)
     for b in range(B):
         for g in range(Hkv):
             if groups is not None and g not in groups:
                 continue
             k_cache[b, g] = rope_keys(wl.k_pre[b, g], spec.rope_theta, pos)
-        for r, h in enumerate(rheads):
-            if heads is not None and r not in heads:
+        for i in range(len(rheads) // ig):
+            if heads is not None and not any(r // ig == i for r in heads):
                 continue
-            k_idx[b, r] = index_project(wl.k_pre[b, h // G], wl.w_k[r])
+            k_idx[b, i] = index_project(wl.k_pre[b, rheads[i * ig] // G], wl.w_k[i])
     return k_cache, k_idx

@@ -84,7 +84,8 @@ def layer_of(spec, rtp, N=None, Ncap=None, p=None, window=None, n_sink=None):
     return rtp.Layer(B=spec.B, Hq=spec.Hq, Hkv=spec.Hkv, N=spec.N if N is None else N,
                      head_mode=[int(x) for x in spec.head_mode()], nq=spec.nq, Ncap=Ncap,
                      p=spec.p if p is None else p, window=spec.window if window is None else window,
-                     n_sink=spec.n_sink if n_sink is None else n_sink, rope_theta=spec.rope_theta)
+                     n_sink=spec.n_sink if n_sink is None else n_sink, rope_theta=spec.rope_theta,
+                     idx_group=spec.idx_group)
 
 
 def edge_fraction(logits):

@@ -75,7 +75,8 @@ def test_decode_step_full_size_sampled(case):
     say(f"{case}: oracle caches built for groups {groups}, retrieval heads {r_sample}")
     res = O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
                         n_sink=spec.n_sink, rope_base=spec.rope_theta, heads=[rheads[r] for r in r_sample] + loc_heads,
-                        batches=[0], want_logits=True)
+                        batches=[0], want_logits=True,
+                        idx_group=spec.idx_group)
     verdicts = []
     for (b, h, i), ref in res["out"].items():
         check_output(out[b, h, i], ref, f"{case} b{b} h{h}")
@@ -135,7 +136,8 @@ def test_prefill_full_size_sampled():
     queries = [0, 1, spec.nq // 2, spec.nq // 2 + 1, spec.nq - 2, spec.nq - 1]
     kc, ki = O.build_caches(wl)
     res = O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
-                        n_sink=spec.n_sink, rope_base=spec.rope_theta, queries=queries, want_logits=True)
+                        n_sink=spec.n_sink, rope_base=spec.rope_theta, queries=queries, want_logits=True,
+                        idx_group=spec.idx_group)
     for (b, h, i), ref in res["out"].items():
         check_output(out[b, h, i], ref, f"prefill b{b} h{h} i{i}")
     verdicts = [check_set(gpu_set(r, i), int(cnt_h[b, r, i]), cap, t, res["logits"][(b, r, i)], spec.p,

@@ -48,10 +48,10 @@ def test_rope_keys_bit_exact(n0, n1, Ncap):
     assert np.array_equal(host_bf16(d)[:, :, n0:n1], got)
 
 
-@pytest.mark.parametrize("shared", [True, False])
-def test_index_keys_bit_exact(shared):
-    say(f"index_keys shared={shared}")
-    spec = gen.spec_for(2, B=2, N=1500, shared_w=shared)
+@pytest.mark.parametrize("shared,ig", [(True, 1), (False, 1), (True, 4), (False, 4)])
+def test_index_keys_bit_exact(shared, ig):
+    say(f"index_keys shared_w={shared} idx_group={ig}")
+    spec = gen.spec_for(2, B=2, N=1500, shared_w=shared, idx_group=ig)
     wl = gen.make_workload(spec, 11)
     lay = layer_of(spec, rtp)
     out = rtp.index_keys(lay, dev_bf16(wl.k_pre), dev_bf16(wl.w_k))
@@ -79,6 +79,24 @@ def test_index_score_bit_exact(nq):
                 ref = O.indexer_logits(qi, kidx[b, r, :m + 1])
                 assert np.array_equal(got[b, r, i, :m + 1], ref)
                 assert np.all(np.isneginf(got[b, r, i, m + 1:]))
+
+
+def test_index_score_shared_keys():
+    say("index_score idx_group=2")
+    rng = np.random.default_rng(17)
+    B, Hq, Hkv, N, nq = 2, 4, 2, 2500, 2
+    hm = [1, 1, 0, 0]
+    q = _rand_bf16(rng, (B, Hq, nq, 128), 2.0)
+    w = _rand_bf16(rng, (2, 128, 16), 1 / np.sqrt(128))
+    kidx = _rand_bf16(rng, (B, 1, N, 16))          # one indexer-key head for the group's two heads
+    lay = rtp.Layer(B=B, Hq=Hq, Hkv=Hkv, N=N, nq=nq, head_mode=hm, idx_group=2)
+    got = rtp.index_score(lay, dev_bf16(q), dev_bf16(w), dev_bf16(kidx)).cpu().numpy()
+    for b in range(B):
+        for r in range(2):
+            for i in range(nq):
+                m = N - nq + i
+                ref = O.indexer_logits(O.index_project(q[b, r, i], w[r]), kidx[b, 0, :m + 1])
+                assert np.array_equal(got[b, r, i, :m + 1], ref)
 
 
 # ----------------------------------------------------------------------------- Top-P
@@ -220,6 +238,10 @@ DECODE_CASES = {
     "cfg4-small": (4, dict(N=40000, window=2048, query_scale="unit"), 0.3),
     "p1": (2, dict(B=1, N=2500, window=300, p=1.0), None),
     "tiny": (2, dict(B=1, N=3, window=2, n_sink=1, n_needles=0), None),
+    # shared indexer keys: one indexer-key head per KV group
+    "cfg2-shared-keys": (2, dict(B=2, N=3000, window=512, idx_group=4), None),
+    "cfg2-shared-keys-indepW": (2, dict(B=2, N=3000, window=512, idx_group=4, shared_w=False), None),
+    "cfg4-shared-keys": (4, dict(N=40000, window=2048, query_scale="unit", idx_group=8), 0.3),
 }
 
 
@@ -250,7 +272,8 @@ def test_decode_step_matches_oracle(case):
     out, out2, idx, cnt = _run_decode(spec, wl, kc, ki)
     assert np.array_equal(out, out2), "two runs differ (non-deterministic)"
     res = O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
-                        n_sink=spec.n_sink, rope_base=spec.rope_theta, want_logits=True)
+                        n_sink=spec.n_sink, rope_base=spec.rope_theta, want_logits=True,
+                        idx_group=spec.idx_group)
     verdicts = []
     for (b, h, i), ref in res["out"].items():
         check_output(out[b, h, i], ref, f"{case} b{b} h{h}")
@@ -270,6 +293,7 @@ PREFILL_CASES = {
     "pf-every-position": (5, dict(N=48, nq=48, conc=(0, 4.0), diffuse=(0, 0.5)), None, None),
     "pf-query-chunks": (5, dict(N=5000, nq=80, diffuse=(300, 0.5)), None, "16"),
     "pf-layer-with-local-heads": (2, dict(B=2, N=3000, nq=24, n_needles=16, window=512), {}, None),
+    "pf-shared-keys": (5, dict(N=3000, nq=40, diffuse=(200, 0.5), idx_group=4), None, None),
 }
 
 
@@ -300,7 +324,8 @@ def test_prefill_step_matches_oracle(case, monkeypatch):
     assert np.array_equal(out, out2), "two runs differ (non-deterministic)"
     idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
     res = O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
-                        n_sink=spec.n_sink, rope_base=spec.rope_theta, want_logits=True)
+                        n_sink=spec.n_sink, rope_base=spec.rope_theta, want_logits=True,
+                        idx_group=spec.idx_group)
     for (b, h, i), ref in res["out"].items():
         check_output(out[b, h, i], ref, f"{case} b{b} h{h} i{i}")
     verdicts = [check_set(idx[b, r, i], int(cnt[b, r, i]), cap, t, res["logits"][(b, r, i)], spec.p,

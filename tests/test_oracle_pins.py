@@ -329,3 +329,27 @@ def test_decode_step_selects_planted_needles():
     sel = res["sel"][(0, 0, 0)]
     assert 1 <= len(sel) <= 32
     assert np.isin(sel, wl.needles[(0, 0)]).all()
+
+
+def test_shared_indexer_keys_reduce_to_per_head_keys():
+    """Shared indexer keys (one W_k per KV group) give the same sets and outputs
+    as per-head keys whose W_k are all that group's matrix (a pure re-indexing)."""
+    import gen
+    spec_s = gen.spec_for(2, B=1, N=600, window=64, idx_group=4, n_needles=8)
+    wl = gen.make_workload(spec_s, 5)
+    kc, ki_s = O.build_caches(wl)
+    assert ki_s.shape[1] == spec_s.Hi == 1
+    # the per-head view: W_k of every retrieval head = the group's shared matrix
+    w_k_per_head = np.repeat(wl.w_k, spec_s.idx_group, axis=0)
+    rheads = spec_s.retrieval_heads()
+    ki_p = np.stack([O.index_project(wl.k_pre[0, rheads[r] // spec_s.G], w_k_per_head[r])
+                     for r in range(spec_s.Hr)])[None]
+    common = dict(N=spec_s.N, p=spec_s.p, window=spec_s.window, n_sink=spec_s.n_sink, rope_base=spec_s.rope_theta)
+    a = O.decode_step(wl.q_pre, wl.w_q, ki_s, kc, wl.v, wl.head_mode, idx_group=4, **common)
+    b = O.decode_step(wl.q_pre, wl.w_q, ki_p, kc, wl.v, wl.head_mode, idx_group=1, **common)
+    for key in a["sel"]:
+        assert np.array_equal(a["sel"][key], b["sel"][key])
+    for key in a["out"]:
+        assert np.array_equal(a["out"][key], b["out"][key])
+    # with shared W every retrieval head of the group projects with the group's matrix
+    assert all(np.array_equal(wl.w_q[r], wl.w_k[r // 4]) for r in range(spec_s.Hr))
