@@ -67,7 +67,7 @@ class Case:
         log(f"[bench] cfg{cfg} {spec.name}: drew inputs in {time.time() - t0:.1f}s")
         self.layer = rtp.Layer(B=spec.B, Hq=spec.Hq, Hkv=spec.Hkv, N=spec.N,
                                head_mode=[int(h) for h in spec.head_mode()], p=spec.p, window=spec.window,
-                               n_sink=spec.n_sink, rope_theta=spec.rope_theta)
+                               n_sink=spec.n_sink, rope_theta=spec.rope_theta, idx_group=spec.idx_group)
         t0 = time.time()
         self.q = up(wl.q_pre)
         self.w_q = up(wl.w_q)
@@ -107,7 +107,7 @@ class Case:
                 total += sum(len(s) for s in sets)
         self.gather_rows_union, self.gather_rows_sum = union, total
         # algorithmic bytes of one step
-        n_scan = spec.B * Hr * spec.N
+        n_scan = spec.B * spec.Hi * spec.N      # indexer-key rows: one per position and indexer-key head
         lo = max(0, spec.N - spec.window)
         swa_rows = min(spec.n_sink, lo) + (spec.N - lo)
         n_local_groups = spec.Hkv - len(spec.ret_groups)
@@ -248,7 +248,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", type=int, default=0, help="run only this config (3 or 4)")
+    ap.add_argument("--only", type=int, default=0, help="run only this config (3, 4 or 6)")
     ap.add_argument("--calib", action="store_true", help="run the known-size copy used to scale HBM counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -262,13 +262,14 @@ def main():
     copy_gbps = copy_ceiling_gbps()
     log(f"[bench] device copy ceiling {copy_gbps:.0f} GB/s")
 
-    cfgs = [args.only] if args.only else [4, 3]
+    cfgs = [args.only] if args.only else [4, 3, 6]
     summ, cpu = {}, None
     for cfg in cfgs:
         case = Case(cfg, args.replicas)
         ms, ms_pa = case.run(args.steps, args.warmup)
         gbps = case.bytes_total / (ms * 1e-3) / 1e9
-        ms_dense = case.run_dense(max(5, args.steps // 10), 3)
+        # the dense comparator ignores the indexer, so the shared-key layer would repeat the 1M figure
+        ms_dense = case.run_dense(max(5, args.steps // 10), 3) if cfg != 6 else float("nan")
         dense_bytes = 512 * case.spec.B * case.spec.Hkv * case.spec.N
         pa_bytes = case.bytes_scan + case.bytes_swa
         summ[cfg] = dict(ms=ms, us=ms * 1e3, gbps=gbps, frac=gbps / HBM_PEAK_GBPS, pa_us=ms_pa * 1e3,
@@ -339,6 +340,13 @@ def main():
                            "dense_comparator_us": round(s3["dense_us"], 2),
                            "sparse_speedup_vs_dense": round(s3["dense_us"] / s3["us"], 3),
                            "selected_tokens": s3["counts"].ravel().tolist()}
+    if 6 in summ and main_cfg != 6:
+        s6 = summ[6]
+        out["shared_keys_1m"] = {"workload": s6["spec"].name, "indexer_key_heads": s6["spec"].Hi,
+                                 "us_per_step": round(s6["us"], 2), "GBps": round(s6["gbps"], 1),
+                                 "hbm_frac": round(s6["frac"], 4), "algorithmic_bytes_per_step": s6["bytes"],
+                                 "phase_a_kernel_us": round(s6["pa_us"], 2), "phase_a_GBps": round(s6["pa_gbps"], 1),
+                                 "selected_tokens": s6["counts"].ravel().tolist()}
     print(json.dumps(out), flush=True)
 
 

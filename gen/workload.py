@@ -139,6 +139,9 @@ CONFIGS = {
                     needle_mode="classes", query_scale="table"),
     4: WorkloadSpec("qwen3-32b-layer-1m-b1", B=1, Hq=64, Hkv=8, N=1048576, ret_groups=(0, 1),
                     needle_mode="classes", query_scale="table"),
+    # the 1M layer with shared indexer keys (one indexer-key head per KV group)
+    6: WorkloadSpec("qwen3-32b-layer-1m-b1-shared-keys", B=1, Hq=64, Hkv=8, N=1048576, ret_groups=(0, 1),
+                    needle_mode="classes", query_scale="table", idx_group=8),
     5: WorkloadSpec("prefill-128k-4096q-4h", B=1, Hq=4, Hkv=1, N=131072, nq=4096, ret_groups=(0,),
                     needle_mode="topics", query_scale="table"),
 }

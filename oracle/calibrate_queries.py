@@ -15,7 +15,10 @@ The chunked-prefill workload (config 5) plants a concentrated and a diffuse
 topic per head; all its queries of one topic share a scale, found the same
 way on the last query of that topic (the longest prefix).
 
-Usage:  python oracle/calibrate_queries.py [cfg ...]     (default: 3 4 5)
+The 1M layer with shared indexer keys (config 6) is calibrated like the 1M
+layer, each query against its group's shared indexer keys.
+
+Usage:  python oracle/calibrate_queries.py [cfg ...]     (default: 3 4 5 6)
 """
 import json
 import math
@@ -62,7 +65,7 @@ def calibrate_topics(cfg: int, iters: int = 34):
     for b in range(spec.B):
         for r, h in enumerate(rheads):
             g = h // spec.G
-            kidx = O.index_project(wl.k_pre[b, g], wl.w_k[r])
+            kidx = O.index_project(wl.k_pre[b, g], wl.w_k[r // spec.idx_group])
             for tpc in (0, 1):
                 t0 = time.time()
                 i = spec.nq - 1 if (spec.nq - 1) % 2 == tpc else spec.nq - 2
@@ -90,12 +93,16 @@ def calibrate(cfg: int, iters: int = 34):
     wl = gen.make_workload(spec, seed, scales={})
     rheads = spec.retrieval_heads()
     entries = []
+    kidx_of = {}                  # indexer keys per (b, indexer-key head), shared by the group's heads
     for b in range(spec.B):
         for r, h in enumerate(rheads):
             t0 = time.time()
             g = h // spec.G
             m = spec.N - 1
-            kidx = O.index_project(wl.k_pre[b, g, :m + 1], wl.w_k[r])
+            ih = r // spec.idx_group
+            if (b, ih) not in kidx_of:
+                kidx_of = {(b, ih): O.index_project(wl.k_pre[b, g, :m + 1], wl.w_k[ih])}
+            kidx = kidx_of[(b, ih)]
             cnt_needles, alpha, cls = spec.needle_recipe(b, r)
             target = spec.budget_targets[cls]
             u = wl.u[b, h, 0].astype(np.float64)
@@ -138,4 +145,4 @@ def main(cfgs):
 
 
 if __name__ == "__main__":
-    main([int(a) for a in sys.argv[1:]] or [3, 4, 5])
+    main([int(a) for a in sys.argv[1:]] or [3, 4, 5, 6])
