@@ -28,6 +28,11 @@ Readings of the pages (where they are silent the plainest reading is taken):
     255.  b* = first bin (from the top) whose cumulative mass reaches p*Z;
     bins above b* are taken whole, bin b* is filled in ascending position
     while the mass accumulated before a token is below p*Z.  p >= 1 takes all.
+  * Fixed top-k (the budget-by-count counterpart of Top-P that FASB section
+    2.3 / Table 1 compares against): the first k positions in the order
+    (bin ascending, position ascending) of the same histogram; it differs
+    from the k largest logits only inside the boundary bin, where scores
+    lie within 1/8 of a logit of each other.  k >= m+1 takes all.
   * The candidate set of a query at position m is every cached position
     0..m (the current token included).
   * Local heads attend to the window of the W most recent positions
@@ -259,6 +264,40 @@ def sorted_topp(logits, p: float) -> np.ndarray:
     return np.sort(order[:k])
 
 
+def topk_select(logits, k: int) -> dict:
+    """Fixed top-k on the same 256-bin histogram order [FASB sec. 2.3 / Table 1 (top-k vs top-p); DR].
+
+    The k positions first in the order (bin ascending, position ascending),
+    bins as in ``topp_select``.  Returns ``sel`` (ascending), ``bstar`` (the
+    bin of the last position taken; N_BINS when every position is taken) and
+    ``bins``.
+    """
+    s = np.asarray(logits, dtype=np.float32)
+    n = s.shape[0]
+    if k < 1:
+        raise ValueError("k must be >= 1")
+    if n == 0:
+        return dict(sel=np.zeros(0, np.int64), bstar=-1, bins=np.zeros(0, np.int64))
+    if not np.all(np.isfinite(s)):
+        raise ValueError("non-finite logit")
+    s64 = s.astype(np.float64)
+    cell = np.floor(s64 * CELLS_PER_UNIT).astype(np.int64)
+    c = int(np.floor(s64.max() * CELLS_PER_UNIT))
+    bins = np.minimum(c - cell, N_BINS - 1)
+    if k >= n:
+        return dict(sel=np.arange(n, dtype=np.int64), bstar=N_BINS, bins=bins)
+    order = np.lexsort((np.arange(n), bins))                   # bin, then position
+    taken = order[:k]
+    return dict(sel=np.sort(taken), bstar=int(bins[taken[-1]]), bins=bins)
+
+
+def sorted_topk(logits, k: int) -> np.ndarray:
+    """Textbook top-k: the k largest logits, ties by position; ascending positions."""
+    s64 = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    order = np.lexsort((np.arange(s64.size), -s64))
+    return np.sort(order[:k])
+
+
 # ============================================================================ attention, eq. (5)
 def attention(q_rot, k_rows, v_rows) -> np.ndarray:
     """sum_n softmax_n(q . k_n / sqrt(D)) v_n over the given rows [FASB eq. (5)]; fp64."""
@@ -286,14 +325,16 @@ def query_positions(N: int, nq: int) -> np.ndarray:
 
 
 def decode_step(q_pre, w_q, k_idx, k_cache, v_cache, head_mode, *, N, p, window, n_sink,
-                rope_base, heads=None, batches=None, queries=None, want_logits=False, idx_group=1) -> dict:
+                rope_base, heads=None, batches=None, queries=None, want_logits=False, idx_group=1,
+                top_k=0) -> dict:
     """One decode (nq = 1) or chunked-prefill (nq > 1) step of the layer.
 
     q_pre [B, Hq, nq, D] bf16; w_q [Hr, D, R] bf16; k_idx [B, Hi, >=N, R] bf16
     (indexer keys; retrieval head r reads head r // idx_group);
     k_cache / v_cache [B, Hkv, >=N, D] bf16
     (post-RoPE keys, values); head_mode [Hq] (1 retrieval, 0 local).
-    Retrieval heads: eq. (4) scores, Top-P, eq. (5) over the selected set.
+    Retrieval heads: eq. (4) scores, Top-P (or fixed top-k when top_k > 0),
+    eq. (5) over the selected set.
     Local heads: eq. (5) over the sliding window plus sinks.
     ``heads``/``batches``/``queries`` restrict the work to a sample.
     Returns out[(b, h, i)] fp64 [D], sel[(b, r, i)], topp[(b, r, i)].
@@ -316,7 +357,7 @@ def decode_step(q_pre, w_q, k_idx, k_cache, v_cache, head_mode, *, N, p, window,
                     r = rindex[h]
                     q_idx = index_project(q_pre[b, h, i], w_q[r])
                     s = indexer_logits(q_idx, k_idx[b, r // idx_group, :m + 1])
-                    t = topp_select(s, p)
+                    t = topk_select(s, top_k) if top_k > 0 else topp_select(s, p)
                     rows = t["sel"]
                     sel[(b, r, i)] = rows
                     topp[(b, r, i)] = t

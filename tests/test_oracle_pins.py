@@ -240,6 +240,82 @@ def test_topp_agrees_with_sorted_outside_boundary_bin():
                 assert n not in hist and n not in srt
 
 
+# ---------------------------------------------------------------- fixed top-k on the histogram order
+def test_topk_hand_example():
+    lines = [l.strip() for l in open(os.path.join(GOLDEN, "topk_hand_example.txt")) if l.strip() and not l.startswith("#")]
+    logits = np.array([float(v) for v in lines[0].split(":")[1].split(",")], dtype=np.float32)
+    for line in lines[1:]:
+        k, bstar, sel = (f.strip() for f in line.split(";"))
+        t = O.topk_select(logits, int(k))
+        assert t["bstar"] == int(bstar)
+        assert list(t["sel"]) == [int(v) for v in sel.split(",")]
+
+
+def test_topk_count_all_and_dominant():
+    rng = np.random.default_rng(21)
+    s = (rng.standard_normal(777) * 2).astype(np.float32)
+    for k in (1, 2, 17, 500, 776):
+        assert len(O.topk_select(s, k)["sel"]) == k
+    for k in (777, 778, 10 ** 6):
+        assert list(O.topk_select(s, k)["sel"]) == list(range(777))
+    s[400] = 50.0
+    assert list(O.topk_select(s, 1)["sel"]) == [400]
+
+
+@pytest.mark.parametrize("N", [1, 5, 100, 4097])
+def test_topk_uniform_takes_first_positions(N):
+    s = np.full(N, -0.7, dtype=np.float32)
+    for k in (1, 3, N // 2 + 1, N):
+        assert list(O.topk_select(s, k)["sel"]) == list(range(min(k, N)))
+
+
+def test_topk_agrees_with_sorted_outside_boundary_bin():
+    rng = np.random.default_rng(22)
+    for trial in range(60):
+        n = int(rng.integers(1, 3000))
+        s = (rng.standard_normal(n) * rng.uniform(0.1, 6)).astype(np.float32)
+        if trial % 3 == 0:
+            s = np.round(s * 4) / 4                              # ties
+        k = int(rng.integers(1, n + 1))
+        t = O.topk_select(s, k)
+        hist = set(t["sel"].tolist())
+        srt = set(O.sorted_topk(s, k).tolist())
+        bins = t["bins"]
+        if k >= n:
+            assert hist == srt == set(range(n))
+            continue
+        for x in range(n):
+            if bins[x] < t["bstar"]:
+                assert x in hist and x in srt
+            elif bins[x] > t["bstar"]:
+                assert x not in hist and x not in srt
+        in_b = lambda S: sum(1 for x in S if bins[x] == t["bstar"])
+        assert in_b(hist) == in_b(srt)
+
+
+def test_topk_at_topp_budget_equals_topp():
+    """The count rule and the mass rule share one order: top-k with k = |S_p| is S_p."""
+    rng = np.random.default_rng(23)
+    for trial in range(40):
+        s = (rng.standard_normal(2500) * rng.uniform(0.2, 5)).astype(np.float32)
+        for p in (0.3, 0.9, 0.99):
+            sp = O.topp_select(s, p)["sel"]
+            assert list(O.topk_select(s, len(sp))["sel"]) == list(sp)
+
+
+def test_topk_nested_and_shift_invariant():
+    rng = np.random.default_rng(24)
+    for trial in range(20):
+        s = (np.round(rng.standard_normal(1500) * 64) / 64).astype(np.float32)
+        prev = set()
+        for k in (1, 10, 100, 700, 1499):
+            cur = set(O.topk_select(s, k)["sel"].tolist())
+            assert prev <= cur
+            prev = cur
+            shifted = (s.astype(np.float64) + 3 * 0.125).astype(np.float32)   # exact: |s| < 8, step 1/64
+            assert list(O.topk_select(shifted, k)["sel"]) == sorted(cur)
+
+
 def test_topp_invariants():
     rng = np.random.default_rng(10)
     for trial in range(40):
