@@ -86,6 +86,7 @@ class WorkloadSpec:
     topic_mix: float = 0.3
     # retrieval heads sharing one indexer-key head (1: one per head; G: one per KV group)
     idx_group: int = 1
+    top_k: int = 0              # selection rule of the layer (0: Top-P with p); no effect on the draws
     # "unit": q = u; "table": q = s_(b,r) * u with s from the calibration table
     query_scale: str = "unit"
     shared_w: bool = True

@@ -85,6 +85,11 @@ typedef struct rtp_layer {
                                  group (then retrieval heads come in whole groups).  The indexer-key
                                  heads Hi = Hr / idx_group are numbered in retrieval-head order:
                                  k_idx is [B,Hi,Ncap,R], w_k is [Hi,D,R]; w_q stays [Hr,D,R] */
+  int64_t top_k;              /* 0 = Top-P with mass p (FASB eq. (5)).  > 0 = fixed top-k, the
+                                 budget-by-count counterpart FASB section 2.3 / Table 1 compares
+                                 with Top-P: the first top_k positions in the order (histogram bin
+                                 ascending, position ascending), every position when top_k >= m+1;
+                                 p is then ignored.  < 0 is RTP_ERR_ARG. */
 } rtp_layer;
 
 /* Number of retrieval heads Hr implied by layer->head_mode (or a negative status). */

@@ -39,6 +39,7 @@ class _CLayer(ctypes.Structure):
         ("R", ctypes.c_int32), ("nq", ctypes.c_int32), ("N", ctypes.c_int64), ("Ncap", ctypes.c_int64),
         ("head_mode", ctypes.POINTER(ctypes.c_int8)), ("p", ctypes.c_float), ("window", ctypes.c_int32),
         ("n_sink", ctypes.c_int32), ("rope_theta", ctypes.c_double), ("idx_group", ctypes.c_int32),
+        ("top_k", ctypes.c_int64),
     ]
 
 
@@ -96,6 +97,7 @@ class Layer:
     D: int = 128
     R: int = 16
     idx_group: int = 1        # retrieval heads sharing one indexer-key head (1 or Hq // Hkv)
+    top_k: int = 0            # 0: Top-P with mass p; > 0: fixed top-k on the histogram order
     _keep: list = field(default_factory=list, repr=False, compare=False)
 
     @property
@@ -116,7 +118,7 @@ class Layer:
         self._keep = [hm]
         return _CLayer(self.B, self.Hq, self.Hkv, self.D, self.R, self.nq, self.N, self.cap_rows,
                        ctypes.cast(hm, ctypes.POINTER(ctypes.c_int8)), self.p, self.window, self.n_sink,
-                       self.rope_theta, self.idx_group)
+                       self.rope_theta, self.idx_group, self.top_k)
 
 
 def _check(status: int, what: str):

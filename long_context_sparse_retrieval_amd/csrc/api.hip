@@ -32,6 +32,7 @@ int validate_layer(const rtp_layer *L) {
     if (L->head_mode[h] != 0 && L->head_mode[h] != 1) return RTP_ERR_ARG;
   const int G = L->Hq / L->Hkv;
   if (L->idx_group < 0 || (L->idx_group > 1 && L->idx_group != G)) return RTP_ERR_ARG;
+  if (L->top_k < 0) return RTP_ERR_ARG;
   if (L->idx_group > 1)        // shared indexer keys: retrieval heads come in whole KV groups
     for (int kv = 0; kv < L->Hkv; ++kv)
       for (int h = kv * G + 1; h < (kv + 1) * G; ++h)
@@ -77,6 +78,7 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
   g.N = L->N;
   g.Ncap = L->Ncap;
   g.p = L->p;
+  g.topk = L->top_k;
   g.window = L->window;
   g.n_sink = L->n_sink;
   g.theta = L->rope_theta;

@@ -180,9 +180,9 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
             uint32_t w;
             if (j >= kBins - 1) {
               j = kBins - 1;
-              w = cell_weight(s, cq - (kBins - 1));
+              w = token_weight(g, s, cq - (kBins - 1));
             } else {
-              w = cell_weight(s, cell);
+              w = token_weight(g, s, cell);
             }
             atomicAdd(&sm.h.mass[qc][j], (unsigned long long)w);
             atomicAdd(&sm.h.cnt[qc][j], 1u);
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int j = 4 * lane + k;
-      W[k] = (double)sm.h.mass[q][j] * 0x1p-23 * exp(-(double)j * 0.125);
+      W[k] = (double)sm.h.mass[q][j] * 0x1p-23 * bin_scale(g, -(double)j * 0.125);
       loc += W[k];
     }
     double incl = loc;                                    // wave inclusive scan (fixed order)
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
     }
     const double Z = __shfl(incl, 63);
     double e = incl - loc;
-    const double need = (double)g.p * Z;
+    const double need = g.topk ? (double)g.topk : (double)g.p * Z;     // top-k: Z counts positions
     int cand = kBins;
     double before_c = 0.0;
 #pragma unroll
@@ -227,7 +227,9 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
     for (int off = 32; off > 0; off >>= 1) bstar = min(bstar, __shfl_xor(bstar, off));
     if (bstar >= kBins) bstar = kBins - 1;
     const double before = __shfl(before_c, bstar / 4);
-    const int all = (g.p >= 1.0f || bstar >= kBins - 1) ? 1 : 0;
+    // the query's bins are relative to its own maximum, so for top-k the
+    // clamp bin is an ordinary boundary
+    const int all = (g.topk ? need >= Z : (g.p >= 1.0f || bstar >= kBins - 1)) ? 1 : 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) cnt_lt += (4 * lane + k < bstar) ? (int)sm.h.cnt[q][4 * lane + k] : 0;
 #pragma unroll
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
       PfSel &ps = sm.sel[q];
       ps.all = all;
       ps.bstar = all ? kBins : bstar;
-      ps.r_u = (need - before) * 0x1p23 * exp((double)bstar * 0.125);
+      ps.r_u = (need - before) * 0x1p23 * bin_scale(g, (double)bstar * 0.125);
       ps.n_sure = all ? (int)(mpos0 + qi0 + q + 1) : cnt_lt;
     }
   }
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
                 ++ns;
               } else if (!allq && j == bs) {
                 ++nbb;
-                bm += cell_weight(s, cell);
+                bm += token_weight(g, s, cell);
               }
             }
           },
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
               const int j = min(cq - cell, kBins - 1);
               sure[i] = ok && j < bs;
               bnd[i] = ok && !allq && j == bs;
-              w[i] = (bnd[i] && cur == cs) ? cell_weight(s, cell) : 0u;
+              w[i] = (bnd[i] && cur == cs) ? token_weight(g, s, cell) : 0u;
               ls += sure[i] ? 1 : 0;
               lw += w[i];
             }

@@ -61,6 +61,7 @@ struct Geo {
   int Hi;               // indexer-key heads = Hr / ig
   long long N, Ncap;
   float p;
+  long long topk;       // 0: Top-P with mass p; > 0: fixed top-k on the histogram order
   int window, n_sink;
   double theta;
   // indexer scan tiling
@@ -150,6 +151,19 @@ __device__ __forceinline__ uint32_t cell_weight(float s, int ref) {
   const float e = __builtin_amdgcn_exp2f(__fmul_rn(x, 1.44269504088896341f));
   return (uint32_t)__fmul_rn(e, 8388608.0f);
 }
+
+// Selection weight of one token in the same fixed-point units: its in-cell
+// softmax weight for Top-P; exactly 1 (2^23) for fixed top-k, so the same
+// exact integer sums then count tokens and the same threshold and ordered
+// fill pick the first k positions of the (bin, position) order.
+constexpr uint32_t kUnitWeight = 1u << 23;
+__device__ __forceinline__ uint32_t token_weight(const Geo &g, float s, int ref) {
+  return g.topk ? kUnitWeight : cell_weight(s, ref);
+}
+
+// Factor exp(x) that brings in-cell masses of different cells to one scale
+// (Top-P); counts need none (top-k).
+__device__ __forceinline__ double bin_scale(const Geo &g, double x) { return g.topk ? 1.0 : exp(x); }
 
 // RoPE frequency theta_i = base^(-2i/D), i = 0..D/2-1 (FASB eq. (1)).
 __device__ __forceinline__ double rope_freq(double base, int i) {

@@ -121,7 +121,7 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
     const bool ok = sc != -INFINITY;
     const float s = ok ? sc : 0.f;
     const int cell = score_cell(s);
-    const unsigned long long add = ok ? ((unsigned long long)cell_weight(s, cell) | (1ull << kCountShift)) : 0ull;
+    const unsigned long long add = ok ? ((unsigned long long)token_weight(g, s, cell) | (1ull << kCountShift)) : 0ull;
     atomicAdd(&sm.hist[wv][cell & (kCells - 1)], add);
     mx = fmaxf(mx, sc);
     cmin = min(cmin, ok ? cell : INT32_MAX);
@@ -198,7 +198,7 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
         unsigned long long e = 0;
 #pragma unroll
         for (int w = 0; w < 4; ++w) e += sm.hist[w][cell & (kCells - 1)];
-        cm = (double)(e & kMassMask) * exp(-(double)tid * 0.125);
+        cm = (double)(e & kMassMask) * bin_scale(g, -(double)tid * 0.125);
         cc = e >> kCountShift;
       }
       double tm;
@@ -218,7 +218,7 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
       if (sc == -INFINITY) continue;
       const int cell = score_cell(sc);
       const int jb = c_t - cell >= kBins - 1 ? kBins - 1 : c_t - cell;
-      const uint32_t u = jb == kBins - 1 ? cell_weight(sc, c_t - (kBins - 1)) : cell_weight(sc, cell);
+      const uint32_t u = jb == kBins - 1 ? token_weight(g, sc, c_t - (kBins - 1)) : token_weight(g, sc, cell);
       atomicAdd(&sm.hist[wv][jb], (unsigned long long)u | (1ull << kCountShift));
     }
     __syncthreads();
@@ -334,10 +334,10 @@ __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, 
     // clamp cells c - 255 - j - 256 x, x = 0, 1, ...: the first one (R1) was loaded by the caller
     H = j <= kBnd ? H_ring : 0ull;
     const long long cell1 = (long long)c - (kBins - 1) - j;
-    if (R1) w255 += (double)R1 * exp((double)(cell1 - c) * 0.125);
+    if (R1) w255 += (double)R1 * bin_scale(g, (double)(cell1 - c) * 0.125);
     for (long long cell = cell1 - kWG; cell >= base_min; cell -= kWG) {
       const unsigned long long mj = ring[cell & (kRing - 1)];
-      if (mj) w255 += (double)mj * exp((double)(cell - c) * 0.125);
+      if (mj) w255 += (double)mj * bin_scale(g, (double)(cell - c) * 0.125);
     }
   } else {
     for (int t = 0; t < g.nt; ++t) {
@@ -347,7 +347,7 @@ __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, 
       if (j <= kBnd && j - d >= 0) H += ts[t].mass[j - d];
       if (j + d >= kBins - 1) {
         const unsigned long long mj = ts[t].mass[j];
-        if (mj) w255 += (double)mj * exp(-(double)(j + d) * 0.125);
+        if (mj) w255 += (double)mj * bin_scale(g, -(double)(j + d) * 0.125);
       }
     }
   }
@@ -361,19 +361,40 @@ __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, 
   }
   const double W255 = sm.wcum[0] * 0x1p-23;
   __syncthreads();
-  const double Wj = j <= kBnd ? (double)H * 0x1p-23 * exp(-(double)j * 0.125) : W255;
+  const double Wj = j <= kBnd ? (double)H * 0x1p-23 * bin_scale(g, -(double)j * 0.125) : W255;
   double Z;
   const double excl = block_excl_scan<double>(Wj, Z, sm.red_d);
-  const double need = (double)g.p * Z;
+  // Top-P needs the mass p Z; top-k needs k tokens (every weight is exactly 1,
+  // so Z is the number of positions and every sum here is an exact integer)
+  const double need = g.topk ? (double)g.topk : (double)g.p * Z;
   int bstar = block_min<int>(excl + Wj >= need ? j : kBins, sm.red_i);
   if (bstar >= kBins) bstar = kBins - 1;
   sm.wcum[j] = excl;                      // mass above bin j
   __syncthreads();
   const double before = sm.wcum[bstar];
   __syncthreads();
-  all_out = (g.p >= 1.0f || bstar >= kBins - 1) ? 1 : 0;
-  r_u_out = (need - before) * 0x1p23 * exp((double)bstar * 0.125);
+  // Top-P: p >= 1, or the boundary in the clamp bin (whose in-cell masses
+  // have no common scale; its mass is below e^-31.75 of the top cell, so
+  // everything is taken).  Top-k: k covers every position.
+  all_out = (g.topk ? need >= Z : (g.p >= 1.0f || bstar >= kBins - 1)) ? 1 : 0;
+  r_u_out = (need - before) * 0x1p23 * bin_scale(g, (double)bstar * 0.125);
   bstar_out = bstar;
+}
+
+// Local codes [lo, hi] of a tile (max cell ct) that hold the query's boundary
+// bin b*; codes below lo lie above b*.  A regular b* is one local bin (or none:
+// lo = hi = -1).  The clamp bin, a boundary only for top-k, gathers every
+// local bin at or below the query's cell c - 255.
+__device__ __forceinline__ void bnd_range(int bstar, int c, int ct, int &lo, int &hi) {
+  const long long d = (long long)c - ct;
+  if (bstar <= kBnd) {
+    const long long bl = (long long)bstar - d;
+    lo = hi = bl < 0 ? -1 : (int)bl;
+  } else {
+    const long long l = (long long)(kBins - 1) - d;
+    lo = l < 0 ? 0 : (int)l;
+    hi = kBins - 1;
+  }
 }
 
 struct FinShared {
@@ -473,12 +494,12 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
     int sure = 0, bc = 0;
     const int ctt = t0 == 0 ? ct0 : (tt < g.nt ? ts[tt].c_t : INT32_MIN);
     if (ctt != INT32_MIN && !all) {
-      const long long bl = (long long)bstar - ((long long)c - ctt);
-      if (bl >= 1) sure = (int)ts[tt].cum[(bl < kBins - 1 ? (int)bl : kBins - 1) - 1];
-      if (bl >= 0 && bl <= kBnd) {
-        const uint32_t hi = ts[tt].cum[bl];
-        bc = (int)(hi - (bl ? ts[tt].cum[bl - 1] : 0u));
-        bm = ts[tt].mass[bl];
+      int lo, hi;
+      bnd_range(bstar, c, ctt, lo, hi);
+      if (lo >= 1) sure = (int)ts[tt].cum[lo - 1];
+      if (hi >= 0) {
+        bc = (int)(ts[tt].cum[hi] - (lo ? ts[tt].cum[lo - 1] : 0u));
+        bm = g.topk ? (unsigned long long)bc << 23 : ts[tt].mass[lo];
       }
     }
     unsigned long long totP, totSB;
@@ -517,12 +538,9 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
     const TileSel tl = sm.tsel[t - t_begin];
     const int ct = sm.ct[t - t_begin];
     if (ct == INT32_MIN) continue;                      // no position in the tile
-    int bl = -1;
-    if (!all) {
-      const long long blv = (long long)bstar - ((long long)c - ct);
-      bl = blv < -1 ? -1 : (int)blv;
-    }
-    const bool bnd_ok = !all && bl >= 0 && bl <= kBnd;
+    int lo = -1, hi = -1;
+    if (!all) bnd_range(bstar, c, ct, lo, hi);
+    const bool bnd_ok = !all && hi >= 0;
     const bool crossing = bnd_ok && t == tstar;
     const bool take_all_bnd = bnd_ok && t < tstar;
     // block-uniform skip of a tile that contributes nothing
@@ -557,8 +575,8 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
 #pragma unroll
       for (int k = 0; k < TPT; ++k) {
         const int code = (int)((cw[k >> 2] >> (8 * (k & 3))) & 0xffu);
-        sure_m |= (code < bl ? 1u : 0u) << k;
-        bnd_m |= (code == bl ? 1u : 0u) << k;
+        sure_m |= (code < lo ? 1u : 0u) << k;
+        bnd_m |= (code >= lo && code <= hi ? 1u : 0u) << k;
       }
       sure_m &= valid_m;
       bnd_m = (take_all_bnd || crossing) ? (bnd_m & valid_m) : 0u;
@@ -582,7 +600,9 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
         __syncthreads();
         const int cnt = nbt - r0 < kWG ? nbt - r0 : kWG;
         uint32_t wt = 0;                                  // < 1.14 * 2^23 each, < 2^32 per round
-        if (tid < cnt) {
+        if (tid < cnt && g.topk) {
+          wt = kUnitWeight;                               // top-k: every token counts once
+        } else if (tid < cnt) {
           long long n = sm.blist[tid];
           n = n < 0 ? 0 : (n > m ? m : n);
           float sc;

@@ -73,6 +73,21 @@ def check_set(gpu_list: np.ndarray, gpu_count: int, cap: int, t: dict, logits: n
     return "tolerated"
 
 
+def check_topk_set(gpu_list: np.ndarray, gpu_count: int, cap: int, t: dict, k: int, what: str = ""):
+    """A GPU fixed top-k set must equal the oracle's exactly (only counts decide)."""
+    ref = t["sel"]
+    assert gpu_count == len(ref) == min(k, len(t["bins"])), f"{what}: count {gpu_count} vs {len(ref)}"
+    assert gpu_count <= cap, f"{what}: list truncated"
+    got = np.asarray(gpu_list[:gpu_count], dtype=np.int64)
+    assert np.array_equal(np.sort(got), ref), f"{what}: sets differ"
+    if t["bstar"] < O.N_BINS:
+        # layout: positions above the boundary bin, then those taken from it, each ascending
+        nsure = int(np.sum(t["bins"] < t["bstar"]))
+        assert np.all(np.diff(got[:nsure]) > 0) and np.all(np.diff(got[nsure:]) > 0), f"{what}: order"
+        assert np.all(t["bins"][got[:nsure]] < t["bstar"]), f"{what}: layout"
+    return "exact"
+
+
 def sdpa_f64(q_rot, k_rows, v_rows):
     return torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(np.asarray(q_rot, np.float64))[None, None, None],
@@ -85,7 +100,7 @@ def layer_of(spec, rtp, N=None, Ncap=None, p=None, window=None, n_sink=None):
                      head_mode=[int(x) for x in spec.head_mode()], nq=spec.nq, Ncap=Ncap,
                      p=spec.p if p is None else p, window=spec.window if window is None else window,
                      n_sink=spec.n_sink if n_sink is None else n_sink, rope_theta=spec.rope_theta,
-                     idx_group=spec.idx_group)
+                     idx_group=spec.idx_group, top_k=spec.top_k)
 
 
 def edge_fraction(logits):

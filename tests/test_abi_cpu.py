@@ -65,7 +65,7 @@ def test_workspace_sizing_monotone():
     (dict(D=64), -2), (dict(R=8), -2), (dict(Hkv=3), -2), (dict(N=0), -2), (dict(N=10, Ncap=5), -2),
     (dict(nq=0), -2), (dict(N=1 << 31, Ncap=1 << 31), -2), (dict(p=0.0), -1), (dict(p=float("nan")), -1),
     (dict(window=0), -1), (dict(n_sink=-1), -1), (dict(head_mode=[2, 0, 0, 0, 0, 0, 0, 0]), -1),
-    (dict(rope_theta=0.0), -1),
+    (dict(rope_theta=0.0), -1), (dict(top_k=-1), -1), (dict(idx_group=3), -1), (dict(idx_group=-1), -1),
 ])
 def test_layer_validation(kw, code):
     lay = _layer(**kw)

@@ -10,7 +10,7 @@ import torch
 import gen
 import long_context_sparse_retrieval_amd as rtp
 import oracle as O
-from parity import (check_output, check_set, dev_bf16, host_bf16, layer_of, say, sdpa_f64)
+from parity import (check_output, check_set, check_topk_set, dev_bf16, host_bf16, layer_of, say, sdpa_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -164,6 +164,34 @@ def test_topp_select_truncates_at_cap():
     assert np.all(np.isin(got, t["sel"]))
 
 
+# ----------------------------------------------------------------------------- fixed top-k
+@pytest.mark.parametrize("N", [1, 5, 1000, 4097, 33000])
+@pytest.mark.parametrize("kind", ["gauss1", "uniform", "dominant", "ties", "wide", "huge", "needles"])
+@pytest.mark.parametrize("k", [1, 37, 2048])
+def test_topk_select_matches_oracle(N, kind, k):
+    """Same kernels with every weight 1: the first k of the (bin, position) order, exactly.
+
+    "wide" puts the boundary into the clamp bin whenever fewer than k scores lie
+    within 32 logits of the maximum; "huge" takes the merge path for cells
+    spanning more than the ring.
+    """
+    say(f"topk_select N={N} kind={kind} k={k}")
+    rng = np.random.default_rng(N * 11 + len(kind) + k)
+    B, nq = 2, 2 if N >= 2 else 1
+    lay = rtp.Layer(B=B, Hq=2, Hkv=1, N=N, nq=nq, head_mode=[1, 1], top_k=k)
+    logits = np.stack([np.stack([np.stack([_logit_case(kind, rng, N) for _ in range(nq)]) for _ in range(2)])
+                       for _ in range(B)])
+    ws = rtp.workspace(lay)
+    idx, cnt = rtp.topp_select(lay, torch.from_numpy(logits).cuda(), N, ws)
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        for r in range(2):
+            for i in range(nq):
+                m = N - nq + i
+                t = O.topk_select(logits[b, r, i, :m + 1], k)
+                check_topk_set(idx[b, r, i], int(cnt[b, r, i]), N, t, k, f"b{b} r{r} i{i}")
+
+
 # ----------------------------------------------------------------------------- attention
 @pytest.mark.parametrize("counts", [(0, 1, 37, 600), (5000, 70000, 3, 1)])
 def test_sparse_attn_matches_oracle(counts):
@@ -242,6 +270,12 @@ DECODE_CASES = {
     "cfg2-shared-keys": (2, dict(B=2, N=3000, window=512, idx_group=4), None),
     "cfg2-shared-keys-indepW": (2, dict(B=2, N=3000, window=512, idx_group=4, shared_w=False), None),
     "cfg4-shared-keys": (4, dict(N=40000, window=2048, query_scale="unit", idx_group=8), 0.3),
+    # fixed top-k instead of Top-P
+    "cfg2-topk": (2, dict(B=2, N=3000, window=512, top_k=100), None),
+    "cfg4-small-topk": (4, dict(N=40000, window=2048, query_scale="unit", top_k=2048), 0.3),
+    "cfg4-shared-keys-topk": (4, dict(N=40000, window=2048, query_scale="unit", idx_group=8, top_k=500), 0.3),
+    "topk-all": (2, dict(B=1, N=2500, window=300, top_k=2500), None),
+    "topk-1": (1, dict(top_k=1), None),
 }
 
 
@@ -273,13 +307,17 @@ def test_decode_step_matches_oracle(case):
     assert np.array_equal(out, out2), "two runs differ (non-deterministic)"
     res = O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
                         n_sink=spec.n_sink, rope_base=spec.rope_theta, want_logits=True,
-                        idx_group=spec.idx_group)
+                        idx_group=spec.idx_group, top_k=spec.top_k)
     verdicts = []
     for (b, h, i), ref in res["out"].items():
         check_output(out[b, h, i], ref, f"{case} b{b} h{h}")
     for (b, r, i), t in res["topp"].items():
-        verdicts.append(check_set(idx[b, r, i], int(cnt[b, r, i]), spec.N, t, res["logits"][(b, r, i)], spec.p,
-                                  f"{case} b{b} r{r}"))
+        if spec.top_k:
+            verdicts.append(check_topk_set(idx[b, r, i], int(cnt[b, r, i]), spec.N, t, spec.top_k,
+                                           f"{case} b{b} r{r}"))
+        else:
+            verdicts.append(check_set(idx[b, r, i], int(cnt[b, r, i]), spec.N, t, res["logits"][(b, r, i)],
+                                      spec.p, f"{case} b{b} r{r}"))
     say(f"{case}: sets {verdicts.count('exact')} exact, {verdicts.count('tolerated')} tolerated; "
         f"|S| = {sorted(int(c) for c in cnt.ravel())}")
 
@@ -294,6 +332,8 @@ PREFILL_CASES = {
     "pf-query-chunks": (5, dict(N=5000, nq=80, diffuse=(300, 0.5)), None, "16"),
     "pf-layer-with-local-heads": (2, dict(B=2, N=3000, nq=24, n_needles=16, window=512), {}, None),
     "pf-shared-keys": (5, dict(N=3000, nq=40, diffuse=(200, 0.5), idx_group=4), None, None),
+    "pf-topk": (5, dict(N=3000, nq=40, diffuse=(200, 0.5), top_k=300), None, None),
+    "pf-topk-chunks": (5, dict(N=5000, nq=80, diffuse=(300, 0.5), top_k=1), None, "16"),
 }
 
 
@@ -325,11 +365,15 @@ def test_prefill_step_matches_oracle(case, monkeypatch):
     idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
     res = O.decode_step(wl.q_pre, wl.w_q, ki, kc, wl.v, wl.head_mode, N=spec.N, p=spec.p, window=spec.window,
                         n_sink=spec.n_sink, rope_base=spec.rope_theta, want_logits=True,
-                        idx_group=spec.idx_group)
+                        idx_group=spec.idx_group, top_k=spec.top_k)
     for (b, h, i), ref in res["out"].items():
         check_output(out[b, h, i], ref, f"{case} b{b} h{h} i{i}")
-    verdicts = [check_set(idx[b, r, i], int(cnt[b, r, i]), cap, t, res["logits"][(b, r, i)], spec.p,
-                          f"{case} b{b} r{r} i{i}") for (b, r, i), t in res["topp"].items()]
+    if spec.top_k:
+        verdicts = [check_topk_set(idx[b, r, i], int(cnt[b, r, i]), cap, t, spec.top_k, f"{case} b{b} r{r} i{i}")
+                    for (b, r, i), t in res["topp"].items()]
+    else:
+        verdicts = [check_set(idx[b, r, i], int(cnt[b, r, i]), cap, t, res["logits"][(b, r, i)], spec.p,
+                              f"{case} b{b} r{r} i{i}") for (b, r, i), t in res["topp"].items()]
     say(f"{case}: sets {verdicts.count('exact')} exact, {verdicts.count('tolerated')} tolerated")
 
 
