@@ -18,6 +18,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -35,6 +36,7 @@ import long_context_sparse_retrieval_amd as rtp  # noqa: E402
 
 METRIC = "decode attn µs/step + achieved HBM GB/s at 128K and 1M ctx, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
+TOPK_BENCH = 2048          # fixed budget of the top-k variant line (about the diffuse queries' Top-P budget)
 CSRC = os.path.join(ROOT, "long_context_sparse_retrieval_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "phase_a_kernel.qwen3-32b-layer-1m-b1.traffic.json")
 CPU_SAMPLE_SECONDS = 12.0
@@ -280,6 +282,14 @@ def main():
         log(f"[bench] cfg{cfg}: {ms * 1e3:.1f} us/step, phase-A kernel {ms_pa * 1e3:.1f} us, {gbps:.0f} GB/s "
             f"algorithmic; |S| {case.counts.ravel().tolist()}; dense comparator {ms_dense * 1e3:.1f} us "
             f"({dense_bytes / (ms_dense * 1e-3) / 1e9:.0f} GB/s), sparse step {ms_dense / ms:.2f}x faster")
+        if cfg == 4:
+            # the fixed top-k variant of the same kernels on the same caches
+            top_p_layer = case.layer
+            case.layer = dataclasses.replace(top_p_layer, top_k=TOPK_BENCH)
+            ms_k, ms_pa_k = case.run(max(20, args.steps // 4), args.warmup)
+            case.layer = top_p_layer
+            summ[cfg].update(topk_us=ms_k * 1e3, topk_pa_us=ms_pa_k * 1e3)
+            log(f"[bench] cfg{cfg}: fixed top-k (k = {TOPK_BENCH}) {ms_k * 1e3:.1f} us/step")
         if cfg == 4 and not args.no_cpu_baseline:
             t0 = time.time()
             cpu = cpu_baseline(case)
@@ -329,6 +339,9 @@ def main():
     }
     if main_cfg == 4:
         out["roofline"]["traffic"] = traffic_per_launch(spec.name)
+        out["fixed_top_k"] = {"k": TOPK_BENCH, "us_per_step": round(s["topk_us"], 2),
+                              "phase_a_kernel_us": round(s["topk_pa_us"], 2),
+                              "what": "same step with rtp_layer.top_k = k instead of Top-P, same caches"}
     if cpu is not None:
         out["cpu_baseline"] = cpu
     if 3 in summ and main_cfg != 3:
