@@ -101,7 +101,11 @@ size_t rtp_workspace_bytes(const rtp_layer *layer);
 
 /* Prepare a workspace for first use (enqueues a fill kernel on `stream`).  A
  * workspace must be prepared once before its first use; every call leaves it
- * ready for the next.  Calls that share one workspace must not overlap. */
+ * ready for the next call on a layer of the same shape (B, Hq, Hkv, nq and
+ * head_mode; N, p, top_k, window and the other fields may change between
+ * calls, so a growing decode cache keeps one workspace).  Before a call on a
+ * layer of another shape, prepare it again.  Calls that share one workspace
+ * must not overlap. */
 int rtp_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Static text for a status code. */

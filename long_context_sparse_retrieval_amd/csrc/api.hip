@@ -1,5 +1,6 @@
 // C entry points of librtp.so: argument validation, workspace layout, launch.
 // The operations and their sources are documented in include/rtp.h.
+#include <algorithm>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -50,11 +51,11 @@ int pick_tile(long long units, long long N) {
   return T;
 }
 
-// Fills the geometry and workspace layout; ws may be null (sizing only).
+// Geometry of a call (tiling, split counts; no memory).
 // dense: the comparator's plan -- every head attends like a local head over a
 // window covering the whole cache with no sinks, in chunks of about 2048
 // workgroups in total.
-int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
+int make_geo(const rtp_layer *L, bool dense, Geo &g) {
   const int st = validate_layer(L);
   if (st != RTP_OK) return st;
   int8_t all_local[kMaxHq];
@@ -68,7 +69,6 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
     LD.idx_group = 1;
     L = &LD;
   }
-  Geo g;
   memset(&g, 0, sizeof(g));
   g.B = L->B;
   g.Hq = L->Hq;
@@ -128,19 +128,37 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
     g.swa_chunk = (int)chunk;
     g.swa_nch = (int)((Lrows + chunk - 1) / chunk);
   }
-  // workspace layout
+  return RTP_OK;
+}
+
+// Geometry and workspace layout of a call; ws may be null (sizing only).
+// The workspace starts with the state every call leaves zeroed for the next
+// one (merge ring, cell ranges, arrival counters).  Its layout depends only on
+// B, Hq, Hkv, nq and head_mode -- not on N, so a growing decode cache keeps
+// using one workspace -- and is shared by the step's plan and the dense
+// comparator's plan, whose transient regions follow it.
+int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
+  Geo reg, den;
+  int st = make_geo(L, false, reg);
+  if (st != RTP_OK) return st;
+  st = make_geo(L, true, den);
+  if (st != RTP_OK) return st;
+  Geo g = dense ? den : reg;
   size_t off = 0;
   const size_t units = (size_t)g.units, nt = (size_t)g.nt;
+  const size_t reg_units = (size_t)reg.units;
+  const size_t swa_ctrs = std::max((size_t)reg.swa_units * reg.swa_hb, (size_t)den.swa_units * den.swa_hb);
   const size_t o_ring = off;
-  off = align_up(off + units * kRing * 8);
+  off = align_up(off + reg_units * kRing * 8);
   const size_t o_cmax = off;
-  off = align_up(off + units * 4);
+  off = align_up(off + reg_units * 4);
   const size_t o_cmin = off;
-  off = align_up(off + units * 4);
+  off = align_up(off + reg_units * 4);
   const size_t o_ctr_fin = off;
-  off = align_up(off + units * 4);
+  off = align_up(off + reg_units * 4);
   const size_t o_ctr_swa = off;
-  off = align_up(off + (size_t)g.swa_units * g.swa_hb * 4);
+  off = align_up(off + swa_ctrs * 4);
+  // transient regions of this call
   const size_t o_qprep = off;
   off = align_up(off + units * sizeof(QPrep));
   const size_t o_tsum = off;

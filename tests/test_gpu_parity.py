@@ -3,6 +3,8 @@
 Sizes are small enough for the oracle to finish in seconds while spanning
 several scan tiles (1024..8192 positions) and a ragged tail.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -400,3 +402,42 @@ def test_dense_attn_matches_oracle(N, nq, Hq, Hkv):
                         rope_base=1e6)
     for (b, h, i), ref in res["out"].items():
         check_output(out[b, h, i], ref, f"dense b{b} h{h} i{i}")
+
+
+# ----------------------------------------------------------------------------- one workspace, many calls
+def test_workspace_serves_every_call_in_sequence():
+    """Every call leaves the workspace ready for the next call on a layer of the
+    same shape: the dense comparator's and the stand-alone calls' scratch must
+    not disturb the step's persistent state (merge ring, cell ranges,
+    counters), and N, p and top_k may change between calls."""
+    spec = gen.spec_for(2, B=2, N=6000, window=512)
+    say(f"workspace sequence: {spec}")
+    wl = gen.make_workload(spec, 77)
+    lay = layer_of(spec, rtp)
+    k_pre = dev_bf16(wl.k_pre)
+    k = rtp.rope_keys(lay, k_pre)
+    k_idx = rtp.index_keys(lay, k_pre, dev_bf16(wl.w_k))
+    v = dev_bf16(wl.v)
+    q, wq = dev_bf16(wl.q_pre), dev_bf16(wl.w_q)
+    lay_k = dataclasses.replace(lay, top_k=300)
+    lay_short = dataclasses.replace(lay, N=5000, Ncap=spec.N, p=0.8)      # same caches, shorter context
+
+    def step(layer, ws):
+        return rtp.decode_step(layer, q, wq, k_idx, k, v, ws).cpu().numpy()
+
+    ref = {name: step(l, rtp.workspace(l)) for name, l in (("p", lay), ("k", lay_k), ("short", lay_short))}
+    ref_dense = rtp.dense_attn(lay, q, k, v, rtp.workspace(lay)).cpu().numpy()
+    ws = rtp.workspace(lay)
+    seq = ["p", "dense", "p", "swa", "k", "dense", "short", "logits", "p", "dense", "k", "short", "p"]
+    for j, x in enumerate(seq):
+        if x == "dense":
+            assert np.array_equal(rtp.dense_attn(lay, q, k, v, ws).cpu().numpy(), ref_dense), "dense after others"
+        elif x == "swa":
+            rtp.swa_attn(lay, q, k, v, ws)
+        elif x == "logits":
+            lg = rtp.index_score(lay, q, wq, k_idx)
+            rtp.topp_select(lay, lg, spec.N, ws)
+        else:
+            got = step({"p": lay, "k": lay_k, "short": lay_short}[x], ws)
+            assert np.array_equal(got, ref[x]), f"decode step '{x}' differs after {seq[:j]}"
+    torch.cuda.synchronize()
