@@ -50,11 +50,17 @@ def up(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+# sources that decide what the phase-A kernel reads and writes: the kernel, the
+# headers it includes and the launch plan
+PHASE_A_SOURCES = [os.path.join(CSRC, f) for f in ("topp_kernels.hip", "swa.h", "block_util.h", "rtp_internal.h",
+                                                   "api.hip")] + [os.path.join(ROOT, "include", "rtp.h")]
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    for path in PHASE_A_SOURCES:
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -252,6 +258,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", type=int, default=0, help="run only this config (3, 4 or 6)")
     ap.add_argument("--calib", action="store_true", help="run the known-size copy used to scale HBM counters")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the Top-P step (no dense comparator, no top-k line): for profiling runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -271,7 +279,8 @@ def main():
         ms, ms_pa = case.run(args.steps, args.warmup)
         gbps = case.bytes_total / (ms * 1e-3) / 1e9
         # the dense comparator ignores the indexer, so the shared-key layer would repeat the 1M figure
-        ms_dense = case.run_dense(max(5, args.steps // 10), 3) if cfg != 6 else float("nan")
+        ms_dense = (case.run_dense(max(5, args.steps // 10), 3) if cfg != 6 and not args.no_extras
+                    else float("nan"))
         dense_bytes = 512 * case.spec.B * case.spec.Hkv * case.spec.N
         pa_bytes = case.bytes_scan + case.bytes_swa
         summ[cfg] = dict(ms=ms, us=ms * 1e3, gbps=gbps, frac=gbps / HBM_PEAK_GBPS, pa_us=ms_pa * 1e3,
@@ -282,7 +291,7 @@ def main():
         log(f"[bench] cfg{cfg}: {ms * 1e3:.1f} us/step, phase-A kernel {ms_pa * 1e3:.1f} us, {gbps:.0f} GB/s "
             f"algorithmic; |S| {case.counts.ravel().tolist()}; dense comparator {ms_dense * 1e3:.1f} us "
             f"({dense_bytes / (ms_dense * 1e-3) / 1e9:.0f} GB/s), sparse step {ms_dense / ms:.2f}x faster")
-        if cfg == 4:
+        if cfg == 4 and not args.no_extras:
             # the fixed top-k variant of the same kernels on the same caches
             top_p_layer = case.layer
             case.layer = dataclasses.replace(top_p_layer, top_k=TOPK_BENCH)
@@ -330,15 +339,17 @@ def main():
                      "frac": round(s["pa_gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel_us": round(s["pa_us"], 2), "algorithmic_bytes_per_launch": s["pa_bytes"]},
         "copy_ceiling_GBps": round(copy_gbps, 1),
-        "dense_comparator": {"what": "rtp_dense_attn: every head over every cached position, same caches",
-                             "us_per_step": round(s["dense_us"], 2), "GBps": round(s["dense_gbps"], 1),
-                             "sparse_speedup": round(s["dense_us"] / s["us"], 3),
-                             "dense_at_hbm_peak_us": round(512 * spec.B * spec.Hkv * spec.N / HBM_PEAK_GBPS / 1e3, 2),
-                             "sparse_speedup_vs_dense_at_peak":
-                                 round(512 * spec.B * spec.Hkv * spec.N / HBM_PEAK_GBPS / 1e3 / s["us"], 3)},
     }
+    if s["dense_us"] == s["dense_us"]:          # measured (not NaN)
+        dense_peak_us = 512 * spec.B * spec.Hkv * spec.N / HBM_PEAK_GBPS / 1e3
+        out["dense_comparator"] = {"what": "rtp_dense_attn: every head over every cached position, same caches",
+                                   "us_per_step": round(s["dense_us"], 2), "GBps": round(s["dense_gbps"], 1),
+                                   "sparse_speedup": round(s["dense_us"] / s["us"], 3),
+                                   "dense_at_hbm_peak_us": round(dense_peak_us, 2),
+                                   "sparse_speedup_vs_dense_at_peak": round(dense_peak_us / s["us"], 3)}
     if main_cfg == 4:
         out["roofline"]["traffic"] = traffic_per_launch(spec.name)
+    if main_cfg == 4 and "topk_us" in s:
         out["fixed_top_k"] = {"k": TOPK_BENCH, "us_per_step": round(s["topk_us"], 2),
                               "phase_a_kernel_us": round(s["topk_pa_us"], 2),
                               "what": "same step with rtp_layer.top_k = k instead of Top-P, same caches"}
@@ -350,8 +361,9 @@ def main():
                            "GBps": round(s3["gbps"], 1), "hbm_frac": round(s3["frac"], 4),
                            "algorithmic_bytes_per_step": s3["bytes"], "phase_a_kernel_us": round(s3["pa_us"], 2),
                            "phase_a_GBps": round(s3["pa_gbps"], 1),
-                           "dense_comparator_us": round(s3["dense_us"], 2),
-                           "sparse_speedup_vs_dense": round(s3["dense_us"] / s3["us"], 3),
+                           "dense_comparator_us": round(s3["dense_us"], 2) if s3["dense_us"] == s3["dense_us"] else None,
+                           "sparse_speedup_vs_dense": (round(s3["dense_us"] / s3["us"], 3)
+                                                       if s3["dense_us"] == s3["dense_us"] else None),
                            "selected_tokens": s3["counts"].ravel().tolist()}
     if 6 in summ and main_cfg != 6:
         s6 = summ[6]
