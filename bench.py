@@ -210,6 +210,45 @@ def traffic_per_launch(workload: str):
     return t.get("bytes_per_launch")
 
 
+def time_append(case: Case) -> dict:
+    """rtp_append_kv on the layer's caches (run last: it overwrites a cache replica).
+
+    One token: the GPU time of a single call, queued behind a busy-wait kernel so
+    the host's launch time is not in it (median of 50).  Bulk: every position of
+    the context appended in one call (the caches' initial fill), algorithmic
+    bytes = new keys and values read once, K, V and indexer keys written."""
+    spec, lay = case.spec, case.layer
+    k_idx, k, v = case.reps[-1]
+    w_k = up(case.wl.w_k)
+    # any [B, Hkv, N, D] bf16 tensor outside the written caches serves as new rows
+    src = case.reps[0][2] if len(case.reps) > 1 else case.reps[0][2].clone()
+    one = src[:, :, :1].contiguous()
+    for _ in range(5):
+        rtp.append_kv(lay, one, one, w_k, k, v, k_idx, spec.N - 1)
+    times = []
+    for _ in range(50):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(200_000)
+        e0.record()
+        rtp.append_kv(lay, one, one, w_k, k, v, k_idx, spec.N - 1)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    rtp.append_kv(lay, src, src, w_k, k, v, k_idx, 0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        rtp.append_kv(lay, src, src, w_k, k, v, k_idx, 0)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    nbytes = 4 * spec.B * spec.Hkv * spec.N * 256 + spec.B * spec.Hi * spec.N * 32
+    return {"what": "rtp_append_kv: post-RoPE keys, values and indexer keys of new tokens in one launch",
+            "one_token_us": round(float(np.median(times)), 2), "bulk_rows": spec.N, "bulk_ms": round(ms, 3),
+            "bulk_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "bulk_algorithmic_bytes": nbytes}
+
+
 def cpu_baseline(case: Case) -> dict:
     """The oracle, single-threaded, on a bounded sample of the 1M workload.
 
@@ -303,6 +342,9 @@ def main():
             t0 = time.time()
             cpu = cpu_baseline(case)
             log(f"[bench] cpu baseline {cpu['value']} GB/s ({time.time() - t0:.1f}s incl. cache build)")
+        if cfg == 4 and not args.no_extras:
+            summ[cfg]["append"] = time_append(case)
+            log(f"[bench] cfg{cfg}: cache append {summ[cfg]['append']}")
         del case
         torch.cuda.empty_cache()
 
@@ -353,6 +395,8 @@ def main():
         out["fixed_top_k"] = {"k": TOPK_BENCH, "us_per_step": round(s["topk_us"], 2),
                               "phase_a_kernel_us": round(s["topk_pa_us"], 2),
                               "what": "same step with rtp_layer.top_k = k instead of Top-P, same caches"}
+    if "append" in s:
+        out["cache_append"] = s["append"]
     if cpu is not None:
         out["cpu_baseline"] = cpu
     if 3 in summ and main_cfg != 3:

@@ -119,19 +119,35 @@ const char *rtp_status_str(int status);
 int rtp_rope_keys(const rtp_layer *layer, const rtp_bf16 *k_pre, rtp_bf16 *k_out,
                   int64_t n0, int64_t n1, void *stream);
 
-/* Indexer-key cache rows (FASB eq. (4), key side): k_idx[b,r,n,:] =
- * bf16(k_pre[b, g(r), n, :] . W_k[r]) for n in [n0, n1), every b and retrieval
- * head r (g(r) = KV group of retrieval head r).
- * k_pre: [B, Hkv, Ncap, D] bf16; w_k: [Hr, D, R] bf16; k_idx: [B, Hr, Ncap, R] bf16. */
+/* Indexer-key cache rows (FASB eq. (4), key side): k_idx[b,i,n,:] =
+ * bf16(k_pre[b, g(i), n, :] . W_k[i]) for n in [n0, n1), every b and indexer-key
+ * head i (g(i) = KV group of the retrieval heads it serves; i = r with
+ * idx_group 1).
+ * k_pre: [B, Hkv, Ncap, D] bf16; w_k: [Hi, D, R] bf16; k_idx: [B, Hi, Ncap, R] bf16. */
 int rtp_index_keys(const rtp_layer *layer, const rtp_bf16 *k_pre, const rtp_bf16 *w_k,
                    rtp_bf16 *k_idx, int64_t n0, int64_t n1, void *stream);
+
+/* Append new positions to every cache in one launch (FASB eq. (1) and eq. (4),
+ * key side): for n = n0 + t, t in [0, n_new), every b and KV group g,
+ *   k_cache[b,g,n,:] = bf16(R(n) k_new[b,g,t,:]),  v_cache[b,g,n,:] = v_new[b,g,t,:],
+ * and for every indexer-key head i (KV group g(i)),
+ *   k_idx[b,i,n,:] = bf16(k_new[b,g(i),t,:] . W_k[i]),
+ * bit for bit what rtp_rope_keys and rtp_index_keys write for those rows.
+ * k_new, v_new: [B, Hkv, n_new, D] bf16 (pre-RoPE keys and values of the new
+ * tokens; must not overlap the caches); w_k: [Hi, D, R]; k_cache, v_cache:
+ * [B, Hkv, Ncap, D]; k_idx: [B, Hi, Ncap, R].  Rows outside [n0, n0 + n_new)
+ * are not touched.  Requires 0 <= n0, n0 + n_new <= Ncap (else RTP_ERR_ARG);
+ * w_k and k_idx may be null when the layer has no retrieval head. */
+int rtp_append_kv(const rtp_layer *layer, const rtp_bf16 *k_new, const rtp_bf16 *v_new, const rtp_bf16 *w_k,
+                  rtp_bf16 *k_cache, rtp_bf16 *v_cache, rtp_bf16 *k_idx, int64_t n0, int64_t n_new,
+                  void *stream);
 
 /* ---------------------------------------------------------------- decode-path calls */
 
 /* Indexer scores (FASB eq. (4)): logits[b,r,i,n] = s_n for every retrieval head r,
  * query i and n <= m_i; entries with n > m_i are set to -inf.
  * q_pre: [B, Hq, nq, D] bf16 (pre-RoPE queries); w_q: [Hr, D, R] bf16;
- * k_idx: [B, Hr, Ncap, R] bf16; logits: [B, Hr, nq, N] fp32. */
+ * k_idx: [B, Hi, Ncap, R] bf16; logits: [B, Hr, nq, N] fp32. */
 int rtp_index_score(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *w_q,
                     const rtp_bf16 *k_idx, float *logits, void *stream);
 

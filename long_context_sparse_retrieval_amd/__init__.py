@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "Layer", "RtpError", "library_path", "load", "num_retrieval", "workspace_bytes", "workspace",
     "rope_keys", "index_keys", "index_score", "topp_select", "sparse_attn", "swa_attn", "dense_attn",
-    "decode_step", "SYMBOLS",
+    "decode_step", "append_kv", "SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -25,7 +25,7 @@ _LIB_PATH = os.path.join(_PKG, "librtp.so")
 _lib = None
 
 SYMBOLS = ("rtp_num_retrieval", "rtp_workspace_bytes", "rtp_workspace_init", "rtp_status_str", "rtp_rope_keys",
-           "rtp_index_keys", "rtp_index_score", "rtp_topp_select", "rtp_sparse_attn", "rtp_swa_attn",
+           "rtp_index_keys", "rtp_append_kv", "rtp_index_score", "rtp_topp_select", "rtp_sparse_attn", "rtp_swa_attn",
            "rtp_dense_attn", "rtp_decode_step")
 
 
@@ -64,6 +64,7 @@ def load():
         "rtp_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "rtp_rope_keys": (ctypes.c_int, [L, vp, vp, i64, i64, vp]),
         "rtp_index_keys": (ctypes.c_int, [L, vp, vp, vp, i64, i64, vp]),
+        "rtp_append_kv": (ctypes.c_int, [L, vp, vp, vp, vp, vp, vp, i64, i64, vp]),
         "rtp_index_score": (ctypes.c_int, [L, vp, vp, vp, vp, vp]),
         "rtp_topp_select": (ctypes.c_int, [L, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]),
         "rtp_sparse_attn": (ctypes.c_int, [L, vp, vp, vp, vp, vp, i64, vp, vp, ctypes.c_size_t, vp]),
@@ -196,6 +197,27 @@ def index_keys(layer: Layer, k_pre: torch.Tensor, w_k: torch.Tensor, k_idx: torc
     n1 = layer.cap_rows if n1 is None else n1
     _check(load().rtp_index_keys(ctypes.byref(layer.c()), a, w, b, n0, n1, _stream()), "rtp_index_keys")
     return k_idx
+
+
+def append_kv(layer: Layer, k_new: torch.Tensor, v_new: torch.Tensor, w_k, k_cache: torch.Tensor,
+              v_cache: torch.Tensor, k_idx, n0: int) -> None:
+    """Write positions n0 .. n0 + n_new - 1 of every cache in one launch: post-RoPE keys,
+    values and (for retrieval layers) indexer keys, from the new tokens' pre-RoPE keys
+    and values [B, Hkv, n_new, D]."""
+    if k_new.dim() != 4:
+        raise ValueError("k_new must be [B, Hkv, n_new, D]")
+    n_new = int(k_new.shape[2])
+    shp_new = (layer.B, layer.Hkv, n_new, layer.D)
+    a = _ptr(k_new, torch.bfloat16, shp_new, "k_new")
+    b = _ptr(v_new, torch.bfloat16, shp_new, "v_new")
+    kc = _ptr(k_cache, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k_cache")
+    vc = _ptr(v_cache, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v_cache")
+    w = ki = None
+    if layer.Hi:
+        w = _ptr(w_k, torch.bfloat16, (layer.Hi, layer.D, layer.R), "w_k")
+        ki = _ptr(k_idx, torch.bfloat16, _cache_shape(layer, layer.Hi, layer.R), "k_idx")
+    _check(load().rtp_append_kv(ctypes.byref(layer.c()), a, b, w, kc, vc, ki, n0, n_new, _stream()),
+           "rtp_append_kv")
 
 
 def index_score(layer: Layer, q_pre, w_q, k_idx, logits=None) -> torch.Tensor:

@@ -331,6 +331,18 @@ int rtp_dense_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16
   return launch_phase_a(p.g, q_pre, nullptr, nullptr, nullptr, k, v, out, false, true, as_stream(stream));
 }
 
+int rtp_append_kv(const rtp_layer *layer, const rtp_bf16 *k_new, const rtp_bf16 *v_new, const rtp_bf16 *w_k,
+                  rtp_bf16 *k_cache, rtp_bf16 *v_cache, rtp_bf16 *k_idx, int64_t n0, int64_t n_new, void *stream) {
+  Plan p;
+  int st = make_plan(layer, nullptr, &p);
+  if (st != RTP_OK) return st;
+  if (n0 < 0 || n_new < 0 || n0 > layer->Ncap - n_new || n0 + n_new >= (1ll << 31)) return RTP_ERR_ARG;
+  if (n_new == 0) return RTP_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache) return RTP_ERR_ARG;
+  if (p.g.Hi && (!w_k || !k_idx)) return RTP_ERR_ARG;
+  return launch_append_kv(p.g, k_new, v_new, w_k, k_cache, v_cache, k_idx, n0, n_new, as_stream(stream));
+}
+
 int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
                     const rtp_bf16 *k, const rtp_bf16 *v, float *out, int32_t *idx_opt, int32_t *count_opt,
                     int64_t cap, void *ws, size_t ws_bytes, void *phase_event, void *stream) {

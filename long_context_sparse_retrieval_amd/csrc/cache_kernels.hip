@@ -21,13 +21,9 @@ __global__ __launch_bounds__(kWG) void rope_keys_kernel(Geo g, const rtp_bf16 *k
   const long long n = n0 + (row - bg * rows_per_bg);
   const size_t off = ((size_t)bg * g.Ncap + n) * kD + 2 * lane;
   const uint32_t w = *reinterpret_cast<const uint32_t *>(k_pre + off);
-  const double a = (double)bf_lo(w), b = (double)bf_hi(w);
   double sn, cs;
   sincos((double)n * rope_freq(g.theta, lane), &sn, &cs);
-  const double x = __dsub_rn(__dmul_rn(a, cs), __dmul_rn(b, sn));
-  const double y = __dadd_rn(__dmul_rn(a, sn), __dmul_rn(b, cs));
-  const uint32_t out = (uint32_t)f64_to_bf16(x) | ((uint32_t)f64_to_bf16(y) << 16);
-  *reinterpret_cast<uint32_t *>(k_out + off) = out;
+  *reinterpret_cast<uint32_t *>(k_out + off) = rope_pair_bf16(w, sn, cs);
 }
 
 int launch_rope_keys(const Geo &g, const rtp_bf16 *k_pre, rtp_bf16 *k_out, long long n0, long long n1,

@@ -124,6 +124,16 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
   return (uint16_t)(sign | (uint32_t)keep);              // keep == 128 carries into the exponent field
 }
 
+// RoPE of one channel pair of a bf16 key row (FASB eq. (1)): the pair (a, b)
+// packed in w, rotated by the fp64 angle whose sine and cosine are given,
+// each output rounded once to bf16.
+__device__ __forceinline__ uint32_t rope_pair_bf16(uint32_t w, double sn, double cs) {
+  const double a = (double)bf_lo(w), b = (double)bf_hi(w);
+  const double x = __dsub_rn(__dmul_rn(a, cs), __dmul_rn(b, sn));
+  const double y = __dadd_rn(__dmul_rn(a, sn), __dmul_rn(b, cs));
+  return (uint32_t)f64_to_bf16(x) | ((uint32_t)f64_to_bf16(y) << 16);
+}
+
 // Exact dot of 16 bf16 pairs accumulated in fp64, rounded once to fp32.
 // q: 16 widened bf16 values; a, b: the 32-byte row as two uint4.
 __device__ __forceinline__ float dot16_exact(const double *q, uint4 a, uint4 b) {
@@ -250,6 +260,8 @@ __device__ __forceinline__ void project_query(const rtp_bf16 *__restrict__ q_row
 int launch_rope_keys(const Geo &g, const rtp_bf16 *k_pre, rtp_bf16 *k_out, long long n0, long long n1, hipStream_t s);
 int launch_index_keys(const Geo &g, const rtp_bf16 *k_pre, const rtp_bf16 *w_k, rtp_bf16 *k_idx, long long n0,
                       long long n1, hipStream_t s);
+int launch_append_kv(const Geo &g, const rtp_bf16 *k_new, const rtp_bf16 *v_new, const rtp_bf16 *w_k, rtp_bf16 *kc,
+                     rtp_bf16 *vc, rtp_bf16 *k_idx, long long n0, long long n_new, hipStream_t s);
 int launch_index_score(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
                        float *logits, hipStream_t s);
 // Phase A: SWA workgroups of the local heads and/or scan tiles of the

@@ -90,6 +90,13 @@ def test_calls_reject_before_launch():
     assert lib.rtp_swa_attn(L, None, fake, fake, fake, fake, need, None) == -1
     assert lib.rtp_sparse_attn(L, fake, fake, fake, fake, fake, -1, fake, fake, need, None) == -1
     assert lib.rtp_workspace_init(None, 16, None) == -1
+    cap = lay.cap_rows
+    assert lib.rtp_append_kv(L, fake, fake, fake, fake, fake, fake, cap - 1, 2, None) == -1     # past Ncap
+    assert lib.rtp_append_kv(L, fake, fake, fake, fake, fake, fake, -1, 1, None) == -1
+    assert lib.rtp_append_kv(L, fake, fake, fake, fake, fake, fake, 0, -1, None) == -1
+    assert lib.rtp_append_kv(L, None, fake, fake, fake, fake, fake, 0, 1, None) == -1
+    assert lib.rtp_append_kv(L, fake, fake, None, fake, fake, fake, 0, 1, None) == -1           # retrieval layer needs W_k
+    assert lib.rtp_append_kv(L, None, None, None, None, None, None, 5, 0, None) == 0            # nothing to do
     # misaligned workspace
     assert lib.rtp_swa_attn(L, fake, fake, fake, fake, fake + 8, need, None) == -1
     # chunked prefill (nq > 1) is validated the same way before any launch

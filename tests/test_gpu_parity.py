@@ -101,6 +101,75 @@ def test_index_score_shared_keys():
                 assert np.array_equal(got[b, r, i, :m + 1], ref)
 
 
+# ----------------------------------------------------------------------------- cache append
+@pytest.mark.parametrize("n0,n_new", [(0, 1), (4999, 1), (17, 3), (100, 8), (0, 9), (33, 64), (1000, 777),
+                                      (0, 5000)])
+@pytest.mark.parametrize("ig", [1, 4])
+def test_append_kv_matches_writers_and_oracle(n0, n_new, ig):
+    """One launch writes K (post-RoPE), V and the indexer keys of the new rows:
+    bit for bit what rtp_rope_keys / rtp_index_keys write, the oracle's indexer
+    keys exactly, and nothing outside [n0, n0 + n_new)."""
+    say(f"append_kv n0={n0} n_new={n_new} idx_group={ig}")
+    rng = np.random.default_rng(n0 * 7 + n_new + ig)
+    B, Hq, Hkv, Ncap = 2, 16, 4, 5000
+    hm = [1] * 4 + [0] * 4 + [1] * 4 + [0] * 4           # KV groups 0 and 2 retrieval
+    lay = rtp.Layer(B=B, Hq=Hq, Hkv=Hkv, N=Ncap, head_mode=hm, idx_group=ig)
+    k_new = _rand_bf16(rng, (B, Hkv, n_new, 128), 2.0)
+    v_new = _rand_bf16(rng, (B, Hkv, n_new, 128))
+    w_k = _rand_bf16(rng, (lay.Hi, 128, 16), 128 ** -0.5)
+    sentinel = lambda shape: rng.integers(0, 1 << 16, size=shape, dtype=np.uint16) & np.uint16(0x7f7f)
+    kc0, vc0, ki0 = sentinel((B, Hkv, Ncap, 128)), sentinel((B, Hkv, Ncap, 128)), sentinel((B, lay.Hi, Ncap, 16))
+    kc, vc, ki = dev_bf16(kc0), dev_bf16(vc0), dev_bf16(ki0)
+    rtp.append_kv(lay, dev_bf16(k_new), dev_bf16(v_new), dev_bf16(w_k), kc, vc, ki, n0)
+    kc, vc, ki = host_bf16(kc), host_bf16(vc), host_bf16(ki)
+    sl = slice(n0, n0 + n_new)
+    for a, a0 in ((kc, kc0), (vc, vc0), (ki, ki0)):        # rows outside the range untouched
+        assert np.array_equal(a[:, :, :n0], a0[:, :, :n0]) and np.array_equal(a[:, :, n0 + n_new:], a0[:, :, n0 + n_new:])
+    assert np.array_equal(vc[:, :, sl], v_new)
+    # the stand-alone writers on the same rows
+    k_pre = np.zeros((B, Hkv, Ncap, 128), np.uint16)
+    k_pre[:, :, sl] = k_new
+    ref_k = torch.zeros((B, Hkv, Ncap, 128), dtype=torch.bfloat16, device="cuda")
+    rtp.rope_keys(lay, dev_bf16(k_pre), ref_k, n0, n0 + n_new)
+    ref_i = rtp.index_keys(lay, dev_bf16(k_pre), dev_bf16(w_k), n0=n0, n1=n0 + n_new)
+    assert np.array_equal(kc[:, :, sl], host_bf16(ref_k)[:, :, sl]), "keys differ from rtp_rope_keys"
+    assert np.array_equal(ki[:, :, sl], host_bf16(ref_i)[:, :, sl]), "indexer keys differ from rtp_index_keys"
+    # the oracle: indexer keys exactly; RoPE to the rope_keys test's bar
+    rheads = [h for h in range(Hq) if hm[h]]
+    for b in range(B):
+        for i in range(lay.Hi):
+            g = rheads[i * ig] // (Hq // Hkv)
+            assert np.array_equal(ki[b, i, sl], O.index_project(k_new[b, g], w_k[i])), f"b{b} i{i}"
+    ref = O.rope_keys(k_new, 1e6, np.arange(n0, n0 + n_new))
+    got = kc[:, :, sl]
+    ndiff = int(np.sum(got != ref))
+    assert ndiff <= max(1, got.size // 10 ** 6), f"{ndiff} of {got.size} bf16 values differ"
+
+
+def test_append_kv_builds_the_caches_a_decode_step_reads():
+    """Caches grown by appends (a bulk prefix, then token by token) give the same
+    decode step, bit for bit, as caches written by the stand-alone writers."""
+    spec = gen.spec_for(2, B=2, N=3000, window=512)
+    say(f"append then decode: {spec}")
+    wl = gen.make_workload(spec, 91)
+    lay = layer_of(spec, rtp)
+    k_pre, v, wk = dev_bf16(wl.k_pre), dev_bf16(wl.v), dev_bf16(wl.w_k)
+    k_ref = rtp.rope_keys(lay, k_pre)
+    ki_ref = rtp.index_keys(lay, k_pre, wk)
+    kc = torch.zeros_like(k_ref)
+    vc = torch.zeros_like(v)
+    ki = torch.zeros_like(ki_ref)
+    pieces = [(0, spec.N - 11), (spec.N - 11, 8)] + [(n, 1) for n in range(spec.N - 3, spec.N)]
+    for n0, cnt in pieces:
+        rtp.append_kv(lay, k_pre[:, :, n0:n0 + cnt].contiguous(), v[:, :, n0:n0 + cnt].contiguous(), wk,
+                      kc, vc, ki, n0)
+    assert torch.equal(kc, k_ref) and torch.equal(vc, v) and torch.equal(ki, ki_ref)
+    q, wq = dev_bf16(wl.q_pre), dev_bf16(wl.w_q)
+    a = rtp.decode_step(lay, q, wq, ki, kc, vc, rtp.workspace(lay))
+    b = rtp.decode_step(lay, q, wq, ki_ref, k_ref, v, rtp.workspace(lay))
+    assert torch.equal(a, b)
+
+
 # ----------------------------------------------------------------------------- Top-P
 def _logit_case(kind, rng, n):
     if kind == "gauss1":
