@@ -249,6 +249,43 @@ def time_append(case: Case) -> dict:
             "bulk_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "bulk_algorithmic_bytes": nbytes}
 
 
+PREFILL_N = 32768             # full prefill of a 32K context, the pages' shortest prefill figure
+
+
+def time_prefill() -> dict:
+    """rtp_prefill_attn on the 32K layer (32 q / 8 kv heads, KV group 0 retrieval):
+    RTPurbo prefill (retrieval heads dense, local heads window 4096 + 4 sinks)
+    against every head dense, all 32768 queries causal; seeded synthetic inputs.
+    Algorithmic flops: 4 * 128 per (query, key) pair the attention visits."""
+    B, Hq, Hkv, N, W, S = 1, 32, 8, PREFILL_N, 4096, 4
+    hm = [1] * 4 + [0] * 28
+    lay = rtp.Layer(B=B, Hq=Hq, Hkv=Hkv, N=N, nq=N, head_mode=hm, window=W, n_sink=S)
+    gen_ = torch.Generator(device="cuda").manual_seed(2032)
+    q, k, v = (torch.randn((B, h, N, 128), device="cuda", generator=gen_).to(torch.bfloat16) for h in (Hq, Hkv, Hkv))
+    out = torch.empty((B, Hq, N, 128), dtype=torch.float32, device="cuda")
+    pairs_dense = B * Hq * N * (N + 1) / 2
+    local_pairs = sum(min(m + 1, W) + min(S, max(0, m + 1 - W)) for m in range(N))
+    pairs = {True: pairs_dense, False: B * (4 * N * (N + 1) / 2 + 28 * local_pairs)}
+    res = {}
+    for dense in (False, True):
+        rtp.prefill_attn(lay, q, k, v, out, all_dense=dense)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(3):
+            rtp.prefill_attn(lay, q, k, v, out, all_dense=dense)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 3
+        res[dense] = (ms, pairs[dense] * 512 / (ms * 1e-3) / 1e12)
+    return {"what": "rtp_prefill_attn, 32 q / 8 kv heads (4 retrieval), 32768 causal queries: RTPurbo prefill "
+                    "(retrieval heads dense, local heads window 4096 + 4 sinks) vs every head dense",
+            "rtpurbo_ms": round(res[False][0], 3), "dense_ms": round(res[True][0], 3),
+            "speedup": round(res[True][0] / res[False][0], 3),
+            "rtpurbo_TFLOPs": round(res[False][1], 1), "dense_TFLOPs": round(res[True][1], 1),
+            "peak_bf16_TFLOPs": 2500.0}
+
+
 def cpu_baseline(case: Case) -> dict:
     """The oracle, single-threaded, on a bounded sample of the 1M workload.
 
@@ -348,6 +385,12 @@ def main():
         del case
         torch.cuda.empty_cache()
 
+    prefill = None
+    if not args.only and not args.no_extras:
+        prefill = time_prefill()
+        log(f"[bench] prefill attention 32K: {prefill}")
+        torch.cuda.empty_cache()
+
     main_cfg = cfgs[0]
     s = summ[main_cfg]
     spec = s["spec"]
@@ -397,6 +440,8 @@ def main():
                               "what": "same step with rtp_layer.top_k = k instead of Top-P, same caches"}
     if "append" in s:
         out["cache_append"] = s["append"]
+    if prefill is not None:
+        out["prefill_32k"] = prefill
     if cpu is not None:
         out["cpu_baseline"] = cpu
     if 3 in summ and main_cfg != 3:

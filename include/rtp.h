@@ -183,10 +183,25 @@ int rtp_swa_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *
  * measure their kernels against a dense FlashAttention-2 decode (DeepRead
  * summary, "Key Results"); this call is that baseline built the same way as
  * the rest of this library (GQA: one K/V row read serves the group's heads,
- * split-K over the cache).  Layouts as rtp_swa_attn; writes every row of out.
- * The workspace of rtp_workspace_bytes(layer) covers this call. */
+ * split-K over the cache).  With nq > 1 it runs the matrix-core kernel of
+ * rtp_prefill_attn with every head dense.  Layouts as rtp_swa_attn; writes
+ * every row of out.  The workspace of rtp_workspace_bytes(layer) covers this
+ * call. */
 int rtp_dense_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *k,
                    const rtp_bf16 *v, float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Prefill attention (FASB section 3.2: in prefill the retrieval heads keep the
+ * full KV cache and the local heads attend to a sliding window plus sinks):
+ * for each of the nq causal queries at m_i = N - nq + i, retrieval heads attend
+ * over every position 0..m_i and local heads over max(0, m_i-W+1)..m_i plus
+ * 0..n_sink-1; all_dense != 0 makes every head attend over 0..m_i (the dense
+ * prefill the DeepRead summary's "Key Results" compare against).  Matrix-core
+ * kernel: the rotated query and the softmax weights are each carried as two
+ * bf16 halves, so both products keep fp32-level precision.
+ * q_pre: [B, Hq, nq, D] bf16 (pre-RoPE); k (post-RoPE), v: [B, Hkv, Ncap, D]
+ * bf16; out: [B, Hq, nq, D] fp32, every row written.  No workspace. */
+int rtp_prefill_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *k,
+                     const rtp_bf16 *v, float *out, int32_t all_dense, void *stream);
 
 /* One whole step (FASB eq. (4)-(5) and section 3.2): indexer scan, histogram
  * Top-P, sparse attention for retrieval heads and SWA for local heads; writes

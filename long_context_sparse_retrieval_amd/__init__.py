@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "Layer", "RtpError", "library_path", "load", "num_retrieval", "workspace_bytes", "workspace",
     "rope_keys", "index_keys", "index_score", "topp_select", "sparse_attn", "swa_attn", "dense_attn",
-    "decode_step", "append_kv", "SYMBOLS",
+    "decode_step", "append_kv", "prefill_attn", "SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -26,7 +26,7 @@ _lib = None
 
 SYMBOLS = ("rtp_num_retrieval", "rtp_workspace_bytes", "rtp_workspace_init", "rtp_status_str", "rtp_rope_keys",
            "rtp_index_keys", "rtp_append_kv", "rtp_index_score", "rtp_topp_select", "rtp_sparse_attn", "rtp_swa_attn",
-           "rtp_dense_attn", "rtp_decode_step")
+           "rtp_dense_attn", "rtp_prefill_attn", "rtp_decode_step")
 
 
 class RtpError(RuntimeError):
@@ -70,6 +70,7 @@ def load():
         "rtp_sparse_attn": (ctypes.c_int, [L, vp, vp, vp, vp, vp, i64, vp, vp, ctypes.c_size_t, vp]),
         "rtp_swa_attn": (ctypes.c_int, [L, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "rtp_dense_attn": (ctypes.c_int, [L, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+        "rtp_prefill_attn": (ctypes.c_int, [L, vp, vp, vp, vp, ctypes.c_int32, vp]),
         "rtp_decode_step": (ctypes.c_int, [L, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -288,6 +289,21 @@ def dense_attn(layer: Layer, q_pre, k, v, ws, out=None) -> torch.Tensor:
     op = _ptr(out, torch.float32, (layer.B, layer.Hq, layer.nq, layer.D), "out")
     _check(load().rtp_dense_attn(ctypes.byref(layer.c()), q, kp, vp, op, ws.data_ptr(), ws.numel(), _stream()),
            "rtp_dense_attn")
+    return out
+
+
+def prefill_attn(layer: Layer, q_pre, k, v, out=None, all_dense: bool = False) -> torch.Tensor:
+    """Causal attention of the layer's nq queries on the matrix cores: retrieval heads
+    over every earlier position, local heads over window + sinks (every head dense
+    when all_dense); writes every row of out."""
+    q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
+    kp = _ptr(k, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k")
+    vp = _ptr(v, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v")
+    if out is None:
+        out = torch.empty((layer.B, layer.Hq, layer.nq, layer.D), dtype=torch.float32, device=q_pre.device)
+    op = _ptr(out, torch.float32, (layer.B, layer.Hq, layer.nq, layer.D), "out")
+    _check(load().rtp_prefill_attn(ctypes.byref(layer.c()), q, kp, vp, op, int(bool(all_dense)), _stream()),
+           "rtp_prefill_attn")
     return out
 
 

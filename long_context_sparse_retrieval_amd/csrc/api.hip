@@ -328,7 +328,25 @@ int rtp_dense_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16
   int st = plan_with_ws(layer, ws, ws_bytes, &p, true);
   if (st != RTP_OK) return st;
   if (!q_pre || !k || !v || !out) return RTP_ERR_ARG;
+  if (layer->nq > 1) {            // many queries: the matrix-core kernel, every head dense
+    FlashQuads fq[2];
+    st = make_flash_quads(p.g, true, fq);
+    if (st != RTP_OK) return st;
+    return launch_flash_prefill(p.g, fq, q_pre, k, v, out, as_stream(stream));
+  }
   return launch_phase_a(p.g, q_pre, nullptr, nullptr, nullptr, k, v, out, false, true, as_stream(stream));
+}
+
+int rtp_prefill_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *k, const rtp_bf16 *v, float *out,
+                     int32_t all_dense, void *stream) {
+  Plan p;
+  int st = make_plan(layer, nullptr, &p);
+  if (st != RTP_OK) return st;
+  if (!q_pre || !k || !v || !out) return RTP_ERR_ARG;
+  FlashQuads fq[2];
+  st = make_flash_quads(p.g, all_dense != 0, fq);
+  if (st != RTP_OK) return st;
+  return launch_flash_prefill(p.g, fq, q_pre, k, v, out, as_stream(stream));
 }
 
 int rtp_append_kv(const rtp_layer *layer, const rtp_bf16 *k_new, const rtp_bf16 *v_new, const rtp_bf16 *w_k,

@@ -141,18 +141,23 @@ __device__ __forceinline__ void publish_partial(Partial *dst, const Partial *src
 
 // cos/sin of m * theta_i (FASB eq. (1)) in fp64 for the 64 channel pairs,
 // into tab[64] (x = cos, y = sin).  Threads 0..63; ends with a barrier.
+// Sine and cosine of the RoPE angle m * theta_pair in fp64: the angle is
+// reduced by 2 pi (three-part constant, fused multiply-adds) so that sin/cos
+// take their short-argument path at any position.
+__device__ __forceinline__ void rope_sincos(long long m, double theta, int pair, double &sn, double &cs) {
+  const double x = (double)m * rope_freq(theta, pair);
+  const double k = rint(x * 0.15915494309189535);
+  double y = fma(-k, 6.283185307179586232, x);
+  y = fma(-k, 2.4492935982947064e-16, y);
+  y = fma(-k, -5.9895396194366793e-33, y);
+  sincos(y, &sn, &cs);
+}
+
 __device__ __forceinline__ void rope_table(long long m, double theta, double2 *tab) {
   const int t = threadIdx.x;
   if (t < kD / 2) {
-    // reduce the fp64 angle by 2 pi (three-part constant, fused multiply-adds)
-    // so that sin/cos take their short-argument path at any position
-    const double x = (double)m * rope_freq(theta, t);
-    const double k = rint(x * 0.15915494309189535);
-    double y = fma(-k, 6.283185307179586232, x);
-    y = fma(-k, 2.4492935982947064e-16, y);
-    y = fma(-k, -5.9895396194366793e-33, y);
     double sn, cs;
-    sincos(y, &sn, &cs);
+    rope_sincos(m, theta, t, sn, cs);
     tab[t] = make_double2(cs, sn);
   }
   __syncthreads();

@@ -1,0 +1,271 @@
+// Prefill attention on the matrix cores: causal attention of nq queries per
+// head, dense for retrieval heads and sliding window plus sinks for local
+// heads, or dense for every head (the comparator).
+//
+// "Full Attention Strikes Back" (RTPurbo) section 3.2: during prefill the
+// retrieval heads keep the full KV cache (dense causal attention) while the
+// local heads attend to a sliding window with attention sinks; the attention
+// itself is eq. (5)'s softmax(q . k / sqrt(d_h)) V.  The DeepRead summary's
+// "Key Results" compare this prefill against dense attention for every head.
+//
+// Design for gfx950.  A workgroup takes 16 consecutive queries of up to four
+// q heads of one KV group and one mode (one wave per head), so every K/V block
+// staged in LDS serves four heads.  Scores are computed transposed,
+// S^T = K Q^T, with v_mfma_f32_16x16x16_bf16: the keys are the A operand and
+// the queries the B operand, so each lane ends up with four keys of one query
+// -- exactly the A-operand layout P needs for O += P V, with V staged
+// transposed.  The rotated query (fp64 angles) and the softmax weights P are
+// each split into two bf16 halves, x = hi + lo, so both products carry
+// fp32-level precision (bf16 P alone misses the 2e-3 output bar when a few
+// keys dominate).  The softmax runs online in base 2 (log2(e) / sqrt(d)
+// folded into the query); a query's running maximum and sum sit in the four
+// lanes that hold it.
+#include <string.h>
+
+#include "block_util.h"
+
+namespace rtp {
+
+namespace {
+
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kFq = 16;                 // queries per wave (the matrix-core N dimension)
+constexpr int kFk = 64;                 // keys per staged block
+constexpr int kKPad = kD + 8;           // padded key row in LDS (elements)
+constexpr int kVPad = kFk + 8;          // padded row of transposed values (elements)
+constexpr double kQScale = 1.4426950408889634 / 11.313708498984761;   // log2(e) / sqrt(128)
+
+struct FlashShared {
+  rtp_bf16 k[kFk][kKPad];               // keys of the block, row-major
+  rtp_bf16 vt[kD][kVPad];               // values of the block, transposed
+};
+
+__device__ __forceinline__ short bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (short)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float bf16_f(short b) { return __uint_as_float((uint32_t)(uint16_t)b << 16); }
+
+__global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq, const rtp_bf16 *__restrict__ q_pre,
+                                                            const rtp_bf16 *__restrict__ kc,
+                                                            const rtp_bf16 *__restrict__ vc, float *__restrict__ out,
+                                                            int ntiles) {
+  __shared__ FlashShared sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Workgroups x and x + 8 share an XCD.  Each (quad, sequence) deals its
+  // query tiles to the eight XCDs in turn, so a dense quad's work spreads over
+  // the whole chip (dealing strips of consecutive tiles to one XCD was
+  // measured slower); the longest tiles come first.
+  const int inner = fq.n * g.B;
+  const int y = (int)(blockIdx.x >> 3);
+  const int rank = (y / inner) * 8 + (int)(blockIdx.x & 7);
+  if (rank >= ntiles) return;                                  // padding to whole XCD rounds
+  const int tile = ntiles - 1 - rank;
+  const int rest = y % inner;
+  const int quad = rest % fq.n, b = rest / fq.n;
+  const int h = fq.head[4 * quad + wv];                        // kNoHead: this wave only helps staging
+  const int h0 = fq.head[4 * quad];
+  const bool dense = fq.dense[quad] != 0;
+  const int kvg = h0 / g.G;
+  const int i0 = tile * kFq;
+  const int nqt = g.nq - i0 < kFq ? g.nq - i0 : kFq;
+  const long long m0 = g.N - g.nq + i0, m_hi = m0 + nqt - 1;
+  const int qn = lane & 15, grp = lane >> 4;
+  const size_t cbase = ((size_t)b * g.Hkv + kvg) * g.Ncap;
+
+  // this lane's query (qn) as the B operand: dims 16 c + 4 grp .. + 3, split hi + lo
+  bf16x4_t qh[kD / 16], ql[kD / 16];
+  {
+    const int qi = i0 + (qn < nqt ? qn : nqt - 1);
+    const long long mq = g.N - g.nq + qi;
+    const rtp_bf16 *qr = q_pre + (((size_t)b * g.Hq + (h != kNoHead ? h : h0)) * g.nq + qi) * kD;
+#pragma unroll
+    for (int c = 0; c < kD / 16; ++c) {
+      const int d0 = 16 * c + 4 * grp;
+      const uint2 w = *reinterpret_cast<const uint2 *>(qr + d0);
+      const uint32_t ww[2] = {w.x, w.y};
+      float r[4];
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        double sn, cs;
+        rope_sincos(mq, g.theta, d0 / 2 + pp, sn, cs);
+        const double a = (double)bf_lo(ww[pp]), bb = (double)bf_hi(ww[pp]);
+        r[2 * pp] = (float)((a * cs - bb * sn) * kQScale);
+        r[2 * pp + 1] = (float)((a * sn + bb * cs) * kQScale);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const short hi = bf16_rne(r[e]);
+        qh[c][e] = hi;
+        ql[c][e] = bf16_rne(r[e] - bf16_f(hi));
+      }
+    }
+  }
+
+  // key blocks: the sink blocks (local heads), then the window or the whole prefix
+  const long long lo_pos = dense ? 0 : (m0 - g.window + 1 > 0 ? m0 - g.window + 1 : 0);
+  const long long sink_end = dense ? 0 : (g.n_sink < lo_pos ? g.n_sink : lo_pos);   // sink positions [0, sink_end)
+  const long long sb_end = (sink_end + kFk - 1) / kFk;                                 // sink blocks [0, sb_end)
+  const long long mb_lo = lo_pos / kFk > sb_end ? lo_pos / kFk : sb_end;
+  const long long mb_hi = m_hi / kFk;
+  const long long nblk = sb_end + (mb_hi >= mb_lo ? mb_hi - mb_lo + 1 : 0);
+  const long long qp = m0 + qn;                                // this lane's query position
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4_t o[kD / 16];
+#pragma unroll
+  for (int t = 0; t < kD / 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (long long x = 0; x < nblk; ++x) {
+    const long long kb = x < sb_end ? x : mb_lo + (x - sb_end);
+    __syncthreads();                                           // the previous block is consumed
+    {
+      // stage: thread t takes key row t / 4, channels 32 (t % 4) .. + 31
+      const int r = tid >> 2, part = tid & 3;
+      long long kp = kb * kFk + r;
+      kp = kp < g.N ? kp : g.N - 1;
+      const uint4 *ks = reinterpret_cast<const uint4 *>(kc + (cbase + kp) * kD + 32 * part);
+      const uint4 *vs = reinterpret_cast<const uint4 *>(vc + (cbase + kp) * kD + 32 * part);
+      uint4 kv4[4], vv4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        kv4[u] = ks[u];
+        vv4[u] = vs[u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4 *>(&sm.k[r][32 * part + 8 * u]) = kv4[u];
+      const rtp_bf16 *ve = reinterpret_cast<const rtp_bf16 *>(vv4);
+#pragma unroll
+      for (int e = 0; e < 32; ++e) sm.vt[32 * part + e][r] = ve[e];
+    }
+    __syncthreads();
+    if (h == kNoHead) continue;                                // wave-uniform
+    // S^T for the block's four 16-key subtiles
+    f32x4_t s[kFk / 16];
+#pragma unroll
+    for (int st = 0; st < kFk / 16; ++st) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < kD / 16; ++c) {
+        const bf16x4_t a = *reinterpret_cast<const bf16x4_t *>(&sm.k[16 * st + qn][16 * c + 4 * grp]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, qh[c], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ql[c], acc, 0, 0, 0);
+      }
+      s[st] = acc;
+    }
+    // masks: this lane holds query qn and keys 64 kb + 16 st + 4 grp + e
+    float mb = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < kFk / 16; ++st) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const long long kp = kb * kFk + 16 * st + 4 * grp + e;
+        const bool ok = kp <= qp && (dense || kp < g.n_sink || kp > qp - g.window);
+        s[st][e] = ok ? s[st][e] : -INFINITY;
+        mb = fmaxf(mb, s[st][e]);
+      }
+    }
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float m_new = fmaxf(m_run, mb);
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float ps = 0.f;
+    bf16x4_t pb[kFk / 16], pl[kFk / 16];                      // P = hi + lo, both bf16
+#pragma unroll
+    for (int st = 0; st < kFk / 16; ++st) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pe = s[st][e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[st][e] - m_new);
+        ps += pe;
+        const short hi = bf16_rne(pe);
+        pb[st][e] = hi;
+        pl[st][e] = bf16_rne(pe - bf16_f(hi));
+      }
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    // O rows are queries 4 grp + e: their factors come from the lanes holding those queries
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ae = __shfl(alpha, 4 * grp + e);
+#pragma unroll
+      for (int t = 0; t < kD / 16; ++t) o[t][e] *= ae;
+    }
+    // O += P V
+#pragma unroll
+    for (int t = 0; t < kD / 16; ++t) {
+#pragma unroll
+      for (int st = 0; st < kFk / 16; ++st) {
+        const bf16x4_t bv = *reinterpret_cast<const bf16x4_t *>(&sm.vt[16 * t + qn][16 * st + 4 * grp]);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb[st], bv, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl[st], bv, o[t], 0, 0, 0);
+      }
+    }
+  }
+  if (h == kNoHead) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int qe = 4 * grp + e;
+    const float le = __shfl(l_run, qe);
+    if (qe < nqt) {
+      float *dst = out + (((size_t)b * g.Hq + h) * g.nq + i0 + qe) * kD + qn;
+#pragma unroll
+      for (int t = 0; t < kD / 16; ++t) dst[16 * t] = o[t][e] / le;
+    }
+  }
+}
+
+}  // namespace
+
+// Head quads: up to four q heads of one KV group and one mode per workgroup;
+// dense quads in fq[1], window + sinks quads in fq[0].
+int make_flash_quads(const Geo &g, bool all_dense, FlashQuads fq[2]) {
+  memset(fq, 0, 2 * sizeof(FlashQuads));
+  for (int kv = 0; kv < g.Hkv; ++kv) {
+    for (int mode = 1; mode >= 0; --mode) {
+      FlashQuads &f = fq[mode];
+      int cnt = 0;
+      for (int h = kv * g.G; h < (kv + 1) * g.G; ++h) {
+        const bool local = (g.lmask[h >> 5] >> (h & 31)) & 1u;
+        const int hm = (all_dense || !local) ? 1 : 0;
+        if (hm != mode) continue;
+        if (cnt % 4 == 0) {
+          if (f.n >= kMaxQuads) return RTP_ERR_UNSUPPORTED;
+          for (int w = 0; w < 4; ++w) f.head[4 * f.n + w] = kNoHead;
+          f.dense[f.n] = (uint8_t)mode;
+          ++f.n;
+        }
+        f.head[4 * (f.n - 1) + cnt % 4] = (uint8_t)h;
+        ++cnt;
+      }
+    }
+  }
+  return RTP_OK;
+}
+
+static_assert(sizeof(Geo) + sizeof(FlashQuads) + 5 * sizeof(void *) + sizeof(int) <= 4096,
+              "kernel arguments beyond the 4 KiB argument segment");
+
+// The dense quads and the window quads go in two launches: in one launch, the
+// long dense workgroups and the short window workgroups were measured to run
+// three times slower than the two launches back to back.
+int launch_flash_prefill(const Geo &g, const FlashQuads fq[2], const rtp_bf16 *q_pre, const rtp_bf16 *k,
+                         const rtp_bf16 *v, float *out, hipStream_t s) {
+  const int ntiles = (g.nq + kFq - 1) / kFq;
+  for (int mode = 1; mode >= 0; --mode) {
+    if (fq[mode].n == 0) continue;
+    const long long grid = (long long)(ntiles + 7) / 8 * 8 * fq[mode].n * g.B;
+    hipLaunchKernelGGL(flash_prefill_kernel, dim3((unsigned)grid), dim3(kWG), 0, s, g, fq[mode], q_pre, k, v, out,
+                       ntiles);
+    if (hipGetLastError() != hipSuccess) return RTP_ERR_HIP;
+  }
+  return RTP_OK;
+}
+
+}  // namespace rtp

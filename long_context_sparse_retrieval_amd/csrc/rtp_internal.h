@@ -286,4 +286,17 @@ int launch_pf_attn(const Geo &g, int i0, int nqc, const rtp_bf16 *k, const rtp_b
                    long long capw, const int32_t *cnt_ws, float *out, hipStream_t s);
 int pf_split();
 
+// Prefill attention on the matrix cores: workgroups take "quads" of up to four
+// q heads of one KV group and one mode (dense causal, or window + sinks).
+constexpr int kMaxQuads = kMaxHq;
+constexpr uint8_t kNoHead = 255;
+struct FlashQuads {
+  int n;
+  uint8_t head[4 * kMaxQuads];   // kNoHead pads a quad
+  uint8_t dense[kMaxQuads];      // 1: every earlier position; 0: window + sinks
+};
+int make_flash_quads(const Geo &g, bool all_dense, FlashQuads fq[2]);
+int launch_flash_prefill(const Geo &g, const FlashQuads fq[2], const rtp_bf16 *q_pre, const rtp_bf16 *k,
+                         const rtp_bf16 *v, float *out, hipStream_t s);
+
 }  // namespace rtp

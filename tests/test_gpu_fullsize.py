@@ -144,3 +144,27 @@ def test_prefill_full_size_sampled():
     verdicts = [check_set(gpu_set(r, i), int(cnt_h[b, r, i]), cap, t, res["logits"][(b, r, i)], spec.p,
                           f"prefill b{b} r{r} i{i}") for (b, r, i), t in res["topp"].items()]
     say(f"full-size prefill: sampled sets {verdicts.count('exact')} exact, {verdicts.count('tolerated')} tolerated")
+
+
+def test_prefill_attn_full_size_sampled():
+    """The benchmark's 32K prefill (32 q / 8 kv heads, group 0 retrieval, 32768
+    causal queries): sampled queries of a retrieval and a local head, both
+    modes, against the oracle."""
+    rng = np.random.default_rng(2032)
+    B, Hq, Hkv, N, W, S = 1, 32, 8, 32768, 4096, 4
+    hm = [1] * 4 + [0] * 28
+    q = gen.f32_to_bf16_bits(rng.standard_normal((B, Hq, N, 128), dtype=np.float32))
+    k = gen.f32_to_bf16_bits(rng.standard_normal((B, Hkv, N, 128), dtype=np.float32))
+    v = gen.f32_to_bf16_bits(rng.standard_normal((B, Hkv, N, 128), dtype=np.float32))
+    lay = rtp.Layer(B=B, Hq=Hq, Hkv=Hkv, N=N, nq=N, head_mode=hm, window=W, n_sink=S)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    for dense in (False, True):
+        out = rtp.prefill_attn(lay, qd, kd, vd, all_dense=dense).cpu().numpy()
+        assert np.all(np.isfinite(out))
+        for h in (1, 5, 30):                  # a retrieval head, local heads of groups 1 and 7
+            for i in (0, 1, 63, 4095, 4096, 4100, 17000, N - 1):
+                rows = np.arange(i + 1) if (dense or hm[h]) else O.swa_positions(i, W, S)
+                q_rot = O.rope_rotate(O.bf16_to_f64(q[0, h, i]), i, 1e6)
+                ref = O.attention(q_rot, O.bf16_to_f64(k[0, h // 4, rows]), O.bf16_to_f64(v[0, h // 4, rows]))
+                check_output(out[0, h, i], ref, f"prefill dense={dense} h{h} i{i}")
+        say(f"full-size prefill attention (dense={dense}): sampled queries match")

@@ -473,6 +473,47 @@ def test_dense_attn_matches_oracle(N, nq, Hq, Hkv):
         check_output(out[b, h, i], ref, f"dense b{b} h{h} i{i}")
 
 
+# ----------------------------------------------------------------------------- prefill attention
+# (N, nq, Hq, Hkv, head_mode, window, n_sink, all_dense)
+FLASH_CASES = {
+    "mixed-group": (300, 300, 8, 2, [1, 1, 0, 0, 0, 0, 0, 0], 64, 4, False),
+    "ragged-tail": (1000, 77, 8, 1, [1, 0, 1, 0, 0, 0, 0, 1], 200, 4, False),
+    "long-window": (5000, 40, 16, 4, [1] * 4 + [0] * 12, 1000, 4, False),
+    "no-sinks": (700, 150, 4, 1, [0, 0, 0, 0], 100, 0, False),
+    "window-covers-all": (500, 33, 4, 2, [0, 0, 1, 1], 4096, 4, False),
+    "dense-all": (2000, 200, 8, 2, [1] * 2 + [0] * 6, 300, 4, True),
+    "one-query": (4096, 1, 4, 1, [1, 0, 0, 0], 1024, 4, False),
+    "six-heads-per-group": (900, 50, 12, 2, [1] * 6 + [0] * 6, 128, 4, False),
+}
+
+
+@pytest.mark.parametrize("case", list(FLASH_CASES))
+def test_prefill_attn_matches_oracle(case):
+    N, nq, Hq, Hkv, hm, window, n_sink, all_dense = FLASH_CASES[case]
+    say(f"prefill_attn {case}: N={N} nq={nq} Hq={Hq} Hkv={Hkv} window={window} sinks={n_sink} dense={all_dense}")
+    rng = np.random.default_rng(N + nq + Hq)
+    B = 2
+    q = _rand_bf16(rng, (B, Hq, nq, 128), 1.5)
+    k = _rand_bf16(rng, (B, Hkv, N, 128))
+    v = _rand_bf16(rng, (B, Hkv, N, 128))
+    lay = rtp.Layer(B=B, Hq=Hq, Hkv=Hkv, N=N, nq=nq, head_mode=hm, window=window, n_sink=n_sink)
+    out = rtp.prefill_attn(lay, dev_bf16(q), dev_bf16(k), dev_bf16(v), all_dense=all_dense)
+    out2 = rtp.prefill_attn(lay, dev_bf16(q), dev_bf16(k), dev_bf16(v), all_dense=all_dense)
+    torch.cuda.synchronize()
+    out, out2 = out.cpu().numpy(), out2.cpu().numpy()
+    assert np.array_equal(out, out2), "two runs differ (non-deterministic)"
+    G = Hq // Hkv
+    queries = range(nq) if nq <= 80 else sorted(set(range(0, nq, 7)) | {nq - 1, nq - 2, 1})
+    for b in range(B):
+        for h in range(Hq):
+            for i in queries:
+                m = N - nq + i
+                rows = np.arange(m + 1) if (all_dense or hm[h]) else O.swa_positions(m, window, n_sink)
+                q_rot = O.rope_rotate(O.bf16_to_f64(q[b, h, i]), m, 1e6)
+                ref = O.attention(q_rot, O.bf16_to_f64(k[b, h // G, rows]), O.bf16_to_f64(v[b, h // G, rows]))
+                check_output(out[b, h, i], ref, f"{case} b{b} h{h} i{i}")
+
+
 # ----------------------------------------------------------------------------- one workspace, many calls
 def test_workspace_serves_every_call_in_sequence():
     """Every call leaves the workspace ready for the next call on a layer of the
