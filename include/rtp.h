@@ -222,6 +222,49 @@ int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf1
                     int32_t *idx_opt, int32_t *count_opt, int64_t cap,
                     void *ws, size_t ws_bytes, void *phase_event, void *stream);
 
+/* ---------------------------------------------------------------- cluster index */
+/* The coarse-to-fine decode of the RTPurboV2 article (finding three): the cached
+ * tokens of each indexer-key head are grouped into K clusters in the indexer
+ * space, a query is matched against the K centres, and attention runs only over
+ * the clusters it hits.  The article names neither the clustering method nor the
+ * hit rule; this library takes Lloyd's k-means on the bf16 indexer keys (exact
+ * fp64 squared distances, ties to the lowest index, centre j initialised to the
+ * key at position floor(j N / K), centres rounded to bf16 after each round; the
+ * index is the assignment against the final centres) and a dynamic top-p over
+ * clusters weighing cluster j as n_j exp(s_j), s_j = fp32(q_idx . c_j), with the
+ * token path's 256-bin histogram (bins above b* whole, clusters of bin b* in
+ * ascending index while the mass before them is below p Z).  K <= min(N, 256). */
+
+/* Workspace bytes of rtp_cluster_build / rtp_cluster_step for this layer and K (0 on
+ * invalid arguments).  It begins with the regular workspace of the layer and
+ * serves every call that one serves; prepare it with rtp_workspace_init. */
+size_t rtp_cluster_workspace_bytes(const rtp_layer *layer, int32_t K);
+
+/* Cluster positions 0..N-1 of every (b, indexer-key head i) into K clusters with
+ * `iters` k-means rounds.  k_idx: [B, Hi, Ncap, R] bf16.  Outputs (device, caller-
+ * owned): centroids [B, Hi, K, R] bf16; counts [B, Hi, K] int32; offsets
+ * [B, Hi, K+1] int32 (offsets[K] = N); members [B, Hi, N] int32, the positions of
+ * cluster j at members[offsets[j] .. offsets[j+1]), ascending.  RTP_ERR_ARG for
+ * K outside [1, min(N, 256)], iters < 0, a layer without retrieval heads or a null
+ * pointer. */
+int rtp_cluster_build(const rtp_layer *layer, const rtp_bf16 *k_idx, int32_t K, int32_t iters,
+                      rtp_bf16 *centroids, int32_t *counts, int32_t *offsets, int32_t *members,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* One decode step (nq = 1, top_k = 0, else RTP_ERR_UNSUPPORTED) over a cluster
+ * index built for this N: each retrieval head r (indexer-key head i = r /
+ * idx_group) scores the centres of (b, i), picks the hit clusters and attends
+ * (eq. (5)) over all their members; local heads attend over window + sinks as in
+ * rtp_decode_step.  idx_opt [B, Hr, 1, cap] receives the member positions (hit
+ * clusters in ascending index, positions ascending in each; truncated at cap),
+ * count_opt [B, Hr, 1] their number.  Layouts of the other arguments as
+ * rtp_decode_step and rtp_cluster_build. */
+int rtp_cluster_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, int32_t K,
+                     const rtp_bf16 *centroids, const int32_t *counts, const int32_t *offsets,
+                     const int32_t *members, const rtp_bf16 *k, const rtp_bf16 *v, float *out,
+                     int32_t *idx_opt, int32_t *count_opt, int64_t cap, void *ws, size_t ws_bytes,
+                     void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "Layer", "RtpError", "library_path", "load", "num_retrieval", "workspace_bytes", "workspace",
     "rope_keys", "index_keys", "index_score", "topp_select", "sparse_attn", "swa_attn", "dense_attn",
-    "decode_step", "append_kv", "prefill_attn", "SYMBOLS",
+    "decode_step", "append_kv", "prefill_attn", "cluster_workspace", "cluster_build", "cluster_step", "SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -26,7 +26,8 @@ _lib = None
 
 SYMBOLS = ("rtp_num_retrieval", "rtp_workspace_bytes", "rtp_workspace_init", "rtp_status_str", "rtp_rope_keys",
            "rtp_index_keys", "rtp_append_kv", "rtp_index_score", "rtp_topp_select", "rtp_sparse_attn", "rtp_swa_attn",
-           "rtp_dense_attn", "rtp_prefill_attn", "rtp_decode_step")
+           "rtp_dense_attn", "rtp_prefill_attn", "rtp_decode_step", "rtp_cluster_workspace_bytes",
+           "rtp_cluster_build", "rtp_cluster_step")
 
 
 class RtpError(RuntimeError):
@@ -72,6 +73,11 @@ def load():
         "rtp_dense_attn": (ctypes.c_int, [L, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "rtp_prefill_attn": (ctypes.c_int, [L, vp, vp, vp, vp, ctypes.c_int32, vp]),
         "rtp_decode_step": (ctypes.c_int, [L, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp, vp]),
+        "rtp_cluster_workspace_bytes": (ctypes.c_size_t, [L, ctypes.c_int32]),
+        "rtp_cluster_build": (ctypes.c_int, [L, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp,
+                                             ctypes.c_size_t, vp]),
+        "rtp_cluster_step": (ctypes.c_int, [L, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp,
+                                            ctypes.c_size_t, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -168,6 +174,62 @@ def workspace(layer: Layer, device="cuda") -> torch.Tensor:
     ws = ws[off:off + n]
     _check(load().rtp_workspace_init(ws.data_ptr(), n, _stream()), "rtp_workspace_init")
     return ws
+
+
+def cluster_workspace(layer: Layer, K: int, device="cuda") -> torch.Tensor:
+    """A prepared workspace for the cluster-index calls of ``layer`` with K clusters
+    (it also serves every call ``workspace(layer)`` serves)."""
+    n = int(load().rtp_cluster_workspace_bytes(ctypes.byref(layer.c()), int(K)))
+    if n == 0:
+        raise RtpError("invalid layer or cluster count")
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:off + n]
+    _check(load().rtp_workspace_init(ws.data_ptr(), n, _stream()), "rtp_workspace_init")
+    return ws
+
+
+def cluster_build(layer: Layer, k_idx, K: int, iters: int, ws) -> dict:
+    """Cluster index of positions 0..N-1 of every (sequence, indexer-key head):
+    centroids [B, Hi, K, R] bf16, counts [B, Hi, K], offsets [B, Hi, K+1] and
+    members [B, Hi, N] (positions grouped by cluster, ascending in each)."""
+    dev = k_idx.device
+    ki = _ptr(k_idx, torch.bfloat16, _cache_shape(layer, layer.Hi, layer.R), "k_idx")
+    cent = torch.empty((layer.B, layer.Hi, K, layer.R), dtype=torch.bfloat16, device=dev)
+    counts = torch.empty((layer.B, layer.Hi, K), dtype=torch.int32, device=dev)
+    offsets = torch.empty((layer.B, layer.Hi, K + 1), dtype=torch.int32, device=dev)
+    members = torch.empty((layer.B, layer.Hi, layer.N), dtype=torch.int32, device=dev)
+    _check(load().rtp_cluster_build(ctypes.byref(layer.c()), ki, int(K), int(iters), cent.data_ptr(),
+                                    counts.data_ptr(), offsets.data_ptr(), members.data_ptr(), ws.data_ptr(),
+                                    ws.numel(), _stream()), "rtp_cluster_build")
+    return dict(K=int(K), centroids=cent, counts=counts, offsets=offsets, members=members)
+
+
+def cluster_step(layer: Layer, q_pre, w_q, index: dict, k, v, ws, out=None, idx=None, count=None) -> torch.Tensor:
+    """Decode step over a cluster index: retrieval heads attend over the members of
+    their hit clusters, local heads over window + sinks; writes every row of out."""
+    K = index["K"]
+    q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
+    wq = _ptr(w_q, torch.bfloat16, (layer.Hr, layer.D, layer.R), "w_q")
+    cent = _ptr(index["centroids"], torch.bfloat16, (layer.B, layer.Hi, K, layer.R), "centroids")
+    cnt = _ptr(index["counts"], torch.int32, (layer.B, layer.Hi, K), "counts")
+    offs = _ptr(index["offsets"], torch.int32, (layer.B, layer.Hi, K + 1), "offsets")
+    mem = _ptr(index["members"], torch.int32, (layer.B, layer.Hi, layer.N), "members")
+    kp = _ptr(k, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k")
+    vp = _ptr(v, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v")
+    if out is None:
+        out = torch.empty((layer.B, layer.Hq, layer.nq, layer.D), dtype=torch.float32, device=q_pre.device)
+    op = _ptr(out, torch.float32, (layer.B, layer.Hq, layer.nq, layer.D), "out")
+    cap = 0
+    ip = cp = None
+    if idx is not None:
+        cap = int(idx.shape[-1])
+        ip = _ptr(idx, torch.int32, (layer.B, layer.Hr, layer.nq, cap), "idx")
+    if count is not None:
+        cp = _ptr(count, torch.int32, (layer.B, layer.Hr, layer.nq), "count")
+    _check(load().rtp_cluster_step(ctypes.byref(layer.c()), q, wq, int(K), cent, cnt, offs, mem, kp, vp, op, ip, cp,
+                                   cap, ws.data_ptr(), ws.numel(), _stream()), "rtp_cluster_step")
+    return out
 
 
 def _cache_shape(layer: Layer, heads: int, width: int):

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librtp.so")
 SOURCES = ["api.hip", "cache_kernels.hip", "append_kernels.hip", "topp_kernels.hip", "attn_kernels.hip",
-           "prefill_kernels.hip", "flash_prefill.hip"]
+           "prefill_kernels.hip", "flash_prefill.hip", "cluster_kernels.hip"]
 ARCH = "gfx950"
 
 COMMON = [

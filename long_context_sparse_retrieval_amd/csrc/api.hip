@@ -224,6 +224,50 @@ int plan_with_ws(const rtp_layer *L, void *ws, size_t ws_bytes, Plan *p, bool de
   return RTP_OK;
 }
 
+// Cluster-index scratch after the regular workspace; ws may be null (sizing).
+int cluster_plan(const rtp_layer *L, int K, void *ws, Geo *g_out, ClGeo *cg, size_t *bytes) {
+  Plan p, pd;
+  int st = make_plan(L, ws, &p);
+  if (st != RTP_OK) return st;
+  st = make_plan(L, nullptr, &pd, true);
+  if (st != RTP_OK) return st;
+  if (K < 1 || K > kMaxClusters || K > L->N) return RTP_ERR_ARG;
+  const Geo &g = p.g;
+  const size_t nu = (size_t)g.B * g.Hi, units = (size_t)g.units;
+  const int ntiles = (int)((g.N + cluster_tile() - 1) / cluster_tile());
+  size_t off = align_up(p.ws_bytes > pd.ws_bytes ? p.ws_bytes : pd.ws_bytes);
+  const size_t o_sum = off;
+  off = align_up(off + nu * K * kR * sizeof(double));
+  const size_t o_cnt = off;
+  off = align_up(off + nu * K * 4);
+  const size_t o_assign = off;
+  off = align_up(off + nu * (size_t)g.N * 4);
+  const size_t o_hist = off;
+  off = align_up(off + nu * (size_t)ntiles * K * 4);
+  const size_t o_start = off;
+  off = align_up(off + units * K * 4);
+  const size_t o_total = off;
+  off = align_up(off + units * 4);
+  const size_t o_list = off;
+  off = align_up(off + units * (size_t)g.N * 4);
+  memset(cg, 0, sizeof(*cg));
+  cg->K = K;
+  cg->ntiles = ntiles;
+  if (ws) {
+    char *base = static_cast<char *>(ws);
+    cg->sum = reinterpret_cast<double *>(base + o_sum);
+    cg->cnt = reinterpret_cast<uint32_t *>(base + o_cnt);
+    cg->assign = reinterpret_cast<int32_t *>(base + o_assign);
+    cg->hist = reinterpret_cast<uint32_t *>(base + o_hist);
+    cg->start = reinterpret_cast<int32_t *>(base + o_start);
+    cg->total = reinterpret_cast<int32_t *>(base + o_total);
+    cg->list = reinterpret_cast<int32_t *>(base + o_list);
+  }
+  *g_out = g;
+  *bytes = off;
+  return RTP_OK;
+}
+
 // The launch wrappers report failures through hipGetLastError(); clear an
 // error left by earlier, unrelated runtime calls so it is not taken for ours.
 hipStream_t as_stream(void *s) {
@@ -363,6 +407,50 @@ int rtp_append_kv(const rtp_layer *layer, const rtp_bf16 *k_new, const rtp_bf16 
   if (!k_new || !v_new || !k_cache || !v_cache) return RTP_ERR_ARG;
   if (p.g.Hi && (!w_k || !k_idx)) return RTP_ERR_ARG;
   return launch_append_kv(p.g, k_new, v_new, w_k, k_cache, v_cache, k_idx, n0, n_new, as_stream(stream));
+}
+
+size_t rtp_cluster_workspace_bytes(const rtp_layer *layer, int32_t K) {
+  Geo g;
+  ClGeo cg;
+  size_t bytes = 0;
+  return cluster_plan(layer, K, nullptr, &g, &cg, &bytes) == RTP_OK ? bytes : 0;
+}
+
+int rtp_cluster_build(const rtp_layer *layer, const rtp_bf16 *k_idx, int32_t K, int32_t iters, rtp_bf16 *centroids,
+                      int32_t *counts, int32_t *offsets, int32_t *members, void *ws, size_t ws_bytes, void *stream) {
+  Geo g;
+  ClGeo cg;
+  size_t need = 0;
+  int st = cluster_plan(layer, K, ws, &g, &cg, &need);
+  if (st != RTP_OK) return st;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return RTP_ERR_ARG;
+  if (ws_bytes < need) return RTP_ERR_WS_TOO_SMALL;
+  if (iters < 0 || g.Hi == 0 || !k_idx || !centroids || !counts || !offsets || !members) return RTP_ERR_ARG;
+  return launch_cluster_build(g, cg, k_idx, iters, centroids, counts, offsets, members, as_stream(stream));
+}
+
+int rtp_cluster_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, int32_t K,
+                     const rtp_bf16 *centroids, const int32_t *counts, const int32_t *offsets, const int32_t *members,
+                     const rtp_bf16 *k, const rtp_bf16 *v, float *out, int32_t *idx_opt, int32_t *count_opt,
+                     int64_t cap, void *ws, size_t ws_bytes, void *stream) {
+  Geo g;
+  ClGeo cg;
+  size_t need = 0;
+  int st = cluster_plan(layer, K, ws, &g, &cg, &need);
+  if (st != RTP_OK) return st;
+  if (layer->nq != 1 || layer->top_k != 0) return RTP_ERR_UNSUPPORTED;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return RTP_ERR_ARG;
+  if (ws_bytes < need) return RTP_ERR_WS_TOO_SMALL;
+  if (!q_pre || !k || !v || !out) return RTP_ERR_ARG;
+  if (g.units && (!w_q || !centroids || !counts || !offsets || !members)) return RTP_ERR_ARG;
+  if (idx_opt && cap < 0) return RTP_ERR_ARG;
+  hipStream_t s = as_stream(stream);
+  st = launch_phase_a(g, q_pre, nullptr, nullptr, nullptr, k, v, out, false, true, s);      // local heads
+  if (st != RTP_OK) return st;
+  st = launch_cluster_select(g, cg, q_pre, w_q, centroids, counts, offsets, members, idx_opt, count_opt,
+                             idx_opt ? cap : 0, s);
+  if (st != RTP_OK) return st;
+  return launch_sparse_attn(g, q_pre, k, v, cg.list, cg.total, g.N, out, s);
 }
 
 int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,

@@ -286,6 +286,26 @@ int launch_pf_attn(const Geo &g, int i0, int nqc, const rtp_bf16 *k, const rtp_b
                    long long capw, const int32_t *cnt_ws, float *out, hipStream_t s);
 int pf_split();
 
+// Cluster index (coarse-to-fine decode): device scratch of the build and the
+// decode's per-query member lists.
+constexpr int kMaxClusters = 256;
+struct ClGeo {
+  int K, ntiles;            // clusters per indexer-key head; assignment tiles per head
+  double *sum;              // [B*Hi][K][R] member sums of a round
+  uint32_t *cnt;            // [B*Hi][K] member counts of a round
+  int32_t *assign;          // [B*Hi][N] final assignment
+  uint32_t *hist;           // [B*Hi][ntiles][K] per-tile counts, then their exclusive prefix
+  int32_t *start;           // [units][K] start of each hit cluster in the query's list (-1: not hit)
+  int32_t *total;           // [units] list length
+  int32_t *list;            // [units][N] member positions of the hit clusters
+};
+int launch_cluster_build(const Geo &g, const ClGeo &cg, const rtp_bf16 *k_idx, int iters, rtp_bf16 *cent,
+                         int32_t *counts, int32_t *offsets, int32_t *members, hipStream_t s);
+int launch_cluster_select(const Geo &g, const ClGeo &cg, const rtp_bf16 *q_pre, const rtp_bf16 *w_q,
+                          const rtp_bf16 *cent, const int32_t *counts, const int32_t *offsets,
+                          const int32_t *members, int32_t *idx_opt, int32_t *count_opt, long long cap, hipStream_t s);
+int cluster_tile();
+
 // Prefill attention on the matrix cores: workgroups take "quads" of up to four
 // q heads of one KV group and one mode (dense causal, or window + sinks).
 constexpr int kMaxQuads = kMaxHq;

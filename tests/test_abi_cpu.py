@@ -107,6 +107,28 @@ def test_calls_reject_before_launch():
     assert lib.rtp_decode_step(L2, fake, None, fake, fake, fake, fake, None, None, 0, fake, need2, None, None) == -1
 
 
+@needs_lib
+def test_cluster_calls_validate_before_launch():
+    lib = rtp.load()
+    fake = 1 << 40
+    lay = _layer()
+    L = ctypes.byref(lay.c())
+    need = lib.rtp_cluster_workspace_bytes(L, 16)
+    assert need > rtp.workspace_bytes(lay)
+    assert lib.rtp_cluster_workspace_bytes(L, 0) == 0 and lib.rtp_cluster_workspace_bytes(L, 257) == 0
+    assert lib.rtp_cluster_workspace_bytes(ctypes.byref(_layer(N=10).c()), 11) == 0      # K > N
+    assert lib.rtp_cluster_build(L, fake, 16, -1, fake, fake, fake, fake, fake, need, None) == -1
+    assert lib.rtp_cluster_build(L, fake, 16, 2, fake, fake, fake, fake, fake, need - 1, None) == -3
+    assert lib.rtp_cluster_build(L, None, 16, 2, fake, fake, fake, fake, fake, need, None) == -1
+    for kw in (dict(top_k=5), dict(nq=4)):
+        lk = _layer(**kw)
+        nk = lib.rtp_cluster_workspace_bytes(ctypes.byref(lk.c()), 16)
+        assert lib.rtp_cluster_step(ctypes.byref(lk.c()), fake, fake, 16, fake, fake, fake, fake, fake, fake, fake,
+                                    None, None, 0, fake, nk, None) == -4
+    assert lib.rtp_cluster_step(L, fake, fake, 16, fake, fake, fake, fake, fake, fake, fake, None, None, 0, fake,
+                                need - 1, None) == -3
+
+
 def test_binding_checks_tensors_without_gpu():
     import torch
     lay = _layer()

@@ -1,0 +1,117 @@
+"""GPU parity of the cluster index (build and decode step) against the oracle.
+
+The build must reproduce the oracle's k-means exactly (centres, counts, the
+member lists); the decode step's member sets must equal the oracle's (except
+when the oracle reports a cluster decision within rounding of p Z, then the
+set must still be a union of whole clusters reaching p) and its outputs must
+meet the attention bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import long_context_sparse_retrieval_amd as rtp
+import oracle as O
+from parity import MARGIN, check_output, dev_bf16, host_bf16, layer_of, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    rtp.load()
+    torch.cuda.init()
+
+
+def _csr(assign, K):
+    order = np.argsort(assign, kind="stable")
+    counts = np.bincount(assign, minlength=K)
+    return counts, np.concatenate(([0], np.cumsum(counts))), order
+
+
+@pytest.mark.parametrize("N,K,iters,Hi", [(300, 1, 2, 1), (300, 7, 0, 2), (5000, 128, 4, 2), (20000, 256, 3, 1),
+                                          (4099, 128, 1, 3), (200, 200, 1, 1)])
+def test_cluster_build_matches_oracle(N, K, iters, Hi):
+    say(f"cluster build N={N} K={K} iters={iters} Hi={Hi}")
+    rng = np.random.default_rng(N + K + iters)
+    B = 2
+    lay = rtp.Layer(B=B, Hq=Hi, Hkv=1, N=N, head_mode=[1] * Hi)
+    k_idx = gen.f32_to_bf16_bits((rng.standard_normal((B, Hi, N, 16)) * 0.7).astype(np.float32))
+    ws = rtp.cluster_workspace(lay, K)
+    idx = rtp.cluster_build(lay, dev_bf16(k_idx), K, iters, ws)
+    idx2 = rtp.cluster_build(lay, dev_bf16(k_idx), K, iters, ws)       # the workspace is reusable
+    cent, counts = host_bf16(idx["centroids"]), idx["counts"].cpu().numpy()
+    offs, mem = idx["offsets"].cpu().numpy(), idx["members"].cpu().numpy()
+    assert torch.equal(idx["members"], idx2["members"]) and torch.equal(idx["centroids"], idx2["centroids"])
+    for b in range(B):
+        for i in range(Hi):
+            ref = O.kmeans_index(k_idx[b, i], K, iters)
+            assert np.array_equal(cent[b, i], ref["centroids"]), f"b{b} i{i}: centres differ"
+            c, o, order = _csr(ref["assign"], K)
+            assert np.array_equal(counts[b, i], c), f"b{b} i{i}: counts differ"
+            assert np.array_equal(offs[b, i], o), f"b{b} i{i}: offsets differ"
+            assert np.array_equal(mem[b, i], order), f"b{b} i{i}: members differ"
+
+
+STEP_CASES = {
+    "cfg2-K64": (2, dict(B=2, N=3000, window=512), 64, 4),
+    "cfg2-K128-shared-keys": (2, dict(B=2, N=5000, window=512, idx_group=4), 128, 3),
+    "cfg4-small-K128": (4, dict(N=40000, window=2048, query_scale="unit"), 128, 4),
+    "one-cluster-per-key": (2, dict(B=1, N=200, window=64, n_needles=4), 200, 1),
+    "p1": (2, dict(B=1, N=2500, window=300, p=1.0), 32, 2),
+}
+
+
+@pytest.mark.parametrize("case", list(STEP_CASES))
+def test_cluster_step_matches_oracle(case):
+    cfg, over, K, iters = STEP_CASES[case]
+    spec = gen.spec_for(cfg, **over)
+    say(f"cluster step {case}: {spec} K={K}")
+    wl = gen.make_workload(spec, 500 + cfg)
+    kc, ki = O.build_caches(wl)
+    lay = layer_of(spec, rtp)
+    ws = rtp.cluster_workspace(lay, K)
+    index = rtp.cluster_build(lay, dev_bf16(ki), K, iters, ws)
+    cap = spec.N
+    idx = torch.full((spec.B, spec.Hr, 1, cap), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((spec.B, spec.Hr, 1), dtype=torch.int32, device="cuda")
+    args = (dev_bf16(wl.q_pre), dev_bf16(wl.w_q), index, dev_bf16(kc), dev_bf16(wl.v), ws)
+    out = rtp.cluster_step(lay, *args, idx=idx, count=cnt).cpu().numpy()
+    out2 = rtp.cluster_step(lay, *args).cpu().numpy()
+    assert np.array_equal(out, out2), "two runs differ"
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    rheads = spec.retrieval_heads()
+    G = spec.G
+    m = spec.N - 1
+    tolerated = 0
+    for b in range(spec.B):
+        refs = {}
+        for r, h in enumerate(rheads):
+            i = r // spec.idx_group
+            if i not in refs:
+                refs[i] = O.kmeans_index(ki[b, i, :spec.N], K, iters)
+            res = O.cluster_decode_head(wl.q_pre[b, h, 0], wl.w_q[r], refs[i], kc[b, h // G], wl.v[b, h // G], m,
+                                        spec.p, spec.rope_theta)
+            got = np.sort(idx[b, r, 0, :cnt[b, r, 0]])
+            if not np.array_equal(got, res["rows"]):
+                t = res["select"]
+                assert t["margin"] < MARGIN, f"b{b} r{r}: member sets differ (margin {t['margin']:.2e})"
+                hit = np.unique(refs[i]["assign"][got])
+                assert np.array_equal(np.sort(O.cluster_members(refs[i]["assign"], hit)), got), "not whole clusters"
+                w = t["weights"]
+                assert w[hit].sum() >= (spec.p - 1e-4) * w.sum(), f"b{b} r{r}: cluster mass below p"
+                tolerated += 1
+                q_rot = O.rope_rotate(O.bf16_to_f64(wl.q_pre[b, h, 0]), m, spec.rope_theta)
+                ref = O.attention(q_rot, O.bf16_to_f64(kc[b, h // G, got]), O.bf16_to_f64(wl.v[b, h // G, got]))
+            else:
+                ref = res["out"]
+            check_output(out[b, h, 0], ref, f"{case} b{b} h{h}")
+        for h in range(spec.Hq):
+            if spec.head_mode()[h]:
+                continue
+            rows = O.swa_positions(m, spec.window, spec.n_sink)
+            q_rot = O.rope_rotate(O.bf16_to_f64(wl.q_pre[b, h, 0]), m, spec.rope_theta)
+            ref = O.attention(q_rot, O.bf16_to_f64(kc[b, h // G, rows]), O.bf16_to_f64(wl.v[b, h // G, rows]))
+            check_output(out[b, h, 0], ref, f"{case} local b{b} h{h}")
+    say(f"{case}: |S| = {sorted(int(c) for c in cnt.ravel())}, {tolerated} tolerated")
