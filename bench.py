@@ -249,6 +249,39 @@ def time_append(case: Case) -> dict:
             "bulk_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "bulk_algorithmic_bytes": nbytes}
 
 
+CLUSTER_K, CLUSTER_ITERS = 128, 8     # cluster index: the article's example K, k-means rounds
+
+
+def time_cluster(case: Case, steps: int) -> dict:
+    """Cluster index on the case's caches: the k-means build once (timed), then
+    the coarse-to-fine decode step over it (timed like the Top-P step)."""
+    spec, lay = case.spec, case.layer
+    ws = rtp.cluster_workspace(lay, CLUSTER_K)
+    k_idx, k, v = case.reps[0]
+    rtp.cluster_build(lay, k_idx, CLUSTER_K, CLUSTER_ITERS, ws)          # warm-up (code load)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    index = rtp.cluster_build(lay, k_idx, CLUSTER_K, CLUSTER_ITERS, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    build_ms = e0.elapsed_time(e1)
+    cnt = torch.zeros((spec.B, spec.Hr, 1), dtype=torch.int32, device="cuda")
+    rtp.cluster_step(lay, case.q, case.w_q, index, k, v, ws, case.out, count=cnt)
+    for _ in range(5):
+        rtp.cluster_step(lay, case.q, case.w_q, index, k, v, ws, case.out)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        rtp.cluster_step(lay, case.q, case.w_q, index, k, v, ws, case.out)
+    e1.record()
+    torch.cuda.synchronize()
+    return {"what": f"rtp_cluster_build (K = {CLUSTER_K}, {CLUSTER_ITERS} k-means rounds per indexer-key head) "
+                    "and rtp_cluster_step over it, same caches",
+            "build_ms": round(build_ms, 3), "us_per_step": round(e0.elapsed_time(e1) / steps * 1e3, 2),
+            "selected_tokens": cnt.cpu().numpy().ravel().tolist()}
+
+
 PREFILL_N = 32768             # full prefill of a 32K context, the pages' shortest prefill figure
 
 
@@ -367,6 +400,9 @@ def main():
         log(f"[bench] cfg{cfg}: {ms * 1e3:.1f} us/step, phase-A kernel {ms_pa * 1e3:.1f} us, {gbps:.0f} GB/s "
             f"algorithmic; |S| {case.counts.ravel().tolist()}; dense comparator {ms_dense * 1e3:.1f} us "
             f"({dense_bytes / (ms_dense * 1e-3) / 1e9:.0f} GB/s), sparse step {ms_dense / ms:.2f}x faster")
+        if cfg in (3, 4) and not args.no_extras:
+            summ[cfg]["cluster"] = time_cluster(case, max(20, args.steps // 4))
+            log(f"[bench] cfg{cfg}: cluster index {summ[cfg]['cluster']}")
         if cfg == 4 and not args.no_extras:
             # the fixed top-k variant of the same kernels on the same caches
             top_p_layer = case.layer
@@ -440,6 +476,8 @@ def main():
                               "what": "same step with rtp_layer.top_k = k instead of Top-P, same caches"}
     if "append" in s:
         out["cache_append"] = s["append"]
+    if "cluster" in s:
+        out["cluster_index"] = s["cluster"]
     if prefill is not None:
         out["prefill_32k"] = prefill
     if cpu is not None:
@@ -454,6 +492,8 @@ def main():
                            "sparse_speedup_vs_dense": (round(s3["dense_us"] / s3["us"], 3)
                                                        if s3["dense_us"] == s3["dense_us"] else None),
                            "selected_tokens": s3["counts"].ravel().tolist()}
+        if "cluster" in s3:
+            out["ctx_128k"]["cluster_index"] = s3["cluster"]
     if 6 in summ and main_cfg != 6:
         s6 = summ[6]
         out["shared_keys_1m"] = {"workload": s6["spec"].name, "indexer_key_heads": s6["spec"].Hi,
