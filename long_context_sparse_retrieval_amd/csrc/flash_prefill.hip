@@ -38,8 +38,8 @@ constexpr int kVPad = kFk + 8;          // padded row of transposed values (elem
 constexpr double kQScale = 1.4426950408889634 / 11.313708498984761;   // log2(e) / sqrt(128)
 
 struct FlashShared {
-  rtp_bf16 k[kFk][kKPad];               // keys of the block, row-major
-  rtp_bf16 vt[kD][kVPad];               // values of the block, transposed
+  rtp_bf16 k[2][kFk][kKPad];            // keys of a block, row-major (double-buffered)
+  rtp_bf16 vt[2][kD][kVPad];            // values of a block, transposed
 };
 
 __device__ __forceinline__ short bf16_rne(float x) {
@@ -120,30 +120,46 @@ __global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq
 #pragma unroll
   for (int t = 0; t < kD / 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (long long x = 0; x < nblk; ++x) {
-    const long long kb = x < sb_end ? x : mb_lo + (x - sb_end);
-    __syncthreads();                                           // the previous block is consumed
-    {
-      // stage: thread t takes key row t / 4, channels 32 (t % 4) .. + 31
-      const int r = tid >> 2, part = tid & 3;
-      long long kp = kb * kFk + r;
-      kp = kp < g.N ? kp : g.N - 1;
-      const uint4 *ks = reinterpret_cast<const uint4 *>(kc + (cbase + kp) * kD + 32 * part);
-      const uint4 *vs = reinterpret_cast<const uint4 *>(vc + (cbase + kp) * kD + 32 * part);
-      uint4 kv4[4], vv4[4];
+  // staging: thread t takes key row t / 4, channels 32 (t % 4) .. + 31 of a
+  // block; the next block's rows are loaded into registers while this block
+  // is computed, then written to the other LDS buffer (one barrier per block)
+  const int sr = tid >> 2, spart = tid & 3;
+  uint4 k0v, k1v, k2v, k3v, v0v, v1v, v2v, v3v;               // the next block's slice, in flight
+#define RTP_FLASH_LOAD(KB)                                                                       \
+  {                                                                                              \
+    long long kp = (KB) * kFk + sr;                                                              \
+    kp = kp < g.N ? kp : g.N - 1;                                                                \
+    const uint4 *ks = reinterpret_cast<const uint4 *>(kc + (cbase + kp) * kD + 32 * spart);     \
+    const uint4 *vs = reinterpret_cast<const uint4 *>(vc + (cbase + kp) * kD + 32 * spart);     \
+    k0v = ks[0]; k1v = ks[1]; k2v = ks[2]; k3v = ks[3];                                          \
+    v0v = vs[0]; v1v = vs[1]; v2v = vs[2]; v3v = vs[3];                                          \
+  }
+  auto store_v = [&](int buf, int u, const uint4 &vw) {
+    const uint32_t w4[4] = {vw.x, vw.y, vw.z, vw.w};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        kv4[u] = ks[u];
-        vv4[u] = vs[u];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4 *>(&sm.k[r][32 * part + 8 * u]) = kv4[u];
-      const rtp_bf16 *ve = reinterpret_cast<const rtp_bf16 *>(vv4);
-#pragma unroll
-      for (int e = 0; e < 32; ++e) sm.vt[32 * part + e][r] = ve[e];
+    for (int c = 0; c < 4; ++c) {
+      sm.vt[buf][32 * spart + 8 * u + 2 * c][sr] = (rtp_bf16)(w4[c] & 0xffffu);
+      sm.vt[buf][32 * spart + 8 * u + 2 * c + 1][sr] = (rtp_bf16)(w4[c] >> 16);
     }
-    __syncthreads();
-    if (h == kNoHead) continue;                                // wave-uniform
+  };
+#define RTP_FLASH_STORE(BUF)                                                                     \
+  {                                                                                              \
+    uint4 *kd = reinterpret_cast<uint4 *>(&sm.k[BUF][sr][32 * spart]);                          \
+    kd[0] = k0v; kd[1] = k1v; kd[2] = k2v; kd[3] = k3v;                                          \
+    store_v(BUF, 0, v0v); store_v(BUF, 1, v1v); store_v(BUF, 2, v2v); store_v(BUF, 3, v3v);      \
+  }
+  auto block_of = [&](long long x) { return x < sb_end ? x : mb_lo + (x - sb_end); };
+  if (nblk > 0) {
+    RTP_FLASH_LOAD(block_of(0));
+    RTP_FLASH_STORE(0);
+  }
+  __syncthreads();
+
+  for (long long x = 0; x < nblk; ++x) {
+    const long long kb = block_of(x);
+    const int buf = (int)(x & 1);
+    RTP_FLASH_LOAD(block_of(x + 1 < nblk ? x + 1 : x));       // clamped: the last block reloads itself
+    if (h != kNoHead) {                                        // wave-uniform
     // S^T for the block's four 16-key subtiles
     f32x4_t s[kFk / 16];
 #pragma unroll
@@ -151,21 +167,27 @@ __global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < kD / 16; ++c) {
-        const bf16x4_t a = *reinterpret_cast<const bf16x4_t *>(&sm.k[16 * st + qn][16 * c + 4 * grp]);
+        const bf16x4_t a = *reinterpret_cast<const bf16x4_t *>(&sm.k[buf][16 * st + qn][16 * c + 4 * grp]);
         acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, qh[c], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ql[c], acc, 0, 0, 0);
       }
       s[st] = acc;
     }
-    // masks: this lane holds query qn and keys 64 kb + 16 st + 4 grp + e
+    // masks (this lane holds query qn and keys 64 kb + 16 st + 4 grp + e), only
+    // on blocks that straddle the causal edge, the window's start or the sinks
+    const int k0 = (int)(kb * kFk), k1 = k0 + kFk - 1;
+    const bool inside = k1 <= (int)m0 &&
+                        (dense || k1 < g.n_sink || (long long)k0 > m_hi - g.window);      // block-uniform
     float mb = -INFINITY;
 #pragma unroll
     for (int st = 0; st < kFk / 16; ++st) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const long long kp = kb * kFk + 16 * st + 4 * grp + e;
-        const bool ok = kp <= qp && (dense || kp < g.n_sink || kp > qp - g.window);
-        s[st][e] = ok ? s[st][e] : -INFINITY;
+        if (!inside) {
+          const int kp = k0 + 16 * st + 4 * grp + e, q32 = (int)qp;
+          const bool ok = kp <= q32 && (dense || kp < g.n_sink || kp > q32 - g.window);
+          s[st][e] = ok ? s[st][e] : -INFINITY;
+        }
         mb = fmaxf(mb, s[st][e]);
       }
     }
@@ -202,12 +224,17 @@ __global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq
     for (int t = 0; t < kD / 16; ++t) {
 #pragma unroll
       for (int st = 0; st < kFk / 16; ++st) {
-        const bf16x4_t bv = *reinterpret_cast<const bf16x4_t *>(&sm.vt[16 * t + qn][16 * st + 4 * grp]);
+        const bf16x4_t bv = *reinterpret_cast<const bf16x4_t *>(&sm.vt[buf][16 * t + qn][16 * st + 4 * grp]);
         o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb[st], bv, o[t], 0, 0, 0);
         o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl[st], bv, o[t], 0, 0, 0);
       }
     }
+    }                                                          // h != kNoHead
+    if (x + 1 < nblk) RTP_FLASH_STORE((int)((x + 1) & 1));
+    __syncthreads();
   }
+#undef RTP_FLASH_LOAD
+#undef RTP_FLASH_STORE
   if (h == kNoHead) return;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
