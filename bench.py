@@ -282,6 +282,70 @@ def time_cluster(case: Case, steps: int) -> dict:
             "selected_tokens": cnt.cpu().numpy().ravel().tolist()}
 
 
+def time_cluster_topics(steps: int) -> dict:
+    """The cluster index where its premise holds: the 1M layer (64 q / 8 kv
+    heads, KV groups 0-1 retrieval) with pre-RoPE keys of the retrieval groups
+    drawn around 128 topic centres (k = mu_t + 0.3 eps, topics uniform over
+    positions) and each retrieval query along one topic centre; local groups
+    and values plain Gaussian.  Caches written by rtp_append_kv.  Reports the
+    cluster step against the Top-P step on the same caches, the member-set
+    sizes and the fraction of the query's topic the set covers (recall)."""
+    B, Hq, Hkv, N, T = 1, 64, 8, 1 << 20, 128
+    hm = [1] * 16 + [0] * 48
+    lay = rtp.Layer(B=B, Hq=Hq, Hkv=Hkv, N=N, head_mode=hm)
+    gen_ = torch.Generator(device="cuda").manual_seed(4242)
+    mu = torch.randn((2, T, 128), device="cuda", generator=gen_)
+    topic = torch.randint(0, T, (2, N), device="cuda", generator=gen_)
+    k_pre = torch.randn((B, Hkv, N, 128), device="cuda", generator=gen_)
+    for g in range(2):
+        k_pre[0, g] = mu[g, topic[g]] + 0.3 * k_pre[0, g]
+    k_pre = k_pre.to(torch.bfloat16)
+    v = torch.randn((B, Hkv, N, 128), device="cuda", generator=gen_).to(torch.bfloat16)
+    w = (torch.randn((16, 128, 16), device="cuda", generator=gen_) / 128 ** 0.5).to(torch.bfloat16)
+    tq = torch.randint(0, T, (16,), device="cuda", generator=gen_)
+    q = torch.randn((B, Hq, 1, 128), device="cuda", generator=gen_)
+    for r in range(16):
+        q[0, r, 0] = mu[r // 8, tq[r]]
+    q = q.to(torch.bfloat16)
+    kc, vc = torch.empty_like(k_pre), torch.empty_like(v)
+    ki = torch.empty((B, 16, N, 16), dtype=torch.bfloat16, device="cuda")
+    rtp.append_kv(lay, k_pre, v, w, kc, vc, ki, 0)
+    del k_pre
+    ws = rtp.cluster_workspace(lay, CLUSTER_K)
+    index = rtp.cluster_build(lay, ki, CLUSTER_K, CLUSTER_ITERS, ws)
+    out = torch.empty((B, Hq, 1, 128), dtype=torch.float32, device="cuda")
+    idx = torch.full((B, 16, 1, N), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((B, 16, 1), dtype=torch.int32, device="cuda")
+    rtp.cluster_step(lay, q, w, index, kc, vc, ws, out, idx=idx, count=cnt)
+    torch.cuda.synchronize()
+    cnt_h = cnt.cpu().numpy().ravel()
+    recall = []
+    for r in range(16):
+        sel = idx[0, r, 0, :int(cnt_h[r])].long()
+        in_topic = int((topic[r // 8, sel] == tq[r]).sum().item())
+        recall.append(in_topic / max(1, int((topic[r // 8] == tq[r]).sum().item())))
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    us_cluster = timed(lambda: rtp.cluster_step(lay, q, w, index, kc, vc, ws, out))
+    us_topp = timed(lambda: rtp.decode_step(lay, q, w, ki, kc, vc, ws, out))
+    return {"what": "1M layer with 128-topic retrieval keys (k = mu_t + 0.3 eps), queries along a topic centre: "
+                    f"cluster step (K = {CLUSTER_K}) vs the Top-P step on the same caches",
+            "cluster_us_per_step": round(us_cluster, 2), "topp_us_per_step": round(us_topp, 2),
+            "speedup": round(us_topp / us_cluster, 3), "selected_tokens": cnt_h.tolist(),
+            "topic_recall_min": round(min(recall), 4)}
+
+
 PREFILL_N = 32768             # full prefill of a 32K context, the pages' shortest prefill figure
 
 
@@ -421,10 +485,13 @@ def main():
         del case
         torch.cuda.empty_cache()
 
-    prefill = None
+    prefill = topics = None
     if not args.only and not args.no_extras:
         prefill = time_prefill()
         log(f"[bench] prefill attention 32K: {prefill}")
+        torch.cuda.empty_cache()
+        topics = time_cluster_topics(max(20, args.steps // 4))
+        log(f"[bench] cluster index on topic keys: {topics}")
         torch.cuda.empty_cache()
 
     main_cfg = cfgs[0]
@@ -480,6 +547,8 @@ def main():
         out["cluster_index"] = s["cluster"]
     if prefill is not None:
         out["prefill_32k"] = prefill
+    if topics is not None:
+        out["cluster_index_topic_keys"] = topics
     if cpu is not None:
         out["cpu_baseline"] = cpu
     if 3 in summ and main_cfg != 3:

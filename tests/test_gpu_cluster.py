@@ -115,3 +115,50 @@ def test_cluster_step_matches_oracle(case):
             ref = O.attention(q_rot, O.bf16_to_f64(kc[b, h // G, rows]), O.bf16_to_f64(wl.v[b, h // G, rows]))
             check_output(out[b, h, 0], ref, f"{case} local b{b} h{h}")
     say(f"{case}: |S| = {sorted(int(c) for c in cnt.ravel())}, {tolerated} tolerated")
+
+
+def test_cluster_step_on_topic_keys_is_selective_and_matches_oracle():
+    """Keys drawn around 16 topic centres, each query along one centre: the index
+    recovers the topics, the hit set is the query's topic, and the step matches
+    the oracle."""
+    rng = np.random.default_rng(77)
+    B, Hq, Hkv, N, T, K = 1, 8, 2, 8192, 16, 64          # about four clusters per topic
+    hm = [1] * 4 + [0] * 4
+    lay = rtp.Layer(B=B, Hq=Hq, Hkv=Hkv, N=N, head_mode=hm, window=512)
+    mu = rng.standard_normal((T, 128))
+    topic = rng.integers(0, T, N)
+    k_pre = rng.standard_normal((B, Hkv, N, 128))
+    k_pre[0, 0] = mu[topic] + 0.3 * k_pre[0, 0]
+    k_pre = gen.f32_to_bf16_bits(k_pre.astype(np.float32))
+    v = gen.f32_to_bf16_bits(rng.standard_normal((B, Hkv, N, 128)).astype(np.float32))
+    w = gen.f32_to_bf16_bits((rng.standard_normal((4, 128, 16)) / np.sqrt(128)).astype(np.float32))
+    tq = rng.integers(0, T, 4)
+    q = rng.standard_normal((B, Hq, 1, 128))
+    for r in range(4):
+        q[0, r, 0] = mu[tq[r]]
+    q = gen.f32_to_bf16_bits(q.astype(np.float32))
+    kc, vc = torch.empty((B, Hkv, N, 128), dtype=torch.bfloat16, device="cuda"), torch.empty(
+        (B, Hkv, N, 128), dtype=torch.bfloat16, device="cuda")
+    ki = torch.empty((B, 4, N, 16), dtype=torch.bfloat16, device="cuda")
+    rtp.append_kv(lay, dev_bf16(k_pre), dev_bf16(v), dev_bf16(w), kc, vc, ki, 0)
+    ws = rtp.cluster_workspace(lay, K)
+    index = rtp.cluster_build(lay, ki, K, 8, ws)
+    idx = torch.full((B, 4, 1, N), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((B, 4, 1), dtype=torch.int32, device="cuda")
+    out = rtp.cluster_step(lay, dev_bf16(q), dev_bf16(w), index, kc, vc, ws, idx=idx, count=cnt).cpu().numpy()
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    kc_h, ki_h = host_bf16(kc), host_bf16(ki)
+    recalls = []
+    for r in range(4):
+        ref_idx = O.kmeans_index(ki_h[0, r, :N], K, 8)
+        res = O.cluster_decode_head(q[0, r, 0], w[r], ref_idx, kc_h[0, 0], v[0, 0], N - 1, 0.9, 1e6)
+        got = np.sort(idx[0, r, 0, :cnt[0, r, 0]])
+        assert np.array_equal(got, res["rows"]), f"r{r}: member sets differ"
+        check_output(out[0, r, 0], res["out"], f"topic r{r}")
+        # k-means may split a topic or merge two (a local optimum of Lloyd's
+        # rounds from positional seeds), so coverage is checked loosely
+        in_topic = np.sum(topic[got] == tq[r]) / np.sum(topic == tq[r])
+        assert in_topic >= 0.5, f"r{r}: only {in_topic:.2f} of the query's topic in the hit set"
+        assert len(got) <= N // 4, f"r{r}: hit set not selective ({len(got)} of {N})"
+        recalls.append(round(float(in_topic), 3))
+    say(f"topic keys: |S| = {cnt.ravel().tolist()}, topic coverage {recalls}")
