@@ -146,6 +146,8 @@ class Case:
         torch.cuda.synchronize()
         ms_step = t_begin.elapsed_time(t_end) / steps
         ms_pa = float(np.mean([starts[s].elapsed_time(mids[s]) for s in range(steps)]))
+        per = [starts[s].elapsed_time(starts[s + 1]) for s in range(steps - 1)] + [starts[-1].elapsed_time(t_end)]
+        self.pct = {f"p{q}": round(float(np.percentile(per, q)) * 1e3, 2) for q in (10, 50, 90)}
         return ms_step, ms_pa
 
 
@@ -460,7 +462,8 @@ def main():
                          pa_gbps=pa_bytes / (ms_pa * 1e-3) / 1e9, pa_bytes=pa_bytes,
                          bytes=case.bytes_total, spec=case.spec, counts=case.counts,
                          union=case.gather_rows_union, rsum=case.gather_rows_sum,
-                         dense_us=ms_dense * 1e3, dense_gbps=dense_bytes / (ms_dense * 1e-3) / 1e9)
+                         dense_us=ms_dense * 1e3, dense_gbps=dense_bytes / (ms_dense * 1e-3) / 1e9,
+                         pct=case.pct)
         log(f"[bench] cfg{cfg}: {ms * 1e3:.1f} us/step, phase-A kernel {ms_pa * 1e3:.1f} us, {gbps:.0f} GB/s "
             f"algorithmic; |S| {case.counts.ravel().tolist()}; dense comparator {ms_dense * 1e3:.1f} us "
             f"({dense_bytes / (ms_dense * 1e-3) / 1e9:.0f} GB/s), sparse step {ms_dense / ms:.2f}x faster")
@@ -527,6 +530,7 @@ def main():
                      "frac": round(s["pa_gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel_us": round(s["pa_us"], 2), "algorithmic_bytes_per_launch": s["pa_bytes"]},
         "copy_ceiling_GBps": round(copy_gbps, 1),
+        "step_us_percentiles": s["pct"],
     }
     if s["dense_us"] == s["dense_us"]:          # measured (not NaN)
         dense_peak_us = 512 * spec.B * spec.Hkv * spec.N / HBM_PEAK_GBPS / 1e3
@@ -554,6 +558,7 @@ def main():
     if 3 in summ and main_cfg != 3:
         s3 = summ[3]
         out["ctx_128k"] = {"workload": s3["spec"].name, "us_per_step": round(s3["us"], 2),
+                           "step_us_percentiles": s3["pct"],
                            "GBps": round(s3["gbps"], 1), "hbm_frac": round(s3["frac"], 4),
                            "algorithmic_bytes_per_step": s3["bytes"], "phase_a_kernel_us": round(s3["pa_us"], 2),
                            "phase_a_GBps": round(s3["pa_gbps"], 1),
