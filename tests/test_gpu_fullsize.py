@@ -1,7 +1,7 @@
 """Parity at the full workload sizes, in the launch configuration the benchmark times.
 
-The GPU runs one whole decode step of the 128K (batch 4) and 1M layers (the
-latter also with one indexer-key head per KV group): every
+The GPU runs one whole decode step of the 32K (batch 8), 128K (batch 4) and 1M
+layers (the latter also with one indexer-key head per KV group): every
 head, caches written by the library's own cache writers, the same tile and
 workgroup plan as the benchmark.  The oracle, which cannot redo the whole step
 in seconds, builds its own caches for a sample and recomputes, one by one:
@@ -22,7 +22,7 @@ from parity import check_output, check_set, dev_bf16, layer_of, say
 pytestmark = pytest.mark.gpu
 
 # config -> sampled retrieval heads r of sequence 0 (r = 0 concentrated, r = 1 diffuse)
-FULL = {"128k-b4": (3, [0, 1]), "1m-b1": (4, [0, 1]), "1m-b1-shared-keys": (6, [0, 1])}
+FULL = {"32k-b8": (2, [0, 1]), "128k-b4": (3, [0, 1]), "1m-b1": (4, [0, 1]), "1m-b1-shared-keys": (6, [0, 1])}
 
 
 @pytest.fixture(scope="module", autouse=True)
