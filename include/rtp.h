@@ -61,7 +61,7 @@ enum rtp_status {
   RTP_ERR_ARG = -1,           /* null pointer, p <= 0 or NaN, window < 1, bad head_mode entry, n0/n1 out of range */
   RTP_ERR_SHAPE = -2,         /* D != 128, R != 16, Hq % Hkv != 0, nq < 1, N < nq, N > Ncap, N >= 2^31, Hq > 256 */
   RTP_ERR_WS_TOO_SMALL = -3,  /* ws_bytes < rtp_workspace_bytes(layer) */
-  RTP_ERR_UNSUPPORTED = -4,   /* a valid request this build does not implement */
+  RTP_ERR_UNSUPPORTED = -4,   /* a valid request the library does not implement */
   RTP_ERR_HIP = -5            /* a HIP launch failed */
 };
 

@@ -288,7 +288,7 @@ const char *rtp_status_str(int status) {
     case RTP_ERR_ARG: return "invalid argument";
     case RTP_ERR_SHAPE: return "unsupported or inconsistent shape";
     case RTP_ERR_WS_TOO_SMALL: return "workspace too small";
-    case RTP_ERR_UNSUPPORTED: return "not supported by this build";
+    case RTP_ERR_UNSUPPORTED: return "not supported by this library";
     case RTP_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";
   }

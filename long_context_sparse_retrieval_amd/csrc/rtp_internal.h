@@ -286,7 +286,7 @@ int launch_pf_attn(const Geo &g, int i0, int nqc, const rtp_bf16 *k, const rtp_b
                    long long capw, const int32_t *cnt_ws, float *out, hipStream_t s);
 int pf_split();
 
-// Cluster index (coarse-to-fine decode): device scratch of the build and the
+// Cluster index (coarse-to-fine decode): device scratch of the index build and the
 // decode's per-query member lists.
 constexpr int kMaxClusters = 256;
 struct ClGeo {
