@@ -11,10 +11,12 @@
 // Design for gfx950.  A workgroup takes 16 consecutive queries of up to four
 // q heads of one KV group and one mode (one wave per head), so every K/V block
 // staged in LDS serves four heads.  Scores are computed transposed,
-// S^T = K Q^T, with v_mfma_f32_16x16x16_bf16: the keys are the A operand and
-// the queries the B operand, so each lane ends up with four keys of one query
-// -- exactly the A-operand layout P needs for O += P V, with V staged
-// transposed.  The rotated query (fp64 angles) and the softmax weights P are
+// S^T = K Q^T, with v_mfma_f32_16x16x32_bf16 (K = 32 per instruction, twice
+// the rate of the K = 16 form on gfx950): the keys are the A operand and the
+// queries the B operand, so each lane ends up with four keys of one query per
+// 16-key subtile; two subtiles fill the eight slots of P's A operand for a
+// K = 32 step of O += P V, and V, staged transposed, is read in the same slot
+// order.  The rotated query (fp64 angles) and the softmax weights P are
 // each split into two bf16 halves, x = hi + lo, so both products carry
 // fp32-level precision (bf16 P alone misses the 2e-3 output bar when a few
 // keys dominate).  The softmax runs online in base 2 (log2(e) / sqrt(d)
@@ -29,6 +31,7 @@ namespace rtp {
 namespace {
 
 typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kFq = 16;                 // queries per wave (the matrix-core N dimension)
@@ -77,20 +80,21 @@ __global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq
   const int qn = lane & 15, grp = lane >> 4;
   const size_t cbase = ((size_t)b * g.Hkv + kvg) * g.Ncap;
 
-  // this lane's query (qn) as the B operand: dims 16 c + 4 grp .. + 3, split hi + lo
-  bf16x4_t qh[kD / 16], ql[kD / 16];
+  // this lane's query (qn) as the B operand of the K = 32 products: dims
+  // 32 c + 8 grp .. + 7, split hi + lo
+  bf16x8_t qh[kD / 32], ql[kD / 32];
   {
     const int qi = i0 + (qn < nqt ? qn : nqt - 1);
     const long long mq = g.N - g.nq + qi;
     const rtp_bf16 *qr = q_pre + (((size_t)b * g.Hq + (h != kNoHead ? h : h0)) * g.nq + qi) * kD;
 #pragma unroll
-    for (int c = 0; c < kD / 16; ++c) {
-      const int d0 = 16 * c + 4 * grp;
-      const uint2 w = *reinterpret_cast<const uint2 *>(qr + d0);
-      const uint32_t ww[2] = {w.x, w.y};
-      float r[4];
+    for (int c = 0; c < kD / 32; ++c) {
+      const int d0 = 32 * c + 8 * grp;
+      const uint4 w = *reinterpret_cast<const uint4 *>(qr + d0);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+      float r[8];
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
+      for (int pp = 0; pp < 4; ++pp) {
         double sn, cs;
         rope_sincos(mq, g.theta, d0 / 2 + pp, sn, cs);
         const double a = (double)bf_lo(ww[pp]), bb = (double)bf_hi(ww[pp]);
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq
         r[2 * pp + 1] = (float)((a * sn + bb * cs) * kQScale);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 8; ++e) {
         const short hi = bf16_rne(r[e]);
         qh[c][e] = hi;
         ql[c][e] = bf16_rne(r[e] - bf16_f(hi));
@@ -166,10 +170,10 @@ __global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq
     for (int st = 0; st < kFk / 16; ++st) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < kD / 16; ++c) {
-        const bf16x4_t a = *reinterpret_cast<const bf16x4_t *>(&sm.k[buf][16 * st + qn][16 * c + 4 * grp]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, qh[c], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ql[c], acc, 0, 0, 0);
+      for (int c = 0; c < kD / 32; ++c) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&sm.k[buf][16 * st + qn][32 * c + 8 * grp]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[c], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[c], acc, 0, 0, 0);
       }
       s[st] = acc;
     }
@@ -219,14 +223,29 @@ __global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq
 #pragma unroll
       for (int t = 0; t < kD / 16; ++t) o[t][e] *= ae;
     }
-    // O += P V
+    // O += P V in K = 32 steps over subtile pairs (2 j, 2 j + 1): slot 8 grp + e
+    // of a step is key 16 (2 j) + 4 grp + e and slot 8 grp + 4 + e is key
+    // 16 (2 j + 1) + 4 grp + e, the same order for P and for V
+    bf16x8_t ph[kFk / 32], plo[kFk / 32];
+#pragma unroll
+    for (int j = 0; j < kFk / 32; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ph[j][e] = pb[2 * j][e];
+        ph[j][4 + e] = pb[2 * j + 1][e];
+        plo[j][e] = pl[2 * j][e];
+        plo[j][4 + e] = pl[2 * j + 1][e];
+      }
+    }
 #pragma unroll
     for (int t = 0; t < kD / 16; ++t) {
 #pragma unroll
-      for (int st = 0; st < kFk / 16; ++st) {
-        const bf16x4_t bv = *reinterpret_cast<const bf16x4_t *>(&sm.vt[buf][16 * t + qn][16 * st + 4 * grp]);
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb[st], bv, o[t], 0, 0, 0);
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl[st], bv, o[t], 0, 0, 0);
+      for (int j = 0; j < kFk / 32; ++j) {
+        const bf16x4_t v0 = *reinterpret_cast<const bf16x4_t *>(&sm.vt[buf][16 * t + qn][32 * j + 4 * grp]);
+        const bf16x4_t v1 = *reinterpret_cast<const bf16x4_t *>(&sm.vt[buf][16 * t + qn][32 * j + 16 + 4 * grp]);
+        const bf16x8_t bv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[j], bv, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[j], bv, o[t], 0, 0, 0);
       }
     }
     }                                                          // h != kNoHead
