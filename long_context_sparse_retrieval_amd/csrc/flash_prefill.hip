@@ -45,10 +45,8 @@ struct FlashShared {
   rtp_bf16 vt[2][kD][kVPad];            // values of a block, transposed
 };
 
-__device__ __forceinline__ short bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (short)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
+// fp32 -> bf16, nearest even (one v_cvt_pk_bf16_f32 per pair on gfx950)
+__device__ __forceinline__ short bf16_rne(float x) { return __builtin_bit_cast(short, (__bf16)x); }
 
 __device__ __forceinline__ float bf16_f(short b) { return __uint_as_float((uint32_t)(uint16_t)b << 16); }
 
