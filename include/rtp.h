@@ -25,6 +25,12 @@
  *    failed launch (the HIP error is left for hipGetLastError()).
  *  - Non-finite inputs are undefined behaviour.
  *  - Row-major layouts; "cap" rows of the caches are strided by Ncap.
+ *  - "[B, Hkv, Ncap, D]" for the K/V caches (k, v, k_cache, v_cache) stands for
+ *    the layout rtp_layer.local_ring selects; it is exactly that shape when
+ *    local_ring is 0.  With ring groups present, calls that need more than the
+ *    window of the newest position -- rtp_dense_attn, rtp_prefill_attn and
+ *    nq > 1 -- return RTP_ERR_UNSUPPORTED.  Pre-RoPE key inputs (k_pre) and the
+ *    indexer keys keep their stated shapes.
  *  - Retrieval heads are numbered r = 0..Hr-1 in ascending q-head order; the
  *    q head h belongs to KV group h / (Hq / Hkv).
  *  - The query of a decode step sits at position m = N - 1.  With nq > 1 the
@@ -90,10 +96,25 @@ typedef struct rtp_layer {
                                  with Top-P: the first top_k positions in the order (histogram bin
                                  ascending, position ascending), every position when top_k >= m+1;
                                  p is then ignored.  < 0 is RTP_ERR_ARG. */
+  int32_t local_ring;         /* K/V cache layout.  0: k, v are [B, Hkv, Ncap, D].  1: a KV group
+                                 whose q heads are all local heads keeps only the rows its heads
+                                 can attend to (FASB abstract and section 3.2: only retrieval
+                                 heads retain the full cache; local heads see a window plus
+                                 sinks): n_sink + window rows, position n in row n for n < n_sink
+                                 and in row n_sink + (n - n_sink) mod window otherwise.  Per
+                                 sequence the groups follow in order, a full group taking Ncap
+                                 rows and a ring group n_sink + window rows; rtp_kv_rows gives
+                                 the rows per sequence, so k, v are [B, rtp_kv_rows(layer), D].
+                                 Other values are RTP_ERR_ARG. */
 } rtp_layer;
 
 /* Number of retrieval heads Hr implied by layer->head_mode (or a negative status). */
 int32_t rtp_num_retrieval(const rtp_layer *layer);
+
+/* Rows per sequence of the K/V caches in the layout of layer->local_ring:
+ * Hkv * Ncap without ring groups, else (full groups) * Ncap + (ring groups) *
+ * (n_sink + window).  A negative status on an invalid layer. */
+int64_t rtp_kv_rows(const rtp_layer *layer);
 
 /* Workspace bytes the calls taking `ws` need for this layer (0 on invalid layer).
  * The same workspace serves every call below. */
@@ -137,7 +158,9 @@ int rtp_index_keys(const rtp_layer *layer, const rtp_bf16 *k_pre, const rtp_bf16
  * tokens; must not overlap the caches); w_k: [Hi, D, R]; k_cache, v_cache:
  * [B, Hkv, Ncap, D]; k_idx: [B, Hi, Ncap, R].  Rows outside [n0, n0 + n_new)
  * are not touched.  Requires 0 <= n0, n0 + n_new <= Ncap (else RTP_ERR_ARG);
- * w_k and k_idx may be null when the layer has no retrieval head. */
+ * w_k and k_idx may be null when the layer has no retrieval head.  In a ring
+ * group (local_ring) position n goes to its ring row, and of new positions
+ * that share a row only the last is written. */
 int rtp_append_kv(const rtp_layer *layer, const rtp_bf16 *k_new, const rtp_bf16 *v_new, const rtp_bf16 *w_k,
                   rtp_bf16 *k_cache, rtp_bf16 *v_cache, rtp_bf16 *k_idx, int64_t n0, int64_t n_new,
                   void *stream);

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "Layer", "RtpError", "library_path", "load", "num_retrieval", "workspace_bytes", "workspace",
     "rope_keys", "index_keys", "index_score", "topp_select", "sparse_attn", "swa_attn", "dense_attn",
-    "decode_step", "append_kv", "prefill_attn", "cluster_workspace", "cluster_build", "cluster_step", "SYMBOLS",
+    "decode_step", "append_kv", "prefill_attn", "cluster_workspace", "cluster_build", "cluster_step", "kv_rows",
+    "kv_shape", "SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +28,7 @@ _lib = None
 SYMBOLS = ("rtp_num_retrieval", "rtp_workspace_bytes", "rtp_workspace_init", "rtp_status_str", "rtp_rope_keys",
            "rtp_index_keys", "rtp_append_kv", "rtp_index_score", "rtp_topp_select", "rtp_sparse_attn", "rtp_swa_attn",
            "rtp_dense_attn", "rtp_prefill_attn", "rtp_decode_step", "rtp_cluster_workspace_bytes",
-           "rtp_cluster_build", "rtp_cluster_step")
+           "rtp_cluster_build", "rtp_cluster_step", "rtp_kv_rows")
 
 
 class RtpError(RuntimeError):
@@ -40,7 +41,7 @@ class _CLayer(ctypes.Structure):
         ("R", ctypes.c_int32), ("nq", ctypes.c_int32), ("N", ctypes.c_int64), ("Ncap", ctypes.c_int64),
         ("head_mode", ctypes.POINTER(ctypes.c_int8)), ("p", ctypes.c_float), ("window", ctypes.c_int32),
         ("n_sink", ctypes.c_int32), ("rope_theta", ctypes.c_double), ("idx_group", ctypes.c_int32),
-        ("top_k", ctypes.c_int64),
+        ("top_k", ctypes.c_int64), ("local_ring", ctypes.c_int32),
     ]
 
 
@@ -61,6 +62,7 @@ def load():
     sig = {
         "rtp_num_retrieval": (ctypes.c_int32, [L]),
         "rtp_workspace_bytes": (ctypes.c_size_t, [L]),
+        "rtp_kv_rows": (ctypes.c_int64, [L]),
         "rtp_workspace_init": (ctypes.c_int, [vp, ctypes.c_size_t, vp]),
         "rtp_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "rtp_rope_keys": (ctypes.c_int, [L, vp, vp, i64, i64, vp]),
@@ -106,6 +108,7 @@ class Layer:
     R: int = 16
     idx_group: int = 1        # retrieval heads sharing one indexer-key head (1 or Hq // Hkv)
     top_k: int = 0            # 0: Top-P with mass p; > 0: fixed top-k on the histogram order
+    local_ring: int = 0       # 1: all-local KV groups keep only n_sink + window rows (K/V caches [B, kv_rows, D])
     _keep: list = field(default_factory=list, repr=False, compare=False)
 
     @property
@@ -126,7 +129,7 @@ class Layer:
         self._keep = [hm]
         return _CLayer(self.B, self.Hq, self.Hkv, self.D, self.R, self.nq, self.N, self.cap_rows,
                        ctypes.cast(hm, ctypes.POINTER(ctypes.c_int8)), self.p, self.window, self.n_sink,
-                       self.rope_theta, self.idx_group, self.top_k)
+                       self.rope_theta, self.idx_group, self.top_k, self.local_ring)
 
 
 def _check(status: int, what: str):
@@ -215,8 +218,8 @@ def cluster_step(layer: Layer, q_pre, w_q, index: dict, k, v, ws, out=None, idx=
     cnt = _ptr(index["counts"], torch.int32, (layer.B, layer.Hi, K), "counts")
     offs = _ptr(index["offsets"], torch.int32, (layer.B, layer.Hi, K + 1), "offsets")
     mem = _ptr(index["members"], torch.int32, (layer.B, layer.Hi, layer.N), "members")
-    kp = _ptr(k, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k")
-    vp = _ptr(v, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v")
+    kp = _ptr(k, torch.bfloat16, kv_shape(layer), "k")
+    vp = _ptr(v, torch.bfloat16, kv_shape(layer), "v")
     if out is None:
         out = torch.empty((layer.B, layer.Hq, layer.nq, layer.D), dtype=torch.float32, device=q_pre.device)
     op = _ptr(out, torch.float32, (layer.B, layer.Hq, layer.nq, layer.D), "out")
@@ -234,6 +237,21 @@ def cluster_step(layer: Layer, q_pre, w_q, index: dict, k, v, ws, out=None, idx=
 
 def _cache_shape(layer: Layer, heads: int, width: int):
     return (layer.B, heads, layer.cap_rows, width)
+
+
+def kv_rows(layer: Layer) -> int:
+    """K/V cache rows per sequence in the layer's layout (rtp_kv_rows)."""
+    r = int(load().rtp_kv_rows(ctypes.byref(layer.c())))
+    if r < 0:
+        _check(r, "rtp_kv_rows")
+    return r
+
+
+def kv_shape(layer: Layer) -> tuple:
+    """Shape of the K/V caches: [B, Hkv, Ncap, D], or [B, kv_rows, D] with local_ring."""
+    if layer.local_ring:
+        return (layer.B, kv_rows(layer), layer.D)
+    return _cache_shape(layer, layer.Hkv, layer.D)
 
 
 def rope_keys(layer: Layer, k_pre: torch.Tensor, k_out: torch.Tensor | None = None, n0: int = 0,
@@ -273,8 +291,8 @@ def append_kv(layer: Layer, k_new: torch.Tensor, v_new: torch.Tensor, w_k, k_cac
     shp_new = (layer.B, layer.Hkv, n_new, layer.D)
     a = _ptr(k_new, torch.bfloat16, shp_new, "k_new")
     b = _ptr(v_new, torch.bfloat16, shp_new, "v_new")
-    kc = _ptr(k_cache, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k_cache")
-    vc = _ptr(v_cache, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v_cache")
+    kc = _ptr(k_cache, torch.bfloat16, kv_shape(layer), "k_cache")
+    vc = _ptr(v_cache, torch.bfloat16, kv_shape(layer), "v_cache")
     w = ki = None
     if layer.Hi:
         w = _ptr(w_k, torch.bfloat16, (layer.Hi, layer.D, layer.R), "w_k")
@@ -316,8 +334,8 @@ def sparse_attn(layer: Layer, q_pre, k, v, idx, count, ws, out=None) -> torch.Te
     """Sparse attention of the retrieval heads over given sets (eq. 5); writes their rows of out."""
     cap = idx.shape[-1]
     q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
-    kp = _ptr(k, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k")
-    vp = _ptr(v, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v")
+    kp = _ptr(k, torch.bfloat16, kv_shape(layer), "k")
+    vp = _ptr(v, torch.bfloat16, kv_shape(layer), "v")
     ip = _ptr(idx, torch.int32, (layer.B, layer.Hr, layer.nq, cap), "idx")
     cp = _ptr(count, torch.int32, (layer.B, layer.Hr, layer.nq), "count")
     if out is None:
@@ -331,8 +349,8 @@ def sparse_attn(layer: Layer, q_pre, k, v, idx, count, ws, out=None) -> torch.Te
 def swa_attn(layer: Layer, q_pre, k, v, ws, out=None) -> torch.Tensor:
     """Sliding-window attention with sinks of the local heads; writes their rows of out."""
     q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
-    kp = _ptr(k, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k")
-    vp = _ptr(v, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v")
+    kp = _ptr(k, torch.bfloat16, kv_shape(layer), "k")
+    vp = _ptr(v, torch.bfloat16, kv_shape(layer), "v")
     if out is None:
         out = torch.zeros((layer.B, layer.Hq, layer.nq, layer.D), dtype=torch.float32, device=q_pre.device)
     op = _ptr(out, torch.float32, (layer.B, layer.Hq, layer.nq, layer.D), "out")
@@ -344,8 +362,8 @@ def swa_attn(layer: Layer, q_pre, k, v, ws, out=None) -> torch.Tensor:
 def dense_attn(layer: Layer, q_pre, k, v, ws, out=None) -> torch.Tensor:
     """Dense attention of every head over every cached position (the comparator); writes every row of out."""
     q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
-    kp = _ptr(k, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k")
-    vp = _ptr(v, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v")
+    kp = _ptr(k, torch.bfloat16, kv_shape(layer), "k")
+    vp = _ptr(v, torch.bfloat16, kv_shape(layer), "v")
     if out is None:
         out = torch.empty((layer.B, layer.Hq, layer.nq, layer.D), dtype=torch.float32, device=q_pre.device)
     op = _ptr(out, torch.float32, (layer.B, layer.Hq, layer.nq, layer.D), "out")
@@ -359,8 +377,8 @@ def prefill_attn(layer: Layer, q_pre, k, v, out=None, all_dense: bool = False) -
     over every earlier position, local heads over window + sinks (every head dense
     when all_dense); writes every row of out."""
     q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
-    kp = _ptr(k, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k")
-    vp = _ptr(v, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v")
+    kp = _ptr(k, torch.bfloat16, kv_shape(layer), "k")
+    vp = _ptr(v, torch.bfloat16, kv_shape(layer), "v")
     if out is None:
         out = torch.empty((layer.B, layer.Hq, layer.nq, layer.D), dtype=torch.float32, device=q_pre.device)
     op = _ptr(out, torch.float32, (layer.B, layer.Hq, layer.nq, layer.D), "out")
@@ -375,8 +393,8 @@ def decode_step(layer: Layer, q_pre, w_q, k_idx, k, v, ws, out=None, idx=None, c
     q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
     w = _ptr(w_q, torch.bfloat16, (layer.Hr, layer.D, layer.R), "w_q") if layer.Hr else None
     ki = _ptr(k_idx, torch.bfloat16, _cache_shape(layer, layer.Hi, layer.R), "k_idx") if layer.Hr else None
-    kp = _ptr(k, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "k")
-    vp = _ptr(v, torch.bfloat16, _cache_shape(layer, layer.Hkv, layer.D), "v")
+    kp = _ptr(k, torch.bfloat16, kv_shape(layer), "k")
+    vp = _ptr(v, torch.bfloat16, kv_shape(layer), "v")
     if out is None:
         out = torch.empty((layer.B, layer.Hq, layer.nq, layer.D), dtype=torch.float32, device=q_pre.device)
     op = _ptr(out, torch.float32, (layer.B, layer.Hq, layer.nq, layer.D), "out")

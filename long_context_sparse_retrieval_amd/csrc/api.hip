@@ -34,6 +34,7 @@ int validate_layer(const rtp_layer *L) {
   const int G = L->Hq / L->Hkv;
   if (L->idx_group < 0 || (L->idx_group > 1 && L->idx_group != G)) return RTP_ERR_ARG;
   if (L->top_k < 0) return RTP_ERR_ARG;
+  if (L->local_ring != 0 && L->local_ring != 1) return RTP_ERR_ARG;
   if (L->idx_group > 1)        // shared indexer keys: retrieval heads come in whole KV groups
     for (int kv = 0; kv < L->Hkv; ++kv)
       for (int h = kv * G + 1; h < (kv + 1) * G; ++h)
@@ -71,6 +72,7 @@ int make_geo(const rtp_layer *L, bool dense, Geo &g) {
     LD.window = (int32_t)(L->N < 0x7fffffff ? L->N : 0x7fffffff);
     LD.n_sink = 0;
     LD.idx_group = 1;
+    LD.local_ring = 0;
     L = &LD;
   }
   memset(&g, 0, sizeof(g));
@@ -99,6 +101,12 @@ int make_geo(const rtp_layer *L, bool dense, Geo &g) {
     for (int h = kv * g.G; h < (kv + 1) * g.G; ++h) nl += L->head_mode[h] ? 0 : 1;
     if (nl) g.lgroup[g.nlg++] = (uint8_t)kv;
     if (nl > max_local) max_local = nl;
+    if (L->local_ring && nl == g.G) g.gring[kv >> 5] |= 1u << (kv & 31);
+  }
+  {
+    int nring = 0;
+    for (int w = 0; w < kMaxHq / 32; ++w) nring += __builtin_popcount(g.gring[w]);
+    g.rows_b = (long long)(g.Hkv - nring) * g.Ncap + (long long)nring * ((long long)g.n_sink + g.window);
   }
   g.units = g.B * g.Hr * g.nq;
   g.T = pick_tile(g.N);
@@ -215,6 +223,12 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
   return RTP_OK;
 }
 
+bool has_ring(const Geo &g) {
+  for (int w = 0; w < kMaxHq / 32; ++w)
+    if (g.gring[w]) return true;
+  return false;
+}
+
 int plan_with_ws(const rtp_layer *L, void *ws, size_t ws_bytes, Plan *p, bool dense = false) {
   const int st = make_plan(L, ws, p, dense);
   if (st != RTP_OK) return st;
@@ -299,6 +313,12 @@ int32_t rtp_num_retrieval(const rtp_layer *layer) {
   return st != RTP_OK ? st : count_retrieval(layer);
 }
 
+int64_t rtp_kv_rows(const rtp_layer *layer) {
+  Geo g;
+  const int st = make_geo(layer, false, g);
+  return st != RTP_OK ? st : g.rows_b;
+}
+
 size_t rtp_workspace_bytes(const rtp_layer *layer) {
   Plan p, pd;
   if (make_plan(layer, nullptr, &p) != RTP_OK || make_plan(layer, nullptr, &pd, true) != RTP_OK) return 0;
@@ -367,6 +387,7 @@ int rtp_swa_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *
   int st = plan_with_ws(layer, ws, ws_bytes, &p);
   if (st != RTP_OK) return st;
   if (p.g.swa_units && (!q_pre || !k || !v || !out)) return RTP_ERR_ARG;
+  if (has_ring(p.g) && p.g.nq > 1) return RTP_ERR_UNSUPPORTED;     // a ring holds the newest window only
   return launch_phase_a(p.g, q_pre, nullptr, nullptr, nullptr, k, v, out, false, true, as_stream(stream));
 }
 
@@ -376,6 +397,12 @@ int rtp_dense_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16
   int st = plan_with_ws(layer, ws, ws_bytes, &p, true);
   if (st != RTP_OK) return st;
   if (!q_pre || !k || !v || !out) return RTP_ERR_ARG;
+  if (layer->local_ring) {                    // every head needs every position
+    Geo reg;
+    st = make_geo(layer, false, reg);
+    if (st != RTP_OK) return st;
+    if (has_ring(reg)) return RTP_ERR_UNSUPPORTED;
+  }
   if (layer->nq > 1) {            // many queries: the matrix-core kernel, every head dense
     FlashQuads fq[2];
     st = make_flash_quads(p.g, true, fq);
@@ -391,6 +418,7 @@ int rtp_prefill_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf
   int st = make_plan(layer, nullptr, &p);
   if (st != RTP_OK) return st;
   if (!q_pre || !k || !v || !out) return RTP_ERR_ARG;
+  if (has_ring(p.g)) return RTP_ERR_UNSUPPORTED;     // earlier queries need rows a ring no longer holds
   FlashQuads fq[2];
   st = make_flash_quads(p.g, all_dense != 0, fq);
   if (st != RTP_OK) return st;
@@ -464,6 +492,7 @@ int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf1
   if (idx_opt && cap < 0) return RTP_ERR_ARG;
   hipStream_t s = as_stream(stream);
   if (layer->nq > 1) {
+    if (has_ring(p.g)) return RTP_ERR_UNSUPPORTED;   // earlier queries' windows left the ring
     // chunked prefill: matrix-core selection and attention per chunk of queries
     st = launch_pf_qprep(p.g, q_pre, w_q, s);
     if (st != RTP_OK) return st;

@@ -32,7 +32,8 @@ __device__ __forceinline__ double bf16_val(rtp_bf16 v) { return (double)__uint_a
 __device__ __forceinline__ void append_kv_pairs(const Geo &g, const rtp_bf16 *__restrict__ k_new,
                                                 const rtp_bf16 *__restrict__ v_new, rtp_bf16 *__restrict__ kc,
                                                 rtp_bf16 *__restrict__ vc, int b, int kv0, long long t,
-                                                long long n_new, long long n, int pair, double sn, double cs) {
+                                                long long n_new, long long n, long long n_end, int pair,
+                                                double sn, double cs) {
   uint32_t kw[kApKvBatch], vw[kApKvBatch];
 #pragma unroll
   for (int u = 0; u < kApKvBatch; ++u) {
@@ -43,8 +44,9 @@ __device__ __forceinline__ void append_kv_pairs(const Geo &g, const rtp_bf16 *__
   }
 #pragma unroll
   for (int u = 0; u < kApKvBatch; ++u) {
-    if (kv0 + u < g.Hkv) {
-      const size_t dst = (((size_t)b * g.Hkv + kv0 + u) * g.Ncap + n) * kD + 2 * pair;
+    const bool ring = kv0 + u < g.Hkv && kv_is_ring(g, kv0 + u);
+    if (kv0 + u < g.Hkv && kv_keep(g, ring, n, n_end)) {
+      const size_t dst = (kv_group_base(g, b, kv0 + u) + kv_row(g, ring, n)) * kD + 2 * pair;
       *reinterpret_cast<uint32_t *>(kc + dst) = rope_pair_bf16(kw[u], sn, cs);
       *reinterpret_cast<uint32_t *>(vc + dst) = vw[u];
     }
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(kWG) void append_small_kernel(Geo g, const rtp_bf16
   double sn, cs;
   sincos((double)n * rope_freq(g.theta, pair), &sn, &cs);
   for (int kv0 = (tid >> 6) * kApKvBatch; kv0 < g.Hkv; kv0 += 4 * kApKvBatch)
-    append_kv_pairs(g, k_new, v_new, kc, vc, b, kv0, t, n_new, n, pair, sn, cs);
+    append_kv_pairs(g, k_new, v_new, kc, vc, b, kv0, t, n_new, n, n0 + n_new, pair, sn, cs);
   // indexer keys: thread (indexer-key head, output channel)
   for (int x = tid; x < g.Hi * kR; x += kWG) {
     const int i = x / kR, j = x % kR;
@@ -113,7 +115,8 @@ __global__ __launch_bounds__(kWG) void append_bulk_kernel(Geo g, const rtp_bf16 
   const long long t0 = (long long)blk * kApRows;
   const int nr = (int)(n_new - t0 < kApRows ? n_new - t0 : kApRows);
   const size_t src0 = ((size_t)bg * n_new + t0) * kD;                 // first new row of this block
-  const size_t dst0 = ((size_t)bg * g.Ncap + n0 + t0) * kD;
+  const bool ring = kv_is_ring(g, kv);
+  const size_t gbase = kv_group_base(g, b, kv) * kD;
   // indexer-key heads fed by this KV group: a contiguous range [i0, i1)
   int i0 = g.Hi, i1 = g.Hi;
   for (int i = 0; i < g.Hi; ++i) {
@@ -133,11 +136,13 @@ __global__ __launch_bounds__(kWG) void append_bulk_kernel(Geo g, const rtp_bf16 
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (r0 + u < nr) {
+      const long long n = n0 + t0 + r0 + u;
+      if (r0 + u < nr && kv_keep(g, ring, n, n0 + n_new)) {
         double sn, cs;
-        sincos((double)(n0 + t0 + r0 + u) * th, &sn, &cs);
-        *reinterpret_cast<uint32_t *>(kc + dst0 + (size_t)(r0 + u) * kD + 2 * lane) = rope_pair_bf16(kw[u], sn, cs);
-        *reinterpret_cast<uint32_t *>(vc + dst0 + (size_t)(r0 + u) * kD + 2 * lane) = vw[u];
+        sincos((double)n * th, &sn, &cs);
+        const size_t dst = gbase + (size_t)kv_row(g, ring, n) * kD + 2 * lane;
+        *reinterpret_cast<uint32_t *>(kc + dst) = rope_pair_bf16(kw[u], sn, cs);
+        *reinterpret_cast<uint32_t *>(vc + dst) = vw[u];
       }
     }
   }

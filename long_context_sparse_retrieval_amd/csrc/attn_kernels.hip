@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kWG) void sparse_attn_kernel(Geo g, const rtp_bf16 
   const long long per = (cnt + kSpChunks - 1) / kSpChunks;
   const long long a0 = (long long)ch * per;
   const long long a1 = a0 + per < cnt ? a0 + per : cnt;
-  const size_t cbase = ((size_t)b * g.Hkv + kvg) * g.Ncap * kD;
+  const size_t cbase = kv_group_base(g, b, kvg) * kD;
   // running state of this chunk: thread d < 128 holds channel d
   float run_m = -INFINITY, run_l = 0.f, run_o = 0.f;
   for (long long s0 = a0; s0 < a1; s0 += 1024) {

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq
   const int nqt = g.nq - i0 < kFq ? g.nq - i0 : kFq;
   const long long m0 = g.N - g.nq + i0, m_hi = m0 + nqt - 1;
   const int qn = lane & 15, grp = lane >> 4;
-  const size_t cbase = ((size_t)b * g.Hkv + kvg) * g.Ncap;
+  const size_t cbase = kv_group_base(g, b, kvg);
 
   // this lane's query (qn) as the B operand of the K = 32 products: dims
   // 32 c + 8 grp .. + 7, split hi + lo

@@ -457,7 +457,7 @@ __global__ __launch_bounds__(kWG) void pf_attn_kernel(Geo g, int i0, int nqc, co
   const long long per = (cnt + kPfSplit - 1) / kPfSplit;
   const long long a0 = (long long)sp * per;
   const long long a1 = a0 + per < cnt ? a0 + per : cnt;
-  const size_t cbase = ((size_t)b * g.Hkv + kvg) * g.Ncap * kD;
+  const size_t cbase = kv_group_base(g, b, kvg) * kD;
   const int32_t *list = idx_ws + (size_t)ul * capw;
   float run_m = -INFINITY, run_l = 0.f, run_o = 0.f;
   for (long long s0 = a0; s0 < a1; s0 += 1024) {

@@ -79,6 +79,11 @@ struct Geo {
   uint8_t rhead[kMaxHq];     // q head of retrieval head r
   uint8_t lgroup[kMaxHq];    // KV groups with local heads
   uint32_t lmask[kMaxHq / 32];
+  // K/V cache layout: per sequence, the KV groups in order; a full group
+  // holds Ncap rows, a ring group (every head local, layer.local_ring) holds
+  // n_sink + window rows
+  uint32_t gring[kMaxHq / 32];   // KV groups stored as rings
+  long long rows_b;              // cache rows per sequence
   // workspace
   uint8_t *codes;        // [units][nt*T] local bin of every token
   TileSum *tsum;         // [units][nt]
@@ -94,6 +99,34 @@ struct Geo {
   int32_t *pf_cnt;       // [B * Hr * pf_qch]
   uint32_t *ctr_swa;     // [swa_units * swa_hb]
 };
+
+// ------------------------------------------------------------------ K/V cache addressing
+__host__ __device__ __forceinline__ bool kv_is_ring(const Geo &g, int kvg) {
+  return (g.gring[kvg >> 5] >> (kvg & 31)) & 1u;
+}
+
+// First cache row of KV group kvg of sequence b (multiply by kD for elements).
+__host__ __device__ __forceinline__ size_t kv_group_base(const Geo &g, int b, int kvg) {
+  int nring = 0;
+  for (int w = 0; w < (kvg >> 5); ++w) nring += __builtin_popcount(g.gring[w]);
+  nring += __builtin_popcount(g.gring[kvg >> 5] & ((1u << (kvg & 31)) - 1u));
+  return (size_t)b * g.rows_b + (size_t)(kvg - nring) * g.Ncap + (size_t)nring * ((size_t)g.n_sink + g.window);
+}
+
+// Row of position n (0 <= n < 2^31) inside its group: n itself, or for a ring
+// group the sinks in rows 0..n_sink-1 and position n >= n_sink in row
+// n_sink + (n - n_sink) mod window.
+__host__ __device__ __forceinline__ long long kv_row(const Geo &g, bool ring, long long n) {
+  if (!ring || n < g.n_sink) return n;
+  return g.n_sink + (long long)((uint32_t)(n - g.n_sink) % (uint32_t)g.window);
+}
+
+// Whether an append of positions [.., n_end) writes position n: in a ring
+// group a later position of the same append takes the row of every position
+// n_sink <= n < n_end - window, so only the last one is stored.
+__host__ __device__ __forceinline__ bool kv_keep(const Geo &g, bool ring, long long n, long long n_end) {
+  return !ring || n < g.n_sink || n >= n_end - g.window;
+}
 
 // ------------------------------------------------------------------ numerics
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -70,7 +70,8 @@ __device__ __forceinline__ void swa_block(const Geo &g, long long x, const rtp_b
   const long long L = ns + (m - lo + 1);
   const long long r0 = (long long)ch * g.swa_chunk;
   const long long r1 = r0 + g.swa_chunk < L ? r0 + g.swa_chunk : L;
-  const size_t cbase = ((size_t)b * g.Hkv + kvg) * g.Ncap * kD;
+  const size_t cbase = kv_group_base(g, b, kvg) * kD;
+  const bool ring = kv_is_ring(g, kvg);
   const rtp_bf16 *kb = kc + cbase, *vb = vc + cbase;
 
   // request the first rows before preparing the queries
@@ -83,7 +84,7 @@ __device__ __forceinline__ void swa_block(const Geo &g, long long x, const rtp_b
     ok[u] = ri < r1;
     kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
     if (ok[u]) {
-      const long long n = swa_row(ri, lo, ns);
+      const long long n = kv_row(g, ring, swa_row(ri, lo, ns));
       kr[u] = *reinterpret_cast<const uint4 *>(kb + n * kD + sub * 8);
       vr[u] = *reinterpret_cast<const uint4 *>(vb + n * kD + sub * 8);
     }
@@ -155,7 +156,7 @@ __device__ __forceinline__ void swa_block(const Geo &g, long long x, const rtp_b
       ok[u] = ri < r1;
       kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
       if (ok[u]) {
-        const long long n = swa_row(ri, lo, ns);
+        const long long n = kv_row(g, ring, swa_row(ri, lo, ns));
         kr[u] = *reinterpret_cast<const uint4 *>(kb + n * kD + sub * 8);
         vr[u] = *reinterpret_cast<const uint4 *>(vb + n * kD + sub * 8);
       }

@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
   const int t_begin = w * g.fin_tpw;
   const int t_end = t_begin + g.fin_tpw < g.nt ? t_begin + g.fin_tpw : g.nt;
   const int kvg = hq / g.G;
-  const size_t cbase = ((size_t)b * g.Hkv + kvg) * g.Ncap * kD;
+  const size_t cbase = kv_group_base(g, b, kvg) * kD;
   const TileSum *ts = g.tsum + (size_t)unit * g.nt;
 
   // Loads are counted in issue order (vmcnt), so everything the threshold

@@ -66,6 +66,7 @@ def test_workspace_sizing_monotone():
     (dict(nq=0), -2), (dict(N=1 << 31, Ncap=1 << 31), -2), (dict(p=0.0), -1), (dict(p=float("nan")), -1),
     (dict(window=0), -1), (dict(n_sink=-1), -1), (dict(head_mode=[2, 0, 0, 0, 0, 0, 0, 0]), -1),
     (dict(rope_theta=0.0), -1), (dict(top_k=-1), -1), (dict(idx_group=3), -1), (dict(idx_group=-1), -1),
+    (dict(local_ring=2), -1), (dict(local_ring=-1), -1),
 ])
 def test_layer_validation(kw, code):
     lay = _layer(**kw)
@@ -105,6 +106,37 @@ def test_calls_reject_before_launch():
     need2 = rtp.workspace_bytes(lay2)
     assert lib.rtp_decode_step(L2, fake, fake, fake, fake, fake, fake, None, None, 0, fake, need2 - 1, None, None) == -3
     assert lib.rtp_decode_step(L2, fake, None, fake, fake, fake, fake, None, None, 0, fake, need2, None, None) == -1
+
+
+@needs_lib
+def test_ring_layout_rows_and_limits():
+    """K/V rows per sequence with local_ring (closed form), and the calls that
+    need positions a ring no longer holds refuse it before any launch."""
+    lib = rtp.load()
+    fake = 1 << 40
+    N, W, S = 5000, 4096, 4
+    # KV group 0 retrieval, group 1 all local
+    assert rtp.kv_rows(_layer()) == 2 * N
+    assert rtp.kv_rows(_layer(local_ring=1)) == N + (S + W)
+    assert rtp.kv_rows(_layer(local_ring=1, head_mode=[1, 0, 0, 0] + [0] * 4)) == N + (S + W)   # mixed group: full
+    assert rtp.kv_rows(_layer(local_ring=1, head_mode=[0] * 8, window=100, n_sink=0)) == 2 * 100
+    assert rtp.kv_rows(_layer(local_ring=1, head_mode=[1] * 8)) == 2 * N
+    assert rtp.kv_rows(_layer(local_ring=1, Ncap=9000)) == 9000 + (S + W)
+    assert lib.rtp_kv_rows(ctypes.byref(_layer(local_ring=3).c())) == -1
+    ring = _layer(local_ring=1)
+    L = ctypes.byref(ring.c())
+    need = rtp.workspace_bytes(ring)
+    assert lib.rtp_prefill_attn(L, fake, fake, fake, fake, 0, None) == -4
+    assert lib.rtp_dense_attn(L, fake, fake, fake, fake, fake, need, None) == -4
+    r4 = _layer(local_ring=1, nq=4)
+    L4 = ctypes.byref(r4.c())
+    n4 = rtp.workspace_bytes(r4)
+    assert lib.rtp_decode_step(L4, fake, fake, fake, fake, fake, fake, None, None, 0, fake, n4, None, None) == -4
+    assert lib.rtp_swa_attn(L4, fake, fake, fake, fake, fake, n4, None) == -4
+    # no ring group (every KV group has a retrieval head): local_ring changes nothing
+    nr = _layer(local_ring=1, head_mode=[1, 0, 0, 0, 0, 0, 0, 1])
+    assert rtp.kv_rows(nr) == 2 * N
+    assert lib.rtp_prefill_attn(ctypes.byref(nr.c()), None, fake, fake, fake, 0, None) == -1    # reaches the checks
 
 
 @needs_lib
