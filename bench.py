@@ -251,6 +251,45 @@ def time_append(case: Case) -> dict:
             "bulk_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "bulk_algorithmic_bytes": nbytes}
 
 
+def time_local_ring(case: Case, steps: int, warmup: int) -> dict:
+    """The same step over ring-buffer caches (rtp_layer.local_ring): all-local KV
+    groups keep n_sink + window rows.  The ring caches are written by one bulk
+    rtp_append_kv of the whole context; the step must equal the full layout's
+    bit for bit, and is timed like the Top-P step."""
+    spec = case.spec
+    lay = dataclasses.replace(case.layer, local_ring=1)
+    shape = rtp.kv_shape(lay)
+    k_idx0, _, v0 = case.reps[0]
+    kr, vr = torch.empty(shape, dtype=torch.bfloat16, device="cuda"), torch.empty(shape, dtype=torch.bfloat16,
+                                                                                  device="cuda")
+    ki = torch.empty_like(k_idx0)
+    k_pre = up(case.wl.k_pre)
+    rtp.append_kv(lay, k_pre, v0, up(case.wl.w_k), kr, vr, ki, 0)
+    del k_pre
+    same_keys = bool(torch.equal(ki, k_idx0))
+    del ki
+    reps = [(case.reps[i][0], kr.clone() if i else kr, vr.clone() if i else vr) for i in range(len(case.reps))]
+    ws = rtp.workspace(lay)
+    out_full = rtp.decode_step(case.layer, case.q, case.w_q, *case.reps[0], case.ws)
+    out_ring = rtp.decode_step(lay, case.q, case.w_q, *reps[0], ws)
+    identical = bool(torch.equal(out_full, out_ring))
+    for s in range(warmup):
+        rtp.decode_step(lay, case.q, case.w_q, *reps[s % len(reps)], ws, case.out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for s in range(steps):
+        rtp.decode_step(lay, case.q, case.w_q, *reps[s % len(reps)], ws, case.out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    full_bytes = 2 * 2 * spec.B * spec.Hkv * spec.N * spec.D
+    return {"what": "same step over ring-buffer K/V caches for the all-local KV groups (local_ring = 1)",
+            "us_per_step": round(us, 2), "kv_cache_bytes_full": full_bytes,
+            "kv_cache_bytes_ring": 2 * 2 * spec.B * rtp.kv_rows(lay) * spec.D,
+            "outputs_identical_to_full_layout": identical, "indexer_keys_identical": same_keys}
+
+
 CLUSTER_K, CLUSTER_ITERS = 128, 8     # cluster index: the article's example K, k-means rounds
 
 
@@ -478,6 +517,10 @@ def main():
             case.layer = top_p_layer
             summ[cfg].update(topk_us=ms_k * 1e3, topk_pa_us=ms_pa_k * 1e3)
             log(f"[bench] cfg{cfg}: fixed top-k (k = {TOPK_BENCH}) {ms_k * 1e3:.1f} us/step")
+        if cfg == 4 and not args.no_extras:
+            summ[cfg]["ring"] = time_local_ring(case, max(20, args.steps // 4), args.warmup)
+            log(f"[bench] cfg{cfg}: ring-buffer local caches {summ[cfg]['ring']}")
+            torch.cuda.empty_cache()
         if cfg == 4 and not args.no_cpu_baseline:
             t0 = time.time()
             cpu = cpu_baseline(case)
@@ -547,6 +590,8 @@ def main():
                               "what": "same step with rtp_layer.top_k = k instead of Top-P, same caches"}
     if "append" in s:
         out["cache_append"] = s["append"]
+    if "ring" in s:
+        out["local_ring"] = s["ring"]
     if "cluster" in s:
         out["cluster_index"] = s["cluster"]
     if prefill is not None:

@@ -105,7 +105,8 @@ typedef struct rtp_layer {
                                  sequence the groups follow in order, a full group taking Ncap
                                  rows and a ring group n_sink + window rows; rtp_kv_rows gives
                                  the rows per sequence, so k, v are [B, rtp_kv_rows(layer), D].
-                                 Other values are RTP_ERR_ARG. */
+                                 Other values, or 1 with n_sink + window >= 2^31, are
+                                 RTP_ERR_ARG. */
 } rtp_layer;
 
 /* Number of retrieval heads Hr implied by layer->head_mode (or a negative status). */

@@ -35,6 +35,7 @@ int validate_layer(const rtp_layer *L) {
   if (L->idx_group < 0 || (L->idx_group > 1 && L->idx_group != G)) return RTP_ERR_ARG;
   if (L->top_k < 0) return RTP_ERR_ARG;
   if (L->local_ring != 0 && L->local_ring != 1) return RTP_ERR_ARG;
+  if (L->local_ring && (int64_t)L->n_sink + L->window >= (1ll << 31)) return RTP_ERR_ARG;   // ring rows < 2^31
   if (L->idx_group > 1)        // shared indexer keys: retrieval heads come in whole KV groups
     for (int kv = 0; kv < L->Hkv; ++kv)
       for (int h = kv * G + 1; h < (kv + 1) * G; ++h)
@@ -106,6 +107,7 @@ int make_geo(const rtp_layer *L, bool dense, Geo &g) {
   {
     int nring = 0;
     for (int w = 0; w < kMaxHq / 32; ++w) nring += __builtin_popcount(g.gring[w]);
+    g.any_ring = nring > 0;
     g.rows_b = (long long)(g.Hkv - nring) * g.Ncap + (long long)nring * ((long long)g.n_sink + g.window);
   }
   g.units = g.B * g.Hr * g.nq;
@@ -223,11 +225,7 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
   return RTP_OK;
 }
 
-bool has_ring(const Geo &g) {
-  for (int w = 0; w < kMaxHq / 32; ++w)
-    if (g.gring[w]) return true;
-  return false;
-}
+bool has_ring(const Geo &g) { return g.any_ring != 0; }
 
 int plan_with_ws(const rtp_layer *L, void *ws, size_t ws_bytes, Plan *p, bool dense = false) {
   const int st = make_plan(L, ws, p, dense);

@@ -79,11 +79,6 @@ struct Geo {
   uint8_t rhead[kMaxHq];     // q head of retrieval head r
   uint8_t lgroup[kMaxHq];    // KV groups with local heads
   uint32_t lmask[kMaxHq / 32];
-  // K/V cache layout: per sequence, the KV groups in order; a full group
-  // holds Ncap rows, a ring group (every head local, layer.local_ring) holds
-  // n_sink + window rows
-  uint32_t gring[kMaxHq / 32];   // KV groups stored as rings
-  long long rows_b;              // cache rows per sequence
   // workspace
   uint8_t *codes;        // [units][nt*T] local bin of every token
   TileSum *tsum;         // [units][nt]
@@ -98,19 +93,49 @@ struct Geo {
   int32_t *pf_idx;       // [B * Hr * pf_qch][N] selected positions of one chunk (shares the codes' space)
   int32_t *pf_cnt;       // [B * Hr * pf_qch]
   uint32_t *ctr_swa;     // [swa_units * swa_hb]
+  // K/V cache layout: per sequence, the KV groups in order; a full group
+  // holds Ncap rows, a ring group (every head local, layer.local_ring) holds
+  // n_sink + window rows.  (Last in the struct: the kernels' other fields
+  // keep their argument offsets.)
+  uint32_t gring[kMaxHq / 32];   // KV groups stored as rings
+  int any_ring;                  // any bit of gring set
+  long long rows_b;              // cache rows per sequence
 };
 
 // ------------------------------------------------------------------ K/V cache addressing
+// Every gring word is read at a constant index (one load the compiler can
+// issue at the kernel's start) and the group's word picked arithmetically: an
+// index that depends on the group would put a load between the head's
+// decode and its first K/V access.
 __host__ __device__ __forceinline__ bool kv_is_ring(const Geo &g, int kvg) {
-  return (g.gring[kvg >> 5] >> (kvg & 31)) & 1u;
+  bool ring = false;
+#pragma unroll
+  for (int w = 0; w < kMaxHq / 32; ++w) {
+    const uint32_t word = g.gring[w];
+    ring = (kvg >> 5) == w ? ((word >> (kvg & 31)) & 1u) != 0 : ring;
+  }
+  return ring;
 }
 
 // First cache row of KV group kvg of sequence b (multiply by kD for elements).
 __host__ __device__ __forceinline__ size_t kv_group_base(const Geo &g, int b, int kvg) {
-  int nring = 0;
-  for (int w = 0; w < (kvg >> 5); ++w) nring += __builtin_popcount(g.gring[w]);
-  nring += __builtin_popcount(g.gring[kvg >> 5] & ((1u << (kvg & 31)) - 1u));
+  int nring = 0;                                   // ring groups before kvg
+#pragma unroll
+  for (int w = 0; w < kMaxHq / 32; ++w) {
+    const uint32_t word = g.gring[w];
+    const uint32_t below = (kvg >> 5) > w ? ~0u : (kvg >> 5) == w ? (1u << (kvg & 31)) - 1u : 0u;
+    nring += __builtin_popcount(word & below);
+  }
   return (size_t)b * g.rows_b + (size_t)(kvg - nring) * g.Ncap + (size_t)nring * ((size_t)g.n_sink + g.window);
+}
+
+// Elements of the cache before KV group kvg of sequence b.  The hot kernels
+// come in two builds: RING_LAYOUT false (no ring group: the plain
+// [B, Hkv, Ncap, D] stride, nothing else read) and true (any layout).
+template <bool RING_LAYOUT>
+__host__ __device__ __forceinline__ size_t kv_group_elems(const Geo &g, int b, int kvg) {
+  if (!RING_LAYOUT) return ((size_t)b * g.Hkv + kvg) * g.Ncap * kD;
+  return kv_group_base(g, b, kvg) * kD;
 }
 
 // Row of position n (0 <= n < 2^31) inside its group: n itself, or for a ring

@@ -40,9 +40,16 @@ __device__ __forceinline__ int local_head(const Geo &g, int kvg, int k) {
   return -1;
 }
 
-// Position of window row ri for a query at m: the sinks first, then the window.
-__device__ __forceinline__ long long swa_row(long long ri, long long lo, long long ns) {
-  return ri < ns ? ri : lo + (ri - ns);
+// Cache row of window row ri: the ns sinks first (row = position), then the
+// window, whose j-th position lies in row wbase + j of a full group (wbase =
+// its first position), and for a ring group in row wbase + j, less W once
+// j >= wwrap (the rows wrap; the window spans at most W positions, so once).
+// Positions and ring rows stay below 2^31, so 32-bit arithmetic holds.
+template <bool RING>
+__device__ __forceinline__ int swa_row(int ri, int ns, int wbase, int wwrap, int W) {
+  const int j = ri - ns;
+  if (!RING) return ri < ns ? ri : wbase + j;
+  return ri < ns ? ri : (j < wwrap ? wbase : wbase - W) + j;
 }
 
 // Number of SWA workgroups of a launch (a multiple of 8 for the XCD mapping).
@@ -52,9 +59,12 @@ __host__ __device__ __forceinline__ long long swa_blocks(const Geo &g) {
 }
 
 // One SWA workgroup; x = its index among the SWA workgroups of the launch.
-__device__ __forceinline__ void swa_block(const Geo &g, long long x, const rtp_bf16 *__restrict__ q_pre,
-                                          const rtp_bf16 *__restrict__ kc, const rtp_bf16 *__restrict__ vc,
-                                          float *__restrict__ out, SwaShared &sm) {
+// RING: the block's KV group is stored as a ring (rows wrap); RING_LAYOUT:
+// the layer has ring groups (group bases follow the ring layout).
+template <bool RING, bool RING_LAYOUT>
+__device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const rtp_bf16 *__restrict__ q_pre,
+                                               const rtp_bf16 *__restrict__ kc, const rtp_bf16 *__restrict__ vc,
+                                               float *__restrict__ out, SwaShared &sm) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, sub = lane & 15;
   // XCD-aware mapping: blocks x and x + 8 hold the head blocks of one chunk (same XCD)
   const long long xcd = x & 7, y = x >> 3;
@@ -64,15 +74,23 @@ __device__ __forceinline__ void swa_block(const Geo &g, long long x, const rtp_b
   const int unit = (int)(chunk_id / g.swa_nch), ch = (int)(chunk_id % g.swa_nch);
   const int i = unit % g.nq, bl = unit / g.nq, lgi = bl % g.nlg, b = bl / g.nlg;
   const int kvg = g.lgroup[lgi];
-  const long long m = g.N - g.nq + i;
-  const long long lo = m - g.window + 1 > 0 ? m - g.window + 1 : 0;
-  const long long ns = g.n_sink < lo ? g.n_sink : lo;
-  const long long L = ns + (m - lo + 1);
-  const long long r0 = (long long)ch * g.swa_chunk;
-  const long long r1 = r0 + g.swa_chunk < L ? r0 + g.swa_chunk : L;
-  const size_t cbase = kv_group_base(g, b, kvg) * kD;
-  const bool ring = kv_is_ring(g, kvg);
+  const int m = (int)(g.N - g.nq + i);          // N < 2^31
+  const int lo = m - g.window + 1 > 0 ? m - g.window + 1 : 0;
+  const int ns = g.n_sink < lo ? g.n_sink : lo;
+  const int L = ns + (m - lo + 1);
+  const int r0 = ch * g.swa_chunk;
+  const int r1 = r0 + g.swa_chunk < L ? r0 + g.swa_chunk : L;
+  const size_t cbase = kv_group_elems<RING_LAYOUT>(g, b, kvg);
   const rtp_bf16 *kb = kc + cbase, *vb = vc + cbase;
+  // window rows: positions lo.. in rows lo.. of a full group; in a ring group
+  // position n >= n_sink sits in row n_sink + (n - n_sink) mod W (below n_sink
+  // and, when lo < n_sink, everywhere in the window that is row n as well)
+  int wbase = lo, wwrap = INT_MAX;
+  if (RING && lo >= g.n_sink) {
+    const int r_lo = (lo - g.n_sink) % g.window;
+    wbase = g.n_sink + r_lo;
+    wwrap = g.window - r_lo;
+  }
 
   // request the first rows before preparing the queries
   constexpr int U = 4;
@@ -80,11 +98,11 @@ __device__ __forceinline__ void swa_block(const Geo &g, long long x, const rtp_b
   bool ok[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const long long ri = r0 + u * 16 + wv * 4 + grp;
+    const int ri = r0 + u * 16 + wv * 4 + grp;
     ok[u] = ri < r1;
     kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
     if (ok[u]) {
-      const long long n = kv_row(g, ring, swa_row(ri, lo, ns));
+      const size_t n = (size_t)swa_row<RING>(ri, ns, wbase, wwrap, g.window);
       kr[u] = *reinterpret_cast<const uint4 *>(kb + n * kD + sub * 8);
       vr[u] = *reinterpret_cast<const uint4 *>(vb + n * kD + sub * 8);
     }
@@ -119,7 +137,7 @@ __device__ __forceinline__ void swa_block(const Geo &g, long long x, const rtp_b
 #pragma unroll
     for (int e = 0; e < 8; ++e) oo[hh][e] = 0.f;
   }
-  for (long long base = r0;;) {
+  for (int base = r0;;) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
@@ -152,11 +170,11 @@ __device__ __forceinline__ void swa_block(const Geo &g, long long x, const rtp_b
     if (base >= r1) break;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const long long ri = base + u * 16 + wv * 4 + grp;
+      const int ri = base + u * 16 + wv * 4 + grp;
       ok[u] = ri < r1;
       kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
       if (ok[u]) {
-        const long long n = kv_row(g, ring, swa_row(ri, lo, ns));
+        const size_t n = (size_t)swa_row<RING>(ri, ns, wbase, wwrap, g.window);
         kr[u] = *reinterpret_cast<const uint4 *>(kb + n * kD + sub * 8);
         vr[u] = *reinterpret_cast<const uint4 *>(vb + n * kD + sub * 8);
       }
@@ -202,6 +220,26 @@ __device__ __forceinline__ void swa_block(const Geo &g, long long x, const rtp_b
   const int h = sm.heads[wv];
   if (h >= 0)
     wave_combine(parts + (size_t)wv * g.swa_nch, g.swa_nch, out + (((size_t)b * g.Hq + h) * g.nq + i) * kD);
+}
+
+// One SWA workgroup; x = its index among the SWA workgroups of the launch.
+// In a layer with ring groups the layout of the block's KV group is uniform
+// over the workgroup, so the full and the ring rows each get their own code.
+template <bool RING_LAYOUT>
+__device__ __forceinline__ void swa_block(const Geo &g, long long x, const rtp_bf16 *__restrict__ q_pre,
+                                          const rtp_bf16 *__restrict__ kc, const rtp_bf16 *__restrict__ vc,
+                                          float *__restrict__ out, SwaShared &sm) {
+  if (!RING_LAYOUT) {
+    swa_block_rows<false, false>(g, x, q_pre, kc, vc, out, sm);
+    return;
+  }
+  const long long chunk_id = ((x >> 3) / g.swa_hb) * 8 + (x & 7);
+  if (chunk_id >= (long long)g.swa_units * g.swa_nch) return;
+  const int unit = (int)(chunk_id / g.swa_nch);
+  if (kv_is_ring(g, g.lgroup[(unit / g.nq) % g.nlg]))
+    swa_block_rows<true, true>(g, x, q_pre, kc, vc, out, sm);
+  else
+    swa_block_rows<false, true>(g, x, q_pre, kc, vc, out, sm);
 }
 
 }  // namespace rtp

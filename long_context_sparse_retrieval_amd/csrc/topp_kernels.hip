@@ -289,8 +289,8 @@ union PhaseAShared {
 };
 
 // Phase A: the local heads' sliding-window workgroups (first) and the
-// retrieval heads' scan tiles in one launch.
-template <int T, bool FROM_LOGITS>
+// retrieval heads' scan tiles in one launch.  RING: the layer has ring groups.
+template <int T, bool FROM_LOGITS, bool RING>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4, 8))) void phase_a_kernel(Geo g, const rtp_bf16 *__restrict__ q_pre,
                                                       const rtp_bf16 *__restrict__ w_q,
                                                       const rtp_bf16 *__restrict__ k_idx,
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   __shared__ PhaseAShared<T> sm;
   const long long x = blockIdx.x;
   if (x < n_swa)
-    swa_block(g, x, q_pre, kc, vc, out, sm.swa);
+    swa_block<RING>(g, x, q_pre, kc, vc, out, sm.swa);
   else
     scan_block<T, FROM_LOGITS>(g, x - n_swa, q_pre, w_q, k_idx, logits, sm.scan);
 }
@@ -425,7 +425,7 @@ struct FinShared {
 // recomputed in parallel).  Selected positions are written (optional) and
 // attended (optional); the last workgroup of the query combines the states
 // and resets the ring.
-template <int T, bool FROM_LOGITS, bool ATTEND>
+template <int T, bool FROM_LOGITS, bool ATTEND, bool RING>
 __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__restrict__ k_idx,
                                                      const float *__restrict__ logits,
                                                      const rtp_bf16 *__restrict__ kc,
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
   const int t_begin = w * g.fin_tpw;
   const int t_end = t_begin + g.fin_tpw < g.nt ? t_begin + g.fin_tpw : g.nt;
   const int kvg = hq / g.G;
-  const size_t cbase = kv_group_base(g, b, kvg) * kD;
+  const size_t cbase = kv_group_elems<RING>(g, b, kvg);
   const TileSum *ts = g.tsum + (size_t)unit * g.nt;
 
   // Loads are counted in issue order (vmcnt), so everything the threshold
@@ -715,12 +715,16 @@ int launch_phase_a_t(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, c
   const long long n_swa = with_swa ? swa_blocks(g) : 0;
   const long long grid = n_swa + (g.units ? scan_blocks(g) : 0);
   if (grid == 0) return RTP_OK;
+  // scores given as logits come without local heads (no K/V read)
   if (logits)
-    hipLaunchKernelGGL((phase_a_kernel<T, true>), dim3((unsigned)grid), dim3(kWG), 0, s, g, q_pre, w_q, k_idx, logits,
-                       k, v, out, n_swa);
-  else
-    hipLaunchKernelGGL((phase_a_kernel<T, false>), dim3((unsigned)grid), dim3(kWG), 0, s, g, q_pre, w_q, k_idx,
+    hipLaunchKernelGGL((phase_a_kernel<T, true, false>), dim3((unsigned)grid), dim3(kWG), 0, s, g, q_pre, w_q, k_idx,
                        logits, k, v, out, n_swa);
+  else if (g.any_ring && n_swa)
+    hipLaunchKernelGGL((phase_a_kernel<T, false, true>), dim3((unsigned)grid), dim3(kWG), 0, s, g, q_pre, w_q, k_idx,
+                       logits, k, v, out, n_swa);
+  else
+    hipLaunchKernelGGL((phase_a_kernel<T, false, false>), dim3((unsigned)grid), dim3(kWG), 0, s, g, q_pre, w_q,
+                       k_idx, logits, k, v, out, n_swa);
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ERR_HIP;
 }
 
@@ -730,13 +734,16 @@ int launch_finish_t(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, co
                     int32_t *count, long long cap, hipStream_t s) {
   const unsigned grid = (unsigned)((long long)g.units * g.fin_nwg);
   if (grid == 0) return RTP_OK;
-#define RTP_FIN(FL, AT)                                                                                         \
-  hipLaunchKernelGGL((finish_kernel<T, FL, AT>), dim3(grid), dim3(kWG), 0, s, g, k_idx, logits, k, v, out, idx, \
-                     count, cap)
+#define RTP_FIN(FL, AT, RG)                                                                                     \
+  hipLaunchKernelGGL((finish_kernel<T, FL, AT, RG>), dim3(grid), dim3(kWG), 0, s, g, k_idx, logits, k, v, out, \
+                     idx, count, cap)
+  // only the attending build reads K/V, so only it has a ring-layout twin
   if (logits) {
-    if (out) RTP_FIN(true, true); else RTP_FIN(true, false);
+    if (out) RTP_FIN(true, true, false); else RTP_FIN(true, false, false);
+  } else if (out) {
+    if (g.any_ring) RTP_FIN(false, true, true); else RTP_FIN(false, true, false);
   } else {
-    if (out) RTP_FIN(false, true); else RTP_FIN(false, false);
+    RTP_FIN(false, false, false);
   }
 #undef RTP_FIN
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ERR_HIP;
