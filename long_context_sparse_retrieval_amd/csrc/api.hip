@@ -505,10 +505,13 @@ int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf1
     }
     return launch_phase_a(p.g, q_pre, nullptr, nullptr, nullptr, k, v, out, false, true, s);
   }
-  st = launch_phase_a(p.g, q_pre, w_q, k_idx, nullptr, k, v, out, true, true, s);
+  // with retrieval heads the finish kernel follows; it also merges the local
+  // heads' window chunks, which takes that merge off phase A's critical path
+  const bool defer = p.g.units > 0 && p.g.swa_units > 0;
+  st = launch_phase_a(p.g, q_pre, w_q, k_idx, nullptr, k, v, out, true, true, s, defer);
   if (st != RTP_OK) return st;
   if (phase_event && hipEventRecord(reinterpret_cast<hipEvent_t>(phase_event), s) != hipSuccess) return RTP_ERR_HIP;
-  return launch_finish(p.g, q_pre, w_q, k_idx, nullptr, k, v, out, idx_opt, count_opt, idx_opt ? cap : 0, s);
+  return launch_finish(p.g, q_pre, w_q, k_idx, nullptr, k, v, out, idx_opt, count_opt, idx_opt ? cap : 0, s, defer);
 }
 
 }  // extern "C"

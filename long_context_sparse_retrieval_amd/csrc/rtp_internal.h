@@ -324,13 +324,16 @@ int launch_index_score(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q,
                        float *logits, hipStream_t s);
 // Phase A: SWA workgroups of the local heads and/or scan tiles of the
 // retrieval queries (scores from k_idx + q, or from given logits).
+// defer_swa_combine: the window workgroups only publish their chunk states;
+// the launch_finish that follows (with swa_combine) merges them.
 int launch_phase_a(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
                    const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, bool with_scan,
-                   bool with_swa, hipStream_t s);
-// Finish phase: global threshold, selection, optional attention + combine.
+                   bool with_swa, hipStream_t s, bool defer_swa_combine = false);
+// Finish phase: global threshold, selection, optional attention + combine;
+// swa_combine adds workgroups that merge deferred window chunk states.
 int launch_finish(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
                   const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, int32_t *idx,
-                  int32_t *count, long long cap, hipStream_t s);
+                  int32_t *count, long long cap, hipStream_t s, bool swa_combine = false);
 int launch_sparse_attn(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *k, const rtp_bf16 *v,
                        const int32_t *idx, const int32_t *count, long long cap, float *out, hipStream_t s);
 int launch_fill_zero(void *ws, size_t bytes, hipStream_t s);

@@ -61,10 +61,11 @@ __host__ __device__ __forceinline__ long long swa_blocks(const Geo &g) {
 // One SWA workgroup; x = its index among the SWA workgroups of the launch.
 // RING: the block's KV group is stored as a ring (rows wrap); RING_LAYOUT:
 // the layer has ring groups (group bases follow the ring layout).
+// defer: publish the chunk states only (a later kernel merges them).
 template <bool RING, bool RING_LAYOUT>
 __device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const rtp_bf16 *__restrict__ q_pre,
                                                const rtp_bf16 *__restrict__ kc, const rtp_bf16 *__restrict__ vc,
-                                               float *__restrict__ out, SwaShared &sm) {
+                                               float *__restrict__ out, SwaShared &sm, bool defer) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, sub = lane & 15;
   // XCD-aware mapping: blocks x and x + 8 hold the head blocks of one chunk (same XCD)
   const long long xcd = x & 7, y = x >> 3;
@@ -215,7 +216,7 @@ __device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const 
       st_coherent(&p->l, l_);
     }
   }
-  if (!arrive_last(g.ctr_swa + unit * g.swa_hb + hb, (uint32_t)g.swa_nch, &sm.flag)) return;
+  if (defer || !arrive_last(g.ctr_swa + unit * g.swa_hb + hb, (uint32_t)g.swa_nch, &sm.flag)) return;
   // wave hh combines head hh's chunk states (all heads in one round of loads)
   const int h = sm.heads[wv];
   if (h >= 0)
@@ -228,18 +229,35 @@ __device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const 
 template <bool RING_LAYOUT>
 __device__ __forceinline__ void swa_block(const Geo &g, long long x, const rtp_bf16 *__restrict__ q_pre,
                                           const rtp_bf16 *__restrict__ kc, const rtp_bf16 *__restrict__ vc,
-                                          float *__restrict__ out, SwaShared &sm) {
+                                          float *__restrict__ out, SwaShared &sm, bool defer) {
   if (!RING_LAYOUT) {
-    swa_block_rows<false, false>(g, x, q_pre, kc, vc, out, sm);
+    swa_block_rows<false, false>(g, x, q_pre, kc, vc, out, sm, defer);
     return;
   }
   const long long chunk_id = ((x >> 3) / g.swa_hb) * 8 + (x & 7);
   if (chunk_id >= (long long)g.swa_units * g.swa_nch) return;
   const int unit = (int)(chunk_id / g.swa_nch);
   if (kv_is_ring(g, g.lgroup[(unit / g.nq) % g.nlg]))
-    swa_block_rows<true, true>(g, x, q_pre, kc, vc, out, sm);
+    swa_block_rows<true, true>(g, x, q_pre, kc, vc, out, sm, defer);
   else
-    swa_block_rows<false, true>(g, x, q_pre, kc, vc, out, sm);
+    swa_block_rows<false, true>(g, x, q_pre, kc, vc, out, sm, defer);
+}
+
+// Number of workgroups that merge deferred chunk states: one per (unit, head block).
+__host__ __device__ __forceinline__ long long swa_combine_blocks(const Geo &g) {
+  return (long long)g.swa_units * g.swa_hb;
+}
+
+// Merge of the deferred chunk states of one (unit, head block): wave w takes
+// the block's w-th local head (the same split the window workgroups use).
+__device__ __forceinline__ void swa_combine_block(const Geo &g, long long y, float *__restrict__ out) {
+  const int hb = (int)(y % g.swa_hb), unit = (int)(y / g.swa_hb);
+  const int i = unit % g.nq, bl = unit / g.nq, lgi = bl % g.nlg, b = bl / g.nlg;
+  const int wv = threadIdx.x >> 6;
+  const int h = local_head(g, g.lgroup[lgi], hb * kSwaHeads + wv);
+  if (h < 0) return;
+  const Partial *parts = g.swa_part + ((size_t)(unit * g.swa_hb + hb) * kSwaHeads + wv) * g.swa_nch;
+  wave_combine(parts, g.swa_nch, out + (((size_t)b * g.Hq + h) * g.nq + i) * kD);
 }
 
 }  // namespace rtp

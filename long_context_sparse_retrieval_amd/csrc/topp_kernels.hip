@@ -297,11 +297,11 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
                                                       const float *__restrict__ logits,
                                                       const rtp_bf16 *__restrict__ kc,
                                                       const rtp_bf16 *__restrict__ vc, float *__restrict__ out,
-                                                      long long n_swa) {
+                                                      long long n_swa, int defer_swa) {
   __shared__ PhaseAShared<T> sm;
   const long long x = blockIdx.x;
   if (x < n_swa)
-    swa_block<RING>(g, x, q_pre, kc, vc, out, sm.swa);
+    swa_block<RING>(g, x, q_pre, kc, vc, out, sm.swa, defer_swa != 0);
   else
     scan_block<T, FROM_LOGITS>(g, x - n_swa, q_pre, w_q, k_idx, logits, sm.scan);
 }
@@ -435,6 +435,10 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
   constexpr int TPT = T / kWG;             // positions per thread per tile (consecutive)
   static_assert(T <= FinShared::kCodes, "tile larger than the code staging area");
   __shared__ FinShared sm;
+  if (ATTEND && blockIdx.x >= (unsigned)(g.units * g.fin_nwg)) {   // deferred window chunk states
+    swa_combine_block(g, (long long)blockIdx.x - (long long)g.units * g.fin_nwg, out);
+    return;
+  }
   const int tid = threadIdx.x;
   const int unit = blockIdx.x / g.fin_nwg, w = blockIdx.x % g.fin_nwg;
   const int i = unit % g.nq, br = unit / g.nq, r = br % g.Hr, b = br / g.Hr;
@@ -711,28 +715,28 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
 template <int T>
 int launch_phase_a_t(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
                      const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, bool with_swa,
-                     hipStream_t s) {
+                     bool defer, hipStream_t s) {
   const long long n_swa = with_swa ? swa_blocks(g) : 0;
   const long long grid = n_swa + (g.units ? scan_blocks(g) : 0);
   if (grid == 0) return RTP_OK;
   // scores given as logits come without local heads (no K/V read)
   if (logits)
     hipLaunchKernelGGL((phase_a_kernel<T, true, false>), dim3((unsigned)grid), dim3(kWG), 0, s, g, q_pre, w_q, k_idx,
-                       logits, k, v, out, n_swa);
+                       logits, k, v, out, n_swa, 0);
   else if (g.any_ring && n_swa)
     hipLaunchKernelGGL((phase_a_kernel<T, false, true>), dim3((unsigned)grid), dim3(kWG), 0, s, g, q_pre, w_q, k_idx,
-                       logits, k, v, out, n_swa);
+                       logits, k, v, out, n_swa, defer ? 1 : 0);
   else
     hipLaunchKernelGGL((phase_a_kernel<T, false, false>), dim3((unsigned)grid), dim3(kWG), 0, s, g, q_pre, w_q,
-                       k_idx, logits, k, v, out, n_swa);
+                       k_idx, logits, k, v, out, n_swa, defer ? 1 : 0);
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ERR_HIP;
 }
 
 template <int T>
 int launch_finish_t(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
                     const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, int32_t *idx,
-                    int32_t *count, long long cap, hipStream_t s) {
-  const unsigned grid = (unsigned)((long long)g.units * g.fin_nwg);
+                    int32_t *count, long long cap, bool swa_combine, hipStream_t s) {
+  const unsigned grid = (unsigned)((long long)g.units * g.fin_nwg + (swa_combine ? swa_combine_blocks(g) : 0));
   if (grid == 0) return RTP_OK;
 #define RTP_FIN(FL, AT, RG)                                                                                     \
   hipLaunchKernelGGL((finish_kernel<T, FL, AT, RG>), dim3(grid), dim3(kWG), 0, s, g, k_idx, logits, k, v, out, \
@@ -753,28 +757,30 @@ int launch_finish_t(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, co
 
 int launch_phase_a(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
                    const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, bool with_scan,
-                   bool with_swa, hipStream_t s) {
+                   bool with_swa, hipStream_t s, bool defer_swa_combine) {
   Geo gg = g;
   if (!with_scan) gg.units = 0;
   if (!with_swa && gg.units == 0) return RTP_OK;
+  const bool df = with_swa && defer_swa_combine;
   switch (gg.T) {
-    case 1024: return launch_phase_a_t<1024>(gg, q_pre, w_q, k_idx, logits, k, v, out, with_swa, s);
-    case 2048: return launch_phase_a_t<2048>(gg, q_pre, w_q, k_idx, logits, k, v, out, with_swa, s);
-    case 4096: return launch_phase_a_t<4096>(gg, q_pre, w_q, k_idx, logits, k, v, out, with_swa, s);
-    case 8192: return launch_phase_a_t<8192>(gg, q_pre, w_q, k_idx, logits, k, v, out, with_swa, s);
+    case 1024: return launch_phase_a_t<1024>(gg, q_pre, w_q, k_idx, logits, k, v, out, with_swa, df, s);
+    case 2048: return launch_phase_a_t<2048>(gg, q_pre, w_q, k_idx, logits, k, v, out, with_swa, df, s);
+    case 4096: return launch_phase_a_t<4096>(gg, q_pre, w_q, k_idx, logits, k, v, out, with_swa, df, s);
+    case 8192: return launch_phase_a_t<8192>(gg, q_pre, w_q, k_idx, logits, k, v, out, with_swa, df, s);
     default: return RTP_ERR_UNSUPPORTED;
   }
 }
 
 int launch_finish(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
                   const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, int32_t *idx,
-                  int32_t *count, long long cap, hipStream_t s) {
+                  int32_t *count, long long cap, hipStream_t s, bool swa_combine) {
   if (g.units == 0) return RTP_OK;
+  const bool sc = swa_combine && out && !logits;       // only the attending build merges window states
   switch (g.T) {
-    case 1024: return launch_finish_t<1024>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, s);
-    case 2048: return launch_finish_t<2048>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, s);
-    case 4096: return launch_finish_t<4096>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, s);
-    case 8192: return launch_finish_t<8192>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, s);
+    case 1024: return launch_finish_t<1024>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, sc, s);
+    case 2048: return launch_finish_t<2048>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, sc, s);
+    case 4096: return launch_finish_t<4096>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, sc, s);
+    case 8192: return launch_finish_t<8192>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, sc, s);
     default: return RTP_ERR_UNSUPPORTED;
   }
 }
