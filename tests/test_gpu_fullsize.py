@@ -10,6 +10,8 @@ context), and the local heads of one KV group.  Every other query is checked
 through properties that hold at any size (positions unique, in range, count
 within [1, m + 1]).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -168,3 +170,40 @@ def test_prefill_attn_full_size_sampled():
                 ref = O.attention(q_rot, O.bf16_to_f64(k[0, h // 4, rows]), O.bf16_to_f64(v[0, h // 4, rows]))
                 check_output(out[0, h, i], ref, f"prefill dense={dense} h{h} i{i}")
         say(f"full-size prefill attention (dense={dense}): sampled queries match")
+
+
+def test_ring_layout_full_size():
+    """The 1M layer over ring-buffer local caches (local_ring), written by one
+    bulk rtp_append_kv of the whole context: the step (outputs, sets, counts)
+    equals the full layout's step bit for bit, in the benchmark's launch plan;
+    the full layout's step is itself checked against the oracle above."""
+    cfg = 4
+    spec = gen.spec_for(cfg)
+    say(f"full-size ring layout: {spec.name} N={spec.N}")
+    wl = gen.make_workload(spec, gen.workload.default_seed(cfg))
+    full = layer_of(spec, rtp)
+    ring = dataclasses.replace(full, local_ring=1)
+    k_pre = dev_bf16(wl.k_pre)
+    w_k = dev_bf16(wl.w_k)
+    k = rtp.rope_keys(full, k_pre)
+    k_idx = rtp.index_keys(full, k_pre, w_k)
+    v = dev_bf16(wl.v)
+    kr = torch.empty(rtp.kv_shape(ring), dtype=torch.bfloat16, device="cuda")
+    vr = torch.empty_like(kr)
+    ki = torch.empty_like(k_idx)
+    rtp.append_kv(ring, k_pre, v, w_k, kr, vr, ki, 0)
+    del k_pre
+    assert torch.equal(ki, k_idx)
+    del ki
+    n_ring = spec.Hkv - len(spec.ret_groups)                 # all-local KV groups
+    assert rtp.kv_rows(ring) == len(spec.ret_groups) * spec.N + n_ring * (spec.n_sink + spec.window)
+    q, w_q = dev_bf16(wl.q_pre), dev_bf16(wl.w_q)
+    res = []
+    for lay, kc, vc in ((full, k, v), (ring, kr, vr)):
+        idx = torch.full((spec.B, spec.Hr, 1, spec.N), -1, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros((spec.B, spec.Hr, 1), dtype=torch.int32, device="cuda")
+        out = rtp.decode_step(lay, q, w_q, k_idx, kc, vc, rtp.workspace(lay), idx=idx, count=cnt)
+        res.append((out, idx, cnt))
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+    say(f"ring layout at 1M: K/V rows per sequence {rtp.kv_rows(ring)} vs {rtp.kv_rows(full)}")
