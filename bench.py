@@ -18,7 +18,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import contextlib
 import dataclasses
+import gc
 import hashlib
 import json
 import os
@@ -44,6 +46,20 @@ CPU_SAMPLE_SECONDS = 12.0
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+@contextlib.contextmanager
+def quiet_gc():
+    """Collect garbage first and keep Python's collector off while GPU work is
+    timed: a full collection inside a loop of launches stalls the launches
+    (seen once as 720 us of host time per step over a round of 50 steps,
+    against 35 us normally)."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
 
 
 def up(a: np.ndarray) -> torch.Tensor:
@@ -125,31 +141,44 @@ class Case:
         self.bytes_total = self.bytes_scan + self.bytes_swa + self.bytes_gather
 
     def run(self, steps: int, warmup: int):
-        """Warm up, then time exactly `steps` steps; returns (ms/step, ms of the phase-A kernel per step)."""
+        """Warm up, then time exactly `steps` plain steps (the headline: only a
+        begin and an end event around them); then a second, instrumented pass of
+        as many steps records an event before every step and after its phase A,
+        for the per-step percentiles and the phase-A kernel time (each event
+        record costs a few microseconds of GPU time, so that pass is slower).
+        Returns (ms/step, ms of the phase-A kernel per step)."""
         R = len(self.reps)
         for s in range(warmup):
             k_idx, k, v = self.reps[s % R]
             rtp.decode_step(self.layer, self.q, self.w_q, k_idx, k, v, self.ws, self.out)
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        for e in mids:
-            e.record()          # materialise the underlying hipEvent
         t_begin = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t_begin.record()
         for s in range(steps):
             k_idx, k, v = self.reps[s % R]
-            starts[s].record()
-            rtp.decode_step(self.layer, self.q, self.w_q, k_idx, k, v, self.ws, self.out, phase_event=mids[s])
+            rtp.decode_step(self.layer, self.q, self.w_q, k_idx, k, v, self.ws, self.out)
         t_end.record()
         torch.cuda.synchronize()
         ms_step = t_begin.elapsed_time(t_end) / steps
+        # instrumented pass
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for e in mids:
+            e.record()          # materialise the underlying hipEvent
+        i_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        for s in range(steps):
+            k_idx, k, v = self.reps[s % R]
+            starts[s].record()
+            rtp.decode_step(self.layer, self.q, self.w_q, k_idx, k, v, self.ws, self.out, phase_event=mids[s])
+        i_end.record()
+        torch.cuda.synchronize()
         ms_pa = float(np.mean([starts[s].elapsed_time(mids[s]) for s in range(steps)]))
-        per = [starts[s].elapsed_time(starts[s + 1]) for s in range(steps - 1)] + [starts[-1].elapsed_time(t_end)]
+        per = [starts[s].elapsed_time(starts[s + 1]) for s in range(steps - 1)] + [starts[-1].elapsed_time(i_end)]
         self.pct = {f"p{q}": round(float(np.percentile(per, q)) * 1e3, 2) for q in (10, 50, 90)}
+        self.instr_us = round(starts[0].elapsed_time(i_end) / steps * 1e3, 2)
         return ms_step, ms_pa
-
 
     def run_dense(self, steps: int, warmup: int) -> float:
         """ms per call of the dense comparator (every head over every cached position) on the same caches."""
@@ -483,18 +512,21 @@ def main():
     rtp.load()
     if args.calib:
         calibration_copy()
-    copy_gbps = copy_ceiling_gbps()
+    with quiet_gc():
+        copy_gbps = copy_ceiling_gbps()
     log(f"[bench] device copy ceiling {copy_gbps:.0f} GB/s")
 
     cfgs = [args.only] if args.only else [4, 3, 6]
     summ, cpu = {}, None
     for cfg in cfgs:
         case = Case(cfg, args.replicas)
-        ms, ms_pa = case.run(args.steps, args.warmup)
+        with quiet_gc():
+            ms, ms_pa = case.run(args.steps, args.warmup)
         gbps = case.bytes_total / (ms * 1e-3) / 1e9
         # the dense comparator ignores the indexer, so the shared-key layer would repeat the 1M figure
-        ms_dense = (case.run_dense(max(5, args.steps // 10), 3) if cfg != 6 and not args.no_extras
-                    else float("nan"))
+        with quiet_gc():
+            ms_dense = (case.run_dense(max(5, args.steps // 10), 3) if cfg != 6 and not args.no_extras
+                        else float("nan"))
         dense_bytes = 512 * case.spec.B * case.spec.Hkv * case.spec.N
         pa_bytes = case.bytes_scan + case.bytes_swa
         summ[cfg] = dict(ms=ms, us=ms * 1e3, gbps=gbps, frac=gbps / HBM_PEAK_GBPS, pa_us=ms_pa * 1e3,
@@ -502,23 +534,26 @@ def main():
                          bytes=case.bytes_total, spec=case.spec, counts=case.counts,
                          union=case.gather_rows_union, rsum=case.gather_rows_sum,
                          dense_us=ms_dense * 1e3, dense_gbps=dense_bytes / (ms_dense * 1e-3) / 1e9,
-                         pct=case.pct)
+                         pct=case.pct, instr_us=case.instr_us)
         log(f"[bench] cfg{cfg}: {ms * 1e3:.1f} us/step, phase-A kernel {ms_pa * 1e3:.1f} us, {gbps:.0f} GB/s "
             f"algorithmic; |S| {case.counts.ravel().tolist()}; dense comparator {ms_dense * 1e3:.1f} us "
             f"({dense_bytes / (ms_dense * 1e-3) / 1e9:.0f} GB/s), sparse step {ms_dense / ms:.2f}x faster")
         if cfg in (3, 4) and not args.no_extras:
-            summ[cfg]["cluster"] = time_cluster(case, max(20, args.steps // 4))
+            with quiet_gc():
+                summ[cfg]["cluster"] = time_cluster(case, max(20, args.steps // 4))
             log(f"[bench] cfg{cfg}: cluster index {summ[cfg]['cluster']}")
         if cfg == 4 and not args.no_extras:
             # the fixed top-k variant of the same kernels on the same caches
             top_p_layer = case.layer
             case.layer = dataclasses.replace(top_p_layer, top_k=TOPK_BENCH)
-            ms_k, ms_pa_k = case.run(max(20, args.steps // 4), args.warmup)
+            with quiet_gc():
+                ms_k, ms_pa_k = case.run(max(20, args.steps // 4), args.warmup)
             case.layer = top_p_layer
             summ[cfg].update(topk_us=ms_k * 1e3, topk_pa_us=ms_pa_k * 1e3)
             log(f"[bench] cfg{cfg}: fixed top-k (k = {TOPK_BENCH}) {ms_k * 1e3:.1f} us/step")
         if cfg == 4 and not args.no_extras:
-            summ[cfg]["ring"] = time_local_ring(case, max(20, args.steps // 4), args.warmup)
+            with quiet_gc():
+                summ[cfg]["ring"] = time_local_ring(case, max(20, args.steps // 4), args.warmup)
             log(f"[bench] cfg{cfg}: ring-buffer local caches {summ[cfg]['ring']}")
             torch.cuda.empty_cache()
         if cfg == 4 and not args.no_cpu_baseline:
@@ -526,17 +561,20 @@ def main():
             cpu = cpu_baseline(case)
             log(f"[bench] cpu baseline {cpu['value']} GB/s ({time.time() - t0:.1f}s incl. cache build)")
         if cfg == 4 and not args.no_extras:
-            summ[cfg]["append"] = time_append(case)
+            with quiet_gc():
+                summ[cfg]["append"] = time_append(case)
             log(f"[bench] cfg{cfg}: cache append {summ[cfg]['append']}")
         del case
         torch.cuda.empty_cache()
 
     prefill = topics = None
     if not args.only and not args.no_extras:
-        prefill = time_prefill()
+        with quiet_gc():
+            prefill = time_prefill()
         log(f"[bench] prefill attention 32K: {prefill}")
         torch.cuda.empty_cache()
-        topics = time_cluster_topics(max(20, args.steps // 4))
+        with quiet_gc():
+            topics = time_cluster_topics(max(20, args.steps // 4))
         log(f"[bench] cluster index on topic keys: {topics}")
         torch.cuda.empty_cache()
 
@@ -574,6 +612,7 @@ def main():
                      "kernel_us": round(s["pa_us"], 2), "algorithmic_bytes_per_launch": s["pa_bytes"]},
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "step_us_percentiles": s["pct"],
+        "instrumented_us_per_step": s["instr_us"],
     }
     if s["dense_us"] == s["dense_us"]:          # measured (not NaN)
         dense_peak_us = 512 * spec.B * spec.Hkv * spec.N / HBM_PEAK_GBPS / 1e3
@@ -604,6 +643,7 @@ def main():
         s3 = summ[3]
         out["ctx_128k"] = {"workload": s3["spec"].name, "us_per_step": round(s3["us"], 2),
                            "step_us_percentiles": s3["pct"],
+                           "instrumented_us_per_step": s3["instr_us"],
                            "GBps": round(s3["gbps"], 1), "hbm_frac": round(s3["frac"], 4),
                            "algorithmic_bytes_per_step": s3["bytes"], "phase_a_kernel_us": round(s3["pa_us"], 2),
                            "phase_a_GBps": round(s3["pa_gbps"], 1),

@@ -109,7 +109,9 @@ class Layer:
     idx_group: int = 1        # retrieval heads sharing one indexer-key head (1 or Hq // Hkv)
     top_k: int = 0            # 0: Top-P with mass p; > 0: fixed top-k on the histogram order
     local_ring: int = 0       # 1: all-local KV groups keep only n_sink + window rows (K/V caches [B, kv_rows, D])
-    _keep: list = field(default_factory=list, repr=False, compare=False)
+    # the C struct of the current field values and the head_mode array it points
+    # to (not an init field: dataclasses.replace gives the copy its own)
+    _memo: dict = field(default_factory=dict, init=False, repr=False, compare=False)
 
     @property
     def cap_rows(self) -> int:
@@ -124,12 +126,21 @@ class Layer:
         """Indexer-key heads (rows of k_idx / w_k)."""
         return self.Hr // max(1, self.idx_group)
 
+    def _key(self) -> tuple:
+        return (self.B, self.Hq, self.Hkv, self.D, self.R, self.nq, self.N, self.cap_rows, tuple(self.head_mode),
+                self.p, self.window, self.n_sink, self.rope_theta, self.idx_group, self.top_k, self.local_ring)
+
     def c(self) -> _CLayer:
-        hm = (ctypes.c_int8 * len(self.head_mode))(*[int(h) for h in self.head_mode])
-        self._keep = [hm]
-        return _CLayer(self.B, self.Hq, self.Hkv, self.D, self.R, self.nq, self.N, self.cap_rows,
-                       ctypes.cast(hm, ctypes.POINTER(ctypes.c_int8)), self.p, self.window, self.n_sink,
-                       self.rope_theta, self.idx_group, self.top_k, self.local_ring)
+        """The C struct of the current field values (rebuilt only when a field changed)."""
+        key = self._key()
+        if self._memo.get("key") != key:
+            hm = (ctypes.c_int8 * len(self.head_mode))(*[int(h) for h in self.head_mode])
+            cl = _CLayer(self.B, self.Hq, self.Hkv, self.D, self.R, self.nq, self.N, self.cap_rows,
+                         ctypes.cast(hm, ctypes.POINTER(ctypes.c_int8)), self.p, self.window, self.n_sink,
+                         self.rope_theta, self.idx_group, self.top_k, self.local_ring)
+            self._memo.clear()
+            self._memo.update(key=key, c=cl, head_mode=hm)
+        return self._memo["c"]
 
 
 def _check(status: int, what: str):
@@ -250,7 +261,10 @@ def kv_rows(layer: Layer) -> int:
 def kv_shape(layer: Layer) -> tuple:
     """Shape of the K/V caches: [B, Hkv, Ncap, D], or [B, kv_rows, D] with local_ring."""
     if layer.local_ring:
-        return (layer.B, kv_rows(layer), layer.D)
+        layer.c()                                   # refreshes the memo when a field changed
+        if "rows" not in layer._memo:
+            layer._memo["rows"] = kv_rows(layer)
+        return (layer.B, layer._memo["rows"], layer.D)
     return _cache_shape(layer, layer.Hkv, layer.D)
 
 
