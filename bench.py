@@ -453,6 +453,58 @@ def time_prefill() -> dict:
             "peak_bf16_TFLOPs": 2500.0}
 
 
+def time_other_decode(cfg: int, steps: int, warmup: int, replicas: int) -> dict:
+    """The decode step of another workload of the benchmark description, timed
+    like the headline (needle 4K: a launch-latency case, its bytes fraction is
+    not meaningful; 32K batch 8: the window-attention-dominated case)."""
+    case = Case(cfg, replicas)
+    ms, ms_pa = case.run(steps, warmup)
+    gbps = case.bytes_total / (ms * 1e-3) / 1e9
+    return {"workload": case.spec.name, "us_per_step": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_step": case.bytes_total,
+            "phase_a_kernel_us": round(ms_pa * 1e3, 2), "instrumented_us_per_step": case.instr_us,
+            "selected_tokens": case.counts.ravel().tolist()}
+
+
+def time_chunked_prefill(calls: int = 3) -> dict:
+    """rtp_decode_step with nq = 4096 causal queries against 128K positions (4
+    retrieval heads, topic-structured keys and queries): the decode-path
+    selection applied to every prefill query.  Work: the sum over queries and
+    heads of the prefix length (logits scored in each of the selection's
+    passes) and the rows the attention gathers."""
+    spec = gen.spec_for(5)
+    wl = gen.make_workload(spec, gen.workload.default_seed(5))
+    lay = rtp.Layer(B=spec.B, Hq=spec.Hq, Hkv=spec.Hkv, N=spec.N, nq=spec.nq,
+                    head_mode=[int(h) for h in spec.head_mode()], p=spec.p, window=spec.window,
+                    n_sink=spec.n_sink, rope_theta=spec.rope_theta, idx_group=spec.idx_group)
+    k_pre = up(wl.k_pre)
+    k = rtp.rope_keys(lay, k_pre)
+    k_idx = rtp.index_keys(lay, k_pre, up(wl.w_k))
+    del k_pre
+    v, q, w_q = up(wl.v), up(wl.q_pre), up(wl.w_q)
+    ws = rtp.workspace(lay)
+    out = torch.empty((spec.B, spec.Hq, spec.nq, spec.D), dtype=torch.float32, device="cuda")
+    cnt = torch.zeros((spec.B, spec.Hr, spec.nq), dtype=torch.int32, device="cuda")
+    idx = torch.empty((spec.B, spec.Hr, spec.nq, 1), dtype=torch.int32, device="cuda")
+    rtp.decode_step(lay, q, w_q, k_idx, k, v, ws, out, idx=idx, count=cnt)      # counts (one position each kept)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(calls):
+        rtp.decode_step(lay, q, w_q, k_idx, k, v, ws, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    prefix = sum(spec.N - spec.nq + i + 1 for i in range(spec.nq))
+    logits = spec.B * spec.Hr * prefix
+    rows = int(cnt.sum().item())
+    return {"workload": spec.name, "what": "rtp_decode_step, nq = 4096 causal queries (chunked prefill selection "
+                                            "and sparse attention of 4 retrieval heads)",
+            "ms_per_call": round(ms, 3), "logits_per_call": logits,
+            "logits_per_s": round(logits / (ms * 1e-3), 1), "gathered_rows": rows,
+            "gathered_GB": round(rows * 512 / 1e9, 3)}
+
+
 def cpu_baseline(case: Case) -> dict:
     """The oracle, single-threaded, on a bounded sample of the 1M workload.
 
@@ -567,8 +619,18 @@ def main():
         del case
         torch.cuda.empty_cache()
 
-    prefill = topics = None
+    prefill = topics = others = None
     if not args.only and not args.no_extras:
+        others = {}
+        for cfg, key in ((2, "ctx_32k_b8"), (1, "needle_4k")):
+            with quiet_gc():
+                others[key] = time_other_decode(cfg, args.steps, args.warmup, args.replicas)
+            log(f"[bench] {key}: {others[key]}")
+            torch.cuda.empty_cache()
+        with quiet_gc():
+            others["chunked_prefill_128k"] = time_chunked_prefill()
+        log(f"[bench] chunked prefill: {others['chunked_prefill_128k']}")
+        torch.cuda.empty_cache()
         with quiet_gc():
             prefill = time_prefill()
         log(f"[bench] prefill attention 32K: {prefill}")
@@ -635,6 +697,8 @@ def main():
         out["cluster_index"] = s["cluster"]
     if prefill is not None:
         out["prefill_32k"] = prefill
+    if others is not None:
+        out.update(others)
     if topics is not None:
         out["cluster_index_topic_keys"] = topics
     if cpu is not None:
