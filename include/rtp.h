@@ -17,6 +17,8 @@
  *  - Every array pointer is a DEVICE pointer owned by the caller, except
  *    rtp_layer.head_mode, which lives in host memory.  The library never
  *    allocates or frees memory and keeps no state between calls.
+ *  - Device pointers must be 16-byte aligned (the kernels use 16-byte vector
+ *    accesses); a misaligned one is RTP_ERR_ARG.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call only enqueues work on that stream and returns; results are
  *    ready once the stream has reached that point.

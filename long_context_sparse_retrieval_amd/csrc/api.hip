@@ -1,6 +1,7 @@
 // C entry points of librtp.so: argument validation, workspace layout, launch.
 // The operations and their sources are documented in include/rtp.h.
 #include <algorithm>
+#include <initializer_list>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -227,6 +228,14 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
 
 bool has_ring(const Geo &g) { return g.any_ring != 0; }
 
+// The kernels access every device array with 16-byte vector loads and
+// stores; null pointers count as aligned (their calls check them apart).
+bool aligned16(std::initializer_list<const void *> ps) {
+  for (const void *p : ps)
+    if (reinterpret_cast<uintptr_t>(p) & 15) return false;
+  return true;
+}
+
 int plan_with_ws(const rtp_layer *L, void *ws, size_t ws_bytes, Plan *p, bool dense = false) {
   const int st = make_plan(L, ws, p, dense);
   if (st != RTP_OK) return st;
@@ -335,6 +344,7 @@ int rtp_rope_keys(const rtp_layer *layer, const rtp_bf16 *k_pre, rtp_bf16 *k_out
   int st = make_plan(layer, nullptr, &p);
   if (st != RTP_OK) return st;
   if (!k_pre || !k_out || n0 < 0 || n1 < n0 || n1 > layer->Ncap) return RTP_ERR_ARG;
+  if (!aligned16({k_pre, k_out})) return RTP_ERR_ARG;
   return launch_rope_keys(p.g, k_pre, k_out, n0, n1, as_stream(stream));
 }
 
@@ -344,6 +354,7 @@ int rtp_index_keys(const rtp_layer *layer, const rtp_bf16 *k_pre, const rtp_bf16
   int st = make_plan(layer, nullptr, &p);
   if (st != RTP_OK) return st;
   if (!k_pre || !w_k || !k_idx || n0 < 0 || n1 < n0 || n1 > layer->Ncap) return RTP_ERR_ARG;
+  if (!aligned16({k_pre, w_k, k_idx})) return RTP_ERR_ARG;
   return launch_index_keys(p.g, k_pre, w_k, k_idx, n0, n1, as_stream(stream));
 }
 
@@ -353,6 +364,7 @@ int rtp_index_score(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf1
   int st = make_plan(layer, nullptr, &p);
   if (st != RTP_OK) return st;
   if (p.g.units && (!q_pre || !w_q || !k_idx || !logits)) return RTP_ERR_ARG;
+  if (!aligned16({q_pre, w_q, k_idx, logits})) return RTP_ERR_ARG;
   return launch_index_score(p.g, q_pre, w_q, k_idx, logits, as_stream(stream));
 }
 
@@ -362,6 +374,7 @@ int rtp_topp_select(const rtp_layer *layer, const float *logits, int32_t *idx, i
   int st = plan_with_ws(layer, ws, ws_bytes, &p);
   if (st != RTP_OK) return st;
   if (p.g.units && (!logits || !count || cap < 0 || (cap > 0 && !idx))) return RTP_ERR_ARG;
+  if (!aligned16({logits, idx, count})) return RTP_ERR_ARG;
   hipStream_t s = as_stream(stream);
   st = launch_phase_a(p.g, nullptr, nullptr, nullptr, logits, nullptr, nullptr, nullptr, true, false, s);
   if (st != RTP_OK) return st;
@@ -376,6 +389,7 @@ int rtp_sparse_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf1
   int st = plan_with_ws(layer, ws, ws_bytes, &p);
   if (st != RTP_OK) return st;
   if (p.g.units && (!q_pre || !k || !v || !count || !out || cap < 0 || (cap > 0 && !idx))) return RTP_ERR_ARG;
+  if (!aligned16({q_pre, k, v, idx, count, out})) return RTP_ERR_ARG;
   return launch_sparse_attn(p.g, q_pre, k, v, idx, count, cap, out, as_stream(stream));
 }
 
@@ -385,6 +399,7 @@ int rtp_swa_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *
   int st = plan_with_ws(layer, ws, ws_bytes, &p);
   if (st != RTP_OK) return st;
   if (p.g.swa_units && (!q_pre || !k || !v || !out)) return RTP_ERR_ARG;
+  if (!aligned16({q_pre, k, v, out})) return RTP_ERR_ARG;
   if (has_ring(p.g) && p.g.nq > 1) return RTP_ERR_UNSUPPORTED;     // a ring holds the newest window only
   return launch_phase_a(p.g, q_pre, nullptr, nullptr, nullptr, k, v, out, false, true, as_stream(stream));
 }
@@ -395,6 +410,7 @@ int rtp_dense_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16
   int st = plan_with_ws(layer, ws, ws_bytes, &p, true);
   if (st != RTP_OK) return st;
   if (!q_pre || !k || !v || !out) return RTP_ERR_ARG;
+  if (!aligned16({q_pre, k, v, out})) return RTP_ERR_ARG;
   if (layer->local_ring) {                    // every head needs every position
     Geo reg;
     st = make_geo(layer, false, reg);
@@ -416,6 +432,7 @@ int rtp_prefill_attn(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf
   int st = make_plan(layer, nullptr, &p);
   if (st != RTP_OK) return st;
   if (!q_pre || !k || !v || !out) return RTP_ERR_ARG;
+  if (!aligned16({q_pre, k, v, out})) return RTP_ERR_ARG;
   if (has_ring(p.g)) return RTP_ERR_UNSUPPORTED;     // earlier queries need rows a ring no longer holds
   FlashQuads fq[2];
   st = make_flash_quads(p.g, all_dense != 0, fq);
@@ -432,6 +449,7 @@ int rtp_append_kv(const rtp_layer *layer, const rtp_bf16 *k_new, const rtp_bf16 
   if (n_new == 0) return RTP_OK;
   if (!k_new || !v_new || !k_cache || !v_cache) return RTP_ERR_ARG;
   if (p.g.Hi && (!w_k || !k_idx)) return RTP_ERR_ARG;
+  if (!aligned16({k_new, v_new, w_k, k_cache, v_cache, k_idx})) return RTP_ERR_ARG;
   return launch_append_kv(p.g, k_new, v_new, w_k, k_cache, v_cache, k_idx, n0, n_new, as_stream(stream));
 }
 
@@ -452,6 +470,7 @@ int rtp_cluster_build(const rtp_layer *layer, const rtp_bf16 *k_idx, int32_t K, 
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return RTP_ERR_ARG;
   if (ws_bytes < need) return RTP_ERR_WS_TOO_SMALL;
   if (iters < 0 || g.Hi == 0 || !k_idx || !centroids || !counts || !offsets || !members) return RTP_ERR_ARG;
+  if (!aligned16({k_idx, centroids, counts, offsets, members})) return RTP_ERR_ARG;
   return launch_cluster_build(g, cg, k_idx, iters, centroids, counts, offsets, members, as_stream(stream));
 }
 
@@ -470,6 +489,7 @@ int rtp_cluster_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf
   if (!q_pre || !k || !v || !out) return RTP_ERR_ARG;
   if (g.units && (!w_q || !centroids || !counts || !offsets || !members)) return RTP_ERR_ARG;
   if (idx_opt && cap < 0) return RTP_ERR_ARG;
+  if (!aligned16({q_pre, w_q, centroids, counts, offsets, members, k, v, out, idx_opt, count_opt})) return RTP_ERR_ARG;
   hipStream_t s = as_stream(stream);
   st = launch_phase_a(g, q_pre, nullptr, nullptr, nullptr, k, v, out, false, true, s);      // local heads
   if (st != RTP_OK) return st;
@@ -488,6 +508,7 @@ int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf1
   if (!q_pre || !k || !v || !out) return RTP_ERR_ARG;
   if (p.g.units && (!w_q || !k_idx)) return RTP_ERR_ARG;
   if (idx_opt && cap < 0) return RTP_ERR_ARG;
+  if (!aligned16({q_pre, w_q, k_idx, k, v, out, idx_opt, count_opt})) return RTP_ERR_ARG;
   hipStream_t s = as_stream(stream);
   if (layer->nq > 1) {
     if (has_ring(p.g)) return RTP_ERR_UNSUPPORTED;   // earlier queries' windows left the ring

@@ -98,8 +98,12 @@ def test_calls_reject_before_launch():
     assert lib.rtp_append_kv(L, None, fake, fake, fake, fake, fake, 0, 1, None) == -1
     assert lib.rtp_append_kv(L, fake, fake, None, fake, fake, fake, 0, 1, None) == -1           # retrieval layer needs W_k
     assert lib.rtp_append_kv(L, None, None, None, None, None, None, 5, 0, None) == 0            # nothing to do
-    # misaligned workspace
+    # misaligned workspace or arrays (the kernels use 16-byte vector accesses)
     assert lib.rtp_swa_attn(L, fake, fake, fake, fake, fake + 8, need, None) == -1
+    assert lib.rtp_swa_attn(L, fake + 2, fake, fake, fake, fake, need, None) == -1
+    assert lib.rtp_decode_step(L, fake, fake, fake, fake + 8, fake, fake, None, None, 0, fake, need, None, None) == -1
+    assert lib.rtp_index_keys(L, fake, fake, fake + 4, 0, 10, None) == -1
+    assert lib.rtp_append_kv(L, fake, fake, fake, fake, fake + 16 + 8, fake, 0, 1, None) == -1
     # chunked prefill (nq > 1) is validated the same way before any launch
     lay2 = _layer(nq=4)
     L2 = ctypes.byref(lay2.c())
