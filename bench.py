@@ -72,11 +72,36 @@ PHASE_A_SOURCES = [os.path.join(CSRC, f) for f in ("topp_kernels.hip", "swa.h", 
                                                    "api.hip")] + [os.path.join(ROOT, "include", "rtp.h")]
 
 
+def _code_only(src: str) -> str:
+    """C/C++ source without comments and with whitespace collapsed, so that
+    edits to comments alone keep a recorded measurement valid."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        if src.startswith("//", i):
+            i = src.find("\n", i)
+            i = n if i < 0 else i
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif src[i] in "\"'":                                 # string or character literal, kept whole
+            q, j = src[i], i + 1
+            while j < n and src[j] != q:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(src[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the code (not the comments) of the phase-A sources."""
     h = hashlib.sha256()
     for path in PHASE_A_SOURCES:
-        with open(path, "rb") as fh:
-            h.update(os.path.basename(path).encode() + fh.read())
+        with open(path, encoding="utf-8") as fh:
+            h.update(os.path.basename(path).encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -26,6 +26,14 @@
  *    launched and a negative RTP_ERR_* code is returned.  RTP_ERR_HIP reports a
  *    failed launch (the HIP error is left for hipGetLastError()).
  *  - Non-finite inputs are undefined behaviour.
+ *  - Tuning overrides, read from the environment when a call plans its work:
+ *    RTP_SCAN_TILE (1024, 2048, 4096 or 8192 positions per scan tile),
+ *    RTP_SWA_CHUNK (a multiple of 64: cache rows per window workgroup) and
+ *    RTP_PF_QCH (a multiple of 16: queries per chunked-prefill selection
+ *    chunk).  They change how the work is split, not what is computed
+ *    (fp32 results may change in their last bits through the order of
+ *    split-K merges); other values are ignored.  rtp_workspace_bytes reads
+ *    them too, so keep them fixed between sizing a workspace and using it.
  *  - Row-major layouts; "cap" rows of the caches are strided by Ncap.
  *  - "[B, Hkv, Ncap, D]" for the K/V caches (k, v, k_cache, v_cache) stands for
  *    the layout rtp_layer.local_ring selects; it is exactly that shape when
