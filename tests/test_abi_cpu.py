@@ -165,6 +165,24 @@ def test_cluster_calls_validate_before_launch():
                                 need - 1, None) == -3
 
 
+def test_layer_struct_follows_field_changes():
+    """The binding memoises the C struct of a layer: a changed field rebuilds
+    it, and a dataclasses.replace copy owns its own struct and head_mode array."""
+    import dataclasses
+    lay = _layer()
+    c1 = lay.c()
+    assert lay.c() is c1                                   # unchanged fields: the same struct
+    lay.N = 4000
+    c2 = lay.c()
+    assert c2 is not c1 and c2.N == 4000 and c2.Ncap == 4000
+    ring = dataclasses.replace(lay, local_ring=1)
+    assert ring._memo is not lay._memo
+    assert ring.c().local_ring == 1 and lay.c().local_ring == 0
+    lay.head_mode = [0] * 8
+    assert [lay.c().head_mode[h] for h in range(8)] == [0] * 8
+    assert [ring.c().head_mode[h] for h in range(8)] == [1, 1, 1, 1, 0, 0, 0, 0]
+
+
 def test_binding_checks_tensors_without_gpu():
     import torch
     lay = _layer()
