@@ -3,8 +3,9 @@
   python prof_summary.py stats DIR OUT.txt --cmd "..."
       per-kernel dispatch counts and durations from a --kernel-trace run
   python prof_summary.py traffic FETCH_DIR WRITE_DIR OUT.json --workload NAME --cmd "..."
-      HBM bytes per phase-A launch from two --pmc runs (FETCH_SIZE, then WRITE_SIZE),
-      each scaled by what the same counter reads for bench.py's known-size copy
+      HBM bytes per phase-A launch (and per finish launch) from two --pmc runs
+      (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter reads for
+      bench.py's known-size copy
 
 DIR holds the rocpd SQLite database(s) rocprofv3 wrote (-d DIR).
 """
@@ -21,6 +22,7 @@ from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PHASE_A = "phase_a_kernel"
+FINISH = "finish_kernel"
 CALIB = "neg"                     # bench.calibration_copy: torch.neg over 1 GiB of float32
 CALIB_BYTES = 1 << 30
 
@@ -109,6 +111,14 @@ def cmd_traffic(a):
                            "fetch_scale": round(s_fetch, 4), "write_scale": round(s_write, 4)},
            "read_bytes_per_launch": int(rd), "write_bytes_per_launch": int(wr),
            "bytes_per_launch": int(rd + wr), "commands": a.cmd}
+    # the step's other kernel, from the same passes and scales
+    f_fi, nff = mean_kib(fetch, lambda n: n.startswith(FINISH))
+    w_fi, nfw = mean_kib(write, lambda n: n.startswith(FINISH))
+    if f_fi is not None and w_fi is not None:
+        out["other_kernels"] = {FINISH: {"launches": [nff, nfw], "fetch_kib_per_launch": round(f_fi, 1),
+                                         "write_kib_per_launch": round(w_fi, 1),
+                                         "read_bytes_per_launch": int(f_fi * 1024 * s_fetch),
+                                         "write_bytes_per_launch": int(w_fi * 1024 * s_write)}}
     with open(a.out, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
