@@ -28,7 +28,10 @@ constexpr int kApKvBatch = 8;      // KV groups whose rows are loaded together
 __device__ __forceinline__ double bf16_val(rtp_bf16 v) { return (double)__uint_as_float((uint32_t)v << 16); }
 
 // Post-RoPE key and value of KV groups kv0 .. kv0 + kApKvBatch - 1 at new row t
-// (position n), channel pair `pair`; loads first, then the stores.
+// (position n), channel pair `pair`; loads first, then the stores.  RING: the
+// layer has ring groups (without them the rows follow the plain
+// [B, Hkv, Ncap, D] stride and no ring lookup is made).
+template <bool RING>
 __device__ __forceinline__ void append_kv_pairs(const Geo &g, const rtp_bf16 *__restrict__ k_new,
                                                 const rtp_bf16 *__restrict__ v_new, rtp_bf16 *__restrict__ kc,
                                                 rtp_bf16 *__restrict__ vc, int b, int kv0, long long t,
@@ -44,9 +47,11 @@ __device__ __forceinline__ void append_kv_pairs(const Geo &g, const rtp_bf16 *__
   }
 #pragma unroll
   for (int u = 0; u < kApKvBatch; ++u) {
-    const bool ring = kv0 + u < g.Hkv && kv_is_ring(g, kv0 + u);
-    if (kv0 + u < g.Hkv && kv_keep(g, ring, n, n_end)) {
-      const size_t dst = (kv_group_base(g, b, kv0 + u) + kv_row(g, ring, n)) * kD + 2 * pair;
+    const bool ring = RING && kv0 + u < g.Hkv && kv_is_ring(g, kv0 + u);
+    if (kv0 + u < g.Hkv && (!RING || kv_keep(g, ring, n, n_end))) {
+      const size_t row = RING ? kv_group_base(g, b, kv0 + u) + kv_row(g, ring, n)
+                              : ((size_t)b * g.Hkv + kv0 + u) * g.Ncap + n;
+      const size_t dst = row * kD + 2 * pair;
       *reinterpret_cast<uint32_t *>(kc + dst) = rope_pair_bf16(kw[u], sn, cs);
       *reinterpret_cast<uint32_t *>(vc + dst) = vw[u];
     }
@@ -56,6 +61,7 @@ __device__ __forceinline__ void append_kv_pairs(const Geo &g, const rtp_bf16 *__
 // A few new rows: one workgroup per (sequence, new row).  Every load a thread
 // needs is issued before its first use, so the projection costs one memory
 // round trip and a 128-deep FMA chain.
+template <bool RING>
 __global__ __launch_bounds__(kWG) void append_small_kernel(Geo g, const rtp_bf16 *__restrict__ k_new,
                                                            const rtp_bf16 *__restrict__ v_new,
                                                            const rtp_bf16 *__restrict__ w_k, rtp_bf16 *__restrict__ kc,
@@ -69,7 +75,7 @@ __global__ __launch_bounds__(kWG) void append_small_kernel(Geo g, const rtp_bf16
   double sn, cs;
   sincos((double)n * rope_freq(g.theta, pair), &sn, &cs);
   for (int kv0 = (tid >> 6) * kApKvBatch; kv0 < g.Hkv; kv0 += 4 * kApKvBatch)
-    append_kv_pairs(g, k_new, v_new, kc, vc, b, kv0, t, n_new, n, n0 + n_new, pair, sn, cs);
+    append_kv_pairs<RING>(g, k_new, v_new, kc, vc, b, kv0, t, n_new, n, n0 + n_new, pair, sn, cs);
   // indexer keys: thread (indexer-key head, output channel)
   for (int x = tid; x < g.Hi * kR; x += kWG) {
     const int i = x / kR, j = x % kR;
@@ -98,6 +104,7 @@ struct AppendShared {
   double w[kD][kR];                        // one indexer-key head's matrix, widened
 };
 
+template <bool RING>
 __global__ __launch_bounds__(kWG) void append_bulk_kernel(Geo g, const rtp_bf16 *__restrict__ k_new,
                                                           const rtp_bf16 *__restrict__ v_new,
                                                           const rtp_bf16 *__restrict__ w_k, rtp_bf16 *__restrict__ kc,
@@ -115,8 +122,8 @@ __global__ __launch_bounds__(kWG) void append_bulk_kernel(Geo g, const rtp_bf16 
   const long long t0 = (long long)blk * kApRows;
   const int nr = (int)(n_new - t0 < kApRows ? n_new - t0 : kApRows);
   const size_t src0 = ((size_t)bg * n_new + t0) * kD;                 // first new row of this block
-  const bool ring = kv_is_ring(g, kv);
-  const size_t gbase = kv_group_base(g, b, kv) * kD;
+  const bool ring = RING && kv_is_ring(g, kv);
+  const size_t gbase = RING ? kv_group_base(g, b, kv) * kD : (size_t)bg * g.Ncap * kD;
   // indexer-key heads fed by this KV group: a contiguous range [i0, i1)
   int i0 = g.Hi, i1 = g.Hi;
   for (int i = 0; i < g.Hi; ++i) {
@@ -137,10 +144,10 @@ __global__ __launch_bounds__(kWG) void append_bulk_kernel(Geo g, const rtp_bf16 
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const long long n = n0 + t0 + r0 + u;
-      if (r0 + u < nr && kv_keep(g, ring, n, n0 + n_new)) {
+      if (r0 + u < nr && (!RING || kv_keep(g, ring, n, n0 + n_new))) {
         double sn, cs;
         sincos((double)n * th, &sn, &cs);
-        const size_t dst = gbase + (size_t)kv_row(g, ring, n) * kD + 2 * lane;
+        const size_t dst = gbase + (size_t)(RING ? kv_row(g, ring, n) : n) * kD + 2 * lane;
         *reinterpret_cast<uint32_t *>(kc + dst) = rope_pair_bf16(kw[u], sn, cs);
         *reinterpret_cast<uint32_t *>(vc + dst) = vw[u];
       }
@@ -211,14 +218,20 @@ __global__ __launch_bounds__(kWG) void append_bulk_kernel(Geo g, const rtp_bf16 
 int launch_append_kv(const Geo &g, const rtp_bf16 *k_new, const rtp_bf16 *v_new, const rtp_bf16 *w_k, rtp_bf16 *kc,
                      rtp_bf16 *vc, rtp_bf16 *k_idx, long long n0, long long n_new, hipStream_t s) {
   if (n_new == 0) return RTP_OK;
-  if (n_new <= kApSmall) {
-    hipLaunchKernelGGL(append_small_kernel, dim3((unsigned)(g.B * n_new)), dim3(kWG), 0, s, g, k_new, v_new, w_k, kc,
-                       vc, k_idx, n0, n_new);
-  } else {
-    const long long bpb = (n_new + kApRows - 1) / kApRows;                    // runs per (b, group)
-    hipLaunchKernelGGL(append_bulk_kernel, dim3((unsigned)((long long)g.B * g.Hkv * bpb)), dim3(kWG), 0, s, g, k_new,
-                       v_new, w_k, kc, vc, k_idx, n0, n_new);
-  }
+  const dim3 small_grid((unsigned)(g.B * n_new));
+  const dim3 bulk_grid((unsigned)((long long)g.B * g.Hkv * ((n_new + kApRows - 1) / kApRows)));  // runs per (b, group)
+  if (n_new <= kApSmall && g.any_ring)
+    hipLaunchKernelGGL(append_small_kernel<true>, small_grid, dim3(kWG), 0, s, g, k_new, v_new, w_k, kc, vc, k_idx,
+                       n0, n_new);
+  else if (n_new <= kApSmall)
+    hipLaunchKernelGGL(append_small_kernel<false>, small_grid, dim3(kWG), 0, s, g, k_new, v_new, w_k, kc, vc, k_idx,
+                       n0, n_new);
+  else if (g.any_ring)
+    hipLaunchKernelGGL(append_bulk_kernel<true>, bulk_grid, dim3(kWG), 0, s, g, k_new, v_new, w_k, kc, vc, k_idx,
+                       n0, n_new);
+  else
+    hipLaunchKernelGGL(append_bulk_kernel<false>, bulk_grid, dim3(kWG), 0, s, g, k_new, v_new, w_k, kc, vc, k_idx,
+                       n0, n_new);
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ERR_HIP;
 }
 
