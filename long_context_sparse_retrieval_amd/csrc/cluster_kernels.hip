@@ -30,6 +30,7 @@ namespace rtp {
 namespace {
 
 constexpr int kClTile = 4096;          // tokens per assignment workgroup
+constexpr int kClKeys = 4;             // keys scored together by one thread (centre reads shared)
 
 struct ClAssignShared {
   double c[kMaxClusters][kR];          // centres, widened
@@ -78,38 +79,64 @@ __global__ __launch_bounds__(kWG) void cl_assign_kernel(Geo g, ClGeo cg, const r
   __syncthreads();
   const long long n0 = (long long)tile * kClTile;
   const long long n1 = n0 + kClTile < g.N ? n0 + kClTile : g.N;
-  for (long long n = n0 + tid; n < n1; n += kWG) {
-    const uint4 *row = reinterpret_cast<const uint4 *>(k_idx + ((size_t)u * g.Ncap + n) * kR);
-    const uint4 a = row[0], b2 = row[1];
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b2.x, b2.y, b2.z, b2.w};
-    double x[kR];
+  // kClKeys keys per thread (n, n + kWG, ...): every centre value read from
+  // LDS serves all of them; each key keeps its own FMA chain in channel order
+  for (long long nbase = n0 + tid; nbase < n1; nbase += (long long)kClKeys * kWG) {
+    double x[kClKeys][kR], xx[kClKeys];
+    long long nk[kClKeys];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      x[2 * t] = (double)bf_lo(w[t]);
-      x[2 * t + 1] = (double)bf_hi(w[t]);
+    for (int k = 0; k < kClKeys; ++k) {
+      nk[k] = nbase + (long long)k * kWG;
+      const long long n = nk[k] < n1 ? nk[k] : nbase;             // absent keys repeat the first
+      const uint4 *row = reinterpret_cast<const uint4 *>(k_idx + ((size_t)u * g.Ncap + n) * kR);
+      const uint4 a = row[0], b2 = row[1];
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b2.x, b2.y, b2.z, b2.w};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        x[k][2 * t] = (double)bf_lo(w[t]);
+        x[k][2 * t + 1] = (double)bf_hi(w[t]);
+      }
+      xx[k] = 0.0;
+#pragma unroll
+      for (int t = 0; t < kR; ++t) xx[k] = fma(x[k][t], x[k][t], xx[k]);
     }
-    double xx = 0.0;
+    double best[kClKeys];
+    int bj[kClKeys];
 #pragma unroll
-    for (int t = 0; t < kR; ++t) xx = fma(x[t], x[t], xx);
-    double best = INFINITY;
-    int bj = 0;
+    for (int k = 0; k < kClKeys; ++k) {
+      best[k] = INFINITY;
+      bj[k] = 0;
+    }
     for (int j = 0; j < K; ++j) {
-      double xc = 0.0;
+      double xc[kClKeys];
 #pragma unroll
-      for (int t = 0; t < kR; ++t) xc = fma(x[t], sm.c[j][t], xc);
-      const double d = __dadd_rn(__dsub_rn(xx, __dmul_rn(2.0, xc)), sm.cc[j]);
-      if (d < best) {                                            // strict: ties keep the lower index
-        best = d;
-        bj = j;
+      for (int k = 0; k < kClKeys; ++k) xc[k] = 0.0;
+#pragma unroll
+      for (int t = 0; t < kR; ++t) {
+        const double c = sm.c[j][t];
+#pragma unroll
+        for (int k = 0; k < kClKeys; ++k) xc[k] = fma(x[k][t], c, xc[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < kClKeys; ++k) {
+        const double d = __dadd_rn(__dsub_rn(xx[k], __dmul_rn(2.0, xc[k])), sm.cc[j]);
+        if (d < best[k]) {                                       // strict: ties keep the lower index
+          best[k] = d;
+          bj[k] = j;
+        }
       }
     }
-    if (MODE == 0) {
 #pragma unroll
-      for (int t = 0; t < kR; ++t) atomicAdd(&sm.sum[bj][t], x[t]);
-      atomicAdd(&sm.cnt[bj], 1u);
-    } else {
-      cg.assign[(size_t)u * g.N + n] = bj;
-      atomicAdd(&sm.cnt[bj], 1u);
+    for (int k = 0; k < kClKeys; ++k) {
+      if (nk[k] >= n1) break;
+      if (MODE == 0) {
+#pragma unroll
+        for (int t = 0; t < kR; ++t) atomicAdd(&sm.sum[bj[k]][t], x[k][t]);
+        atomicAdd(&sm.cnt[bj[k]], 1u);
+      } else {
+        cg.assign[(size_t)u * g.N + nk[k]] = bj[k];
+        atomicAdd(&sm.cnt[bj[k]], 1u);
+      }
     }
   }
   __syncthreads();
