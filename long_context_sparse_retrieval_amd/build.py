@@ -27,6 +27,12 @@ COMMON = [
 ]
 
 
+# per-file additions: the prefill attention kernel keeps its matrix-core
+# accumulators in ordinary VGPRs (with accumulation registers the compiler
+# shuffled the score and output tiles through them on every key block)
+EXTRA = {"flash_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -37,7 +43,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

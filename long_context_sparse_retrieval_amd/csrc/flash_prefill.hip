@@ -37,8 +37,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kFq = 16;                 // queries per wave (the matrix-core N dimension)
 constexpr int kFk = 64;                 // keys per staged block
 constexpr int kKPad = kD + 8;           // padded key row in LDS (elements)
-constexpr int kVPad = kFk + 8;          // padded row of transposed values (elements)
+constexpr int kVPad = kFk + 4;          // padded row of transposed values (elements)
 constexpr double kQScale = 1.4426950408889634 / 11.313708498984761;   // log2(e) / sqrt(128)
+constexpr float kLazy = 8.f;            // headroom of the running maximum (base 2)
 
 struct FlashShared {
   rtp_bf16 k[2][kFk][kKPad];            // keys of a block, row-major (double-buffered)
@@ -122,33 +123,47 @@ __global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq
 #pragma unroll
   for (int t = 0; t < kD / 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // staging: thread t takes key row t / 4, channels 32 (t % 4) .. + 31 of a
-  // block; the next block's rows are loaded into registers while this block
-  // is computed, then written to the other LDS buffer (one barrier per block)
+  // staging: the next block is loaded into registers while this block is
+  // computed, then written to the other LDS buffer (one barrier per block).
+  // Keys: thread t takes key row t / 4, channels 32 (t % 4) .. + 31.  Values:
+  // thread t takes the four keys 4 vq .. + 3 (vq = t % 16) of channels
+  // 8 vo .. + 7 (vo = 4 wave + lane / 16) and writes each channel's four keys
+  // as one 8-byte word of the transposed block; with the 144-byte row pitch
+  // the 32 lanes of a half-wave land on 64 distinct banks.
   const int sr = tid >> 2, spart = tid & 3;
+  const int vq = tid & 15, vo = 4 * wv + (lane >> 4);
   uint4 k0v, k1v, k2v, k3v, v0v, v1v, v2v, v3v;               // the next block's slice, in flight
 #define RTP_FLASH_LOAD(KB)                                                                       \
   {                                                                                              \
     long long kp = (KB) * kFk + sr;                                                              \
     kp = kp < g.N ? kp : g.N - 1;                                                                \
     const uint4 *ks = reinterpret_cast<const uint4 *>(kc + (cbase + kp) * kD + 32 * spart);     \
-    const uint4 *vs = reinterpret_cast<const uint4 *>(vc + (cbase + kp) * kD + 32 * spart);     \
     k0v = ks[0]; k1v = ks[1]; k2v = ks[2]; k3v = ks[3];                                          \
-    v0v = vs[0]; v1v = vs[1]; v2v = vs[2]; v3v = vs[3];                                          \
+    long long vp = (KB) * kFk + 4 * vq;                                                          \
+    const long long vl = g.N - 1;                                                                \
+    const rtp_bf16 *vs = vc + cbase * kD + 8 * vo;                                               \
+    v0v = *reinterpret_cast<const uint4 *>(vs + (vp < vl ? vp : vl) * kD);                       \
+    v1v = *reinterpret_cast<const uint4 *>(vs + (vp + 1 < vl ? vp + 1 : vl) * kD);               \
+    v2v = *reinterpret_cast<const uint4 *>(vs + (vp + 2 < vl ? vp + 2 : vl) * kD);               \
+    v3v = *reinterpret_cast<const uint4 *>(vs + (vp + 3 < vl ? vp + 3 : vl) * kD);               \
   }
-  auto store_v = [&](int buf, int u, const uint4 &vw) {
-    const uint32_t w4[4] = {vw.x, vw.y, vw.z, vw.w};
+  // channel 8 vo + c of the four keys: element c of each row's 16 bytes
+  auto store_v = [&](int buf) {
+    const uint32_t r0[4] = {v0v.x, v0v.y, v0v.z, v0v.w}, r1[4] = {v1v.x, v1v.y, v1v.z, v1v.w};
+    const uint32_t r2[4] = {v2v.x, v2v.y, v2v.z, v2v.w}, r3[4] = {v3v.x, v3v.y, v3v.z, v3v.w};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      sm.vt[buf][32 * spart + 8 * u + 2 * c][sr] = (rtp_bf16)(w4[c] & 0xffffu);
-      sm.vt[buf][32 * spart + 8 * u + 2 * c + 1][sr] = (rtp_bf16)(w4[c] >> 16);
+    for (int w = 0; w < 4; ++w) {
+      const uint2 ev = {(r0[w] & 0xffffu) | (r1[w] << 16), (r2[w] & 0xffffu) | (r3[w] << 16)};
+      const uint2 od = {(r0[w] >> 16) | (r1[w] & 0xffff0000u), (r2[w] >> 16) | (r3[w] & 0xffff0000u)};
+      *reinterpret_cast<uint2 *>(&sm.vt[buf][8 * vo + 2 * w][4 * vq]) = ev;
+      *reinterpret_cast<uint2 *>(&sm.vt[buf][8 * vo + 2 * w + 1][4 * vq]) = od;
     }
   };
 #define RTP_FLASH_STORE(BUF)                                                                     \
   {                                                                                              \
     uint4 *kd = reinterpret_cast<uint4 *>(&sm.k[BUF][sr][32 * spart]);                          \
     kd[0] = k0v; kd[1] = k1v; kd[2] = k2v; kd[3] = k3v;                                          \
-    store_v(BUF, 0, v0v); store_v(BUF, 1, v1v); store_v(BUF, 2, v2v); store_v(BUF, 3, v3v);      \
+    store_v(BUF);                                                                                \
   }
   auto block_of = [&](long long x) { return x < sb_end ? x : mb_lo + (x - sb_end); };
   if (nblk > 0) {
@@ -195,15 +210,31 @@ __global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq
     }
     mb = fmaxf(mb, __shfl_xor(mb, 16));
     mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float m_new = fmaxf(m_run, mb);
-    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    // The reference maximum m_run moves only when a score of some query of
+    // the wave exceeds it by more than kLazy (wave-uniform branch).  Any
+    // reference gives the same o / l: the weights carry a common factor that
+    // cancels, and a weight stays below 2^kLazy, so nothing overflows.
+    if (__any(mb > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mb);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+      // O rows are queries 4 grp + e: their factors come from the lanes holding those queries
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ae = __shfl(alpha, 4 * grp + e);
+#pragma unroll
+        for (int t = 0; t < kD / 16; ++t) o[t][e] *= ae;
+      }
+    }
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;       // masked scores: exp2(-inf) = 0
     float ps = 0.f;
     bf16x4_t pb[kFk / 16], pl[kFk / 16];                      // P = hi + lo, both bf16
 #pragma unroll
     for (int st = 0; st < kFk / 16; ++st) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float pe = s[st][e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[st][e] - m_new);
+        const float pe = __builtin_amdgcn_exp2f(s[st][e] - m_ref);
         ps += pe;
         const short hi = bf16_rne(pe);
         pb[st][e] = hi;
@@ -212,15 +243,7 @@ __global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq
     }
     ps += __shfl_xor(ps, 16);
     ps += __shfl_xor(ps, 32);
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-    // O rows are queries 4 grp + e: their factors come from the lanes holding those queries
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float ae = __shfl(alpha, 4 * grp + e);
-#pragma unroll
-      for (int t = 0; t < kD / 16; ++t) o[t][e] *= ae;
-    }
+    l_run += ps;
     // O += P V in K = 32 steps over subtile pairs (2 j, 2 j + 1): slot 8 grp + e
     // of a step is key 16 (2 j) + 4 grp + e and slot 8 grp + 4 + e is key
     // 16 (2 j + 1) + 4 grp + e, the same order for P and for V
