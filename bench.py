@@ -580,6 +580,8 @@ def main():
     ap.add_argument("--calib", action="store_true", help="run the known-size copy used to scale HBM counters")
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the Top-P step (no dense comparator, no top-k line): for profiling runs")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time only the 32K prefill attention (RTPurbo and all-dense) and print its line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
@@ -587,6 +589,10 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     rtp.load()
+    if args.prefill:
+        with quiet_gc():
+            print(json.dumps({"prefill_32k": time_prefill()}), flush=True)
+        return
     if args.calib:
         calibration_copy()
     with quiet_gc():

@@ -2,6 +2,9 @@
 
   python prof_summary.py stats DIR OUT.txt --cmd "..."
       per-kernel dispatch counts and durations from a --kernel-trace run
+  python prof_summary.py counters DIR OUT.txt --kernel NAME --cmd "..."
+      per-dispatch averages of every counter a --pmc run collected for one kernel,
+      by grid size, with the LDS bank-conflict and matrix-core busy fractions
   python prof_summary.py traffic FETCH_DIR WRITE_DIR OUT.json --workload NAME --cmd "..."
       HBM bytes per phase-A launch (and per finish launch) from two --pmc runs
       (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter reads for
@@ -78,6 +81,50 @@ def cmd_stats(a):
     print("\n".join(lines))
 
 
+CUS, SIMDS, CLOCK_HZ = 256, 1024, 2.4e9
+
+
+def cmd_counters(a):
+    """Averages per dispatch (counters summed over the device's instances)."""
+    per = defaultdict(float)
+    info = {}
+    for db in dbs(a.dir):
+        con = sqlite3.connect(db)
+        q = ("select c.dispatch_id, k.name, k.grid_x / k.workgroup_x, k.duration, c.counter_name, c.value "
+             "from counters_collection c join kernels k on c.dispatch_id = k.dispatch_id")
+        for did, name, grid, dur, cn, v in con.execute(q).fetchall():
+            if a.kernel not in name:
+                continue
+            per[(db, did, cn)] += v
+            info[(db, did)] = (grid, dur)
+    groups = defaultdict(lambda: defaultdict(list))
+    for (db, did, cn), v in per.items():
+        groups[info[(db, did)][0]][cn].append(v)
+    for grid, dur in info.values():
+        groups[grid]["_dur"].append(dur)
+    lines = [f"# rocprofv3 counters: {a.title or a.kernel}", "", "command:", f"    {a.cmd}", "",
+             "per dispatch, averaged over the dispatches of each grid size; fractions use",
+             f"{CUS} CUs / {SIMDS} SIMDs at {CLOCK_HZ / 1e9:.1f} GHz over the dispatch's duration", ""]
+    for grid in sorted(groups):
+        c = groups[grid]
+        dur_ns = sum(c["_dur"]) / len(c["_dur"])
+        cyc = dur_ns * 1e-9 * CLOCK_HZ
+        lines.append(f"{a.kernel}  grid {grid} workgroups  ({len(c['_dur'])} dispatches, avg {dur_ns / 1e6:.3f} ms)")
+        for cn in sorted(k for k in c if k != "_dur"):
+            lines.append(f"    {cn:32s} {sum(c[cn]) / len(c[cn]):14.4g}")
+        if "SQ_LDS_BANK_CONFLICT" in c:
+            v = sum(c["SQ_LDS_BANK_CONFLICT"]) / len(c["SQ_LDS_BANK_CONFLICT"])
+            lines.append(f"    LDS bank-conflict stall / CU cycles  {v / CUS / cyc:.3f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            v = sum(c["SQ_VALU_MFMA_BUSY_CYCLES"]) / len(c["SQ_VALU_MFMA_BUSY_CYCLES"])
+            lines.append(f"    matrix-core busy / SIMD cycles       {v / SIMDS / cyc:.3f}")
+        lines.append("")
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def mean_kib(rows, pred):
     v = [x for n, x in rows if pred(short(n))]
     if not v:
@@ -133,6 +180,12 @@ def main():
     s.add_argument("out")
     s.add_argument("--cmd", required=True)
     s.add_argument("--title", default="")
+    c = sp.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("out")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--title", default="")
     t = sp.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
@@ -140,7 +193,7 @@ def main():
     t.add_argument("--workload", required=True)
     t.add_argument("--cmd", action="append", required=True)
     a = ap.parse_args()
-    cmd_stats(a) if a.what == "stats" else cmd_traffic(a)
+    {"stats": cmd_stats, "counters": cmd_counters, "traffic": cmd_traffic}[a.what](a)
 
 
 if __name__ == "__main__":
