@@ -40,10 +40,11 @@ constexpr int kKPad = kD + 8;           // padded key row in LDS (elements)
 constexpr int kVPad = kFk + 4;          // padded row of transposed values (elements)
 constexpr double kQScale = 1.4426950408889634 / 11.313708498984761;   // log2(e) / sqrt(128)
 constexpr float kLazy = 8.f;            // headroom of the running maximum (base 2)
+constexpr int kBufs = 1;               // LDS buffers per K/V block (1: a second barrier per block)
 
 struct FlashShared {
-  rtp_bf16 k[2][kFk][kKPad];            // keys of a block, row-major (double-buffered)
-  rtp_bf16 vt[2][kD][kVPad];            // values of a block, transposed
+  rtp_bf16 k[kBufs][kFk][kKPad];        // keys of a block, row-major
+  rtp_bf16 vt[kBufs][kD][kVPad];        // values of a block, transposed
 };
 
 // fp32 -> bf16, nearest even (one v_cvt_pk_bf16_f32 per pair on gfx950)
@@ -51,7 +52,7 @@ __device__ __forceinline__ short bf16_rne(float x) { return __builtin_bit_cast(s
 
 __device__ __forceinline__ float bf16_f(short b) { return __uint_as_float((uint32_t)(uint16_t)b << 16); }
 
-__global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq, const rtp_bf16 *__restrict__ q_pre,
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3, 8))) void flash_prefill_kernel(Geo g, FlashQuads fq, const rtp_bf16 *__restrict__ q_pre,
                                                             const rtp_bf16 *__restrict__ kc,
                                                             const rtp_bf16 *__restrict__ vc, float *__restrict__ out,
                                                             int ntiles) {
@@ -124,7 +125,9 @@ __global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq
   for (int t = 0; t < kD / 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // staging: the next block is loaded into registers while this block is
-  // computed, then written to the other LDS buffer (one barrier per block).
+  // computed, then written to LDS once every wave is done with this block
+  // (one K/V buffer and two barriers per block: 34 KB of LDS, so three
+  // workgroups share a CU, one more than with two buffers).
   // Keys: thread t takes key row t / 4, channels 32 (t % 4) .. + 31.  Values:
   // thread t takes the four keys 4 vq .. + 3 (vq = t % 16) of channels
   // 8 vo .. + 7 (vo = 4 wave + lane / 16) and writes each channel's four keys
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq
 
   for (long long x = 0; x < nblk; ++x) {
     const long long kb = block_of(x);
-    const int buf = (int)(x & 1);
+    const int buf = (int)(x % kBufs);
     RTP_FLASH_LOAD(block_of(x + 1 < nblk ? x + 1 : x));       // clamped: the last block reloads itself
     if (h != kNoHead) {                                        // wave-uniform
     // S^T for the block's four 16-key subtiles
@@ -270,7 +273,8 @@ __global__ __launch_bounds__(kWG) void flash_prefill_kernel(Geo g, FlashQuads fq
       }
     }
     }                                                          // h != kNoHead
-    if (x + 1 < nblk) RTP_FLASH_STORE((int)((x + 1) & 1));
+    if (kBufs == 1) __syncthreads();                           // every wave is done with the block
+    if (x + 1 < nblk) RTP_FLASH_STORE((int)((x + 1) % kBufs));
     __syncthreads();
   }
 #undef RTP_FLASH_LOAD
