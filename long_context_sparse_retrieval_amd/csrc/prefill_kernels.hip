@@ -44,11 +44,21 @@ struct PfSel {
   int valid;
 };
 
+// PACK: each bin's count rides in the top bits of its mass (one LDS atomic
+// per position, no count array: 34 KB instead of 50 KB of LDS, so four
+// workgroups share a CU instead of three).  A bin's mass is below
+// (prefix length) * 1.14 * 2^23, so with the count from bit 41 up the packing
+// holds for prefixes of up to 2^17 positions; longer ones keep the counts apart.
+constexpr int kPfCountShift = 41;
+constexpr unsigned long long kPfMassMask = (1ull << kPfCountShift) - 1;
+constexpr long long kPfPackMaxN = 1ll << 17;
+
+template <bool PACK>
 struct PfShared {
   union {
     struct {
       unsigned long long mass[kQB][kBins];
-      uint32_t cnt[kQB][kBins];
+      uint32_t cnt[PACK ? 1 : kQB][kBins];
     } h;
     struct {
       unsigned long long bm[kQB][kMaxCh];   // bin-b* mass per chunk, then its exclusive prefix
@@ -63,11 +73,12 @@ struct PfShared {
 // Selection: one workgroup per (b, r, block of 16 queries of the chunk [i0, i0 + nqc)).
 // Writes the selected positions of each query to idx_ws[unit_local][capw] (and,
 // optionally, to idx[unit][cap], truncated) and its count to cnt_ws / count.
-__global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *__restrict__ k_idx, int i0, int nqc,
+template <bool PACK>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4, 8))) void pf_select_kernel(Geo g, const rtp_bf16 *__restrict__ k_idx, int i0, int nqc,
                                                         int kc, int32_t *__restrict__ idx_ws, long long capw,
                                                         int32_t *__restrict__ cnt_ws, int32_t *__restrict__ idx,
                                                         int32_t *__restrict__ count, long long cap) {
-  __shared__ PfShared sm;
+  __shared__ PfShared<PACK> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, row = lane >> 4, col = lane & 15;
   const int nblk = (nqc + kQB - 1) / kQB;
   const int br = blockIdx.x / nblk, qb = blockIdx.x % nblk;
@@ -158,7 +169,7 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
   if (row == 0) sm.wmax[wv][qc] = mx;
   for (int x = tid; x < kQB * kBins; x += kWG) {
     (&sm.h.mass[0][0])[x] = 0ull;
-    (&sm.h.cnt[0][0])[x] = 0u;
+    if (!PACK) (&sm.h.cnt[0][0])[x] = 0u;
   }
   __syncthreads();
   if (tid < kQB) {
@@ -184,8 +195,12 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
             } else {
               w = token_weight(g, s, cell);
             }
-            atomicAdd(&sm.h.mass[qc][j], (unsigned long long)w);
-            atomicAdd(&sm.h.cnt[qc][j], 1u);
+            if (PACK) {
+              atomicAdd(&sm.h.mass[qc][j], (unsigned long long)w | (1ull << kPfCountShift));
+            } else {
+              atomicAdd(&sm.h.mass[qc][j], (unsigned long long)w);
+              atomicAdd(&sm.h.cnt[qc][j], 1u);
+            }
           }
         },
         nop, nop);
@@ -200,7 +215,8 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int j = 4 * lane + k;
-      W[k] = (double)sm.h.mass[q][j] * 0x1p-23 * bin_scale(g, -(double)j * 0.125);
+      W[k] = (double)(PACK ? sm.h.mass[q][j] & kPfMassMask : sm.h.mass[q][j]) * 0x1p-23 *
+             bin_scale(g, -(double)j * 0.125);
       loc += W[k];
     }
     double incl = loc;                                    // wave inclusive scan (fixed order)
@@ -231,7 +247,11 @@ __global__ __launch_bounds__(kWG) void pf_select_kernel(Geo g, const rtp_bf16 *_
     // clamp bin is an ordinary boundary
     const int all = (g.topk ? need >= Z : (g.p >= 1.0f || bstar >= kBins - 1)) ? 1 : 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) cnt_lt += (4 * lane + k < bstar) ? (int)sm.h.cnt[q][4 * lane + k] : 0;
+    for (int k = 0; k < 4; ++k) {
+      const int j = 4 * lane + k;
+      const int cj = PACK ? (int)(sm.h.mass[q][j] >> kPfCountShift) : (int)sm.h.cnt[PACK ? 0 : q][j];
+      cnt_lt += j < bstar ? cj : 0;
+    }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) cnt_lt += __shfl_xor(cnt_lt, off);
     if (lane == 0) {
@@ -499,8 +519,12 @@ int launch_pf_select(const Geo &g, const rtp_bf16 *k_idx, int i0, int nqc, int32
   if (kc < 1024) kc = 1024;
   const int nblk = (nqc + kQB - 1) / kQB;
   const long long grid = (long long)g.B * g.Hr * nblk;
-  hipLaunchKernelGGL(pf_select_kernel, dim3((unsigned)grid), dim3(kWG), 0, s, g, k_idx, i0, nqc, (int)kc, idx_ws, capw,
-                     cnt_ws, idx, count, cap);
+  if (g.N <= kPfPackMaxN)
+    hipLaunchKernelGGL(pf_select_kernel<true>, dim3((unsigned)grid), dim3(kWG), 0, s, g, k_idx, i0, nqc, (int)kc,
+                       idx_ws, capw, cnt_ws, idx, count, cap);
+  else
+    hipLaunchKernelGGL(pf_select_kernel<false>, dim3((unsigned)grid), dim3(kWG), 0, s, g, k_idx, i0, nqc, (int)kc,
+                       idx_ws, capw, cnt_ws, idx, count, cap);
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ERR_HIP;
 }
 

@@ -405,6 +405,9 @@ PREFILL_CASES = {
     "pf-shared-keys": (5, dict(N=3000, nq=40, diffuse=(200, 0.5), idx_group=4), None, None),
     "pf-topk": (5, dict(N=3000, nq=40, diffuse=(200, 0.5), top_k=300), None, None),
     "pf-topk-chunks": (5, dict(N=5000, nq=80, diffuse=(300, 0.5), top_k=1), None, "16"),
+    # prefixes longer than 2^17 positions: the selection keeps its bin counts
+    # apart from the masses (shorter prefixes pack them into one word)
+    "pf-long-prefix": (5, dict(N=140000, nq=16, diffuse=(2000, 0.5)), None, None),
 }
 
 
