@@ -582,6 +582,8 @@ def main():
                     help="time only the Top-P step (no dense comparator, no top-k line): for profiling runs")
     ap.add_argument("--prefill", action="store_true",
                     help="time only the 32K prefill attention (RTPurbo and all-dense) and print its line")
+    ap.add_argument("--chunked-prefill", action="store_true",
+                    help="time only the 128K chunked-prefill call (4 heads x 4096 queries) and print its line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
@@ -592,6 +594,10 @@ def main():
     if args.prefill:
         with quiet_gc():
             print(json.dumps({"prefill_32k": time_prefill()}), flush=True)
+        return
+    if args.chunked_prefill:
+        with quiet_gc():
+            print(json.dumps({"chunked_prefill_128k": time_chunked_prefill()}), flush=True)
         return
     if args.calib:
         calibration_copy()
