@@ -517,6 +517,36 @@ def test_prefill_attn_matches_oracle(case):
                 check_output(out[b, h, i], ref, f"{case} b{b} h{h} i{i}")
 
 
+def test_prefill_attn_rising_scores():
+    """Scores that grow along the key axis, so the running maximum of every
+    query moves again and again (each time a score outgrows the reference by
+    the kernel's rescale headroom) and the weight piles up on the newest
+    keys.  The query lives in the slowest-rotating RoPE pairs, so its rotation
+    barely changes across positions and the ramp holds for every query."""
+    B, Hq, Hkv, N, nq, window, n_sink = 1, 8, 2, 2048, 40, 256, 4
+    hm = [1] * 4 + [0] * 4
+    rng = np.random.default_rng(2024)
+    say(f"prefill_attn rising scores: N={N} nq={nq}")
+    u = np.zeros(128)
+    u[112:] = rng.standard_normal(16)
+    u /= np.linalg.norm(u)
+    q = O.f64_to_bf16(np.broadcast_to(4.0 * u, (B, Hq, nq, 128)) + 0.05 * rng.standard_normal((B, Hq, nq, 128)))
+    # score of key n for |q| = 4: about 0.03 n (natural units), 61 at the last key
+    ramp = 0.03 * np.arange(N) * np.sqrt(128.0) / 4.0
+    k = O.f64_to_bf16(ramp[None, None, :, None] * u + 0.5 * rng.standard_normal((B, Hkv, N, 128)))
+    v = _rand_bf16(rng, (B, Hkv, N, 128))
+    lay = rtp.Layer(B=B, Hq=Hq, Hkv=Hkv, N=N, nq=nq, head_mode=hm, window=window, n_sink=n_sink)
+    out = rtp.prefill_attn(lay, dev_bf16(q), dev_bf16(k), dev_bf16(v)).cpu().numpy()
+    G = Hq // Hkv
+    for h in range(Hq):
+        for i in range(nq):
+            m = N - nq + i
+            rows = np.arange(m + 1) if hm[h] else O.swa_positions(m, window, n_sink)
+            q_rot = O.rope_rotate(O.bf16_to_f64(q[0, h, i]), m, 1e6)
+            ref = O.attention(q_rot, O.bf16_to_f64(k[0, h // G, rows]), O.bf16_to_f64(v[0, h // G, rows]))
+            check_output(out[0, h, i], ref, f"rising b0 h{h} i{i}")
+
+
 # ----------------------------------------------------------------------------- one workspace, many calls
 def test_workspace_serves_every_call_in_sequence():
     """Every call leaves the workspace ready for the next call on a layer of the
