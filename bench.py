@@ -241,6 +241,45 @@ def copy_ceiling_gbps() -> float:
     return 2 * n * 4 / (ms * 1e-3) / 1e9
 
 
+def read_ceiling() -> dict:
+    """The box's streaming-read rate: libreadprobe.so's read kernel over a 2 GiB
+    buffer (read once per pass, nothing written), swept over grid sizes and
+    loads in flight per thread; the best configuration is the ceiling the
+    bandwidth-bound kernels are compared with."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_sparse_retrieval_amd", "libreadprobe.so"))
+    lib.readprobe_stream.restype = ctypes.c_int
+    lib.readprobe_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    best, sweep = None, {}
+    for blocks in (1024, 2048, 4096, 8192):
+        for unroll in (4, 8, 16):
+            def one():
+                st = lib.readprobe_stream(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, unroll, stream)
+                if st != 0:
+                    raise RuntimeError(f"readprobe_stream: status {st}")
+            for _ in range(2):
+                one()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(5):
+                one()
+            e1.record()
+            torch.cuda.synchronize()
+            gbps = nbytes * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            sweep[f"{blocks}x{unroll}"] = round(gbps, 1)
+            if best is None or gbps > best[0]:
+                best = (gbps, blocks, unroll)
+    del buf
+    return {"GBps": round(best[0], 1), "blocks": best[1], "loads_in_flight_per_thread": best[2],
+            "bytes": nbytes, "sweep": sweep}
+
+
 def calibration_copy(n_bytes: int = 1 << 30, reps: int = 3) -> None:
     """A plain streaming copy of known size (negation: read n_bytes, write n_bytes).
 
@@ -582,6 +621,8 @@ def main():
                     help="time only the Top-P step (no dense comparator, no top-k line): for profiling runs")
     ap.add_argument("--prefill", action="store_true",
                     help="time only the 32K prefill attention (RTPurbo and all-dense) and print its line")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="measure only the streaming-read and copy ceilings and print them")
     ap.add_argument("--chunked-prefill", action="store_true",
                     help="time only the 128K chunked-prefill call (4 heads x 4096 queries) and print its line")
     args = ap.parse_args()
@@ -603,7 +644,12 @@ def main():
         calibration_copy()
     with quiet_gc():
         copy_gbps = copy_ceiling_gbps()
-    log(f"[bench] device copy ceiling {copy_gbps:.0f} GB/s")
+        rc = read_ceiling()
+    log(f"[bench] device copy ceiling {copy_gbps:.0f} GB/s, streaming read ceiling {rc['GBps']:.0f} GB/s "
+        f"({rc['blocks']} workgroups x {rc['loads_in_flight_per_thread']} loads in flight)")
+    if args.read_ceiling:
+        print(json.dumps({"read_ceiling": rc, "copy_ceiling_GBps": round(copy_gbps, 1)}), flush=True)
+        return
 
     cfgs = [args.only] if args.only else [4, 3, 6]
     summ, cpu = {}, None
@@ -710,6 +756,11 @@ def main():
                      "frac": round(s["pa_gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel_us": round(s["pa_us"], 2), "algorithmic_bytes_per_launch": s["pa_bytes"]},
         "copy_ceiling_GBps": round(copy_gbps, 1),
+        "read_ceiling": {"GBps": rc["GBps"], "what": "in-tree streaming-read kernel (libreadprobe.so) over 2 GiB, "
+                                                     "best of a grid / loads-in-flight sweep",
+                         "blocks": rc["blocks"], "loads_in_flight_per_thread": rc["loads_in_flight_per_thread"],
+                         "phase_a_frac_of_read_ceiling": round(s["pa_gbps"] / rc["GBps"], 4),
+                         "step_frac_of_read_ceiling": round(s["gbps"] / rc["GBps"], 4)},
         "step_us_percentiles": s["pct"],
         "instrumented_us_per_step": s["instr_us"],
     }

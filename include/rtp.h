@@ -26,14 +26,10 @@
  *    launched and a negative RTP_ERR_* code is returned.  RTP_ERR_HIP reports a
  *    failed launch (the HIP error is left for hipGetLastError()).
  *  - Non-finite inputs are undefined behaviour.
- *  - Tuning overrides, read from the environment when a call plans its work:
- *    RTP_SCAN_TILE (1024, 2048, 4096 or 8192 positions per scan tile),
- *    RTP_SWA_CHUNK (a multiple of 64: cache rows per window workgroup) and
- *    RTP_PF_QCH (a multiple of 16: queries per chunked-prefill selection
- *    chunk).  They change how the work is split, not what is computed
- *    (fp32 results may change in their last bits through the order of
- *    split-K merges); other values are ignored.  rtp_workspace_bytes reads
- *    them too, so keep them fixed between sizing a workspace and using it.
+ *  - rtp_layer's three tuning fields (scan_tile, swa_chunk, pf_qch) change how
+ *    the work is split, not what is computed (fp32 results may change in
+ *    their last bits through the order of split-K merges); 0 picks the
+ *    library's choice.  The workspace size depends on them.
  *  - Row-major layouts; "cap" rows of the caches are strided by Ncap.
  *  - "[B, Hkv, Ncap, D]" for the K/V caches (k, v, k_cache, v_cache) stands for
  *    the layout rtp_layer.local_ring selects; it is exactly that shape when
@@ -53,7 +49,8 @@
  *  - Indexer (eq. (4)): q_idx = bf16(q_pre . W_q) and K_idx = bf16(k_pre . W_k),
  *    each the exact dot product rounded once to nearest-even; the score
  *    s_n = fp32(q_idx . K_idx[n]) is the exact dot product rounded once.
- *  - Top-P (eq. (5)): over softmax(s).  Bins are 1/8 logit unit wide on edges
+ *  - Top-P (eq. (5)): over softmax(s), mass p * Z (Z the total, the product
+ *    rounded once to double).  Bins are 1/8 logit unit wide on edges
  *    k/8, bin 0 = cell of the maximum score, deeper cells clamped into bin 255.
  *    Bins above the boundary bin b* are taken whole; bin b* is filled in
  *    ascending position while the mass before a token is below p * Z.
@@ -92,7 +89,9 @@ typedef struct rtp_layer {
   int64_t N;                  /* cached positions, current token(s) included; 1 <= N < 2^31 */
   int64_t Ncap;               /* row capacity of every cache (its row stride), >= N */
   const int8_t *head_mode;    /* HOST array [Hq]: 1 = retrieval head, 0 = local head */
-  float p;                    /* Top-P mass, > 0; >= 1 keeps every position */
+  double p;                   /* Top-P mass, > 0; >= 1 keeps every position.  Used as given: the
+                                 mass a boundary-bin token is compared with is p * Z rounded once
+                                 to double (Z the total softmax mass of the query's scores) */
   int32_t window;             /* local heads: window W >= 1 (positions m-W+1..m) */
   int32_t n_sink;             /* local heads: sink positions 0..n_sink-1, >= 0 */
   double rope_theta;          /* RoPE base of eq. (1), > 0 */
@@ -117,6 +116,12 @@ typedef struct rtp_layer {
                                  the rows per sequence, so k, v are [B, rtp_kv_rows(layer), D].
                                  Other values, or 1 with n_sink + window >= 2^31, are
                                  RTP_ERR_ARG. */
+  int32_t scan_tile;          /* 0 = automatic; else positions per indexer scan tile: 1024, 2048, 4096
+                                 or 8192 (other values are RTP_ERR_ARG) */
+  int32_t swa_chunk;          /* 0 = automatic; else cache rows per window workgroup, a multiple of 64
+                                 (other values are RTP_ERR_ARG) */
+  int32_t pf_qch;             /* 0 = automatic; else queries per chunked-prefill selection chunk (nq > 1),
+                                 a multiple of 16 (other values are RTP_ERR_ARG) */
 } rtp_layer;
 
 /* Number of retrieval heads Hr implied by layer->head_mode (or a negative status). */

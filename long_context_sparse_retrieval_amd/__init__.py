@@ -39,9 +39,10 @@ class _CLayer(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
         ("R", ctypes.c_int32), ("nq", ctypes.c_int32), ("N", ctypes.c_int64), ("Ncap", ctypes.c_int64),
-        ("head_mode", ctypes.POINTER(ctypes.c_int8)), ("p", ctypes.c_float), ("window", ctypes.c_int32),
+        ("head_mode", ctypes.POINTER(ctypes.c_int8)), ("p", ctypes.c_double), ("window", ctypes.c_int32),
         ("n_sink", ctypes.c_int32), ("rope_theta", ctypes.c_double), ("idx_group", ctypes.c_int32),
-        ("top_k", ctypes.c_int64), ("local_ring", ctypes.c_int32),
+        ("top_k", ctypes.c_int64), ("local_ring", ctypes.c_int32), ("scan_tile", ctypes.c_int32),
+        ("swa_chunk", ctypes.c_int32), ("pf_qch", ctypes.c_int32),
     ]
 
 
@@ -109,6 +110,9 @@ class Layer:
     idx_group: int = 1        # retrieval heads sharing one indexer-key head (1 or Hq // Hkv)
     top_k: int = 0            # 0: Top-P with mass p; > 0: fixed top-k on the histogram order
     local_ring: int = 0       # 1: all-local KV groups keep only n_sink + window rows (K/V caches [B, kv_rows, D])
+    scan_tile: int = 0        # tuning (0 = the library's choice): positions per indexer scan tile
+    swa_chunk: int = 0        # tuning: cache rows per window workgroup
+    pf_qch: int = 0           # tuning: queries per chunked-prefill selection chunk
     # the C struct of the current field values and the head_mode array it points
     # to (not an init field: dataclasses.replace gives the copy its own)
     _memo: dict = field(default_factory=dict, init=False, repr=False, compare=False)
@@ -128,7 +132,8 @@ class Layer:
 
     def _key(self) -> tuple:
         return (self.B, self.Hq, self.Hkv, self.D, self.R, self.nq, self.N, self.cap_rows, tuple(self.head_mode),
-                self.p, self.window, self.n_sink, self.rope_theta, self.idx_group, self.top_k, self.local_ring)
+                self.p, self.window, self.n_sink, self.rope_theta, self.idx_group, self.top_k, self.local_ring,
+                self.scan_tile, self.swa_chunk, self.pf_qch)
 
     def c(self) -> _CLayer:
         """The C struct of the current field values (rebuilt only when a field changed)."""
@@ -137,7 +142,8 @@ class Layer:
             hm = (ctypes.c_int8 * len(self.head_mode))(*[int(h) for h in self.head_mode])
             cl = _CLayer(self.B, self.Hq, self.Hkv, self.D, self.R, self.nq, self.N, self.cap_rows,
                          ctypes.cast(hm, ctypes.POINTER(ctypes.c_int8)), self.p, self.window, self.n_sink,
-                         self.rope_theta, self.idx_group, self.top_k, self.local_ring)
+                         self.rope_theta, self.idx_group, self.top_k, self.local_ring, self.scan_tile,
+                         self.swa_chunk, self.pf_qch)
             self._memo.clear()
             self._memo.update(key=key, c=cl, head_mode=hm)
         return self._memo["c"]

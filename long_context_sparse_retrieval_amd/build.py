@@ -17,6 +17,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librtp.so")
 SOURCES = ["api.hip", "cache_kernels.hip", "append_kernels.hip", "topp_kernels.hip", "attn_kernels.hip",
            "prefill_kernels.hip", "flash_prefill.hip", "cluster_kernels.hip"]
+PROBE_SRC = "read_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libreadprobe.so")
 ARCH = "gfx950"
 
 COMMON = [
@@ -61,6 +63,14 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # the streaming-read probe (the benchmark's read ceiling), a library of its own
+    probe_obj = compile_one(PROBE_SRC)
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, probe_obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -29,7 +29,7 @@ int validate_layer(const rtp_layer *L) {
   if (L->D != kD || L->R != kR) return RTP_ERR_SHAPE;
   if (L->B < 1 || L->Hq < 1 || L->Hkv < 1 || L->Hq > kMaxHq || L->Hq % L->Hkv != 0) return RTP_ERR_SHAPE;
   if (L->nq < 1 || L->N < L->nq || L->N > L->Ncap || L->N >= (1ll << 31)) return RTP_ERR_SHAPE;
-  if (!(L->p > 0.0f) || L->window < 1 || L->n_sink < 0 || !(L->rope_theta > 0.0)) return RTP_ERR_ARG;
+  if (!(L->p > 0.0) || L->window < 1 || L->n_sink < 0 || !(L->rope_theta > 0.0)) return RTP_ERR_ARG;
   for (int h = 0; h < L->Hq; ++h)
     if (L->head_mode[h] != 0 && L->head_mode[h] != 1) return RTP_ERR_ARG;
   const int G = L->Hq / L->Hkv;
@@ -37,6 +37,10 @@ int validate_layer(const rtp_layer *L) {
   if (L->top_k < 0) return RTP_ERR_ARG;
   if (L->local_ring != 0 && L->local_ring != 1) return RTP_ERR_ARG;
   if (L->local_ring && (int64_t)L->n_sink + L->window >= (1ll << 31)) return RTP_ERR_ARG;   // ring rows < 2^31
+  if (L->scan_tile != 0 && L->scan_tile != 1024 && L->scan_tile != 2048 && L->scan_tile != 4096 &&
+      L->scan_tile != 8192)
+    return RTP_ERR_ARG;
+  if (L->swa_chunk < 0 || L->swa_chunk % 64 != 0 || L->pf_qch < 0 || L->pf_qch % 16 != 0) return RTP_ERR_ARG;
   if (L->idx_group > 1)        // shared indexer keys: retrieval heads come in whole KV groups
     for (int kv = 0; kv < L->Hkv; ++kv)
       for (int h = kv * G + 1; h < (kv + 1) * G; ++h)
@@ -44,11 +48,8 @@ int validate_layer(const rtp_layer *L) {
   return RTP_OK;
 }
 
-int pick_tile(long long N) {
-  if (const char *env = getenv("RTP_SCAN_TILE")) {
-    const int t = atoi(env);
-    if (t == 1024 || t == 2048 || t == 4096 || t == 8192) return t;
-  }
+int pick_tile(long long N, int forced) {
+  if (forced) return forced;
   // The largest tile (up to 8192 positions) that still gives two tiles per
   // query.  Larger tiles shorten the finish (fewer tile summaries and prefix
   // entries per query) and phase A does not mind: measured at 128K x 4
@@ -112,7 +113,7 @@ int make_geo(const rtp_layer *L, bool dense, Geo &g) {
     g.rows_b = (long long)(g.Hkv - nring) * g.Ncap + (long long)nring * ((long long)g.n_sink + g.window);
   }
   g.units = g.B * g.Hr * g.nq;
-  g.T = pick_tile(g.N);
+  g.T = pick_tile(g.N, L->scan_tile);
   g.nt = (int)((g.N + g.T - 1) / g.T);
   {
     // about 512 finishing workgroups, each over at most 32K positions (their
@@ -136,10 +137,7 @@ int make_geo(const rtp_layer *L, bool dense, Geo &g) {
       const long long per = (long long)g.swa_units * g.swa_hb * Lrows / 2048;
       chunk = per < 1024 ? 1024 : (per + 63) / 64 * 64;
     }
-    if (const char *env = getenv("RTP_SWA_CHUNK")) {
-      const long long c = atoll(env);
-      if (c >= 64 && c % 64 == 0) chunk = c;
-    }
+    if (L->swa_chunk) chunk = L->swa_chunk;
     g.swa_chunk = (int)chunk;
     g.swa_nch = (int)((Lrows + chunk - 1) / chunk);
   }
@@ -190,10 +188,7 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
     const long long per_q = (long long)g.B * g.Hr * g.N * 4;      // bytes of positions per query index
     long long qch = (8ll << 30) / per_q;                            // up to 8 GiB of positions per chunk
     qch = qch / 16 * 16;
-    if (const char *env = getenv("RTP_PF_QCH")) {          // tuning / test override
-      const long long v = atoll(env);
-      if (v >= 16 && v % 16 == 0) qch = v;
-    }
+    if (L->pf_qch) qch = L->pf_qch;
     if (qch < 16) qch = 16;
     if (qch > g.nq) qch = g.nq;
     g.pf_qch = (int)qch;

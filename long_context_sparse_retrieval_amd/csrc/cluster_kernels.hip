@@ -272,13 +272,13 @@ __global__ __launch_bounds__(kWG) void cl_select_kernel(Geo g, ClGeo cg, const r
   const double Wb = (double)sm.hist[tid] * 0x1p-23 * exp(-(double)tid * 0.125);
   double Z;
   const double excl = block_excl_scan<double>(Wb, Z, sm.red_d);
-  const double need = (double)g.p * Z;
+  const double need = g.p * Z;
   int bstar = block_min<int>(excl + Wb >= need ? tid : kBins, sm.red_i);
   if (bstar >= kBins) bstar = kBins - 1;
   sm.wcum[tid] = excl;
   __syncthreads();
   const double before = sm.wcum[bstar];
-  const bool all = g.p >= 1.0f || bstar >= kBins - 1;
+  const bool all = g.p >= 1.0 || bstar >= kBins - 1;
   const double r_u = (need - before) * 0x1p23 * exp((double)bstar * 0.125);
   // ordered fill of bin b*: its clusters in ascending index while the mass before them is below the residual
   unsigned long long wtot;

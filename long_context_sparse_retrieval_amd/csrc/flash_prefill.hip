@@ -70,8 +70,9 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   const int tile = ntiles - 1 - rank;
   const int rest = y % inner;
   const int quad = rest % fq.n, b = rest / fq.n;
-  const int h = fq.head[4 * quad + wv];                        // kNoHead: this wave only helps staging
+  const bool has_head = wv < fq.nh[quad];                     // false: this wave only helps staging
   const int h0 = fq.head[4 * quad];
+  const int h = has_head ? fq.head[4 * quad + wv] : h0;
   const bool dense = fq.dense[quad] != 0;
   const int kvg = h0 / g.G;
   const int i0 = tile * kFq;
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   {
     const int qi = i0 + (qn < nqt ? qn : nqt - 1);
     const long long mq = g.N - g.nq + qi;
-    const rtp_bf16 *qr = q_pre + (((size_t)b * g.Hq + (h != kNoHead ? h : h0)) * g.nq + qi) * kD;
+    const rtp_bf16 *qr = q_pre + (((size_t)b * g.Hq + h) * g.nq + qi) * kD;
 #pragma unroll
     for (int c = 0; c < kD / 32; ++c) {
       const int d0 = 32 * c + 8 * grp;
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     const long long kb = block_of(x);
     const int buf = (int)(x % kBufs);
     RTP_FLASH_LOAD(block_of(x + 1 < nblk ? x + 1 : x));       // clamped: the last block reloads itself
-    if (h != kNoHead) {                                        // wave-uniform
+    if (has_head) {                                            // wave-uniform
     // S^T for the block's four 16-key subtiles
     f32x4_t s[kFk / 16];
 #pragma unroll
@@ -272,14 +273,14 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[j], bv, o[t], 0, 0, 0);
       }
     }
-    }                                                          // h != kNoHead
+    }                                                          // has_head
     if (kBufs == 1) __syncthreads();                           // every wave is done with the block
     if (x + 1 < nblk) RTP_FLASH_STORE((int)((x + 1) % kBufs));
     __syncthreads();
   }
 #undef RTP_FLASH_LOAD
 #undef RTP_FLASH_STORE
-  if (h == kNoHead) return;
+  if (!has_head) return;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int qe = 4 * grp + e;
@@ -308,11 +309,11 @@ int make_flash_quads(const Geo &g, bool all_dense, FlashQuads fq[2]) {
         if (hm != mode) continue;
         if (cnt % 4 == 0) {
           if (f.n >= kMaxQuads) return RTP_ERR_UNSUPPORTED;
-          for (int w = 0; w < 4; ++w) f.head[4 * f.n + w] = kNoHead;
           f.dense[f.n] = (uint8_t)mode;
           ++f.n;
         }
         f.head[4 * (f.n - 1) + cnt % 4] = (uint8_t)h;
+        f.nh[f.n - 1] = (uint8_t)(cnt % 4 + 1);
         ++cnt;
       }
     }

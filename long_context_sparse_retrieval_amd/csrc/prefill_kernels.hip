@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     }
     const double Z = __shfl(incl, 63);
     double e = incl - loc;
-    const double need = g.topk ? (double)g.topk : (double)g.p * Z;     // top-k: Z counts positions
+    const double need = g.topk ? (double)g.topk : g.p * Z;     // top-k: Z counts positions
     int cand = kBins;
     double before_c = 0.0;
 #pragma unroll
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     const double before = __shfl(before_c, bstar / 4);
     // the query's bins are relative to its own maximum, so for top-k the
     // clamp bin is an ordinary boundary
-    const int all = (g.topk ? need >= Z : (g.p >= 1.0f || bstar >= kBins - 1)) ? 1 : 0;
+    const int all = (g.topk ? need >= Z : (g.p >= 1.0 || bstar >= kBins - 1)) ? 1 : 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int j = 4 * lane + k;

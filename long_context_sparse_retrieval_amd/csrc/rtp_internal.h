@@ -60,7 +60,7 @@ struct Geo {
   int ig;               // retrieval heads per indexer-key head (1 or G)
   int Hi;               // indexer-key heads = Hr / ig
   long long N, Ncap;
-  float p;
+  double p;             // Top-P mass (the caller's double, never narrowed)
   long long topk;       // 0: Top-P with mass p; > 0: fixed top-k on the histogram order
   int window, n_sink;
   double theta;
@@ -370,10 +370,10 @@ int cluster_tile();
 // Prefill attention on the matrix cores: workgroups take "quads" of up to four
 // q heads of one KV group and one mode (dense causal, or window + sinks).
 constexpr int kMaxQuads = kMaxHq;
-constexpr uint8_t kNoHead = 255;
 struct FlashQuads {
   int n;
-  uint8_t head[4 * kMaxQuads];   // kNoHead pads a quad
+  uint8_t head[4 * kMaxQuads];   // q heads of quad j in head[4j .. 4j + nh[j] - 1]
+  uint8_t nh[kMaxQuads];         // heads in quad j (1..4); the other waves only help staging
   uint8_t dense[kMaxQuads];      // 1: every earlier position; 0: window + sinks
 };
 int make_flash_quads(const Geo &g, bool all_dense, FlashQuads fq[2]);

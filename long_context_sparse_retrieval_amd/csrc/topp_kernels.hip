@@ -366,7 +366,7 @@ __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, 
   const double excl = block_excl_scan<double>(Wj, Z, sm.red_d);
   // Top-P needs the mass p Z; top-k needs k tokens (every weight is exactly 1,
   // so Z is the number of positions and every sum here is an exact integer)
-  const double need = g.topk ? (double)g.topk : (double)g.p * Z;
+  const double need = g.topk ? (double)g.topk : g.p * Z;
   int bstar = block_min<int>(excl + Wj >= need ? j : kBins, sm.red_i);
   if (bstar >= kBins) bstar = kBins - 1;
   sm.wcum[j] = excl;                      // mass above bin j
@@ -376,7 +376,7 @@ __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, 
   // Top-P: p >= 1, or the boundary in the clamp bin (whose in-cell masses
   // have no common scale; its mass is below e^-31.75 of the top cell, so
   // everything is taken).  Top-k: k covers every position.
-  all_out = (g.topk ? need >= Z : (g.p >= 1.0f || bstar >= kBins - 1)) ? 1 : 0;
+  all_out = (g.topk ? need >= Z : (g.p >= 1.0 || bstar >= kBins - 1)) ? 1 : 0;
   r_u_out = (need - before) * 0x1p23 * bin_scale(g, (double)bstar * 0.125);
   bstar_out = bstar;
 }

@@ -25,9 +25,11 @@ Readings of the pages (where they are silent the plainest reading is taken):
   * Top-P acts on softmax(s) (no temperature).  Histogram: 256 bins of width
     1/8 on the logit, edges on the multiples of 1/8, bin 0 holding the cell of
     the maximum logit, everything 255 or more cells below it clamped into bin
-    255.  b* = first bin (from the top) whose cumulative mass reaches p*Z;
-    bins above b* are taken whole, bin b* is filled in ascending position
-    while the mass accumulated before a token is below p*Z.  p >= 1 takes all.
+    255.  b* = first bin (from the top) whose cumulative mass reaches p*Z
+    (the product rounded once to double); bins above b* are taken whole, bin
+    b* is filled in ascending position while the mass accumulated before a
+    token is below p*Z.  p >= 1 takes all, and so does a boundary in the clamp
+    bin 255, whose tokens have no common weight scale to fill it by.
   * Fixed top-k (the budget-by-count counterpart of Top-P that FASB section
     2.3 / Table 1 compares against): the first k positions in the order
     (bin ascending, position ascending) of the same histogram; it differs
@@ -237,6 +239,14 @@ def topp_select(logits, p: float) -> dict:
     bstar = int(np.searchsorted(cum, need, side="left"))      # first bin with cum >= need
     bstar = min(bstar, N_BINS - 1)
     before_bin = float(cum[bstar - 1]) if bstar > 0 else 0.0
+    if bstar == N_BINS - 1:
+        # Boundary in the clamp bin: its tokens lie 255 or more cells below the
+        # top, so the bin carries no common weight scale to fill it by; the
+        # reading takes it whole, i.e. every position.  (This needs a clamp
+        # mass above (1 - p) Z, so p within N e^-31.75 of 1.)
+        margin = min(abs(need - before_bin), abs(float(cum[bstar]) - need)) / Z
+        return dict(sel=np.arange(n, dtype=np.int64), bstar=N_BINS, Z=Z, need=need, margin=margin, bins=bins,
+                    weights=w, clamp_all=True)
     sure = np.nonzero(bins < bstar)[0]
     cand = np.nonzero(bins == bstar)[0]                        # ascending positions
     before_tok = before_bin + np.concatenate(([0.0], np.cumsum(w[cand])[:-1]))

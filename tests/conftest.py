@@ -16,3 +16,15 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def root():
     return ROOT
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """One line per test file: how many Top-P sets matched the oracle exactly
+    and how many were accepted under the bin-edge or the mass-margin rule."""
+    parity = sys.modules.get("parity")
+    stats = getattr(parity, "SET_STATS", None)
+    if not stats:
+        return
+    for f, c in sorted(stats.items()):
+        terminalreporter.write_line(f"Top-P sets {f}: {c['exact']} exact, {c['edge']} edge-tolerated, "
+                                    f"{c['margin']} margin-tolerated")

@@ -66,12 +66,32 @@ def test_workspace_sizing_monotone():
     (dict(nq=0), -2), (dict(N=1 << 31, Ncap=1 << 31), -2), (dict(p=0.0), -1), (dict(p=float("nan")), -1),
     (dict(window=0), -1), (dict(n_sink=-1), -1), (dict(head_mode=[2, 0, 0, 0, 0, 0, 0, 0]), -1),
     (dict(rope_theta=0.0), -1), (dict(top_k=-1), -1), (dict(idx_group=3), -1), (dict(idx_group=-1), -1),
-    (dict(local_ring=2), -1), (dict(local_ring=-1), -1),
+    (dict(local_ring=2), -1), (dict(local_ring=-1), -1), (dict(scan_tile=3000), -1), (dict(scan_tile=512), -1),
+    (dict(swa_chunk=100), -1), (dict(swa_chunk=-64), -1), (dict(pf_qch=24), -1), (dict(pf_qch=-16), -1),
+    (dict(Hq=512, Hkv=2, head_mode=[0] * 512), -2),
 ])
 def test_layer_validation(kw, code):
     lay = _layer(**kw)
     assert rtp.load().rtp_num_retrieval(ctypes.byref(lay.c())) == code
     assert rtp.load().rtp_workspace_bytes(ctypes.byref(lay.c())) == 0
+
+
+@needs_lib
+def test_tuning_fields_change_the_split_not_the_validity():
+    base = rtp.workspace_bytes(_layer(N=40000))
+    for kw in (dict(scan_tile=1024), dict(scan_tile=8192), dict(swa_chunk=64), dict(swa_chunk=1024)):
+        assert rtp.workspace_bytes(_layer(N=40000, **kw)) > 0
+    # smaller scan tiles need more tile summaries
+    assert rtp.workspace_bytes(_layer(N=40000, scan_tile=1024)) > rtp.workspace_bytes(_layer(N=40000, scan_tile=8192))
+    assert base > 0
+
+
+def test_p_crosses_the_abi_as_double():
+    """p is not narrowed: the struct field is a C double."""
+    fields = dict(rtp._CLayer._fields_)
+    assert fields["p"] is ctypes.c_double
+    lay = _layer(p=0.1)
+    assert lay.c().p == 0.1
 
 
 @needs_lib

@@ -199,6 +199,37 @@ def test_topp_uniform_takes_ceil_pN(N, p):
     assert len(O.topp_select(s, p)["sel"]) == math.ceil(p * N)
 
 
+@pytest.mark.parametrize("N", [100, 1000])
+@pytest.mark.parametrize("p", [0.1, 0.3, 0.99])
+def test_topp_uniform_decimal_p(N, p):
+    """p * N rounded once to double is an integer for these decimal p, so the
+    count is the decimal ceil(pN) and the positions are the first ones."""
+    assert p * N == round(p * N)
+    t = O.topp_select(np.full(N, -0.4375, dtype=np.float32), p)
+    assert list(t["sel"]) == list(range(round(p * N)))
+
+
+def test_topp_boundary_in_clamp_bin_takes_all():
+    """Hand-built case: one token at 0 and 1000 tokens 255 cells (31.875) below
+    it, all in the clamp bin 255.  Z = 1 + 1000 e^-31.875 = 1 + 1.43e-11, so
+    with p = 1 - 1e-13 the needed mass p Z exceeds bins 0..254 (mass 1) and the
+    boundary falls in the clamp bin, which is taken whole: every position.
+    At p = 0.9 the top token alone reaches p Z."""
+    s = np.full(1001, -31.875, dtype=np.float32)
+    s[0] = 0.0
+    t = O.topp_select(s, 1.0 - 1e-13)
+    assert t["bins"][0] == 0 and np.all(t["bins"][1:] == 255)
+    assert abs(t["Z"] - (1.0 + 1000 * math.exp(-31.875))) < 1e-15
+    assert t["need"] > 1.0
+    assert len(t["sel"]) == 1001 and t.get("clamp_all")
+    assert list(O.topp_select(s, 0.9)["sel"]) == [0]
+    # cells deeper than 255 below the top clamp into the same bin
+    s2 = s.copy()
+    s2[500:] = -40.0
+    t2 = O.topp_select(s2, 1.0 - 1e-13)
+    assert np.all(t2["bins"][1:] == 255) and len(t2["sel"]) == 1001
+
+
 def test_topp_uniform_integer_pN():
     assert len(O.topp_select(np.zeros(10, np.float32), 0.9)["sel"]) == 9
     assert list(O.topp_select(np.zeros(10, np.float32), 0.9)["sel"]) == list(range(9))
