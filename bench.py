@@ -42,6 +42,7 @@ TOPK_BENCH = 2048          # fixed budget of the top-k variant line (about the d
 CSRC = os.path.join(ROOT, "long_context_sparse_retrieval_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "phase_a_kernel.qwen3-32b-layer-1m-b1.traffic.json")
 CPU_SAMPLE_SECONDS = 12.0
+TUNING = {}                # rtp_layer tuning fields from the command line (sweeps); empty = the library's choice
 
 
 def log(*a):
@@ -116,7 +117,8 @@ class Case:
         log(f"[bench] cfg{cfg} {spec.name}: drew inputs in {time.time() - t0:.1f}s")
         self.layer = rtp.Layer(B=spec.B, Hq=spec.Hq, Hkv=spec.Hkv, N=spec.N,
                                head_mode=[int(h) for h in spec.head_mode()], p=spec.p, window=spec.window,
-                               n_sink=spec.n_sink, rope_theta=spec.rope_theta, idx_group=spec.idx_group)
+                               n_sink=spec.n_sink, rope_theta=spec.rope_theta, idx_group=spec.idx_group,
+                               **TUNING)
         t0 = time.time()
         self.q = up(wl.q_pre)
         self.w_q = up(wl.w_q)
@@ -242,42 +244,46 @@ def copy_ceiling_gbps() -> float:
 
 
 def read_ceiling() -> dict:
-    """The box's streaming-read rate: libreadprobe.so's read kernel over a 2 GiB
-    buffer (read once per pass, nothing written), swept over grid sizes and
-    loads in flight per thread; the best configuration is the ceiling the
-    bandwidth-bound kernels are compared with."""
+    """The box's streaming-read rate: libreadprobe.so's read kernels over a 2 GiB
+    buffer (read once per pass, nothing written), swept over two access
+    patterns (grid-stride; one contiguous chunk per workgroup, as the indexer
+    scan reads), plain or non-temporal loads, grid sizes and loads in flight
+    per thread; the best configuration is the ceiling the bandwidth-bound
+    kernels are compared with."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "long_context_sparse_retrieval_amd", "libreadprobe.so"))
     lib.readprobe_stream.restype = ctypes.c_int
     lib.readprobe_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
-                                     ctypes.c_void_p]
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     nbytes = 2 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
+    configs = [(0, b, u, nt) for b in (2048, 8192) for u in (8, 16) for nt in (0, 1)]
+    configs += [(1, b, u, nt) for b in (1024, 2048, 4096) for u in (8, 16) for nt in (0, 1)]
+    configs += [(2, b, u, nt) for b in (1024, 2048) for u in (4, 8) for nt in (0, 1)]
     best, sweep = None, {}
-    for blocks in (1024, 2048, 4096, 8192):
-        for unroll in (4, 8, 16):
-            def one():
-                st = lib.readprobe_stream(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, unroll, stream)
-                if st != 0:
-                    raise RuntimeError(f"readprobe_stream: status {st}")
-            for _ in range(2):
-                one()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record()
-            for _ in range(5):
-                one()
-            e1.record()
-            torch.cuda.synchronize()
-            gbps = nbytes * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-            sweep[f"{blocks}x{unroll}"] = round(gbps, 1)
-            if best is None or gbps > best[0]:
-                best = (gbps, blocks, unroll)
+    for chunked, blocks, unroll, nt in configs:
+        def one():
+            st = lib.readprobe_stream(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, unroll, chunked, nt, stream)
+            if st != 0:
+                raise RuntimeError(f"readprobe_stream: status {st}")
+        for _ in range(2):
+            one()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            one()
+        e1.record()
+        torch.cuda.synchronize()
+        gbps = nbytes * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        key = f"{('stride', 'chunk', 'rows32')[chunked]}-{blocks}x{unroll}{'-nt' if nt else ''}"
+        sweep[key] = round(gbps, 1)
+        if best is None or gbps > best[0]:
+            best = (gbps, key)
     del buf
-    return {"GBps": round(best[0], 1), "blocks": best[1], "loads_in_flight_per_thread": best[2],
-            "bytes": nbytes, "sweep": sweep}
+    return {"GBps": round(best[0], 1), "config": best[1], "bytes": nbytes, "sweep": sweep}
 
 
 def calibration_copy(n_bytes: int = 1 << 30, reps: int = 3) -> None:
@@ -625,7 +631,10 @@ def main():
                     help="measure only the streaming-read and copy ceilings and print them")
     ap.add_argument("--chunked-prefill", action="store_true",
                     help="time only the 128K chunked-prefill call (4 heads x 4096 queries) and print its line")
+    ap.add_argument("--scan-tile", type=int, default=0, help="tuning sweep: rtp_layer.scan_tile")
+    ap.add_argument("--swa-chunk", type=int, default=0, help="tuning sweep: rtp_layer.swa_chunk")
     args = ap.parse_args()
+    TUNING.update({k: v for k, v in (("scan_tile", args.scan_tile), ("swa_chunk", args.swa_chunk)) if v})
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -646,7 +655,7 @@ def main():
         copy_gbps = copy_ceiling_gbps()
         rc = read_ceiling()
     log(f"[bench] device copy ceiling {copy_gbps:.0f} GB/s, streaming read ceiling {rc['GBps']:.0f} GB/s "
-        f"({rc['blocks']} workgroups x {rc['loads_in_flight_per_thread']} loads in flight)")
+        f"({rc['config']})")
     if args.read_ceiling:
         print(json.dumps({"read_ceiling": rc, "copy_ceiling_GBps": round(copy_gbps, 1)}), flush=True)
         return
@@ -756,9 +765,9 @@ def main():
                      "frac": round(s["pa_gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel_us": round(s["pa_us"], 2), "algorithmic_bytes_per_launch": s["pa_bytes"]},
         "copy_ceiling_GBps": round(copy_gbps, 1),
-        "read_ceiling": {"GBps": rc["GBps"], "what": "in-tree streaming-read kernel (libreadprobe.so) over 2 GiB, "
-                                                     "best of a grid / loads-in-flight sweep",
-                         "blocks": rc["blocks"], "loads_in_flight_per_thread": rc["loads_in_flight_per_thread"],
+        "read_ceiling": {"GBps": rc["GBps"], "what": "in-tree streaming-read kernels (libreadprobe.so) over 2 GiB, "
+                                                     "best of an access-pattern / grid / loads-in-flight sweep",
+                         "config": rc["config"],
                          "phase_a_frac_of_read_ceiling": round(s["pa_gbps"] / rc["GBps"], 4),
                          "step_frac_of_read_ceiling": round(s["gbps"] / rc["GBps"], 4)},
         "step_us_percentiles": s["pct"],

@@ -433,3 +433,4 @@ def decode_step(layer: Layer, q_pre, w_q, k_idx, k, v, ws, out=None, idx=None, c
     _check(load().rtp_decode_step(ctypes.byref(layer.c()), q, w, ki, kp, vp, op, ip, cp, cap, ws.data_ptr(),
                                   ws.numel(), ev, _stream()), "rtp_decode_step")
     return out
+

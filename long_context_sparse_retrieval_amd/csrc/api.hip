@@ -16,6 +16,7 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
   Geo g;
   size_t ws_bytes;
+  size_t header_bytes;      // the persistent state at the workspace's start (left zero by every call)
 };
 
 int count_retrieval(const rtp_layer *L) {
@@ -48,14 +49,20 @@ int validate_layer(const rtp_layer *L) {
   return RTP_OK;
 }
 
+// Workgroups the GPU holds at once for the decode kernels: 256 CUs x 4
+// (each kernel is built for 128 VGPRs and at most 40 KB of LDS).
+constexpr long long kSlots = 1024;
+
 int pick_tile(long long N, int forced) {
   if (forced) return forced;
-  // The largest tile (up to 8192 positions) that still gives two tiles per
-  // query.  Larger tiles shorten the finish (fewer tile summaries and prefix
-  // entries per query) and phase A does not mind: measured at 128K x 4
-  // queries x 4 sequences, 1024 -> 8192 took the step from 66.7 to 59.3 us.
+  // The largest tile that still gives four tiles per query, up to 8192
+  // positions below 2^19 and 4096 from there on: long contexts have tiles
+  // enough to fill the GPU several times over, and the 8192-position build
+  // keeps 32 scores per thread in registers where the 4096 one keeps 16
+  // (measured at 1M: phase A 107 us against 113 us).
+  const int tmax = N < (1ll << 19) ? 8192 : 4096;
   int T = 1024;
-  while (T < 8192 && 4 * T <= N) T *= 2;
+  while (T < tmax && 4 * T <= N) T *= 2;
   return T;
 }
 
@@ -116,11 +123,11 @@ int make_geo(const rtp_layer *L, bool dense, Geo &g) {
   g.T = pick_tile(g.N, L->scan_tile);
   g.nt = (int)((g.N + g.T - 1) / g.T);
   {
-    // about 512 finishing workgroups, each over at most 32K positions (their
-    // codes are staged in LDS); more workgroups only add contention
+    // about 512 selection workgroups, each over at most 16K positions (their
+    // codes are staged in LDS)
     long long per = (long long)g.units * g.N / 512;
     int tpw = 1;
-    while (tpw * 2 <= 32768 / g.T && tpw * 2 <= 32 && (long long)tpw * 2 * g.T <= per) tpw *= 2;
+    while (tpw * 2 <= 16384 / g.T && (long long)tpw * 2 * g.T <= per) tpw *= 2;
     g.fin_tpw = tpw;
     g.fin_nwg = (g.nt + tpw - 1) / tpw;
   }
@@ -131,6 +138,13 @@ int make_geo(const rtp_layer *L, bool dense, Geo &g) {
     const long long ns = g.n_sink < lo ? g.n_sink : lo;
     const long long Lrows = ns + (g.N - lo);
     long long chunk = (Lrows + 15) / 16;
+    // when the scan tiles leave room in one round of workgroups, smaller
+    // window chunks fill it (more rows in flight at once; measured at 128K)
+    const long long n_scan = (long long)g.units * g.nt, per_chunk = (long long)g.B * g.nlg * g.nq * g.swa_hb;
+    if (!dense && per_chunk > 0 && n_scan < kSlots) {
+      const long long nch = (kSlots - n_scan) / per_chunk;
+      if (nch > 16) chunk = (Lrows + nch - 1) / nch;
+    }
     chunk = (chunk + 31) / 32 * 32;
     if (chunk < 64) chunk = 64;
     if (dense) {
@@ -173,6 +187,7 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
   off = align_up(off + swa_ctrs * 4);
   // transient regions of this call
   const size_t o_qprep = off;
+  out->header_bytes = off;
   off = align_up(off + units * sizeof(QPrep));
   const size_t o_tsum = off;
   off = align_up(off + units * nt * sizeof(TileSum));
@@ -180,6 +195,7 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
   off = align_up(off + units * (nt > (size_t)kSpChunks ? nt : (size_t)kSpChunks) * sizeof(Partial));  // >= fin_nwg
   const size_t o_swa = off;
   off = align_up(off + (size_t)g.swa_units * g.swa_hb * g.swa_nch * kSwaHeads * sizeof(Partial));
+
   // the codes of the decode path and, for nq > 1, the chunked prefill's
   // selected positions (never used by the same call) share one region
   g.pf_qch = 0;
@@ -373,7 +389,7 @@ int rtp_topp_select(const rtp_layer *layer, const float *logits, int32_t *idx, i
   hipStream_t s = as_stream(stream);
   st = launch_phase_a(p.g, nullptr, nullptr, nullptr, logits, nullptr, nullptr, nullptr, true, false, s);
   if (st != RTP_OK) return st;
-  return launch_finish(p.g, nullptr, nullptr, nullptr, logits, nullptr, nullptr, nullptr, cap > 0 ? idx : nullptr,
+  return launch_finish(p.g, nullptr, logits, nullptr, nullptr, nullptr, cap > 0 ? idx : nullptr,
                        count, cap, s);
 }
 
@@ -521,13 +537,13 @@ int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf1
     }
     return launch_phase_a(p.g, q_pre, nullptr, nullptr, nullptr, k, v, out, false, true, s);
   }
-  // with retrieval heads the finish kernel follows; it also merges the local
-  // heads' window chunks, which takes that merge off phase A's critical path
+  // with retrieval heads the selection launch follows; it also merges the
+  // local heads' window chunks, which takes that merge off the scan launch
   const bool defer = p.g.units > 0 && p.g.swa_units > 0;
   st = launch_phase_a(p.g, q_pre, w_q, k_idx, nullptr, k, v, out, true, true, s, defer);
   if (st != RTP_OK) return st;
   if (phase_event && hipEventRecord(reinterpret_cast<hipEvent_t>(phase_event), s) != hipSuccess) return RTP_ERR_HIP;
-  return launch_finish(p.g, q_pre, w_q, k_idx, nullptr, k, v, out, idx_opt, count_opt, idx_opt ? cap : 0, s, defer);
+  return launch_finish(p.g, k_idx, nullptr, k, v, out, idx_opt, count_opt, idx_opt ? cap : 0, s, defer);
 }
 
 }  // extern "C"

@@ -190,13 +190,17 @@ __device__ __forceinline__ void attend_rows(const float *q_s, const int *rows, i
                                             const rtp_bf16 *__restrict__ kb, const rtp_bf16 *__restrict__ vb,
                                             Partial *dst, AttnShared *sm) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, grp = lane >> 4, sub = lane & 15;
+  // scores in base 2 (the query carries log2(e)); the reference maximum m
+  // moves only when a score passes it by more than 8 (any reference gives the
+  // same o / l, this one keeps every weight below 2^8), for the whole wave at
+  // once, so a row costs one exponential and one FMA per channel
   float q[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = q_s[sub * 8 + i];
-  float m = -INFINITY, l = 0.f, o[8];
+  for (int i = 0; i < 8; ++i) q[i] = q_s[sub * 8 + i] * 1.4426950408889634f;
+  float m = -1.0e30f, l = 0.f, o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
-  constexpr int U = 4;
+  constexpr int U = 6;             // rows in flight per 16-lane group: 96 per workgroup per round
   for (int base = 0; base < cnt; base += 16 * U) {
     uint4 kr[U], vr[U];
     bool ok[U];
@@ -208,31 +212,40 @@ __device__ __forceinline__ void attend_rows(const float *q_s, const int *rows, i
       kr[u] = make_uint4(0, 0, 0, 0);
       vr[u] = make_uint4(0, 0, 0, 0);
       if (ok[u]) {
-        kr[u] = *reinterpret_cast<const uint4 *>(kb + n * kD + sub * 8);
-        vr[u] = *reinterpret_cast<const uint4 *>(vb + n * kD + sub * 8);
+        kr[u] = ld_stream(kb + n * kD + sub * 8);
+        vr[u] = ld_stream(vb + n * kD + sub * 8);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
       const uint32_t vw[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
-      float d = 0.f;
+      float d = q[0] * bf_lo(kw[0]);
+      d = fmaf(q[1], bf_hi(kw[0]), d);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d += q[2 * i] * bf_lo(kw[i]) + q[2 * i + 1] * bf_hi(kw[i]);
+      for (int i = 1; i < 4; ++i) d = fmaf(q[2 * i + 1], bf_hi(kw[i]), fmaf(q[2 * i], bf_lo(kw[i]), d));
       d = row16_sum(d);
-      if (ok[u]) {
-        const float mn = fmaxf(m, d);
-        const float a = __expf(m - mn), pw = __expf(d - mn);
-        l = l * a + pw;
+      if (!ok[u]) continue;
+      const bool bump = d > m + 8.f;
+      if (__builtin_amdgcn_ballot_w64(bump)) {
+        const float mn = bump ? d : m;
+        const float a = __builtin_amdgcn_exp2f(m - mn);
+        l *= a;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          o[2 * i] = o[2 * i] * a + pw * bf_lo(vw[i]);
-          o[2 * i + 1] = o[2 * i + 1] * a + pw * bf_hi(vw[i]);
-        }
+        for (int i = 0; i < 8; ++i) o[i] *= a;
         m = mn;
+      }
+      const float pw = __builtin_amdgcn_exp2f(d - m);
+      l += pw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[2 * i] = fmaf(pw, bf_lo(vw[i]), o[2 * i]);
+        o[2 * i + 1] = fmaf(pw, bf_hi(vw[i]), o[2 * i + 1]);
       }
     }
   }
+  // back to natural-log units for the merges (an empty state has m = -inf)
+  m = l > 0.f ? m * 0.6931471805599453f : -INFINITY;
   // merge the 4 row groups of the wave
 #pragma unroll
   for (int off = 16; off < 64; off <<= 1) {

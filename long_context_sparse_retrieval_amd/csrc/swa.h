@@ -19,6 +19,10 @@
 namespace rtp {
 
 constexpr float kInvSqrtD = 0.08838834764831845f;   // 1 / sqrt(128)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kScoreFloor = -1.0e30f;               // initial reference maximum (base 2)
+constexpr float kSlack = 8.0f;                        // base-2 headroom before the reference moves
 
 struct SwaShared {
   float q[kSwaHeads][kD];
@@ -61,7 +65,7 @@ __host__ __device__ __forceinline__ long long swa_blocks(const Geo &g) {
 // One SWA workgroup; x = its index among the SWA workgroups of the launch.
 // RING: the block's KV group is stored as a ring (rows wrap); RING_LAYOUT:
 // the layer has ring groups (group bases follow the ring layout).
-// defer: publish the chunk states only (a later kernel merges them).
+// defer: publish the chunk states only (a later launch merges them).
 template <bool RING, bool RING_LAYOUT>
 __device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const rtp_bf16 *__restrict__ q_pre,
                                                const rtp_bf16 *__restrict__ kc, const rtp_bf16 *__restrict__ vc,
@@ -94,7 +98,7 @@ __device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const 
   }
 
   // request the first rows before preparing the queries
-  constexpr int U = 4;
+  constexpr int U = 3;
   uint4 kr[U], vr[U];
   bool ok[U];
 #pragma unroll
@@ -104,8 +108,8 @@ __device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const 
     kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
     if (ok[u]) {
       const size_t n = (size_t)swa_row<RING>(ri, ns, wbase, wwrap, g.window);
-      kr[u] = *reinterpret_cast<const uint4 *>(kb + n * kD + sub * 8);
-      vr[u] = *reinterpret_cast<const uint4 *>(vb + n * kD + sub * 8);
+      kr[u] = ld_stream(kb + n * kD + sub * 8);
+      vr[u] = ld_stream(vb + n * kD + sub * 8);
     }
   }
   // every head's query in one round: thread (hh, t) loads and rotates channel
@@ -125,20 +129,25 @@ __device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const 
     if (pt == 0) sm.heads[hh_mine] = h_mine;
   }
   __syncthreads();
+  // scores in base 2: the query carries log2(e), so a weight is one v_exp
   float q[kSwaHeads][8];
 #pragma unroll
   for (int hh = 0; hh < kSwaHeads; ++hh)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[hh][e] = sm.q[hh][sub * 8 + e];
+    for (int e = 0; e < 8; ++e) q[hh][e] = sm.q[hh][sub * 8 + e] * kLog2e;
+  // running state per head: reference maximum (base 2; starts at a finite
+  // floor so an empty lane group needs no special case), sum, output
   float mm[kSwaHeads], ll[kSwaHeads], oo[kSwaHeads][8];
 #pragma unroll
   for (int hh = 0; hh < kSwaHeads; ++hh) {
-    mm[hh] = -INFINITY;
+    mm[hh] = kScoreFloor;
     ll[hh] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) oo[hh][e] = 0.f;
   }
-  for (int base = r0;;) {
+  // rolling window: slot u is refilled with the row 16 U ahead as soon as it
+  // is used, so about U rows per lane group stay in flight throughout
+  for (int base = r0; base < r1; base += 16 * U) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
@@ -153,34 +162,41 @@ __device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const 
       }
 #pragma unroll
       for (int hh = 0; hh < kSwaHeads; ++hh) {
-        float d = 0.f;
+        float d = q[hh][0] * kf[0];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d += q[hh][e] * kf[e];
+        for (int e = 1; e < 8; ++e) d = fmaf(q[hh][e], kf[e], d);
         d = row16_sum(d);
-        if (ok[u]) {
-          const float mn = fmaxf(mm[hh], d);
-          const float a = __expf(mm[hh] - mn), pw = __expf(d - mn);
-          ll[hh] = ll[hh] * a + pw;
+        if (!ok[u]) continue;
+        // online softmax with a lazy reference: the maximum moves only when a
+        // score passes it by more than kSlack (any reference gives the same
+        // o / l; this one keeps every weight below 2^kSlack), for the whole
+        // wave at once, so a row costs one exponential and one FMA per channel
+        const bool bump = d > mm[hh] + kSlack;
+        if (__builtin_amdgcn_ballot_w64(bump)) {
+          const float mn = bump ? d : mm[hh];
+          const float a = __builtin_amdgcn_exp2f(mm[hh] - mn);
+          ll[hh] *= a;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) oo[hh][e] = oo[hh][e] * a + pw * vf[e];
+          for (int e = 0; e < 8; ++e) oo[hh][e] *= a;
           mm[hh] = mn;
         }
-      }
-    }
-    base += 16 * U;
-    if (base >= r1) break;
+        const float pw = __builtin_amdgcn_exp2f(d - mm[hh]);
+        ll[hh] += pw;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ri = base + u * 16 + wv * 4 + grp;
+        for (int e = 0; e < 8; ++e) oo[hh][e] = fmaf(pw, vf[e], oo[hh][e]);
+      }
+      const int ri = base + (U + u) * 16 + wv * 4 + grp;
       ok[u] = ri < r1;
-      kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
       if (ok[u]) {
         const size_t n = (size_t)swa_row<RING>(ri, ns, wbase, wwrap, g.window);
-        kr[u] = *reinterpret_cast<const uint4 *>(kb + n * kD + sub * 8);
-        vr[u] = *reinterpret_cast<const uint4 *>(vb + n * kD + sub * 8);
+        kr[u] = ld_stream(kb + n * kD + sub * 8);
+        vr[u] = ld_stream(vb + n * kD + sub * 8);
       }
     }
   }
+  // back to natural-log units for the merges (an empty state has m = -inf)
+#pragma unroll
+  for (int hh = 0; hh < kSwaHeads; ++hh) mm[hh] = ll[hh] > 0.f ? mm[hh] * kLn2 : -INFINITY;
   // merge the row groups of each wave, then the waves through LDS
 #pragma unroll
   for (int hh = 0; hh < kSwaHeads; ++hh) {
@@ -216,7 +232,8 @@ __device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const 
       st_coherent(&p->l, l_);
     }
   }
-  if (defer || !arrive_last(g.ctr_swa + unit * g.swa_hb + hb, (uint32_t)g.swa_nch, &sm.flag)) return;
+  if (defer) return;
+  if (!arrive_last(g.ctr_swa + unit * g.swa_hb + hb, (uint32_t)g.swa_nch, &sm.flag)) return;
   // wave hh combines head hh's chunk states (all heads in one round of loads)
   const int h = sm.heads[wv];
   if (h >= 0)
@@ -248,8 +265,9 @@ __host__ __device__ __forceinline__ long long swa_combine_blocks(const Geo &g) {
   return (long long)g.swa_units * g.swa_hb;
 }
 
-// Merge of the deferred chunk states of one (unit, head block): wave w takes
-// the block's w-th local head (the same split the window workgroups use).
+// Merge of the deferred chunk states of one (unit, head block), in the launch
+// after the window workgroups: wave w takes the block's w-th local head (the
+// same split the window workgroups use).
 __device__ __forceinline__ void swa_combine_block(const Geo &g, long long y, float *__restrict__ out) {
   const int hb = (int)(y % g.swa_hb), unit = (int)(y / g.swa_hb);
   const int i = unit % g.nq, bl = unit / g.nq, lgi = bl % g.nlg, b = bl / g.nlg;

@@ -9,19 +9,21 @@
 //
 // Design for gfx950.  The scan is bandwidth-bound (32 bytes of indexer key per
 // token): each workgroup streams one tile of T tokens with coalesced 16-byte
-// loads, keeps the tile's scores in LDS, and builds per-wave 256-bin histograms
-// in LDS with integer atomics.  Bins are 1/8 logit wide on a fixed grid, so
-// tile histograms merge exactly by an integer shift; masses are summed as
-// exact 64-bit integers of in-cell weights (deterministic in any order).  The
-// second kernel re-reads one code byte per token; each of its workgroups first
-// rebuilds the query's global histogram from an exact absolute-cell ring the
-// scan tiles filled with integer atomics (boundary bin b*, residual mass,
-// per-tile prefix of bin-b* mass), then takes every token of its tile above
-// b* and the ordered prefix of bin b* (recomputing only those tokens' scores),
-// gathers their K/V rows and writes a split-K softmax state; the last
-// workgroup of a query combines them.  The sliding-window workgroups of the
-// local heads run inside the scan launch, so their latency hides under the
-// indexer stream.
+// loads, keeps the tile's scores in registers, and builds per-wave
+// histograms in LDS with integer atomics.  Bins are 1/8 logit wide on a fixed
+// grid, so tile histograms merge exactly by an integer shift; masses are
+// summed as exact 64-bit integers of in-cell weights (deterministic in any
+// order).  Each tile adds its masses into an exact absolute-cell ring of its
+// query; the query's last tile to finish reads the ring once and derives the
+// whole selection: the boundary bin b*, the residual mass, and per tile the
+// bin-b* prefix mass, output offsets and the crossing tile.  The selection
+// launch then starts from one round of loads: each of its workgroups re-reads
+// one code byte per token of its tiles, takes every token above b* and the
+// ordered prefix of bin b* in the crossing tile (recomputing only those
+// tokens' scores), gathers their K/V rows and writes a split-K softmax state;
+// the last workgroup of a query combines them.  The sliding-window workgroups
+// of the local heads run inside the scan launch, so their latency hides under
+// the indexer stream.
 #include "block_util.h"
 #include "swa.h"
 
@@ -37,6 +39,20 @@ constexpr int kCells = 512;      // absolute score cells tracked per tile while 
 // in-cell masses (bits 0..39; at most 8192 tokens of < 1.14 * 2^23 each).
 constexpr int kCountShift = 40;
 constexpr unsigned long long kMassMask = (1ull << kCountShift) - 1;
+
+// Per-workgroup scratch of the global threshold.
+struct ThrScratch {
+  uint64_t ring[kRing];                    // the query's absolute-cell masses (cell mod kRing)
+  unsigned long long tot[4][2];            // per-wave totals of the tile prefix
+  int cross_t[4], cross_bo[4];             // per-wave last crossing tile and its offset
+  int hit_j[4];
+  double hit_before[4];
+  double last_before;
+  double red_d[4];
+  unsigned long long red_u[4];
+  uint32_t red_u32[4];
+  int red_i[4];
+};
 
 template <int T>
 struct ScanShared {
@@ -61,6 +77,99 @@ __device__ __forceinline__ int dec_max(uint32_t e) { return (int)(e - 0x80000000
 __device__ __forceinline__ uint32_t enc_min(int c) { return 0x7fffffffu - (uint32_t)c; }
 __device__ __forceinline__ int dec_min(uint32_t e) { return (int)(0x7fffffffu - e); }
 
+
+// The query's global histogram from its ring (in LDS; or, when its cells span
+// more than the ring holds, from every tile histogram): boundary bin b*,
+// residual mass in in-cell units of bin b*, and whether every position is
+// taken.  Every workgroup of a query computes identical values: the integer
+// bins are exact and every floating-point sum has a fixed order.
+__device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, int base_min, ThrScratch &sm,
+                                                 int &bstar_out, double &r_u_out, int &all_out) {
+  const int tid = threadIdx.x, j = tid;
+  const TileSum *ts = g.tsum + (size_t)unit * g.nt;
+  const long long span = (long long)c - base_min;
+  unsigned long long H = 0;
+  double w255 = 0.0;
+  if (span < kRing) {
+    // bin j <= 254 is cell c - j; the clamp bin gathers cells c - 255 - j - 256 x, x = 0, 1, ...
+    H = j <= kBnd ? sm.ring[(c - j) & (kRing - 1)] : 0ull;
+    for (long long cell = (long long)c - (kBins - 1) - j; cell >= base_min; cell -= kWG) {
+      const unsigned long long mj = sm.ring[cell & (kRing - 1)];
+      if (mj) w255 += (double)mj * bin_scale(g, (double)(cell - c) * 0.125);
+    }
+  } else {
+    for (int t = 0; t < g.nt; ++t) {
+      const int ct = ts[t].c_t;
+      if (ct == INT32_MIN) continue;
+      const long long d = (long long)c - ct;
+      if (j <= kBnd && j - d >= 0) H += ts[t].mass[j - d];
+      if (j + d >= kBins - 1) {
+        const unsigned long long mj = ts[t].mass[j];
+        if (mj) w255 += (double)mj * bin_scale(g, -(double)(j + d) * 0.125);
+      }
+    }
+  }
+  // clamp-bin mass, summed in a fixed order (a butterfly inside each wave, the
+  // four wave sums in wave order), so every workgroup gets the same bits
+  const int lane = j & 63, wv = j >> 6;
+  {
+    double v = w255;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) sm.red_d[wv] = v;
+  }
+  __syncthreads();
+  const double W255 = (((sm.red_d[0] + sm.red_d[1]) + sm.red_d[2]) + sm.red_d[3]) * 0x1p-23;
+  __syncthreads();
+  const double Wj = j <= kBnd ? (double)H * 0x1p-23 * bin_scale(g, -(double)j * 0.125) : W255;
+  double Z;
+  const double excl = block_excl_scan<double>(Wj, Z, sm.red_d);
+  // Top-P needs the mass p Z; top-k needs k tokens (every weight is exactly 1,
+  // so Z is the number of positions and every sum here is an exact integer)
+  const double need = g.topk ? (double)g.topk : g.p * Z;
+  // b*: the first bin whose cumulative mass reaches the need, and the mass
+  // above it (the last bin when none does, which only p >= 1 allows)
+  const bool hit = excl + Wj >= need;
+  const unsigned long long bal = __builtin_amdgcn_ballot_w64(hit);
+  if (bal ? lane == __builtin_ctzll(bal) : lane == 0) {
+    sm.hit_j[wv] = bal ? j : kBins;
+    sm.hit_before[wv] = excl;
+  }
+  if (j == kBins - 1) sm.last_before = excl;
+  __syncthreads();
+  int bstar = kBins;
+  double before = sm.last_before;
+#pragma unroll
+  for (int w = 3; w >= 0; --w)
+    if (sm.hit_j[w] < kBins) {
+      bstar = sm.hit_j[w];
+      before = sm.hit_before[w];
+    }
+  if (bstar >= kBins) bstar = kBins - 1;
+  __syncthreads();
+  // Top-P: p >= 1, or the boundary in the clamp bin (whose in-cell masses
+  // have no common scale; its mass is below e^-31.75 of the top cell, so
+  // everything is taken).  Top-k: k covers every position.
+  all_out = (g.topk ? need >= Z : (g.p >= 1.0 || bstar >= kBins - 1)) ? 1 : 0;
+  r_u_out = (need - before) * 0x1p23 * bin_scale(g, (double)bstar * 0.125);
+  bstar_out = bstar;
+}
+
+// Local codes [lo, hi] of a tile (max cell ct) that hold the query's boundary
+// bin b*; codes below lo lie above b*.  A regular b* is one local bin (or none:
+// lo = hi = -1).  The clamp bin, a boundary only for top-k, gathers every
+// local bin at or below the query's cell c - 255.
+__device__ __forceinline__ void bnd_range(int bstar, int c, int ct, int &lo, int &hi) {
+  const long long d = (long long)c - ct;
+  if (bstar <= kBnd) {
+    const long long bl = (long long)bstar - d;
+    lo = hi = bl < 0 ? -1 : (int)bl;
+  } else {
+    const long long l = (long long)(kBins - 1) - d;
+    lo = l < 0 ? 0 : (int)l;
+    hi = kBins - 1;
+  }
+}
 
 // Scan workgroups of a launch: units * nt, or with shared indexer keys one
 // per (retrieval head, tile) in the order below, padded.
@@ -93,13 +202,23 @@ __device__ __forceinline__ bool scan_unit_tile(const Geo &g, long long blk, int 
   return true;
 }
 
+// Position of score k of thread tid in a tile starting at n0: consecutive
+// threads on consecutive positions for given logits; for indexer keys the
+// pairing of the key stream (lane 2j: row R + j, lane 2j + 1: row R + 32 + j,
+// R = n0 + 256 k + 64 wave).
+template <bool FROM_LOGITS>
+__device__ __forceinline__ long long scan_pos(long long n0, int k, int tid) {
+  if (FROM_LOGITS) return n0 + k * kWG + tid;
+  return n0 + k * kWG + (tid & ~63) + ((tid & 1) << 5) + ((tid & 63) >> 1);
+}
+
 // One scan workgroup: tile t of query unit (scan_unit_tile).
 template <int T, bool FROM_LOGITS>
 __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rtp_bf16 *__restrict__ q_pre,
                                            const rtp_bf16 *__restrict__ w_q, const rtp_bf16 *__restrict__ k_idx,
                                            const float *__restrict__ logits, ScanShared<T> &sm) {
   constexpr int TPT = T / kWG;
-  constexpr int BATCH = TPT < 5 ? TPT : 5;
+  constexpr int BATCH = TPT < 4 ? TPT : 4;
   const int tid = threadIdx.x, wv = tid >> 6;
   int unit, t;
   if (!scan_unit_tile(g, blk, unit, t)) return;
@@ -137,40 +256,46 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
       bin_abs(lg[k]);
     }
   } else {
-    // rolling window of BATCH rows per thread: slot u is refilled with the row
-    // BATCH positions ahead as soon as it is consumed, so about BATCH rows per
-    // thread stay in flight; loads are clamped to a valid row and unconditional
+    // Each load instruction covers 1 KB of consecutive key rows: lane 2j + h
+    // of a wave reads half h (8 dims) of row R + j and of row R + 32 + j, so
+    // the two lanes of a pair hold complementary halves of two rows.  Each
+    // lane forms the two exact half-dots, the pair swaps one of them, and lane
+    // 2j keeps the score of row R + j, lane 2j + 1 that of row R + 32 + j
+    // (scan_pos).  Halves of an exact dot add exactly, in either order.
+    // Rolling window of BATCH row pairs per lane: slot u is refilled BATCH
+    // steps ahead as soon as it is consumed; loads are clamped to a valid row
+    // and unconditional.
     const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hi + r / g.ig) * g.Ncap * kR);
+    const int h = tid & 1;
+    const long long rA0 = n0 + (tid & ~63) + ((tid & 63) >> 1);     // row R + j of step 0
     uint4 ra[BATCH], rb[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const long long n = n0 + u * kWG + tid;
-      const long long nc = n <= m ? n : m;
-      ra[u] = rows[2 * nc];
-      rb[u] = rows[2 * nc + 1];
+      const long long na = rA0 + u * kWG, nb = na + 32;
+      ra[u] = ld_stream(rows + 2 * (na <= m ? na : m) + h);
+      rb[u] = ld_stream(rows + 2 * (nb <= m ? nb : m) + h);
     }
     project_query(q_pre + (((size_t)b * g.Hq + g.rhead[r]) * g.nq + i) * kD, w_q + (size_t)r * kD * kR, sm.q,
                   sm.qtmp);
-    double q[kR];
+    double qh[kR / 2];                                   // this lane's half of q_idx
 #pragma unroll
-    for (int x = 0; x < kR; ++x) {
-      const unsigned long long v = (unsigned long long)__double_as_longlong(sm.q[x]);
-      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-      q[x] = __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-    }
+    for (int x = 0; x < kR / 2; ++x) qh[x] = sm.q[8 * h + x];
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
       const int u = k % BATCH;
-      const long long n = n0 + k * kWG + tid;
-      const float sc = dot16_exact(q, ra[u], rb[u]);
+      const double pa = dot8_exact(qh, ra[u]), pb = dot8_exact(qh, rb[u]);
+      // lane 2j sends its half of row R + 32 + j and receives its partner's
+      // half of row R + j; lane 2j + 1 the other way round
+      const double send = h ? pa : pb;
+      const double recv = swap_pair(send);
+      const float sc = (float)((h ? pb : pa) + recv);
+      const long long n = scan_pos<false>(n0, k, tid);
       lg[k] = n <= m ? sc : -INFINITY;
       bin_abs(lg[k]);
       if (k + BATCH < TPT) {
-        const long long nn = n + BATCH * kWG;
-        const long long nc = nn <= m ? nn : m;
-        ra[u] = rows[2 * nc];
-        rb[u] = rows[2 * nc + 1];
+        const long long na = rA0 + (k + BATCH) * kWG, nb = na + 32;
+        ra[u] = ld_stream(rows + 2 * (na <= m ? na : m) + h);
+        rb[u] = ld_stream(rows + 2 * (nb <= m ? nb : m) + h);
       }
     }
   }
@@ -235,7 +360,7 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
       const int jb = c_t - score_cell(sc);
       code = (uint8_t)(jb >= kBins - 1 ? kBins - 1 : jb);
     }
-    sm.codes[k * kWG + tid] = code;
+    sm.codes[scan_pos<FROM_LOGITS>(0, k, tid)] = code;
   }
   __syncthreads();
   {
@@ -252,7 +377,7 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
     }
   }
 
-  // tile summary, read by the merge kernel
+  // tile summary, read by the selection launch
   TileSum *tsum = g.tsum + (size_t)unit * g.nt + t;
   const unsigned long long ms = packed & kMassMask;
   const unsigned int cn = (unsigned int)(packed >> kCountShift);
@@ -272,8 +397,8 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
     }
     if (ms) atomicAdd((unsigned long long *)(g.ring + (size_t)unit * kRing + ((c_t - tid) & (kRing - 1))), ms);
   }
-  // the query's prepared forms for the finishing workgroups: the indexer query
-  // and the rotated, scaled attention query
+  // the query's prepared forms for the selection workgroups: the indexer
+  // query and the rotated, scaled attention query
   if (!FROM_LOGITS && t == 0) {
     QPrep *qp = g.qprep + unit;
     if (tid < kR) qp->qi[tid] = sm.q[tid];
@@ -306,105 +431,14 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     scan_block<T, FROM_LOGITS>(g, x - n_swa, q_pre, w_q, k_idx, logits, sm.scan);
 }
 
-// Per-workgroup scratch of the global threshold.
-struct ThrScratch {
-  double wcum[kBins];
-  double red_d[4];
-  unsigned long long red_u[4];
-  uint32_t red_u32[4];
-  int red_i[4];
-};
-
-// The query's global histogram from the ring (or, when its cells span more
-// than the ring holds, from every tile histogram): boundary bin b*, residual
-// mass in in-cell units of bin b*, and whether every position is taken.
-// H_ring is this thread's ring entry for bin j = tid (cell c - j), loaded by
-// the caller.  Every workgroup of a query computes identical values: the
-// integer bins are exact and every floating-point sum has a fixed order.
-__device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, int base_min,
-                                                 unsigned long long H_ring, unsigned long long R1,
-                                                 ThrScratch &sm, int &bstar_out, double &r_u_out, int &all_out) {
-  const int tid = threadIdx.x, j = tid;
-  const TileSum *ts = g.tsum + (size_t)unit * g.nt;
-  const uint64_t *ring = g.ring + (size_t)unit * kRing;
-  const long long span = (long long)c - base_min;
-  unsigned long long H = 0;
-  double w255 = 0.0;
-  if (span < kRing) {
-    // clamp cells c - 255 - j - 256 x, x = 0, 1, ...: the first one (R1) was loaded by the caller
-    H = j <= kBnd ? H_ring : 0ull;
-    const long long cell1 = (long long)c - (kBins - 1) - j;
-    if (R1) w255 += (double)R1 * bin_scale(g, (double)(cell1 - c) * 0.125);
-    for (long long cell = cell1 - kWG; cell >= base_min; cell -= kWG) {
-      const unsigned long long mj = ring[cell & (kRing - 1)];
-      if (mj) w255 += (double)mj * bin_scale(g, (double)(cell - c) * 0.125);
-    }
-  } else {
-    for (int t = 0; t < g.nt; ++t) {
-      const int ct = ts[t].c_t;
-      if (ct == INT32_MIN) continue;
-      const long long d = (long long)c - ct;
-      if (j <= kBnd && j - d >= 0) H += ts[t].mass[j - d];
-      if (j + d >= kBins - 1) {
-        const unsigned long long mj = ts[t].mass[j];
-        if (mj) w255 += (double)mj * bin_scale(g, -(double)(j + d) * 0.125);
-      }
-    }
-  }
-  // clamp-bin mass: fixed pairwise tree over the threads
-  sm.wcum[j] = w255;
-  __syncthreads();
-#pragma unroll
-  for (int s = kWG / 2; s > 0; s >>= 1) {
-    if (j < s) sm.wcum[j] += sm.wcum[j + s];
-    __syncthreads();
-  }
-  const double W255 = sm.wcum[0] * 0x1p-23;
-  __syncthreads();
-  const double Wj = j <= kBnd ? (double)H * 0x1p-23 * bin_scale(g, -(double)j * 0.125) : W255;
-  double Z;
-  const double excl = block_excl_scan<double>(Wj, Z, sm.red_d);
-  // Top-P needs the mass p Z; top-k needs k tokens (every weight is exactly 1,
-  // so Z is the number of positions and every sum here is an exact integer)
-  const double need = g.topk ? (double)g.topk : g.p * Z;
-  int bstar = block_min<int>(excl + Wj >= need ? j : kBins, sm.red_i);
-  if (bstar >= kBins) bstar = kBins - 1;
-  sm.wcum[j] = excl;                      // mass above bin j
-  __syncthreads();
-  const double before = sm.wcum[bstar];
-  __syncthreads();
-  // Top-P: p >= 1, or the boundary in the clamp bin (whose in-cell masses
-  // have no common scale; its mass is below e^-31.75 of the top cell, so
-  // everything is taken).  Top-k: k covers every position.
-  all_out = (g.topk ? need >= Z : (g.p >= 1.0 || bstar >= kBins - 1)) ? 1 : 0;
-  r_u_out = (need - before) * 0x1p23 * bin_scale(g, (double)bstar * 0.125);
-  bstar_out = bstar;
-}
-
-// Local codes [lo, hi] of a tile (max cell ct) that hold the query's boundary
-// bin b*; codes below lo lie above b*.  A regular b* is one local bin (or none:
-// lo = hi = -1).  The clamp bin, a boundary only for top-k, gathers every
-// local bin at or below the query's cell c - 255.
-__device__ __forceinline__ void bnd_range(int bstar, int c, int ct, int &lo, int &hi) {
-  const long long d = (long long)c - ct;
-  if (bstar <= kBnd) {
-    const long long bl = (long long)bstar - d;
-    lo = hi = bl < 0 ? -1 : (int)bl;
-  } else {
-    const long long l = (long long)(kBins - 1) - d;
-    lo = l < 0 ? 0 : (int)l;
-    hi = kBins - 1;
-  }
-}
-
 struct FinShared {
   static constexpr int kList = 2048;
-  static constexpr int kCodes = 32768;
+  static constexpr int kCodes = 16384;
+  static constexpr int kTiles = kCodes / 1024;
   uint8_t codes[kCodes];                   // codes of this workgroup's tiles
   int list[kList];                         // positions pending attention
   int blist[kWG];                          // bin-b* positions of the crossing tile, one round
-  TileSel tsel[32];                        // selection parameters of this workgroup's tiles
-  int ct[32];
+  TileSel tsel[kTiles];                    // selection parameters of this workgroup's tiles
   float q[kD];
   double qi[kR];
   int flag;
@@ -416,31 +450,29 @@ struct FinShared {
   Partial res;
 };
 
-// Finish kernel: one workgroup per (query unit, run of fin_tpw tiles).
-// Each workgroup first derives the query's threshold from the ring and the
-// per-tile prefix of bin-b* mass over all tiles (identical in every workgroup
-// of the query).  Tiles before the crossing tile take their whole bin b*,
-// tiles after it none; the crossing tile takes the ordered prefix of its
-// bin-b* tokens whose preceding mass is below the residual (their scores are
-// recomputed in parallel).  Selected positions are written (optional) and
-// attended (optional); the last workgroup of the query combines the states
-// and resets the ring.
+// Selection workgroup of query `unit` over its tiles t_begin..t_end-1 (one
+// of fin_nwg per query), after the scan launch.  With two rounds of loads,
+// every selection workgroup
+// of the query derives the same threshold and per-tile parameters: round one
+// brings the query's ring (exact masses per absolute cell), its cell range,
+// every tile's max cell, the prepared query and this workgroup's codes
+// (LDS-DMA); round two the tile summaries' entries at the boundary bin.
+// Tiles before the crossing tile take their whole bin b*, tiles after it
+// none; the crossing tile takes the ordered prefix of its bin-b* tokens whose
+// preceding mass is below the residual (their scores are recomputed in
+// parallel).  Selected positions are written (optional) and attended
+// (optional); the last workgroup of the query combines the split-K states
+// and leaves the query's ring and cell range zero.
 template <int T, bool FROM_LOGITS, bool ATTEND, bool RING>
-__global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__restrict__ k_idx,
-                                                     const float *__restrict__ logits,
-                                                     const rtp_bf16 *__restrict__ kc,
-                                                     const rtp_bf16 *__restrict__ vc, float *__restrict__ out,
-                                                     int32_t *__restrict__ idx, int32_t *__restrict__ count,
-                                                     long long cap) {
+__device__ __forceinline__ void finish_block(const Geo &g, int y, const rtp_bf16 *__restrict__ k_idx,
+                                             const float *__restrict__ logits, const rtp_bf16 *__restrict__ kc,
+                                             const rtp_bf16 *__restrict__ vc, float *__restrict__ out,
+                                             int32_t *__restrict__ idx, int32_t *__restrict__ count, long long cap,
+                                             FinShared &sm) {
   constexpr int TPT = T / kWG;             // positions per thread per tile (consecutive)
   static_assert(T <= FinShared::kCodes, "tile larger than the code staging area");
-  __shared__ FinShared sm;
-  if (ATTEND && blockIdx.x >= (unsigned)(g.units * g.fin_nwg)) {   // deferred window chunk states
-    swa_combine_block(g, (long long)blockIdx.x - (long long)g.units * g.fin_nwg, out);
-    return;
-  }
   const int tid = threadIdx.x;
-  const int unit = blockIdx.x / g.fin_nwg, w = blockIdx.x % g.fin_nwg;
+  const int unit = y / g.fin_nwg, w = y % g.fin_nwg;
   const int i = unit % g.nq, br = unit / g.nq, r = br % g.Hr, b = br / g.Hr;
   const int hq = g.rhead[r];
   const long long m = g.N - g.nq + i;
@@ -450,48 +482,54 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
   const size_t cbase = kv_group_elems<RING>(g, b, kvg);
   const TileSum *ts = g.tsum + (size_t)unit * g.nt;
 
-  // Loads are counted in issue order (vmcnt), so everything the threshold
-  // needs is requested before the bulk of codes: the cell range, the first
-  // tile maxima and the prepared query, then the ring cells, then the codes.
-  const int c = dec_max(g.cmax[unit]);
-  const int base_min = dec_min(g.cmin[unit]);
+  // round one
+  const uint64_t *ring = g.ring + (size_t)unit * kRing;
+  const uint32_t ecmax = g.cmax[unit], ecmin = g.cmin[unit];
   const int ct0 = tid < g.nt ? ts[tid].c_t : INT32_MIN;
   double qi_v = 0.0;
   float qrot_v = 0.f;
   if (!FROM_LOGITS && tid < kR) qi_v = g.qprep[unit].qi[tid];
   if (ATTEND && tid < kD) qrot_v = g.qprep[unit].qrot[tid];
-  const uint64_t *ring = g.ring + (size_t)unit * kRing;
-  const unsigned long long H_ring = ring[(c - tid) & (kRing - 1)];
-  const long long cell1 = (long long)c - (kBins - 1) - tid;
-  const unsigned long long R1 = ((long long)c - base_min < kRing && cell1 >= base_min) ? ring[cell1 & (kRing - 1)] : 0ull;
   {
-    // every code of this run goes straight from memory to LDS (gfx950 LDS-DMA
-    // loads: lane l of a wave lands at the wave's base + 16 l), so nothing is
-    // held in registers while the threshold is worked out
+    // LDS-DMA (gfx950): lane l of a wave lands at the wave's base + 16 l
+    const uint4 *src = reinterpret_cast<const uint4 *>(ring);
+    constexpr int kPerRing = kRing * 8 / 16 / kWG;
+#pragma unroll
+    for (int u = 0; u < kPerRing; ++u) {
+      const int x0 = u * kWG + (tid & ~63);
+      __builtin_amdgcn_global_load_lds(src + x0 + (tid & 63),
+                                       (__attribute__((address_space(3))) void *)(sm.thr.ring + (size_t)x0 * 2), 16,
+                                       0, 0);
+    }
     constexpr int kPer = FinShared::kCodes / 16 / kWG;
-    const uint4 *src = reinterpret_cast<const uint4 *>(g.codes + (size_t)unit * g.nt * T + (size_t)t_begin * T);
+    const uint4 *csrc = reinterpret_cast<const uint4 *>(g.codes + (size_t)unit * g.nt * T + (size_t)t_begin * T);
     const int n16 = (t_end - t_begin) * T / 16;            // a multiple of 64
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int x0 = u * kWG + (tid & ~63);                 // the wave's first 16-byte slot
       if (x0 < n16)
-        __builtin_amdgcn_global_load_lds(src + x0 + (tid & 63),
+        __builtin_amdgcn_global_load_lds(csrc + x0 + (tid & 63),
                                          (__attribute__((address_space(3))) void *)(sm.codes + (size_t)x0 * 16),
                                          16, 0, 0);
     }
   }
   if (!FROM_LOGITS && tid < kR) sm.qi[tid] = qi_v;
   if (ATTEND && tid < kD) sm.q[tid] = qrot_v;
+  __builtin_amdgcn_s_waitcnt(0);                        // this wave's ring and code loads have landed in LDS
+  __syncthreads();
 
+  const int c = dec_max(ecmax), base_min = dec_min(ecmin);
   int bstar, all;
   double r_u;
-  global_threshold(g, unit, c, base_min, H_ring, R1, sm.thr, bstar, r_u, all);
+  global_threshold(g, unit, c, base_min, sm.thr, bstar, r_u, all);
 
-  // per tile of the query: bin-b* prefix mass, counts above b* and in b*,
-  // output offsets; the crossing tile is the last one whose bin-b* tokens
-  // start below the residual, and every bin-b* token before it is taken
-  unsigned long long carryP = 0;
-  int carryS = 0, carryB = 0, tstar = -1, bo_star = -1;
+  // round two: per tile of the query, the bin-b* prefix mass, the counts above
+  // b* and in b*, the output offsets; the crossing tile is the last one whose
+  // bin-b* tokens start below the residual, and every bin-b* token before it
+  // is taken
+  unsigned long long carryP = 0, carrySB = 0;
+  int tstar = -1, bo_star = -1;
+  const int lane = tid & 63, wv = tid >> 6;
   for (int t0 = 0; t0 < g.nt; t0 += kWG) {
     const int tt = t0 + tid;
     unsigned long long bm = 0;
@@ -500,17 +538,42 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
     if (ctt != INT32_MIN && !all) {
       int lo, hi;
       bnd_range(bstar, c, ctt, lo, hi);
-      if (lo >= 1) sure = (int)ts[tt].cum[lo - 1];
+      const unsigned cum_lo = lo >= 1 ? ts[tt].cum[lo - 1] : 0u;
+      if (lo >= 1) sure = (int)cum_lo;
       if (hi >= 0) {
-        bc = (int)(ts[tt].cum[hi] - (lo ? ts[tt].cum[lo - 1] : 0u));
+        bc = (int)(ts[tt].cum[hi] - cum_lo);
         bm = g.topk ? (unsigned long long)bc << 23 : ts[tt].mass[lo];
       }
     }
-    unsigned long long totP, totSB;
-    const unsigned long long P = carryP + block_excl_scan<unsigned long long>(bm, totP, sm.thr.red_u);
-    const unsigned long long sb =
-        block_excl_scan<unsigned long long>(((unsigned long long)sure << 32) | (unsigned)bc, totSB, sm.thr.red_u);
-    const int so = carryS + (int)(sb >> 32), bo = carryB + (int)(sb & 0xffffffffu);
+    // inclusive prefixes inside the wave of the bin-b* mass and of the packed
+    // (above b*, in b*) counts, then the wave totals through LDS
+    const unsigned long long sbv = ((unsigned long long)sure << 32) | (unsigned)bc;
+    unsigned long long xp = bm, xs = sbv;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned long long yp = __shfl_up(xp, off), ys = __shfl_up(xs, off);
+      if (lane >= off) {
+        xp += yp;
+        xs += ys;
+      }
+    }
+    if (lane == 63) {
+      sm.thr.tot[wv][0] = xp;
+      sm.thr.tot[wv][1] = xs;
+    }
+    __syncthreads();
+    unsigned long long bp = carryP, bs = carrySB, tp = 0, tsb = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (w < wv) {
+        bp += sm.thr.tot[w][0];
+        bs += sm.thr.tot[w][1];
+      }
+      tp += sm.thr.tot[w][0];
+      tsb += sm.thr.tot[w][1];
+    }
+    const unsigned long long P = bp + xp - bm, sb = bs + xs - sbv;
+    const int so = (int)(sb >> 32), bo = (int)(sb & 0xffffffffu);
     if (tt >= t_begin && tt < t_end) {
       TileSel &tl = sm.tsel[tt - t_begin];
       tl.P = P;
@@ -518,94 +581,122 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
       tl.bnd_off = bo;
       tl.n_sure = sure;
       tl.n_bnd = bc;
-      sm.ct[tt - t_begin] = ctt;
+      tl.ct = ctt;
     }
+    // the crossing tile: the last with bin-b* tokens whose prefix mass is
+    // below the residual (offsets grow with the tile, so its offset is the
+    // largest among them)
     const bool crossing = tt < g.nt && bc > 0 && (double)P < r_u;
-    tstar = max(tstar, block_max<int>(crossing ? tt : -1, sm.thr.red_i));
-    bo_star = max(bo_star, block_max<int>(crossing ? bo : -1, sm.thr.red_i));
-    carryP += totP;
-    carryS += (int)(totSB >> 32);
-    carryB += (int)(totSB & 0xffffffffu);
+    const unsigned long long cb = __builtin_amdgcn_ballot_w64(crossing);
+    if (lane == 0) sm.thr.cross_t[wv] = -1;
+    if (cb && lane == 63 - __builtin_clzll(cb)) {
+      sm.thr.cross_t[wv] = tt;
+      sm.thr.cross_bo[wv] = bo;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (sm.thr.cross_t[w] >= 0) {
+        tstar = sm.thr.cross_t[w];
+        bo_star = sm.thr.cross_bo[w];
+      }
+    carryP += tp;
+    carrySB += tsb;
+    __syncthreads();
   }
+  const int carryS = (int)(carrySB >> 32);
   const int total_sure = carryS;
   const int count_base = carryS + (tstar >= 0 ? bo_star : 0);
   if (count && tid == 0 && w == 0) {
     if (all) count[unit] = (int)(m + 1);
     else if (tstar < 0) count[unit] = count_base;
   }
-  __builtin_amdgcn_s_waitcnt(0);                        // this wave's code loads have landed in LDS
   __syncthreads();
 
   float run_m = -INFINITY, run_l = 0.f, run_o = 0.f;    // thread d < 128 holds channel d
   int nlist = 0;                                        // block-uniform
+  // Positions this run can take at most (workgroup-uniform): when they fit
+  // the list, every tile is handled in one pass (masks, then one pair of
+  // packed scans for all tiles); otherwise, and when every position is
+  // taken, tile by tile.  Both build the same list in the same order.
+  int bound = 0;
   for (int t = t_begin; t < t_end; ++t) {
-    const TileSel tl = sm.tsel[t - t_begin];
-    const int ct = sm.ct[t - t_begin];
-    if (ct == INT32_MIN) continue;                      // no position in the tile
-    int lo = -1, hi = -1;
-    if (!all) bnd_range(bstar, c, ct, lo, hi);
-    const bool bnd_ok = !all && hi >= 0;
-    const bool crossing = bnd_ok && t == tstar;
-    const bool take_all_bnd = bnd_ok && t < tstar;
-    // block-uniform skip of a tile that contributes nothing
-    if (!all && tl.n_sure == 0 && !((take_all_bnd || crossing) && tl.n_bnd > 0)) continue;
-    const long long n0 = (long long)t * T;
-    const long long nbase = n0 + (long long)tid * TPT;
-    // this thread's TPT consecutive codes, read as words
-    uint32_t cw[TPT / 4];
-    {
-      const uint8_t *cd = sm.codes + (t - t_begin) * T + tid * TPT;
-      if constexpr (TPT >= 16) {
+    const TileSel &tl = sm.tsel[t - t_begin];
+    bound += tl.n_sure + (t <= tstar ? tl.n_bnd : 0);
+  }
+  if (!all && bound <= FinShared::kList) {
+    constexpr int kMaxT = FinShared::kCodes / T;        // tiles per run at most
+    constexpr int kGroups = (kMaxT + 3) / 4;            // tiles per packed scan: 4 fields of 16 bits
+    unsigned sure_m[kMaxT], take_m[kMaxT];
+    unsigned cross_bnd = 0;
+    int cross_tl = -1;
 #pragma unroll
-        for (int v = 0; v < TPT / 16; ++v) {
-          const uint4 x4 = reinterpret_cast<const uint4 *>(cd)[v];
-          cw[4 * v] = x4.x;
-          cw[4 * v + 1] = x4.y;
-          cw[4 * v + 2] = x4.z;
-          cw[4 * v + 3] = x4.w;
+    for (int tl = 0; tl < kMaxT; ++tl) {
+      sure_m[tl] = take_m[tl] = 0u;
+      const int t = t_begin + tl;
+      if (t >= t_end) continue;                         // workgroup-uniform
+      const TileSel &ts_ = sm.tsel[tl];
+      if (ts_.ct == INT32_MIN) continue;
+      int lo, hi;
+      bnd_range(bstar, c, ts_.ct, lo, hi);
+      const bool bnd_ok = hi >= 0;
+      const bool crossing = bnd_ok && t == tstar, take_all_bnd = bnd_ok && t < tstar;
+      if (ts_.n_sure == 0 && !((take_all_bnd || crossing) && ts_.n_bnd > 0)) continue;
+      const long long nbase = (long long)t * T + (long long)tid * TPT;
+      uint32_t cw[TPT / 4];
+      {
+        const uint8_t *cd = sm.codes + tl * T + tid * TPT;
+        if constexpr (TPT >= 16) {
+#pragma unroll
+          for (int v = 0; v < TPT / 16; ++v) {
+            const uint4 x4 = reinterpret_cast<const uint4 *>(cd)[v];
+            cw[4 * v] = x4.x;
+            cw[4 * v + 1] = x4.y;
+            cw[4 * v + 2] = x4.z;
+            cw[4 * v + 3] = x4.w;
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < TPT / 4; ++v) cw[v] = reinterpret_cast<const uint32_t *>(cd)[v];
         }
-      } else {
-#pragma unroll
-        for (int v = 0; v < TPT / 4; ++v) cw[v] = reinterpret_cast<const uint32_t *>(cd)[v];
       }
-    }
-    const long long lim = m - nbase;                    // positions beyond the query are never taken
-    const unsigned valid_m = lim >= TPT - 1 ? (TPT == 32 ? 0xffffffffu : ((1u << TPT) - 1u))
-                                            : (lim < 0 ? 0u : ((1u << (lim + 1)) - 1u));
-    unsigned sure_m = 0, bnd_m = 0;
-    if (all) {
-      sure_m = valid_m;
-    } else {
+      const long long lim = m - nbase;
+      const unsigned valid_m = lim >= TPT - 1 ? (TPT == 32 ? 0xffffffffu : ((1u << TPT) - 1u))
+                                              : (lim < 0 ? 0u : ((1u << (lim + 1)) - 1u));
+      unsigned sm_ = 0, bm_ = 0;
 #pragma unroll
       for (int k = 0; k < TPT; ++k) {
         const int code = (int)((cw[k >> 2] >> (8 * (k & 3))) & 0xffu);
-        sure_m |= (code < lo ? 1u : 0u) << k;
-        bnd_m |= (code >= lo && code <= hi ? 1u : 0u) << k;
+        sm_ |= (code < lo ? 1u : 0u) << k;
+        bm_ |= (code >= lo && code <= hi ? 1u : 0u) << k;
       }
-      sure_m &= valid_m;
-      bnd_m = (take_all_bnd || crossing) ? (bnd_m & valid_m) : 0u;
+      sure_m[tl] = sm_ & valid_m;
+      bm_ &= valid_m;
+      if (take_all_bnd) take_m[tl] = bm_;
+      if (crossing) {
+        cross_bnd = bm_;
+        cross_tl = tl;
+      }
     }
-    unsigned take_m = take_all_bnd ? bnd_m : 0u;
     int emitted_b = 0;
-    if (crossing) {
-      // ordered fill of bin b*: the tile's bin-b* tokens in position order, a
-      // round of 256 at a time, each weighed by one thread; a token is taken
-      // while the mass before it is below the residual, so the taken tokens
-      // are a prefix of that order
+    if (cross_tl >= 0) {                                // workgroup-uniform: this run holds the crossing tile
+      // ordered fill of bin b* in the crossing tile (see the tile-by-tile path)
+      const TileSel &ts_ = sm.tsel[cross_tl];
+      const long long nbase = (long long)(t_begin + cross_tl) * T + (long long)tid * TPT;
       int nbt;
-      const int boff = block_excl_scan<int>(__popc(bnd_m), nbt, sm.thr.red_i);
+      const int boff = block_excl_scan<int>(__popc(cross_bnd), nbt, sm.thr.red_i);
       nbt = nbt < T ? nbt : T;
-      unsigned long long pre = tl.P;
+      unsigned long long pre = ts_.P;
       int ntake = 0;
       for (int r0 = 0; r0 < nbt; r0 += kWG) {
         int jx = boff;
-        for (unsigned mm = bnd_m; mm; mm &= mm - 1, ++jx)
+        for (unsigned mm = cross_bnd; mm; mm &= mm - 1, ++jx)
           if (jx >= r0 && jx < r0 + kWG) sm.blist[jx - r0] = (int)(nbase + __builtin_ctz(mm));
         __syncthreads();
         const int cnt = nbt - r0 < kWG ? nbt - r0 : kWG;
-        uint32_t wt = 0;                                  // < 1.14 * 2^23 each, < 2^32 per round
+        uint32_t wt = 0;
         if (tid < cnt && g.topk) {
-          wt = kUnitWeight;                               // top-k: every token counts once
+          wt = kUnitWeight;
         } else if (tid < cnt) {
           long long n = sm.blist[tid];
           n = n < 0 ? 0 : (n > m ? m : n);
@@ -624,56 +715,199 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
         (void)block_excl_scan<int>(tid < cnt && (double)(pre + ex) < r_u ? 1 : 0, ntk, sm.thr.red_i);
         ntake += ntk;
         pre += tot_w;
-        if (ntk < cnt) break;                           // block-uniform
+        if (ntk < cnt) break;
       }
       int jx = boff;
-      for (unsigned mm = bnd_m; mm; mm &= mm - 1, ++jx)
-        if (jx < ntake) take_m |= 1u << __builtin_ctz(mm);
+      unsigned tk = 0;
+      for (unsigned mm = cross_bnd; mm; mm &= mm - 1, ++jx)
+        if (jx < ntake) tk |= 1u << __builtin_ctz(mm);
+#pragma unroll
+      for (int tl = 0; tl < kMaxT; ++tl)
+        if (tl == cross_tl) take_m[tl] = tk;
       emitted_b = ntake;
+      if (count && tid == 0) count[unit] = count_base + emitted_b;
     }
-    // one scan for both ranks: positions above b* in the low half, bin-b* in the high half
-    int tot;
-    const int ex = block_excl_scan<int>(__popc(sure_m) | (__popc(take_m) << 16), tot, sm.thr.red_i);
-    const int rs = ex & 0xffff, rb = ex >> 16;
-    const int ts_ = min(tot & 0xffff, T), tb_ = min(tot >> 16, T);
-    if (crossing && count && tid == 0) count[unit] = count_base + emitted_b;
-    if (idx) {   // positions above b* first, then the taken bin-b* positions, each ascending
-      int32_t *dst = idx + (size_t)unit * cap;
-      long long a = (all ? n0 : (long long)tl.sure_off) + rs;
-      for (unsigned mm = sure_m; mm; mm &= mm - 1, ++a)
-        if ((unsigned long long)a < (unsigned long long)cap) dst[a] = (int)(nbase + __builtin_ctz(mm));
-      long long c2 = (long long)total_sure + tl.bnd_off + rb;
-      for (unsigned mm = take_m; mm; mm &= mm - 1, ++c2)
-        if ((unsigned long long)c2 < (unsigned long long)cap) dst[c2] = (int)(nbase + __builtin_ctz(mm));
-    }
-    if (ATTEND) {
-      const int add = ts_ + tb_;
-      if (nlist + add > FinShared::kList && nlist > 0) {   // flush the pending list
-        attend_rows(sm.q, sm.list, nlist, g.N, kc + cbase, vc + cbase, &sm.res, &sm.at);
-        if (tid < kD) merge_state(run_m, run_l, &run_o, sm.res.m, sm.res.l, &sm.res.o[tid], 1);
-        nlist = 0;
+    // ranks of this thread's positions in every tile: 16-bit fields, four
+    // tiles per 64-bit scan (a tile holds at most 8192 positions)
+#pragma unroll
+    for (int gq = 0; gq < kGroups; ++gq) {
+      unsigned long long ps = 0, pb = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int tl = 4 * gq + q;
+        if (tl < kMaxT) {
+          ps |= (unsigned long long)__popc(sure_m[tl]) << (16 * q);
+          pb |= (unsigned long long)__popc(take_m[tl]) << (16 * q);
+        }
       }
-      if (add <= FinShared::kList) {
-        int a = nlist + rs;
-        for (unsigned mm = sure_m; mm; mm &= mm - 1) sm.list[a++] = (int)(nbase + __builtin_ctz(mm));
-        a = nlist + ts_ + rb;
-        for (unsigned mm = take_m; mm; mm &= mm - 1) sm.list[a++] = (int)(nbase + __builtin_ctz(mm));
-        nlist += add;
-        __syncthreads();
+      unsigned long long tS, tB;
+      const unsigned long long eS = block_excl_scan<unsigned long long>(ps, tS, sm.thr.red_u);
+      const unsigned long long eB = block_excl_scan<unsigned long long>(pb, tB, sm.thr.red_u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int tl = 4 * gq + q;
+        if (tl >= kMaxT || t_begin + tl >= t_end) continue;
+        const int rs = (int)((eS >> (16 * q)) & 0xffffu), rb = (int)((eB >> (16 * q)) & 0xffffu);
+        const int ts_n = (int)((tS >> (16 * q)) & 0xffffu), tb_n = (int)((tB >> (16 * q)) & 0xffffu);
+        const long long nbase = (long long)(t_begin + tl) * T + (long long)tid * TPT;
+        if (idx) {   // positions above b* first, then the taken bin-b* positions, each ascending
+          const TileSel &ts_ = sm.tsel[tl];
+          int32_t *dst = idx + (size_t)unit * cap;
+          long long a = (long long)ts_.sure_off + rs;
+          for (unsigned mm = sure_m[tl]; mm; mm &= mm - 1, ++a)
+            if ((unsigned long long)a < (unsigned long long)cap) dst[a] = (int)(nbase + __builtin_ctz(mm));
+          long long c2 = (long long)total_sure + ts_.bnd_off + rb;
+          for (unsigned mm = take_m[tl]; mm; mm &= mm - 1, ++c2)
+            if ((unsigned long long)c2 < (unsigned long long)cap) dst[c2] = (int)(nbase + __builtin_ctz(mm));
+        }
+        if (ATTEND) {
+          int a = nlist + rs;
+          for (unsigned mm = sure_m[tl]; mm; mm &= mm - 1) sm.list[a++] = (int)(nbase + __builtin_ctz(mm));
+          a = nlist + ts_n + rb;
+          for (unsigned mm = take_m[tl]; mm; mm &= mm - 1) sm.list[a++] = (int)(nbase + __builtin_ctz(mm));
+        }
+        nlist += ts_n + tb_n;
+      }
+    }
+    __syncthreads();
+  } else {
+    for (int t = t_begin; t < t_end; ++t) {
+      const TileSel tl = sm.tsel[t - t_begin];
+      const int ct = tl.ct;
+      if (ct == INT32_MIN) continue;                      // no position in the tile
+      int lo = -1, hi = -1;
+      if (!all) bnd_range(bstar, c, ct, lo, hi);
+      const bool bnd_ok = !all && hi >= 0;
+      const bool crossing = bnd_ok && t == tstar;
+      const bool take_all_bnd = bnd_ok && t < tstar;
+      // block-uniform skip of a tile that contributes nothing
+      if (!all && tl.n_sure == 0 && !((take_all_bnd || crossing) && tl.n_bnd > 0)) continue;
+      const long long n0 = (long long)t * T;
+      const long long nbase = n0 + (long long)tid * TPT;
+      // this thread's TPT consecutive codes, read as words
+      uint32_t cw[TPT / 4];
+      {
+        const uint8_t *cd = sm.codes + (t - t_begin) * T + tid * TPT;
+        if constexpr (TPT >= 16) {
+  #pragma unroll
+          for (int v = 0; v < TPT / 16; ++v) {
+            const uint4 x4 = reinterpret_cast<const uint4 *>(cd)[v];
+            cw[4 * v] = x4.x;
+            cw[4 * v + 1] = x4.y;
+            cw[4 * v + 2] = x4.z;
+            cw[4 * v + 3] = x4.w;
+          }
+        } else {
+  #pragma unroll
+          for (int v = 0; v < TPT / 4; ++v) cw[v] = reinterpret_cast<const uint32_t *>(cd)[v];
+        }
+      }
+      const long long lim = m - nbase;                    // positions beyond the query are never taken
+      const unsigned valid_m = lim >= TPT - 1 ? (TPT == 32 ? 0xffffffffu : ((1u << TPT) - 1u))
+                                              : (lim < 0 ? 0u : ((1u << (lim + 1)) - 1u));
+      unsigned sure_m = 0, bnd_m = 0;
+      if (all) {
+        sure_m = valid_m;
       } else {
-        // a tile with more selected positions than the list: attend it in pieces
-        for (int l0 = 0; l0 < add; l0 += FinShared::kList) {
+  #pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+          const int code = (int)((cw[k >> 2] >> (8 * (k & 3))) & 0xffu);
+          sure_m |= (code < lo ? 1u : 0u) << k;
+          bnd_m |= (code >= lo && code <= hi ? 1u : 0u) << k;
+        }
+        sure_m &= valid_m;
+        bnd_m = (take_all_bnd || crossing) ? (bnd_m & valid_m) : 0u;
+      }
+      unsigned take_m = take_all_bnd ? bnd_m : 0u;
+      int emitted_b = 0;
+      if (crossing) {
+        // ordered fill of bin b*: the tile's bin-b* tokens in position order, a
+        // round of 256 at a time, each weighed by one thread; a token is taken
+        // while the mass before it is below the residual, so the taken tokens
+        // are a prefix of that order
+        int nbt;
+        const int boff = block_excl_scan<int>(__popc(bnd_m), nbt, sm.thr.red_i);
+        nbt = nbt < T ? nbt : T;
+        unsigned long long pre = tl.P;
+        int ntake = 0;
+        for (int r0 = 0; r0 < nbt; r0 += kWG) {
+          int jx = boff;
+          for (unsigned mm = bnd_m; mm; mm &= mm - 1, ++jx)
+            if (jx >= r0 && jx < r0 + kWG) sm.blist[jx - r0] = (int)(nbase + __builtin_ctz(mm));
           __syncthreads();
-          int a = rs;
-          for (unsigned mm = sure_m; mm; mm &= mm - 1, ++a)
-            if (a >= l0 && a < l0 + FinShared::kList) sm.list[a - l0] = (int)(nbase + __builtin_ctz(mm));
-          a = ts_ + rb;
-          for (unsigned mm = take_m; mm; mm &= mm - 1, ++a)
-            if (a >= l0 && a < l0 + FinShared::kList) sm.list[a - l0] = (int)(nbase + __builtin_ctz(mm));
-          __syncthreads();
-          const int cnt = add - l0 < FinShared::kList ? add - l0 : FinShared::kList;
-          attend_rows(sm.q, sm.list, cnt, g.N, kc + cbase, vc + cbase, &sm.res, &sm.at);
+          const int cnt = nbt - r0 < kWG ? nbt - r0 : kWG;
+          uint32_t wt = 0;                                  // < 1.14 * 2^23 each, < 2^32 per round
+          if (tid < cnt && g.topk) {
+            wt = kUnitWeight;                               // top-k: every token counts once
+          } else if (tid < cnt) {
+            long long n = sm.blist[tid];
+            n = n < 0 ? 0 : (n > m ? m : n);
+            float sc;
+            if (FROM_LOGITS) {
+              sc = logits[(size_t)unit * g.N + n];
+            } else {
+              const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hi + r / g.ig) * g.Ncap * kR);
+              sc = dot16_exact(sm.qi, rows[2 * n], rows[2 * n + 1]);
+            }
+            wt = cell_weight(sc, score_cell(sc));
+          }
+          uint32_t tot_w;
+          const uint32_t ex = block_excl_scan<uint32_t>(wt, tot_w, sm.thr.red_u32);
+          int ntk;
+          (void)block_excl_scan<int>(tid < cnt && (double)(pre + ex) < r_u ? 1 : 0, ntk, sm.thr.red_i);
+          ntake += ntk;
+          pre += tot_w;
+          if (ntk < cnt) break;                           // block-uniform
+        }
+        int jx = boff;
+        for (unsigned mm = bnd_m; mm; mm &= mm - 1, ++jx)
+          if (jx < ntake) take_m |= 1u << __builtin_ctz(mm);
+        emitted_b = ntake;
+      }
+      // one scan for both ranks: positions above b* in the low half, bin-b* in the high half
+      int tot;
+      const int ex = block_excl_scan<int>(__popc(sure_m) | (__popc(take_m) << 16), tot, sm.thr.red_i);
+      const int rs = ex & 0xffff, rb = ex >> 16;
+      const int ts_ = min(tot & 0xffff, T), tb_ = min(tot >> 16, T);
+      if (crossing && count && tid == 0) count[unit] = count_base + emitted_b;
+      if (idx) {   // positions above b* first, then the taken bin-b* positions, each ascending
+        int32_t *dst = idx + (size_t)unit * cap;
+        long long a = (all ? n0 : (long long)tl.sure_off) + rs;
+        for (unsigned mm = sure_m; mm; mm &= mm - 1, ++a)
+          if ((unsigned long long)a < (unsigned long long)cap) dst[a] = (int)(nbase + __builtin_ctz(mm));
+        long long c2 = (long long)total_sure + tl.bnd_off + rb;
+        for (unsigned mm = take_m; mm; mm &= mm - 1, ++c2)
+          if ((unsigned long long)c2 < (unsigned long long)cap) dst[c2] = (int)(nbase + __builtin_ctz(mm));
+      }
+      if (ATTEND) {
+        const int add = ts_ + tb_;
+        if (nlist + add > FinShared::kList && nlist > 0) {   // flush the pending list
+          attend_rows(sm.q, sm.list, nlist, g.N, kc + cbase, vc + cbase, &sm.res, &sm.at);
           if (tid < kD) merge_state(run_m, run_l, &run_o, sm.res.m, sm.res.l, &sm.res.o[tid], 1);
+          nlist = 0;
+        }
+        if (add <= FinShared::kList) {
+          int a = nlist + rs;
+          for (unsigned mm = sure_m; mm; mm &= mm - 1) sm.list[a++] = (int)(nbase + __builtin_ctz(mm));
+          a = nlist + ts_ + rb;
+          for (unsigned mm = take_m; mm; mm &= mm - 1) sm.list[a++] = (int)(nbase + __builtin_ctz(mm));
+          nlist += add;
+          __syncthreads();
+        } else {
+          // a tile with more selected positions than the list: attend it in pieces
+          for (int l0 = 0; l0 < add; l0 += FinShared::kList) {
+            __syncthreads();
+            int a = rs;
+            for (unsigned mm = sure_m; mm; mm &= mm - 1, ++a)
+              if (a >= l0 && a < l0 + FinShared::kList) sm.list[a - l0] = (int)(nbase + __builtin_ctz(mm));
+            a = ts_ + rb;
+            for (unsigned mm = take_m; mm; mm &= mm - 1, ++a)
+              if (a >= l0 && a < l0 + FinShared::kList) sm.list[a - l0] = (int)(nbase + __builtin_ctz(mm));
+            __syncthreads();
+            const int cnt = add - l0 < FinShared::kList ? add - l0 : FinShared::kList;
+            attend_rows(sm.q, sm.list, cnt, g.N, kc + cbase, vc + cbase, &sm.res, &sm.at);
+            if (tid < kD) merge_state(run_m, run_l, &run_o, sm.res.m, sm.res.l, &sm.res.o[tid], 1);
+          }
         }
       }
     }
@@ -693,14 +927,14 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
     }
   }
   if (!arrive_last(g.ctr_fin + unit, (uint32_t)g.fin_nwg, &sm.flag)) return;
-  // last workgroup of the query (every workgroup has read the ring): reset the
-  // ring and the cell range for the next call, combine the states
+  // last workgroup of the query (every workgroup has read the ring): leave the
+  // query's state zero for the next call, combine the states
   {
-    uint64_t *ring = g.ring + (size_t)unit * kRing;
+    uint64_t *ringw = g.ring + (size_t)unit * kRing;
     if ((long long)c - base_min < kRing) {
-      for (long long cell = (long long)base_min + tid; cell <= c; cell += kWG) ring[cell & (kRing - 1)] = 0ull;
+      for (long long cell = (long long)base_min + tid; cell <= c; cell += kWG) ringw[cell & (kRing - 1)] = 0ull;
     } else {
-      for (int x = tid; x < kRing; x += kWG) ring[x] = 0ull;
+      for (int x = tid; x < kRing; x += kWG) ringw[x] = 0ull;
     }
     if (tid == 0) {
       g.cmax[unit] = 0u;
@@ -710,6 +944,22 @@ __global__ __launch_bounds__(kWG) void finish_kernel(Geo g, const rtp_bf16 *__re
   if (ATTEND)
     combine_partials(g.part + (size_t)unit * g.fin_nwg, g.fin_nwg,
                      out + (((size_t)b * g.Hq + hq) * g.nq + i) * kD, &sm.cb);
+}
+
+// Selection launch after a scan launch: one workgroup per (query, run of tiles).
+template <int T, bool FROM_LOGITS, bool ATTEND, bool RING>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4, 8))) void finish_kernel(Geo g, const rtp_bf16 *__restrict__ k_idx,
+                                                     const float *__restrict__ logits,
+                                                     const rtp_bf16 *__restrict__ kc,
+                                                     const rtp_bf16 *__restrict__ vc, float *__restrict__ out,
+                                                     int32_t *__restrict__ idx, int32_t *__restrict__ count,
+                                                     long long cap) {
+  __shared__ FinShared sm;
+  if (ATTEND && blockIdx.x >= (unsigned)(g.units * g.fin_nwg)) {   // deferred window chunk states
+    swa_combine_block(g, (long long)blockIdx.x - (long long)g.units * g.fin_nwg, out);
+    return;
+  }
+  finish_block<T, FROM_LOGITS, ATTEND, RING>(g, (int)blockIdx.x, k_idx, logits, kc, vc, out, idx, count, cap, sm);
 }
 
 template <int T>
@@ -733,10 +983,10 @@ int launch_phase_a_t(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, c
 }
 
 template <int T>
-int launch_finish_t(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
-                    const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, int32_t *idx,
-                    int32_t *count, long long cap, bool swa_combine, hipStream_t s) {
-  const unsigned grid = (unsigned)((long long)g.units * g.fin_nwg + (swa_combine ? swa_combine_blocks(g) : 0));
+int launch_finish_t(const Geo &g, const rtp_bf16 *k_idx, const float *logits, const rtp_bf16 *k,
+                    const rtp_bf16 *v, float *out, int32_t *idx, int32_t *count, long long cap, bool merges,
+                    hipStream_t s) {
+  const unsigned grid = (unsigned)((long long)g.units * g.fin_nwg + (merges ? swa_combine_blocks(g) : 0));
   if (grid == 0) return RTP_OK;
 #define RTP_FIN(FL, AT, RG)                                                                                     \
   hipLaunchKernelGGL((finish_kernel<T, FL, AT, RG>), dim3(grid), dim3(kWG), 0, s, g, k_idx, logits, k, v, out, \
@@ -757,11 +1007,11 @@ int launch_finish_t(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, co
 
 int launch_phase_a(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
                    const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, bool with_scan,
-                   bool with_swa, hipStream_t s, bool defer_swa_combine) {
+                   bool with_swa, hipStream_t s, bool defer) {
   Geo gg = g;
   if (!with_scan) gg.units = 0;
   if (!with_swa && gg.units == 0) return RTP_OK;
-  const bool df = with_swa && defer_swa_combine;
+  const bool df = with_swa && defer;
   switch (gg.T) {
     case 1024: return launch_phase_a_t<1024>(gg, q_pre, w_q, k_idx, logits, k, v, out, with_swa, df, s);
     case 2048: return launch_phase_a_t<2048>(gg, q_pre, w_q, k_idx, logits, k, v, out, with_swa, df, s);
@@ -771,16 +1021,15 @@ int launch_phase_a(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, con
   }
 }
 
-int launch_finish(const Geo &g, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
-                  const float *logits, const rtp_bf16 *k, const rtp_bf16 *v, float *out, int32_t *idx,
-                  int32_t *count, long long cap, hipStream_t s, bool swa_combine) {
+int launch_finish(const Geo &g, const rtp_bf16 *k_idx, const float *logits, const rtp_bf16 *k, const rtp_bf16 *v,
+                  float *out, int32_t *idx, int32_t *count, long long cap, hipStream_t s, bool merges) {
   if (g.units == 0) return RTP_OK;
-  const bool sc = swa_combine && out && !logits;       // only the attending build merges window states
+  const bool mg = merges && out && !logits;
   switch (g.T) {
-    case 1024: return launch_finish_t<1024>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, sc, s);
-    case 2048: return launch_finish_t<2048>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, sc, s);
-    case 4096: return launch_finish_t<4096>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, sc, s);
-    case 8192: return launch_finish_t<8192>(g, q_pre, w_q, k_idx, logits, k, v, out, idx, count, cap, sc, s);
+    case 1024: return launch_finish_t<1024>(g, k_idx, logits, k, v, out, idx, count, cap, mg, s);
+    case 2048: return launch_finish_t<2048>(g, k_idx, logits, k, v, out, idx, count, cap, mg, s);
+    case 4096: return launch_finish_t<4096>(g, k_idx, logits, k, v, out, idx, count, cap, mg, s);
+    case 8192: return launch_finish_t<8192>(g, k_idx, logits, k, v, out, idx, count, cap, mg, s);
     default: return RTP_ERR_UNSUPPORTED;
   }
 }

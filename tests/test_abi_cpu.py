@@ -218,3 +218,4 @@ def test_package_does_not_touch_the_oracle():
                 txt = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", txt, re.M), f
                 assert "rtp_oracle" not in txt, f
+
