@@ -284,24 +284,25 @@ struct CombineShared {
 };
 
 // Normalised combination of np split-K states into out[0..D) by the whole
-// workgroup, in one round of loads: 8 groups of 32 threads, group x merging
-// states x, x + 8, ... (a float4 of channels per thread, four states in
-// flight), then the 8 group states merged in a fixed order.
+// workgroup, in one round of loads for up to 64 states: 8 groups of 32
+// threads, group x merging states x, x + 8, ... (a float4 of channels per
+// thread, eight states in flight), then the 8 group states merged in a fixed
+// order.
 __device__ __forceinline__ void combine_partials(const Partial *parts, int np, float *out, CombineShared *sm) {
   const int tid = threadIdx.x, d4 = tid & 31, grp = tid >> 5;
   float m = -INFINITY, l = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int x0 = grp; x0 < np; x0 += 32) {
-    float pm[4], pl[4];
-    float4 po[4];
+  for (int x0 = grp; x0 < np; x0 += 64) {
+    float pm[8], pl[8];
+    float4 po[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {          // clamped, unconditional loads
+    for (int u = 0; u < 8; ++u) {          // clamped, unconditional loads: up to 64 states in one round
       const int x = x0 + 8 * u < np ? x0 + 8 * u : np - 1;
       pm[u] = parts[x].m;
       pl[u] = parts[x].l;
       po[u] = reinterpret_cast<const float4 *>(parts[x].o)[d4];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       if (x0 + 8 * u >= np) break;
       const float o2[4] = {po[u].x, po[u].y, po[u].z, po[u].w};
       merge_state(m, l, o, pm[u], pl[u], o2, 4);
