@@ -261,6 +261,25 @@ int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf1
                     int32_t *idx_opt, int32_t *count_opt, int64_t cap,
                     void *ws, size_t ws_bytes, void *phase_event, void *stream);
 
+/* The same step as rtp_decode_step for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): its workspace is a static device array of
+ * RTP_STATIC_SCRATCH_BYTES (64 MiB) that every GPU the library runs on holds
+ * from the library's load to the process's end.  Nothing is allocated or
+ * freed by this call (no hipMalloc, hipFree or allocating library routine);
+ * the first call on a device looks up the array's address on that device.
+ * Layers whose rtp_workspace_bytes exceeds the array are RTP_ERR_WS_TOO_SMALL.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race and give undefined results.  The
+ * array keeps the last call's contents; its persistent part is cleared (a
+ * fill kernel on `stream`) when a call's layer layout (B, Hq, Hkv, nq,
+ * head_mode) differs from the previous call's on that GPU.  Other arguments
+ * and results as rtp_decode_step (no phase event). */
+#define RTP_STATIC_SCRATCH_BYTES (64ull << 20)
+int rtp_decode_step_static(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *w_q,
+                           const rtp_bf16 *k_idx, const rtp_bf16 *k, const rtp_bf16 *v, float *out,
+                           int32_t *idx_opt, int32_t *count_opt, int64_t cap, void *stream);
+
 /* ---------------------------------------------------------------- cluster index */
 /* The coarse-to-fine decode of the RTPurboV2 article (finding three): the cached
  * tokens of each indexer-key head are grouped into K clusters in the indexer

@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "Layer", "RtpError", "library_path", "load", "num_retrieval", "workspace_bytes", "workspace",
     "rope_keys", "index_keys", "index_score", "topp_select", "sparse_attn", "swa_attn", "dense_attn",
-    "decode_step", "append_kv", "prefill_attn", "cluster_workspace", "cluster_build", "cluster_step", "kv_rows",
+    "decode_step", "decode_step_static", "append_kv", "prefill_attn", "cluster_workspace", "cluster_build", "cluster_step", "kv_rows",
     "kv_shape", "SYMBOLS",
 ]
 
@@ -28,7 +28,7 @@ _lib = None
 SYMBOLS = ("rtp_num_retrieval", "rtp_workspace_bytes", "rtp_workspace_init", "rtp_status_str", "rtp_rope_keys",
            "rtp_index_keys", "rtp_append_kv", "rtp_index_score", "rtp_topp_select", "rtp_sparse_attn", "rtp_swa_attn",
            "rtp_dense_attn", "rtp_prefill_attn", "rtp_decode_step", "rtp_cluster_workspace_bytes",
-           "rtp_cluster_build", "rtp_cluster_step", "rtp_kv_rows")
+           "rtp_cluster_build", "rtp_cluster_step", "rtp_kv_rows", "rtp_decode_step_static")
 
 
 class RtpError(RuntimeError):
@@ -76,6 +76,7 @@ def load():
         "rtp_dense_attn": (ctypes.c_int, [L, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "rtp_prefill_attn": (ctypes.c_int, [L, vp, vp, vp, vp, ctypes.c_int32, vp]),
         "rtp_decode_step": (ctypes.c_int, [L, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp, vp]),
+        "rtp_decode_step_static": (ctypes.c_int, [L, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
         "rtp_cluster_workspace_bytes": (ctypes.c_size_t, [L, ctypes.c_int32]),
         "rtp_cluster_build": (ctypes.c_int, [L, vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp,
                                              ctypes.c_size_t, vp]),
@@ -434,3 +435,29 @@ def decode_step(layer: Layer, q_pre, w_q, k_idx, k, v, ws, out=None, idx=None, c
                                   ws.numel(), ev, _stream()), "rtp_decode_step")
     return out
 
+
+STATIC_SCRATCH_BYTES = 64 << 20     # RTP_STATIC_SCRATCH_BYTES
+
+
+def decode_step_static(layer: Layer, q_pre, w_q, k_idx, k, v, out=None, idx=None, count=None) -> torch.Tensor:
+    """rtp_decode_step_static: the decode step on the library's static device
+    scratch (no workspace argument; allocates nothing on the library side).
+    Layers whose workspace exceeds STATIC_SCRATCH_BYTES raise RtpError."""
+    q = _ptr(q_pre, torch.bfloat16, (layer.B, layer.Hq, layer.nq, layer.D), "q_pre")
+    w = _ptr(w_q, torch.bfloat16, (layer.Hr, layer.D, layer.R), "w_q") if layer.Hr else None
+    ki = _ptr(k_idx, torch.bfloat16, _cache_shape(layer, layer.Hi, layer.R), "k_idx") if layer.Hr else None
+    kp = _ptr(k, torch.bfloat16, kv_shape(layer), "k")
+    vp = _ptr(v, torch.bfloat16, kv_shape(layer), "v")
+    if out is None:
+        out = torch.empty((layer.B, layer.Hq, layer.nq, layer.D), dtype=torch.float32, device=q_pre.device)
+    op = _ptr(out, torch.float32, (layer.B, layer.Hq, layer.nq, layer.D), "out")
+    cap = 0
+    ip = cp = None
+    if idx is not None:
+        cap = idx.shape[-1]
+        ip = _ptr(idx, torch.int32, (layer.B, layer.Hr, layer.nq, cap), "idx")
+    if count is not None:
+        cp = _ptr(count, torch.int32, (layer.B, layer.Hr, layer.nq), "count")
+    _check(load().rtp_decode_step_static(ctypes.byref(layer.c()), q, w, ki, kp, vp, op, ip, cp, cap, _stream()),
+           "rtp_decode_step_static")
+    return out

@@ -2,6 +2,7 @@
 // The operations and their sources are documented in include/rtp.h.
 #include <algorithm>
 #include <initializer_list>
+#include <mutex>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -310,6 +311,38 @@ hipStream_t as_stream(void *s) {
 }  // namespace
 }  // namespace rtp
 
+// ---------------------------------------------------------------- the allocation-free step
+// rtp_decode_step_static's scratch: one array per GPU, zero when the library
+// is loaded.  Host code never uses the array's name as an address; the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[RTP_STATIC_SCRATCH_BYTES];
+
+namespace rtp {
+namespace {
+struct StaticScratch {
+  void *ptr = nullptr;           // device address of `scratch` on this device
+  size_t key_hash = 0;           // layout of the persistent header the last call left zero
+  size_t header_bytes = 0;
+  bool used = false;
+};
+constexpr int kMaxDevices = 64;
+StaticScratch g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Layout key of the persistent header: it depends on B, Hq, Hkv, nq and head_mode.
+size_t header_key(const rtp_layer *L) {
+  size_t h = 1469598103934665603ull;
+  auto mix = [&](long long v) { h = (h ^ (size_t)v) * 1099511628211ull; };
+  mix(L->B);
+  mix(L->Hq);
+  mix(L->Hkv);
+  mix(L->nq);
+  for (int i = 0; i < L->Hq; ++i) mix(L->head_mode[i]);
+  return h;
+}
+}  // namespace
+}  // namespace rtp
+
 using namespace rtp;
 
 extern "C" {
@@ -544,6 +577,50 @@ int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf1
   if (st != RTP_OK) return st;
   if (phase_event && hipEventRecord(reinterpret_cast<hipEvent_t>(phase_event), s) != hipSuccess) return RTP_ERR_HIP;
   return launch_finish(p.g, k_idx, nullptr, k, v, out, idx_opt, count_opt, idx_opt ? cap : 0, s, defer);
+}
+
+int rtp_decode_step_static(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *w_q, const rtp_bf16 *k_idx,
+                           const rtp_bf16 *k, const rtp_bf16 *v, float *out, int32_t *idx_opt, int32_t *count_opt,
+                           int64_t cap, void *stream) {
+  Plan p;
+  int st = make_plan(layer, nullptr, &p);
+  if (st != RTP_OK) return st;
+  const size_t need = rtp_workspace_bytes(layer);
+  if (need == 0) return RTP_ERR_ARG;
+  if (need > (size_t)RTP_STATIC_SCRATCH_BYTES) return RTP_ERR_WS_TOO_SMALL;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return RTP_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return RTP_ERR_UNSUPPORTED;
+  void *ws = nullptr;
+  bool clear = false;
+  size_t clear_bytes = 0;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    StaticScratch &ss = g_scratch[dev];
+    if (!ss.ptr) {
+      void *ptr = nullptr;
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return RTP_ERR_HIP;
+      ss.ptr = ptr;
+    }
+    // the persistent header must start zero: it is after every call on a
+    // layer of the same layout, and after loading; another layout clears
+    // what the previous one may have left
+    const size_t key = header_key(layer);
+    if (ss.used && ss.key_hash != key) {
+      clear = true;
+      clear_bytes = std::max(ss.header_bytes, p.header_bytes);
+    }
+    ss.used = true;
+    ss.key_hash = key;
+    ss.header_bytes = p.header_bytes;
+    ws = ss.ptr;
+  }
+  hipStream_t s = as_stream(stream);
+  if (clear) {
+    st = launch_fill_zero(ws, (clear_bytes + 255) & ~(size_t)255, s);
+    if (st != RTP_OK) return st;
+  }
+  return rtp_decode_step(layer, q_pre, w_q, k_idx, k, v, out, idx_opt, count_opt, cap, ws, need, nullptr, stream);
 }
 
 }  // extern "C"

@@ -219,3 +219,14 @@ def test_package_does_not_touch_the_oracle():
                 assert not re.search(r"^\s*(import|from)\s+oracle", txt, re.M), f
                 assert "rtp_oracle" not in txt, f
 
+
+@needs_lib
+def test_static_step_checks_before_any_device_work():
+    """rtp_decode_step_static validates the layer and the scratch bound on the
+    host and returns without touching a device (dummy pointers are never used)."""
+    lib = rtp.load()
+    big = _layer(B=64, Hq=64, Hkv=8, N=1 << 20, head_mode=[1] * 64)
+    assert rtp.workspace_bytes(big) > rtp.STATIC_SCRATCH_BYTES
+    p = 16
+    assert lib.rtp_decode_step_static(ctypes.byref(big.c()), p, p, p, p, p, p, None, None, 0, None) == -3
+    assert lib.rtp_decode_step_static(ctypes.byref(_layer(D=64).c()), p, p, p, p, p, p, None, None, 0, None) == -2
