@@ -272,8 +272,8 @@ int rtp_decode_step(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf1
  * Every call on one GPU shares that GPU's array: calls that overlap on one
  * GPU (other streams, other threads) race and give undefined results.  The
  * array keeps the last call's contents; its persistent part is cleared (a
- * fill kernel on `stream`) when a call's layer layout (B, Hq, Hkv, nq,
- * head_mode) differs from the previous call's on that GPU.  Other arguments
+ * fill kernel on `stream`) on the first call on a GPU and when a call's layer
+ * layout (B, Hq, Hkv, nq, head_mode) differs from the previous call's there.  Other arguments
  * and results as rtp_decode_step (no phase event). */
 #define RTP_STATIC_SCRATCH_BYTES (64ull << 20)
 int rtp_decode_step_static(const rtp_layer *layer, const rtp_bf16 *q_pre, const rtp_bf16 *w_q,

@@ -31,6 +31,7 @@ int validate_layer(const rtp_layer *L) {
   if (L->D != kD || L->R != kR) return RTP_ERR_SHAPE;
   if (L->B < 1 || L->Hq < 1 || L->Hkv < 1 || L->Hq > kMaxHq || L->Hq % L->Hkv != 0) return RTP_ERR_SHAPE;
   if (L->nq < 1 || L->N < L->nq || L->N > L->Ncap || L->N >= (1ll << 31)) return RTP_ERR_SHAPE;
+  if ((int64_t)L->B * L->Hq * L->nq >= (1ll << 31)) return RTP_ERR_SHAPE;     // (b, head, query) units in an int
   if (!(L->p > 0.0) || L->window < 1 || L->n_sink < 0 || !(L->rope_theta > 0.0)) return RTP_ERR_ARG;
   for (int h = 0; h < L->Hq; ++h)
     if (L->head_mode[h] != 0 && L->head_mode[h] != 1) return RTP_ERR_ARG;
@@ -151,11 +152,33 @@ int make_geo(const rtp_layer *L, bool dense, Geo &g) {
     if (dense) {
       const long long per = (long long)g.swa_units * g.swa_hb * Lrows / 2048;
       chunk = per < 1024 ? 1024 : (per + 63) / 64 * 64;
+      if (chunk > (1ll << 30)) chunk = 1ll << 30;     // huge layers: the row count stays an int
     }
     if (L->swa_chunk) chunk = L->swa_chunk;
     g.swa_chunk = (int)chunk;
     g.swa_nch = (int)((Lrows + chunk - 1) / chunk);
+    RTP_HOST_CHECK(g.swa_chunk >= 64 && g.swa_chunk % 32 == 0);
+    RTP_HOST_CHECK((long long)g.swa_nch * g.swa_chunk >= Lrows && (long long)(g.swa_nch - 1) * g.swa_chunk < Lrows);
   }
+#ifdef RTP_HOST_CHECKS
+  {
+    int nloc = 0;
+    for (int w = 0; w < kMaxHq / 32; ++w) nloc += __builtin_popcount(g.lmask[w]);
+    RTP_HOST_CHECK(g.Hr + nloc == g.Hq);
+  }
+  for (int r = 0; r < g.Hr; ++r) RTP_HOST_CHECK(g.rhead[r] < g.Hq && L->head_mode[g.rhead[r]] == 1);
+  for (int j = 0; j < g.nlg; ++j) RTP_HOST_CHECK(g.lgroup[j] < g.Hkv);
+#endif
+  RTP_HOST_CHECK(g.Hi * g.ig == g.Hr && g.nlg <= g.Hkv && g.swa_hb * kSwaHeads >= max_local);
+  RTP_HOST_CHECK(g.T >= 1024 && g.T <= 8192 && (g.T & (g.T - 1)) == 0);
+  RTP_HOST_CHECK((long long)g.nt * g.T >= g.N && (long long)(g.nt - 1) * g.T < g.N);
+  RTP_HOST_CHECK(g.fin_tpw >= 1 && (g.fin_tpw & (g.fin_tpw - 1)) == 0 && (long long)g.fin_tpw * g.T <= 16384);
+  RTP_HOST_CHECK((long long)g.fin_nwg * g.fin_tpw >= g.nt && (long long)(g.fin_nwg - 1) * g.fin_tpw < g.nt);
+  // every launch's workgroup count fits the grid's 32-bit x dimension
+  const long long n_scan = (long long)g.units * g.nt, n_fin = (long long)g.units * g.fin_nwg;
+  const long long n_swa = (long long)g.swa_units * g.swa_hb * g.swa_nch;
+  if (n_scan + n_swa >= (1ll << 31) || n_fin + (long long)g.swa_units * g.swa_hb >= (1ll << 31))
+    return RTP_ERR_UNSUPPORTED;
   return RTP_OK;
 }
 
@@ -218,6 +241,24 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
     const size_t pf_bytes = pf_idx_bytes + pf_cnt_bytes;
     off = align_up(off + (codes_bytes > pf_bytes ? codes_bytes : pf_bytes));
   }
+  // regions in order, each inside the workspace and 256-byte aligned
+  RTP_HOST_CHECK(o_ring == 0 && o_cmax >= o_ring + reg_units * kRing * 8 && o_cmin >= o_cmax + reg_units * 4);
+  RTP_HOST_CHECK(o_ctr_fin >= o_cmin + reg_units * 4 && o_ctr_swa >= o_ctr_fin + reg_units * 4);
+  RTP_HOST_CHECK(o_qprep >= o_ctr_swa + swa_ctrs * 4 && o_tsum >= o_qprep + units * sizeof(QPrep));
+  RTP_HOST_CHECK(o_part >= o_tsum + units * nt * sizeof(TileSum));
+  RTP_HOST_CHECK(o_swa >= o_part + units * (size_t)std::max(g.fin_nwg, kSpChunks) * sizeof(Partial));
+  RTP_HOST_CHECK(o_codes >= o_swa + (size_t)g.swa_units * g.swa_hb * g.swa_nch * kSwaHeads * sizeof(Partial));
+  RTP_HOST_CHECK(off >= o_codes + units * nt * (size_t)g.T && off >= o_codes + pf_idx_bytes + pf_cnt_bytes);
+  RTP_HOST_CHECK(g.nq == 1 || g.units == 0 ||
+                 (g.pf_qch >= 1 && g.pf_qch <= g.nq &&
+                  pf_idx_bytes >= (size_t)g.pf_qch * g.B * g.Hr * (size_t)g.N * 4 &&
+                  pf_cnt_bytes >= (size_t)g.B * g.Hr * g.pf_qch * 4));
+#ifdef RTP_HOST_CHECKS
+  for (size_t o : {o_ring, o_cmax, o_cmin, o_ctr_fin, o_ctr_swa, o_qprep, o_tsum, o_part, o_swa, o_codes, off})
+    RTP_HOST_CHECK(o % 256 == 0);
+#endif
+  // the persistent header does not depend on N: the dense plan's counters fit it too
+  RTP_HOST_CHECK((size_t)den.swa_units * den.swa_hb <= swa_ctrs && den.units == 0);
   if (ws) {
     char *base = static_cast<char *>(ws);
     g.ring = reinterpret_cast<uint64_t *>(base + o_ring);
@@ -312,8 +353,7 @@ hipStream_t as_stream(void *s) {
 }  // namespace rtp
 
 // ---------------------------------------------------------------- the allocation-free step
-// rtp_decode_step_static's scratch: one array per GPU, zero when the library
-// is loaded.  Host code never uses the array's name as an address; the
+// rtp_decode_step_static's scratch: one array per GPU.  Host code never uses the array's name as an address; the
 // device address comes from hipGetSymbolAddress, once per device.
 static __device__ __align__(256) unsigned char scratch[RTP_STATIC_SCRATCH_BYTES];
 
@@ -602,13 +642,13 @@ int rtp_decode_step_static(const rtp_layer *layer, const rtp_bf16 *q_pre, const 
       if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return RTP_ERR_HIP;
       ss.ptr = ptr;
     }
-    // the persistent header must start zero: it is after every call on a
-    // layer of the same layout, and after loading; another layout clears
-    // what the previous one may have left
+    // the persistent header must start zero: every call leaves it zero for
+    // the next call of the same layout; the first call on a device and a
+    // change of layout clear it here
     const size_t key = header_key(layer);
-    if (ss.used && ss.key_hash != key) {
+    if (!ss.used || ss.key_hash != key) {
       clear = true;
-      clear_bytes = std::max(ss.header_bytes, p.header_bytes);
+      clear_bytes = std::max(ss.used ? ss.header_bytes : 0, p.header_bytes);
     }
     ss.used = true;
     ss.key_hash = key;

@@ -312,12 +312,14 @@ int make_flash_quads(const Geo &g, bool all_dense, FlashQuads fq[2]) {
           f.dense[f.n] = (uint8_t)mode;
           ++f.n;
         }
+        RTP_HOST_CHECK(f.n >= 1 && f.n <= kMaxQuads && h < g.Hq && h <= 255);
         f.head[4 * (f.n - 1) + cnt % 4] = (uint8_t)h;
         f.nh[f.n - 1] = (uint8_t)(cnt % 4 + 1);
         ++cnt;
       }
     }
   }
+  RTP_HOST_CHECK(fq[0].n + fq[1].n <= kMaxQuads * 2);
   return RTP_OK;
 }
 

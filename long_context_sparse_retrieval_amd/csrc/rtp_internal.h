@@ -8,8 +8,26 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include "rtp.h"
+
+// Bounds assertions of the host-side planners (tiling, workspace layout, head
+// quads).  Compiled in only with -DRTP_HOST_CHECKS (the checked host build the
+// CPU tests drive under AddressSanitizer); a failed check prints itself and
+// aborts.  Product builds compile them to nothing.
+#ifdef RTP_HOST_CHECKS
+#define RTP_HOST_CHECK(cond)                                                                  \
+  do {                                                                                        \
+    if (!(cond)) {                                                                            \
+      fprintf(stderr, "%s:%d: host check failed: %s\n", __FILE__, __LINE__, #cond);           \
+      abort();                                                                                \
+    }                                                                                         \
+  } while (0)
+#else
+#define RTP_HOST_CHECK(cond) ((void)0)
+#endif
 
 namespace rtp {
 

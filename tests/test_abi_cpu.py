@@ -60,8 +60,7 @@ def test_workspace_sizing_monotone():
     assert rtp.workspace_bytes(_layer(N=5000, Ncap=9000)) == rtp.workspace_bytes(_layer(N=5000))
 
 
-@needs_lib
-@pytest.mark.parametrize("kw,code", [
+INVALID_LAYERS = [
     (dict(D=64), -2), (dict(R=8), -2), (dict(Hkv=3), -2), (dict(N=0), -2), (dict(N=10, Ncap=5), -2),
     (dict(nq=0), -2), (dict(N=1 << 31, Ncap=1 << 31), -2), (dict(p=0.0), -1), (dict(p=float("nan")), -1),
     (dict(window=0), -1), (dict(n_sink=-1), -1), (dict(head_mode=[2, 0, 0, 0, 0, 0, 0, 0]), -1),
@@ -69,7 +68,12 @@ def test_workspace_sizing_monotone():
     (dict(local_ring=2), -1), (dict(local_ring=-1), -1), (dict(scan_tile=3000), -1), (dict(scan_tile=512), -1),
     (dict(swa_chunk=100), -1), (dict(swa_chunk=-64), -1), (dict(pf_qch=24), -1), (dict(pf_qch=-16), -1),
     (dict(Hq=512, Hkv=2, head_mode=[0] * 512), -2),
-])
+    (dict(B=1 << 23, Hq=256, Hkv=2, head_mode=[0] * 256), -2),          # B * Hq * nq >= 2^31
+]
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", INVALID_LAYERS)
 def test_layer_validation(kw, code):
     lay = _layer(**kw)
     assert rtp.load().rtp_num_retrieval(ctypes.byref(lay.c())) == code
@@ -94,50 +98,98 @@ def test_p_crosses_the_abi_as_double():
     assert lay.c().p == 0.1
 
 
+FAKE = 1 << 40     # an address never dereferenced: every call below fails validation first
+
+
+def abi_cases():
+    """(entry point, layer, arguments, expected status) of calls that fail
+    validation before any launch; "L" stands for the layer's address."""
+    f, L = FAKE, "L"
+    cases = []
+    add = lambda name, lay, args, code: cases.append((name, lay, args, code))
+    lay = _layer()
+    need = rtp.workspace_bytes(lay)
+    # workspace too small
+    add("rtp_topp_select", lay, [L, f, f, f, 16, f, need - 1, None], -3)
+    add("rtp_decode_step", lay, [L, f, f, f, f, f, f, None, None, 0, f, need - 1, None, None], -3)
+    # null pointers / bad ranges
+    add("rtp_index_score", lay, [L, None, f, f, f, None], -1)
+    add("rtp_rope_keys", lay, [L, f, f, 10, 5, None], -1)
+    add("rtp_index_keys", lay, [L, f, f, f, 0, lay.N + 1, None], -1)
+    add("rtp_swa_attn", lay, [L, None, f, f, f, f, need, None], -1)
+    add("rtp_sparse_attn", lay, [L, f, f, f, f, f, -1, f, f, need, None], -1)
+    add("rtp_workspace_init", None, [None, 16, None], -1)
+    cap = lay.cap_rows
+    add("rtp_append_kv", lay, [L, f, f, f, f, f, f, cap - 1, 2, None], -1)            # past Ncap
+    add("rtp_append_kv", lay, [L, f, f, f, f, f, f, -1, 1, None], -1)
+    add("rtp_append_kv", lay, [L, f, f, f, f, f, f, 0, -1, None], -1)
+    add("rtp_append_kv", lay, [L, None, f, f, f, f, f, 0, 1, None], -1)
+    add("rtp_append_kv", lay, [L, f, f, None, f, f, f, 0, 1, None], -1)               # retrieval layer needs W_k
+    add("rtp_append_kv", lay, [L, None, None, None, None, None, None, 5, 0, None], 0)  # nothing to do
+    # misaligned workspace or arrays (the kernels use 16-byte vector accesses)
+    add("rtp_swa_attn", lay, [L, f, f, f, f, f + 8, need, None], -1)
+    add("rtp_swa_attn", lay, [L, f + 2, f, f, f, f, need, None], -1)
+    add("rtp_decode_step", lay, [L, f, f, f, f + 8, f, f, None, None, 0, f, need, None, None], -1)
+    add("rtp_index_keys", lay, [L, f, f, f + 4, 0, 10, None], -1)
+    add("rtp_append_kv", lay, [L, f, f, f, f, f + 16 + 8, f, 0, 1, None], -1)
+    # chunked prefill (nq > 1) is validated the same way before any launch
+    lay2 = _layer(nq=4)
+    need2 = rtp.workspace_bytes(lay2)
+    add("rtp_decode_step", lay2, [L, f, f, f, f, f, f, None, None, 0, f, need2 - 1, None, None], -3)
+    add("rtp_decode_step", lay2, [L, f, None, f, f, f, f, None, None, 0, f, need2, None, None], -1)
+    # ring layouts refuse calls that need positions a ring no longer holds
+    ring = _layer(local_ring=1)
+    nr = rtp.workspace_bytes(ring)
+    add("rtp_prefill_attn", ring, [L, f, f, f, f, 0, None], -4)
+    add("rtp_dense_attn", ring, [L, f, f, f, f, f, nr, None], -4)
+    r4 = _layer(local_ring=1, nq=4)
+    n4 = rtp.workspace_bytes(r4)
+    add("rtp_decode_step", r4, [L, f, f, f, f, f, f, None, None, 0, f, n4, None, None], -4)
+    add("rtp_swa_attn", r4, [L, f, f, f, f, f, n4, None], -4)
+    add("rtp_prefill_attn", _layer(local_ring=1, head_mode=[1, 0, 0, 0, 0, 0, 0, 1]), [L, None, f, f, f, 0, None], -1)
+    add("rtp_kv_rows", _layer(local_ring=3), [L], -1)
+    # cluster index
+    nc = rtp.load().rtp_cluster_workspace_bytes(ctypes.byref(lay.c()), 16)
+    add("rtp_cluster_workspace_bytes", lay, [L, 0], 0)
+    add("rtp_cluster_workspace_bytes", lay, [L, 257], 0)
+    add("rtp_cluster_workspace_bytes", _layer(N=10), [L, 11], 0)                        # K > N
+    add("rtp_cluster_build", lay, [L, f, 16, -1, f, f, f, f, f, nc, None], -1)
+    add("rtp_cluster_build", lay, [L, f, 16, 2, f, f, f, f, f, nc - 1, None], -3)
+    add("rtp_cluster_build", lay, [L, None, 16, 2, f, f, f, f, f, nc, None], -1)
+    for kw in (dict(top_k=5), dict(nq=4)):
+        lk = _layer(**kw)
+        nk = rtp.load().rtp_cluster_workspace_bytes(ctypes.byref(lk.c()), 16)
+        add("rtp_cluster_step", lk, [L, f, f, 16, f, f, f, f, f, f, f, None, None, 0, f, nk, None], -4)
+    add("rtp_cluster_step", lay, [L, f, f, 16, f, f, f, f, f, f, f, None, None, 0, f, nc - 1, None], -3)
+    # the allocation-free step: layer checks and the scratch bound, no device work
+    big = _layer(B=64, Hq=64, Hkv=8, N=1 << 20, head_mode=[1] * 64)
+    add("rtp_decode_step_static", big, [L, 16, 16, 16, 16, 16, 16, None, None, 0, None], -3)
+    add("rtp_decode_step_static", _layer(D=64), [L, 16, 16, 16, 16, 16, 16, None, None, 0, None], -2)
+    # invalid layers: every entry point's first check
+    for kw, code in INVALID_LAYERS:
+        bad = _layer(**kw)
+        add("rtp_num_retrieval", bad, [L], code)
+        add("rtp_workspace_bytes", bad, [L], 0)
+        add("rtp_decode_step", bad, [L, f, f, f, f, f, f, None, None, 0, f, 1 << 40, None, None], code)
+    return cases
+
+
+def ctypes_call(lib, name, lay, args):
+    c = lay.c() if lay is not None else None
+    return getattr(lib, name)(*[ctypes.byref(c) if isinstance(a, str) else a for a in args])
+
+
 @needs_lib
 def test_calls_reject_before_launch():
     lib = rtp.load()
-    lay = _layer()
-    L = ctypes.byref(lay.c())
-    need = rtp.workspace_bytes(lay)
-    fake = 1 << 40     # never dereferenced: every call below fails validation first
-    # workspace too small
-    assert lib.rtp_topp_select(L, fake, fake, fake, 16, fake, need - 1, None) == -3
-    assert lib.rtp_decode_step(L, fake, fake, fake, fake, fake, fake, None, None, 0, fake, need - 1, None, None) == -3
-    # null pointers / bad ranges
-    assert lib.rtp_index_score(L, None, fake, fake, fake, None) == -1
-    assert lib.rtp_rope_keys(L, fake, fake, 10, 5, None) == -1
-    assert lib.rtp_index_keys(L, fake, fake, fake, 0, lay.N + 1, None) == -1
-    assert lib.rtp_swa_attn(L, None, fake, fake, fake, fake, need, None) == -1
-    assert lib.rtp_sparse_attn(L, fake, fake, fake, fake, fake, -1, fake, fake, need, None) == -1
-    assert lib.rtp_workspace_init(None, 16, None) == -1
-    cap = lay.cap_rows
-    assert lib.rtp_append_kv(L, fake, fake, fake, fake, fake, fake, cap - 1, 2, None) == -1     # past Ncap
-    assert lib.rtp_append_kv(L, fake, fake, fake, fake, fake, fake, -1, 1, None) == -1
-    assert lib.rtp_append_kv(L, fake, fake, fake, fake, fake, fake, 0, -1, None) == -1
-    assert lib.rtp_append_kv(L, None, fake, fake, fake, fake, fake, 0, 1, None) == -1
-    assert lib.rtp_append_kv(L, fake, fake, None, fake, fake, fake, 0, 1, None) == -1           # retrieval layer needs W_k
-    assert lib.rtp_append_kv(L, None, None, None, None, None, None, 5, 0, None) == 0            # nothing to do
-    # misaligned workspace or arrays (the kernels use 16-byte vector accesses)
-    assert lib.rtp_swa_attn(L, fake, fake, fake, fake, fake + 8, need, None) == -1
-    assert lib.rtp_swa_attn(L, fake + 2, fake, fake, fake, fake, need, None) == -1
-    assert lib.rtp_decode_step(L, fake, fake, fake, fake + 8, fake, fake, None, None, 0, fake, need, None, None) == -1
-    assert lib.rtp_index_keys(L, fake, fake, fake + 4, 0, 10, None) == -1
-    assert lib.rtp_append_kv(L, fake, fake, fake, fake, fake + 16 + 8, fake, 0, 1, None) == -1
-    # chunked prefill (nq > 1) is validated the same way before any launch
-    lay2 = _layer(nq=4)
-    L2 = ctypes.byref(lay2.c())
-    need2 = rtp.workspace_bytes(lay2)
-    assert lib.rtp_decode_step(L2, fake, fake, fake, fake, fake, fake, None, None, 0, fake, need2 - 1, None, None) == -3
-    assert lib.rtp_decode_step(L2, fake, None, fake, fake, fake, fake, None, None, 0, fake, need2, None, None) == -1
+    for name, lay, args, code in abi_cases():
+        assert ctypes_call(lib, name, lay, args) == code, (name, args)
 
 
 @needs_lib
-def test_ring_layout_rows_and_limits():
-    """K/V rows per sequence with local_ring (closed form), and the calls that
-    need positions a ring no longer holds refuse it before any launch."""
-    lib = rtp.load()
-    fake = 1 << 40
+def test_ring_layout_rows():
+    """K/V rows per sequence with local_ring (closed form; the calls a ring
+    cannot serve are among abi_cases)."""
     N, W, S = 5000, 4096, 4
     # KV group 0 retrieval, group 1 all local
     assert rtp.kv_rows(_layer()) == 2 * N
@@ -146,43 +198,9 @@ def test_ring_layout_rows_and_limits():
     assert rtp.kv_rows(_layer(local_ring=1, head_mode=[0] * 8, window=100, n_sink=0)) == 2 * 100
     assert rtp.kv_rows(_layer(local_ring=1, head_mode=[1] * 8)) == 2 * N
     assert rtp.kv_rows(_layer(local_ring=1, Ncap=9000)) == 9000 + (S + W)
-    assert lib.rtp_kv_rows(ctypes.byref(_layer(local_ring=3).c())) == -1
-    ring = _layer(local_ring=1)
-    L = ctypes.byref(ring.c())
-    need = rtp.workspace_bytes(ring)
-    assert lib.rtp_prefill_attn(L, fake, fake, fake, fake, 0, None) == -4
-    assert lib.rtp_dense_attn(L, fake, fake, fake, fake, fake, need, None) == -4
-    r4 = _layer(local_ring=1, nq=4)
-    L4 = ctypes.byref(r4.c())
-    n4 = rtp.workspace_bytes(r4)
-    assert lib.rtp_decode_step(L4, fake, fake, fake, fake, fake, fake, None, None, 0, fake, n4, None, None) == -4
-    assert lib.rtp_swa_attn(L4, fake, fake, fake, fake, fake, n4, None) == -4
     # no ring group (every KV group has a retrieval head): local_ring changes nothing
     nr = _layer(local_ring=1, head_mode=[1, 0, 0, 0, 0, 0, 0, 1])
     assert rtp.kv_rows(nr) == 2 * N
-    assert lib.rtp_prefill_attn(ctypes.byref(nr.c()), None, fake, fake, fake, 0, None) == -1    # reaches the checks
-
-
-@needs_lib
-def test_cluster_calls_validate_before_launch():
-    lib = rtp.load()
-    fake = 1 << 40
-    lay = _layer()
-    L = ctypes.byref(lay.c())
-    need = lib.rtp_cluster_workspace_bytes(L, 16)
-    assert need > rtp.workspace_bytes(lay)
-    assert lib.rtp_cluster_workspace_bytes(L, 0) == 0 and lib.rtp_cluster_workspace_bytes(L, 257) == 0
-    assert lib.rtp_cluster_workspace_bytes(ctypes.byref(_layer(N=10).c()), 11) == 0      # K > N
-    assert lib.rtp_cluster_build(L, fake, 16, -1, fake, fake, fake, fake, fake, need, None) == -1
-    assert lib.rtp_cluster_build(L, fake, 16, 2, fake, fake, fake, fake, fake, need - 1, None) == -3
-    assert lib.rtp_cluster_build(L, None, 16, 2, fake, fake, fake, fake, fake, need, None) == -1
-    for kw in (dict(top_k=5), dict(nq=4)):
-        lk = _layer(**kw)
-        nk = lib.rtp_cluster_workspace_bytes(ctypes.byref(lk.c()), 16)
-        assert lib.rtp_cluster_step(ctypes.byref(lk.c()), fake, fake, 16, fake, fake, fake, fake, fake, fake, fake,
-                                    None, None, 0, fake, nk, None) == -4
-    assert lib.rtp_cluster_step(L, fake, fake, 16, fake, fake, fake, fake, fake, fake, fake, None, None, 0, fake,
-                                need - 1, None) == -3
 
 
 def test_layer_struct_follows_field_changes():
@@ -230,3 +248,135 @@ def test_static_step_checks_before_any_device_work():
     p = 16
     assert lib.rtp_decode_step_static(ctypes.byref(big.c()), p, p, p, p, p, p, None, None, 0, None) == -3
     assert lib.rtp_decode_step_static(ctypes.byref(_layer(D=64).c()), p, p, p, p, p, p, None, None, 0, None) == -2
+
+
+# ---------------------------------------------------------------- the checked host build
+def planner_layers(n=300, seed=7):
+    """Valid layers of many shapes (decode and chunked prefill, shared indexer
+    keys, rings, forced tilings, contexts up to 2^31 - 1) for the planners."""
+    import random
+    rng = random.Random(seed)
+    out = [_layer(), _layer(nq=4), _layer(local_ring=1), _layer(Hq=256, Hkv=2, head_mode=[1] * 128 + [0] * 128),
+           _layer(B=1, Hq=64, Hkv=8, N=1 << 20, head_mode=[1] * 16 + [0] * 48),
+           _layer(B=4, Hq=32, Hkv=8, N=1 << 17, head_mode=[1] * 4 + [0] * 28),
+           _layer(B=1, Hq=64, Hkv=8, N=1 << 20, head_mode=[1] * 16 + [0] * 48, idx_group=8),
+           _layer(B=1, Hq=4, Hkv=1, N=1 << 17, nq=4096, head_mode=[1] * 4),
+           _layer(B=1, Hq=1, Hkv=1, N=1, head_mode=[1]), _layer(B=1, Hq=1, Hkv=1, N=(1 << 31) - 1, head_mode=[0])]
+    while len(out) < n:
+        Hkv = rng.choice([1, 2, 4, 8, 16])
+        G = rng.choice([g for g in (1, 2, 4, 8, 16, 32) if g * Hkv <= 256])
+        Hq = G * Hkv
+        ig = rng.choice([1, G]) if G > 1 else 1
+        if ig > 1:
+            groups = [rng.random() < 0.5 for _ in range(Hkv)]
+            hm = [int(groups[h // G]) for h in range(Hq)]
+        else:
+            hm = [int(rng.random() < 0.4) for _ in range(Hq)]
+        N = rng.choice([1, 2, 17, 1023, 1024, 1025, 4096, 5000, 65537, 1 << 17, 1 << 20, 3 << 20, (1 << 31) - 1])
+        nq = rng.choice([1, 1, 1, 4, 17, 300])
+        if nq > N:
+            nq = 1
+        B = rng.choice([1, 2, 3, 8, 64])
+        kw = dict(B=B, Hq=Hq, Hkv=Hkv, N=N, nq=nq, head_mode=hm, idx_group=ig,
+                  window=rng.choice([1, 64, 4096, 10 ** 6]), n_sink=rng.choice([0, 4, 100]),
+                  top_k=rng.choice([0, 0, 1, 2048]), local_ring=rng.choice([0, 1]),
+                  scan_tile=rng.choice([0, 0, 1024, 2048, 4096, 8192]), swa_chunk=rng.choice([0, 0, 64, 1024]),
+                  pf_qch=rng.choice([0, 0, 16, 64]), p=rng.choice([0.1, 0.9, 0.99, 1.0, 2.0]))
+        if rng.random() < 0.3:
+            kw["Ncap"] = N + rng.choice([0, 1, 4096])
+        out.append(_layer(**kw))
+    return out
+
+
+def planner_calls(lay):
+    """Calls that run a layer's planners and stop before any launch."""
+    f, L = FAKE, "L"
+    return [("rtp_num_retrieval", [L]), ("rtp_kv_rows", [L]), ("rtp_workspace_bytes", [L]),
+            ("rtp_cluster_workspace_bytes", [L, 16]),
+            ("rtp_decode_step", [L, f, f, f, f, f, f, None, None, 0, f, 1, None, None]),
+            ("rtp_dense_attn", [L, f, f, f, f, f, 1, None]),
+            ("rtp_prefill_attn", [L, None, f, f, f, 0, None]),
+            ("rtp_topp_select", [L, f, f, f, 16, f, 1, None])]
+
+
+def quad_cases():
+    import random
+    rng = random.Random(11)
+    out = []
+    for Hq, Hkv in ((1, 1), (4, 1), (8, 2), (32, 8), (64, 8), (40, 8), (256, 1), (256, 2), (256, 64), (256, 256)):
+        for modes in ([1] * Hq, [0] * Hq, [int(rng.random() < 0.5) for _ in range(Hq)],
+                      [int(h % 3 == 0) for h in range(Hq)]):
+            for all_dense in (0, 1):
+                out.append((Hq, Hkv, all_dense, modes))
+    return out
+
+
+def check_quads(lines, Hq, Hkv, all_dense, modes):
+    """The head-quad plan of the prefill attention: every head exactly once, in
+    the mode it needs; quads of one KV group and one mode, up to four heads,
+    ascending, every quad but a group's last one full."""
+    st, n0, n1 = map(int, lines[0].split())
+    assert st == 0 and len(lines) == 1 + n0 + n1
+    G = Hq // Hkv
+    seen = []
+    per = {}
+    for ln in lines[1:]:
+        t = ln.split()
+        assert t[0] == "q"
+        mode, dense, nh = int(t[1]), int(t[3]), int(t[4])
+        heads = [int(x) for x in t[5:]]
+        assert dense == mode and 1 <= nh <= 4 and len(heads) == nh
+        assert heads == sorted(heads) and len({h // G for h in heads}) == 1
+        for h in heads:
+            assert mode == (1 if (all_dense or modes[h]) else 0), (h, mode)
+        per.setdefault((heads[0] // G, mode), []).append(nh)
+        seen += heads
+    assert sorted(seen) == list(range(Hq))
+    for (_, _), nhs in per.items():
+        assert all(x == 4 for x in nhs[:-1])
+
+
+@needs_lib
+def test_checked_host_build():
+    """The library's host code under AddressSanitizer + UBSan with the
+    planners' bounds assertions: the ABI cases give the same statuses, the
+    planners give the same sizes as the product build over many layer shapes,
+    and the prefill attention's head quads cover every head once (Hq = 256
+    included)."""
+    hc = pytest.importorskip("hostcheck")
+    if not hc.available():
+        pytest.skip("hipcc / clang++ not available")
+    lib = rtp.load()
+    lines, want = [], []
+    for name, lay, args, code in abi_cases():
+        lines.append(hc.call_line(name, lay, args))
+        want.append(str(code))
+    for lay in planner_layers():
+        for name, args in planner_calls(lay):
+            lines.append(hc.call_line(name, lay, args))
+            want.append(str(ctypes_call(lib, name, lay, args)))
+    lines.append("call rtp_status_str | -3")
+    want.append("s " + lib.rtp_status_str(-3).decode())
+    qc = quad_cases()
+    for Hq, Hkv, dense, modes in qc:
+        lines.append(f"quads {Hq} {Hkv} {dense} {','.join(map(str, modes))}")
+    rc, out, err = hc.run(lines)
+    assert rc == 0, err[-4000:]
+    assert "runtime error" not in err and "AddressSanitizer" not in err, err[-4000:]
+    got, rest = out[:len(want)], out[len(want):]
+    bad = [(ln[:160], w, g) for ln, w, g in zip(lines, want, got) if w != g]
+    assert not bad and len(got) == len(want), bad[:5]
+    for Hq, Hkv, dense, modes in qc:
+        n = 1 + sum(int(x) for x in rest[0].split()[1:3])
+        check_quads(rest[:n], Hq, Hkv, dense, modes)
+        rest = rest[n:]
+    assert not rest
+
+
+def test_checked_program_covers_every_entry_point():
+    src = open(os.path.join(ROOT, "tests", "host_check.cpp")).read() if os.path.exists(
+        os.path.join(ROOT, "tests", "host_check.cpp")) else None
+    if src is None:
+        pytest.skip("checked host program not present")
+    names = set(re.findall(r"RTP_ENTRY\((rtp_[a-z_0-9]+)\)", src))
+    assert names == set(declared_functions())
