@@ -2,7 +2,7 @@
 
   python prof_summary.py stats DIR OUT.txt --cmd "..."
       per-kernel dispatch counts and durations from a --kernel-trace run
-  python prof_summary.py counters DIR OUT.txt --kernel NAME --cmd "..."
+  python prof_summary.py counters DIR[,DIR2] OUT.txt --kernel NAME --cmd "..." [--units U --unit-name S]
       per-dispatch averages of every counter a --pmc run collected for one kernel,
       by grid size, with the LDS bank-conflict and matrix-core busy fractions
   python prof_summary.py traffic FETCH_DIR WRITE_DIR OUT.json --workload NAME --cmd "..."
@@ -82,13 +82,14 @@ def cmd_stats(a):
 
 
 CUS, SIMDS, CLOCK_HZ = 256, 1024, 2.4e9
+WAVE_SLOTS = 4 * SIMDS            # the decode kernels are built for 4 waves per SIMD (128 VGPRs)
 
 
 def cmd_counters(a):
     """Averages per dispatch (counters summed over the device's instances)."""
     per = defaultdict(float)
     info = {}
-    for db in dbs(a.dir):
+    for db in [x for d in a.dir.split(",") for x in dbs(d)]:
         con = sqlite3.connect(db)
         q = ("select c.dispatch_id, k.name, k.grid_x / k.workgroup_x, k.duration, c.counter_name, c.value "
              "from counters_collection c join kernels k on c.dispatch_id = k.dispatch_id")
@@ -115,6 +116,25 @@ def cmd_counters(a):
         if "SQ_LDS_BANK_CONFLICT" in c:
             v = sum(c["SQ_LDS_BANK_CONFLICT"]) / len(c["SQ_LDS_BANK_CONFLICT"])
             lines.append(f"    LDS bank-conflict stall / CU cycles  {v / CUS / cyc:.3f}")
+        # SQ_WAVE_CYCLES and SQ_ACTIVE_INST_* count in units of 4 cycles (one wave64
+        # VALU instruction occupies a 16-lane SIMD for 4 cycles)
+        if "SQ_ACTIVE_INST_VALU" in c:
+            v = sum(c["SQ_ACTIVE_INST_VALU"]) / len(c["SQ_ACTIVE_INST_VALU"])
+            lines.append(f"    VALU busy / SIMD cycles              {4 * v / SIMDS / cyc:.3f}")
+        if "SQ_ACTIVE_INST_LDS" in c:
+            v = sum(c["SQ_ACTIVE_INST_LDS"]) / len(c["SQ_ACTIVE_INST_LDS"])
+            lines.append(f"    LDS instruction issue / SIMD cycles  {4 * v / SIMDS / cyc:.3f}")
+        if "SQ_WAVE_CYCLES" in c:
+            v = sum(c["SQ_WAVE_CYCLES"]) / len(c["SQ_WAVE_CYCLES"])
+            lines.append(f"    mean resident waves                  {4 * v / cyc:.0f} "
+                         f"(of {WAVE_SLOTS} at 4 waves per SIMD: {4 * v / cyc / WAVE_SLOTS:.3f})")
+        if "SQ_INSTS_VALU" in c and a.units:
+            v = sum(c["SQ_INSTS_VALU"]) / len(c["SQ_INSTS_VALU"])
+            lines.append(f"    VALU lane-instructions per {a.unit_name:10s} {64 * v / a.units:.1f}")
+            for cn in ("SQ_INSTS_VALU_FMA_F64", "SQ_INSTS_VALU_CVT", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD"):
+                if cn in c:
+                    v = sum(c[cn]) / len(c[cn])
+                    lines.append(f"    {cn + ' lanes per ' + a.unit_name:38s} {64 * v / a.units:.2f}")
         if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
             v = sum(c["SQ_VALU_MFMA_BUSY_CYCLES"]) / len(c["SQ_VALU_MFMA_BUSY_CYCLES"])
             lines.append(f"    matrix-core busy / SIMD cycles       {v / SIMDS / cyc:.3f}")
@@ -184,6 +204,8 @@ def main():
     c.add_argument("dir")
     c.add_argument("out")
     c.add_argument("--kernel", required=True)
+    c.add_argument("--units", type=float, default=0.0, help="work units per dispatch (e.g. indexer scores)")
+    c.add_argument("--unit-name", default="unit")
     c.add_argument("--cmd", required=True)
     c.add_argument("--title", default="")
     t = sp.add_parser("traffic")
