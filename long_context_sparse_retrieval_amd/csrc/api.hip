@@ -58,13 +58,11 @@ constexpr long long kSlots = 1024;
 int pick_tile(long long N, int forced) {
   if (forced) return forced;
   // The largest tile that still gives four tiles per query, up to 8192
-  // positions below 2^19 and 4096 from there on: long contexts have tiles
-  // enough to fill the GPU several times over, and the 8192-position build
-  // keeps 32 scores per thread in registers where the 4096 one keeps 16
-  // (measured at 1M: phase A 107 us against 113 us).
-  const int tmax = N < (1ll << 19) ? 8192 : 4096;
+  // positions: fewer, longer tiles mean fewer tile summaries and prefix
+  // entries for the selection launch (measured at 1M: phase A 102.8 us at
+  // 8192 against 106.4 at 4096 and 134.3 at 2048; at 128K 8192 is best too).
   int T = 1024;
-  while (T < tmax && 4 * T <= N) T *= 2;
+  while (T < 8192 && 4 * T <= N) T *= 2;
   return T;
 }
 

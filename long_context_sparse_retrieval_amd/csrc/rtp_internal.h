@@ -183,6 +183,19 @@ __device__ __forceinline__ uint4 ld_stream(const void *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// The same stream through a buffer resource: `bytes` bytes at base (below
+// 2^31), a load at or beyond them returns zeros, so a tile's rows are read
+// with one 32-bit offset per lane and a scalar offset per step (no 64-bit
+// address arithmetic, no clamping).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld_stream(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+  const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2);    // 2: non-temporal
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ------------------------------------------------------------------ numerics
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -252,13 +265,19 @@ __device__ __forceinline__ double dot8_exact(const double *q, uint4 a) {
 // The value of the other lane of an adjacent lane pair (lanes 2j, 2j + 1).
 __device__ __forceinline__ double swap_pair(double v) {
   const unsigned long long b = (unsigned long long)__double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, 0xB1, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), 0xB1, 0xF, 0xF, false);
+  // every lane is a source (full masks), so the "old" operand is never used
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, 0xB1, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), 0xB1, 0xF, 0xF, true);
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
-// Cell of a score: floor(8 s) (exact: 8 s is exact in fp32).
-__device__ __forceinline__ int score_cell(float s) { return (int)floorf(s * 8.0f); }
+// Cell of a score: floor(8 s) (exact: 8 s is exact in fp32), converted by
+// the one instruction that floors and converts.
+__device__ __forceinline__ int score_cell(float s) {
+  int c;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(c) : "v"(s * 8.0f));
+  return c;
+}
 
 // In-cell weight exp(s - ref/8) of a token with score s, as a fixed-point
 // integer with 2^23 = 1.  Regular bins use ref = cell(s), giving a value in

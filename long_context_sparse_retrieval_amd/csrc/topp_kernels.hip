@@ -226,78 +226,116 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
   const long long m = g.N - g.nq + i;
   const long long n0 = (long long)t * T;
 
-  // pass 1: scores in registers; consecutive threads take consecutive positions.
-  // Each score is binned at once by its absolute cell (no tile max needed), so
-  // the histogram work overlaps the stream.  The first batch of key rows is
-  // requested before the query projection.
-  float lg[TPT];
+  // pass 1: every score is binned at once by its absolute cell (no tile max
+  // needed), so the histogram work overlaps the stream, and each lane keeps
+  // its scores' cells as 16-bit integers, two per register (kNoCell: no
+  // position).  A tile whose cells leave 16 bits, or span more than the
+  // streaming histogram holds, recomputes its scores afterwards (rare).  The
+  // first batch of key rows is requested before the query projection.
+  constexpr int kNoCell = -32768;
+  uint32_t cl[(TPT + 1) / 2];
+  // (the byte permute packs the low halves of two cells; the compiler does not
+  // see through it, so it cannot keep the 32-bit cells alive instead)
+  auto put_cell = [&](int k, int c) {
+    cl[k >> 1] = (k & 1) ? __builtin_amdgcn_perm((uint32_t)c, cl[k >> 1], 0x05040100u) : (uint32_t)c;
+  };
+  auto get_cell = [&](int k) -> int {
+    return (k & 1) ? ((int)cl[k >> 1] >> 16) : (int)(int16_t)(cl[k >> 1] & 0xffffu);
+  };
   float mx = -INFINITY;
   int cmin = INT32_MAX;
+  const bool topk = g.topk != 0;
   for (int x = tid; x < 4 * kCells; x += kWG) (&sm.hist[0][0])[x] = 0ull;
+  // bin one score by its absolute cell and return the cell clamped to 16 bits
+  // (kNoCell for an absent score, -inf, which adds nothing when CHECK);
   // branchless, so a whole batch of rows stays one basic block and its loads
-  // can be issued together; absent positions (-inf) add nothing
-  auto bin_abs = [&](float sc) {
-    const bool ok = sc != -INFINITY;
+  // can be issued together
+  auto bin_abs = [&](float sc, auto check_tag) -> int {
+    constexpr bool CHECK = decltype(check_tag)::value;
+    const bool ok = !CHECK || sc != -INFINITY;
     const float s = ok ? sc : 0.f;
     const int cell = score_cell(s);
-    const unsigned long long add = ok ? ((unsigned long long)token_weight(g, s, cell) | (1ull << kCountShift)) : 0ull;
+    const uint32_t w = topk ? kUnitWeight : cell_weight(s, cell);
+    const unsigned long long add = ok ? ((unsigned long long)w | (1ull << kCountShift)) : 0ull;
     atomicAdd(&sm.hist[wv][cell & (kCells - 1)], add);
     mx = fmaxf(mx, sc);
     cmin = min(cmin, ok ? cell : INT32_MAX);
+    const int c16 = min(max(cell, -32767), 32767);
+    return ok ? c16 : kNoCell;
   };
-  if (FROM_LOGITS) {
-    __syncthreads();
-    const float *row = logits + (size_t)unit * g.N;
-#pragma unroll
-    for (int k = 0; k < TPT; ++k) {
-      const long long n = n0 + k * kWG + tid;
-      const float sc = row[n <= m ? n : m];            // clamped, unconditional load
-      lg[k] = n <= m ? sc : -INFINITY;
-      bin_abs(lg[k]);
+  // key path: the tile's rows at or before m form one buffer range (loads
+  // past it return zeros).  Each load instruction covers 1 KB of consecutive
+  // key rows: lane 2j + h of a wave reads half h (8 dims) of row R + j and of
+  // row R + 32 + j, so the two lanes of a pair hold complementary halves of
+  // two rows.  Each lane forms the two exact half-dots, the pair swaps one of
+  // them, and lane 2j keeps the score of row R + j, lane 2j + 1 that of row
+  // R + 32 + j (scan_pos); halves of an exact dot add exactly.  (Lanes that
+  // read different halves of one 128-byte line in two instructions would
+  // fetch the line twice: non-temporal loads do not keep it.)
+  const long long valid = m + 1 - n0 < T ? (m + 1 - n0 > 0 ? m + 1 - n0 : 0) : T;
+  const int lpos = (int)scan_pos<FROM_LOGITS>(0, 0, tid);
+  constexpr int kStep = kWG * 32;                                    // bytes of key rows per step
+  double qh[kR / 2];                                                 // this lane's half of q_idx
+  const int h = tid & 1, jr = (tid & ~63) + ((tid & 63) >> 1);
+  const int voff_a = (jr * 2 + h) * 16, voff_b = ((jr + 32) * 2 + h) * 16;    // rows R + j, R + 32 + j
+  // lane 2j sends its half of row R + 32 + j and keeps row R + j; lane 2j + 1
+  // the other way round
+  auto pair_score = [&](uint4 a, uint4 c) -> float {
+    const double pa = dot8_exact(qh, a), pb = dot8_exact(qh, c);
+    const double recv = swap_pair(h ? pa : pb);
+    return (float)((h ? pb : pa) + recv);
+  };
+  const __amdgpu_buffer_rsrc_t rows =
+      stream_rsrc(FROM_LOGITS ? (const void *)logits
+                              : (const void *)(k_idx + (((size_t)b * g.Hi + r / g.ig) * g.Ncap + n0) * kR),
+                  FROM_LOGITS ? 0u : (uint32_t)valid * 32u);
+  const float *lrow = logits + (size_t)unit * g.N;
+  // score k of this lane recomputed from memory (the stream's arithmetic)
+  auto rescore = [&](int k) -> float {
+    const bool in = k * kWG + lpos < valid;
+    if constexpr (FROM_LOGITS) {
+      const long long n = n0 + k * kWG + lpos;
+      const float sc = lrow[in ? n : m];
+      return in ? sc : -INFINITY;
+    } else {
+      const float sc = pair_score(ld_stream(rows, voff_a, k * kStep), ld_stream(rows, voff_b, k * kStep));
+      return in ? sc : -INFINITY;
     }
+  };
+  if constexpr (FROM_LOGITS) {
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) put_cell(k, bin_abs(rescore(k), std::true_type{}));
   } else {
-    // Each load instruction covers 1 KB of consecutive key rows: lane 2j + h
-    // of a wave reads half h (8 dims) of row R + j and of row R + 32 + j, so
-    // the two lanes of a pair hold complementary halves of two rows.  Each
-    // lane forms the two exact half-dots, the pair swaps one of them, and lane
-    // 2j keeps the score of row R + j, lane 2j + 1 that of row R + 32 + j
-    // (scan_pos).  Halves of an exact dot add exactly, in either order.
-    // Rolling window of BATCH row pairs per lane: slot u is refilled BATCH
-    // steps ahead as soon as it is consumed; loads are clamped to a valid row
-    // and unconditional.
-    const uint4 *rows = reinterpret_cast<const uint4 *>(k_idx + ((size_t)b * g.Hi + r / g.ig) * g.Ncap * kR);
-    const int h = tid & 1;
-    const long long rA0 = n0 + (tid & ~63) + ((tid & 63) >> 1);     // row R + j of step 0
+    // rolling window of BATCH row pairs per lane: slot u is refilled BATCH
+    // steps ahead as soon as it is consumed
     uint4 ra[BATCH], rb[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const long long na = rA0 + u * kWG, nb = na + 32;
-      ra[u] = ld_stream(rows + 2 * (na <= m ? na : m) + h);
-      rb[u] = ld_stream(rows + 2 * (nb <= m ? nb : m) + h);
+      ra[u] = ld_stream(rows, voff_a, u * kStep);
+      rb[u] = ld_stream(rows, voff_b, u * kStep);
     }
     project_query(q_pre + (((size_t)b * g.Hq + g.rhead[r]) * g.nq + i) * kD, w_q + (size_t)r * kD * kR, sm.q,
                   sm.qtmp);
-    double qh[kR / 2];                                   // this lane's half of q_idx
 #pragma unroll
     for (int x = 0; x < kR / 2; ++x) qh[x] = sm.q[8 * h + x];
+    // full tiles (every row at or before m) skip the validity test
+    auto stream = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
-    for (int k = 0; k < TPT; ++k) {
-      const int u = k % BATCH;
-      const double pa = dot8_exact(qh, ra[u]), pb = dot8_exact(qh, rb[u]);
-      // lane 2j sends its half of row R + 32 + j and receives its partner's
-      // half of row R + j; lane 2j + 1 the other way round
-      const double send = h ? pa : pb;
-      const double recv = swap_pair(send);
-      const float sc = (float)((h ? pb : pa) + recv);
-      const long long n = scan_pos<false>(n0, k, tid);
-      lg[k] = n <= m ? sc : -INFINITY;
-      bin_abs(lg[k]);
-      if (k + BATCH < TPT) {
-        const long long na = rA0 + (k + BATCH) * kWG, nb = na + 32;
-        ra[u] = ld_stream(rows + 2 * (na <= m ? na : m) + h);
-        rb[u] = ld_stream(rows + 2 * (nb <= m ? nb : m) + h);
+      for (int k = 0; k < TPT; ++k) {
+        const int u = k % BATCH;
+        float sc = pair_score(ra[u], rb[u]);
+        if (!FULL) sc = k * kWG + lpos < valid ? sc : -INFINITY;
+        put_cell(k, bin_abs(sc, std::integral_constant<bool, !FULL>{}));
+        if (k + BATCH < TPT) {
+          ra[u] = ld_stream(rows, voff_a, (k + BATCH) * kStep);
+          rb[u] = ld_stream(rows, voff_b, (k + BATCH) * kStep);
+        }
       }
-    }
+    };
+    if (valid == T) stream(std::true_type{});
+    else stream(std::false_type{});
   }
   block_max_min(mx, cmin, sm.red_f, sm.red_i);
   const int c_t = (mx == -INFINITY) ? INT32_MIN : score_cell(mx);
@@ -306,8 +344,8 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
   // weighted relative to its base cell c_t - 255
   unsigned long long packed = 0;
   // (a span of at most kCells - 2 keeps every cell unique mod kCells and the clamp
-  // cells c_t - 255 .. cmin within the 256 threads below)
-  if (c_t != INT32_MIN && (long long)c_t - cmin <= kCells - 2) {
+  // cells c_t - 255 .. cmin within the 256 threads below; 16-bit cells are exact)
+  if (c_t != INT32_MIN && (long long)c_t - cmin <= kCells - 2 && c_t <= 32767 && cmin >= -32767) {
     const int j = tid;
     if (j < kBins - 1) {
       const int cell = c_t - j;
@@ -332,35 +370,34 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
       (void)block_excl_scan<unsigned long long>(cc, tc, sm.red_u);
       if (j == kBins - 1) packed = (unsigned long long)tm | (tc << kCountShift);
     }
+    // codes (local bins) from the cells in registers
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) {
+      const int cell = get_cell(k);
+      const int jb = c_t - cell;
+      sm.codes[scan_pos<FROM_LOGITS>(0, k, tid)] =
+          (uint8_t)(cell == kNoCell || jb >= kBins - 1 ? kBins - 1 : jb);
+    }
   } else {
-    // cells of this tile span kCells or more: rebin relative to c_t from the scores in registers
+    // rebin relative to c_t, recomputing the scores
     __syncthreads();
     for (int x = tid; x < 4 * kBins; x += kWG) sm.hist[x / kBins][x % kBins] = 0ull;
     __syncthreads();
-#pragma unroll
     for (int k = 0; k < TPT; ++k) {
-      const float sc = lg[k];
-      if (sc == -INFINITY) continue;
-      const int cell = score_cell(sc);
-      const int jb = c_t - cell >= kBins - 1 ? kBins - 1 : c_t - cell;
-      const uint32_t u = jb == kBins - 1 ? token_weight(g, sc, c_t - (kBins - 1)) : token_weight(g, sc, cell);
-      atomicAdd(&sm.hist[wv][jb], (unsigned long long)u | (1ull << kCountShift));
+      const float sc = rescore(k);
+      uint8_t code = kBins - 1;
+      if (sc != -INFINITY) {
+        const int cell = score_cell(sc);
+        const int jb = c_t - cell >= kBins - 1 ? kBins - 1 : c_t - cell;
+        const uint32_t u = jb == kBins - 1 ? token_weight(g, sc, c_t - (kBins - 1)) : token_weight(g, sc, cell);
+        atomicAdd(&sm.hist[wv][jb], (unsigned long long)u | (1ull << kCountShift));
+        code = (uint8_t)jb;
+      }
+      sm.codes[scan_pos<FROM_LOGITS>(0, k, tid)] = code;
     }
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < 4; ++w) packed += sm.hist[w][tid];
-  }
-
-  // codes (local bins) from the scores in registers
-#pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    const float sc = lg[k];
-    uint8_t code = 255;
-    if (sc != -INFINITY) {
-      const int jb = c_t - score_cell(sc);
-      code = (uint8_t)(jb >= kBins - 1 ? kBins - 1 : jb);
-    }
-    sm.codes[scan_pos<FROM_LOGITS>(0, k, tid)] = code;
   }
   __syncthreads();
   {
