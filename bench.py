@@ -146,6 +146,7 @@ class Case:
         k_idx, k, v = self.reps[0]
         rtp.decode_step(self.layer, self.q, self.w_q, k_idx, k, v, self.ws, self.out, idx=idx, count=cnt)
         torch.cuda.synchronize()
+        self.sel = (idx, cnt)                   # the step's own sets, for selection_stats
         idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
         self.counts = cnt[:, :, 0]
         rheads = spec.retrieval_heads()
@@ -284,6 +285,36 @@ def read_ceiling() -> dict:
             best = (gbps, key)
     del buf
     return {"GBps": round(best[0], 1), "config": best[1], "bytes": nbytes, "sweep": sweep}
+
+
+def exp_lds_ceiling(blocks: int = 4096, rounds: int = 128) -> dict:
+    """Scores per second of libreadprobe.so's exp_lds_kernel: the chunked
+    prefill's per-score histogram work (cell, in-cell exponential weight, one
+    64-bit LDS atomic into one of 16 per-query histograms) with no indexer and
+    no memory traffic -- the arithmetic ceiling of the selection's histogram pass."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_sparse_retrieval_amd", "libreadprobe.so"))
+    lib.readprobe_exp_lds.restype = ctypes.c_int
+    lib.readprobe_exp_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def one():
+        st = lib.readprobe_exp_lds(blocks, rounds, sink.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError(f"readprobe_exp_lds: status {st}")
+    one()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        one()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    scores = blocks * 256 * 16 * rounds
+    return {"scores_per_s": round(scores / (ms * 1e-3), 1), "ms_per_launch": round(ms, 4),
+            "scores_per_launch": scores, "workgroups": blocks}
 
 
 def calibration_copy(n_bytes: int = 1 << 30, reps: int = 3) -> None:
@@ -523,6 +554,41 @@ def time_prefill() -> dict:
             "peak_bf16_TFLOPs": 2500.0}
 
 
+def selection_stats(case: Case) -> dict:
+    """What the Top-P sets of the step keep, per query class of the workload
+    (needle-class queries with a few strong keys, diffuse ones): |S|, the
+    sparsity 1 - |S| / N and the retained indexer mass sum_{n in S} softmax(s)_n
+    (>= p by construction), from the library's own scores (rtp_index_score)
+    and sets, summed in fp64."""
+    spec, lay = case.spec, case.layer
+    idx, cnt = case.sel
+    logits = rtp.index_score(lay, case.q, case.w_q, case.reps[0][0])
+    rows = []
+    for b in range(spec.B):
+        for r in range(spec.Hr):
+            s = logits[b, r, 0].double()
+            w = torch.exp(s - s.max())
+            c = int(cnt[b, r, 0].item())
+            sel = idx[b, r, 0, :c].long()
+            rows.append({"b": b, "r": r, "cls": int(case.wl.classes.get((b, r), -1)), "S": c,
+                         "sparsity": 1.0 - c / spec.N, "mass": float(w[sel].sum() / w.sum())})
+    del logits
+    out = {"p": spec.p, "N": spec.N}
+    for cls, name in ((0, "needle_class"), (1, "diffuse")):
+        q = [x for x in rows if x["cls"] == cls]
+        if not q:
+            continue
+        out[name] = {"queries": len(q),
+                     "S_mean": round(float(np.mean([x["S"] for x in q])), 1),
+                     "S_min": min(x["S"] for x in q), "S_max": max(x["S"] for x in q),
+                     "sparsity_mean": round(float(np.mean([x["sparsity"] for x in q])), 6),
+                     "retained_mass_mean": round(float(np.mean([x["mass"] for x in q])), 6),
+                     "retained_mass_min": round(min(x["mass"] for x in q), 6)}
+    out["per_query"] = [[x["b"], x["r"], x["cls"], x["S"], round(x["mass"], 6)] for x in rows]
+    out["per_query_fields"] = ["b", "retrieval head", "class (0 needle, 1 diffuse)", "|S|", "retained mass"]
+    return out
+
+
 def time_other_decode(cfg: int, steps: int, warmup: int, replicas: int) -> dict:
     """The decode step of another workload of the benchmark description, timed
     like the headline (needle 4K: a launch-latency case, its bytes fraction is
@@ -530,10 +596,22 @@ def time_other_decode(cfg: int, steps: int, warmup: int, replicas: int) -> dict:
     case = Case(cfg, replicas)
     ms, ms_pa = case.run(steps, warmup)
     gbps = case.bytes_total / (ms * 1e-3) / 1e9
-    return {"workload": case.spec.name, "us_per_step": round(ms * 1e3, 2), "GBps": round(gbps, 1),
-            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_step": case.bytes_total,
-            "phase_a_kernel_us": round(ms_pa * 1e3, 2), "instrumented_us_per_step": case.instr_us,
-            "selected_tokens": case.counts.ravel().tolist()}
+    out = {"workload": case.spec.name, "us_per_step": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+           "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_step": case.bytes_total,
+           "phase_a_kernel_us": round(ms_pa * 1e3, 2), "instrumented_us_per_step": case.instr_us,
+           "selected_tokens": case.counts.ravel().tolist()}
+    if case.spec.N >= 32768:
+        # the same step with every head attending over every cached position
+        ms_dense = case.run_dense(max(5, steps // 10), 3)
+        dense_bytes = 512 * case.spec.B * case.spec.Hkv * case.spec.N
+        dense_peak_us = dense_bytes / HBM_PEAK_GBPS / 1e3
+        out["dense_comparator"] = {"what": "rtp_dense_attn: every head over every cached position, same caches",
+                                   "us_per_step": round(ms_dense * 1e3, 2),
+                                   "GBps": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1),
+                                   "sparse_speedup": round(ms_dense / ms, 3),
+                                   "dense_at_hbm_peak_us": round(dense_peak_us, 2),
+                                   "sparse_speedup_vs_dense_at_peak": round(dense_peak_us / (ms * 1e3), 3)}
+    return out
 
 
 def time_chunked_prefill(calls: int = 3) -> dict:
@@ -567,12 +645,66 @@ def time_chunked_prefill(calls: int = 3) -> dict:
     ms = e0.elapsed_time(e1) / calls
     prefix = sum(spec.N - spec.nq + i + 1 for i in range(spec.nq))
     logits = spec.B * spec.Hr * prefix
-    rows = int(cnt.sum().item())
-    return {"workload": spec.name, "what": "rtp_decode_step, nq = 4096 causal queries (chunked prefill selection "
-                                            "and sparse attention of 4 retrieval heads)",
-            "ms_per_call": round(ms, 3), "logits_per_call": logits,
-            "logits_per_s": round(logits / (ms * 1e-3), 1), "gathered_rows": rows,
-            "gathered_GB": round(rows * 512 / 1e9, 3)}
+    c = cnt.cpu().numpy()[0]                                    # [Hr, nq]
+    rows = int(c.sum())
+    # |S| per topic: query i takes topic i mod 2 (0 concentrated, 1 diffuse)
+    per_topic = {}
+    for tpc, name in ((0, "concentrated_topic"), (1, "diffuse_topic")):
+        s = c[:, tpc::2].ravel()
+        per_topic[name] = {"queries": int(s.size), "S_mean": round(float(s.mean()), 1),
+                           "S_p10": int(np.percentile(s, 10)), "S_p50": int(np.percentile(s, 50)),
+                           "S_p90": int(np.percentile(s, 90)), "S_min": int(s.min()), "S_max": int(s.max()),
+                           "per_head_mean": [round(float(x), 1) for x in c[:, tpc::2].mean(axis=1)]}
+    ceil = exp_lds_ceiling()
+    out = {"workload": spec.name, "what": "rtp_decode_step, nq = 4096 causal queries (chunked prefill selection "
+                                          "and sparse attention of 4 retrieval heads)",
+           "ms_per_call": round(ms, 3), "logits_per_call": logits,
+           "logits_per_s": round(logits / (ms * 1e-3), 1), "gathered_rows": rows,
+           "gathered_GB": round(rows * 512 / 1e9, 3),
+           "S_mean_per_query": round(rows / c.size, 1),
+           "calibration": ("one query scale per (head, topic), calibrated on the longest prefix to |S| = 500 / "
+                           "2500; every other query carries its own 0.3 xi perturbation, so the sets drift far "
+                           "from the targets: the workload runs at the |S| reported here, not at 500 / 2500"),
+           "S_per_topic": per_topic,
+           "exp_lds_ceiling": ceil,
+           "histogram_pass_scores": logits}
+    # the kernel split of this call from its committed rocprofv3 trace (same command)
+    split = chunked_prefill_split()
+    if split:
+        sel_us, attn_us = split["pf_select_kernel"], split["pf_attn_kernel"]
+        out["kernel_split"] = {"source": split["source"], "pf_select_kernel_us": sel_us,
+                               "pf_attn_kernel_us": attn_us,
+                               "pf_select_scores_per_s": round(logits / (sel_us * 1e-6), 1),
+                               "pf_select_frac_of_exp_lds_ceiling": round(logits / (sel_us * 1e-6)
+                                                                          / ceil["scores_per_s"], 4),
+                               "attention_gather_GBps": round(rows * 512 / (attn_us * 1e-6) / 1e9, 1)}
+    return out
+
+
+CP_TRACE = os.path.join(ROOT, "profiles", "pf_select_kernel.prefill-128k-4096q-4h.kernel_trace.txt")
+
+
+def chunked_prefill_split() -> dict | None:
+    """Average pf_select_kernel / pf_attn_kernel durations (us) per call from the
+    committed kernel trace of `bench.py --chunked-prefill` (kernels per call:
+    one of each per chunk of queries, summed)."""
+    if not os.path.exists(CP_TRACE):
+        return None
+    per, calls = {}, {}
+    with open(CP_TRACE, encoding="utf-8") as fh:
+        for line in fh:
+            f = line.split()
+            if len(f) >= 7 and f[0].startswith(("pf_select_kernel", "pf_attn_kernel")):
+                name = f[0].split("<")[0]
+                n, avg = int(f[-5]), float(f[-4])
+                per[name] = per.get(name, 0.0) + n * avg
+                calls[name] = calls.get(name, 0) + n
+    if "pf_select_kernel" not in per or "pf_attn_kernel" not in per:
+        return None
+    ncall = 4                                   # the traced command makes one set-up call and three timed calls
+    return {"source": os.path.relpath(CP_TRACE, ROOT),
+            "pf_select_kernel": round(per["pf_select_kernel"] / ncall, 1),
+            "pf_attn_kernel": round(per["pf_attn_kernel"] / ncall, 1)}
 
 
 CPU_WORKERS_MAX = 16       # host cores that go with one GPU on the measuring machines
@@ -811,6 +943,14 @@ def main():
         log(f"[bench] cfg{cfg}: {ms * 1e3:.1f} us/step, phase-A kernel {ms_pa * 1e3:.1f} us, {gbps:.0f} GB/s "
             f"algorithmic; |S| {case.counts.ravel().tolist()}; dense comparator {ms_dense * 1e3:.1f} us "
             f"({dense_bytes / (ms_dense * 1e-3) / 1e9:.0f} GB/s), sparse step {ms_dense / ms:.2f}x faster")
+        if cfg in (3, 4):
+            summ[cfg]["selection"] = selection_stats(case)
+            sel = summ[cfg]["selection"]
+            log(f"[bench] cfg{cfg}: selection " + "; ".join(
+                f"{k}: |S| {v['S_mean']}, sparsity {v['sparsity_mean']}, retained mass {v['retained_mass_mean']}"
+                for k, v in sel.items() if isinstance(v, dict)))
+        case.sel = None
+        torch.cuda.empty_cache()
         if cfg in (3, 4) and not args.no_extras:
             with quiet_gc():
                 summ[cfg]["cluster"] = time_cluster(case, max(20, args.steps // 4))
@@ -911,6 +1051,8 @@ def main():
         out["fixed_top_k"] = {"k": TOPK_BENCH, "us_per_step": round(s["topk_us"], 2),
                               "phase_a_kernel_us": round(s["topk_pa_us"], 2),
                               "what": "same step with rtp_layer.top_k = k instead of Top-P, same caches"}
+    if "selection" in s:
+        out["selection"] = s["selection"]
     if "append" in s:
         out["cache_append"] = s["append"]
     if "ring" in s:
@@ -939,6 +1081,8 @@ def main():
                            "selected_tokens": s3["counts"].ravel().tolist()}
         if "cluster" in s3:
             out["ctx_128k"]["cluster_index"] = s3["cluster"]
+        if "selection" in s3:
+            out["ctx_128k"]["selection"] = s3["selection"]
     if 6 in summ and main_cfg != 6:
         s6 = summ[6]
         out["shared_keys_1m"] = {"workload": s6["spec"].name, "indexer_key_heads": s6["spec"].Hi,

@@ -10,8 +10,14 @@
 //    thread (the access pattern of the indexer scan).
 // Every word read is folded into one register; a word written only when the
 // fold hits a chosen value keeps the loads alive.
+//
+// A third probe, exp_lds_kernel, measures the arithmetic ceiling of the
+// chunked prefill's histogram pass (exponential + LDS integer atomic per
+// score, no memory traffic).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "rtp_internal.h"
 
 namespace {
 
@@ -133,6 +139,44 @@ int launch(const v4u *p, size_t n16, unsigned *sink, int blocks, int unroll, int
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
+// The per-score work of the chunked prefill's histogram pass without the
+// indexer: each lane bins scores of one of 16 queries (lane mod 16) into that
+// query's 256-bin histogram in LDS with one 64-bit integer atomic, the weight
+// being the in-cell exp(s - c/8) as a fixed-point integer (the selection
+// kernels' own score_cell / cell_weight).  Scores: 16 per lane, uniform in
+// [-3, 3) from a per-lane generator, each moved by 2^-12 per round so that no
+// round can reuse the previous one's arithmetic.  The rate of this loop is the
+// ceiling of that pass on this device.
+__global__ __launch_bounds__(256) void exp_lds_kernel(int rounds, unsigned *__restrict__ sink) {
+  __shared__ unsigned long long hist[16][rtp::kBins];
+  for (int x = threadIdx.x; x < 16 * rtp::kBins; x += 256) (&hist[0][0])[x] = 0ull;
+  __syncthreads();
+  const int q = threadIdx.x & 15;
+  constexpr int cq = 24;                                 // max cell of scores below 3
+  uint32_t st = (blockIdx.x * 256u + threadIdx.x) * 2654435761u + 12345u;
+  float s[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    st = st * 1664525u + 1013904223u;
+    s[k] = (float)(st >> 8) * (6.0f / 16777216.0f) - 3.0f;
+  }
+  for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float sc = s[k];
+      const int cell = rtp::score_cell(sc);
+      int j = cq - cell;
+      const int ref = j >= rtp::kBins - 1 ? cq - (rtp::kBins - 1) : cell;
+      j = j >= rtp::kBins - 1 ? rtp::kBins - 1 : j;
+      const uint32_t w = rtp::cell_weight(sc, ref);
+      atomicAdd(&hist[q][j], (unsigned long long)w | (1ull << 41));
+      s[k] = sc + 0.000244140625f;
+    }
+  }
+  __syncthreads();
+  if (hist[q][threadIdx.x >> 4] == 0x9e3779b97f4a7c15ull) sink[0] = 1u;
+}
+
 }  // namespace
 
 extern "C" {
@@ -145,6 +189,16 @@ extern "C" {
 // nontemporal != 0 uses non-temporal loads.  sink: one device word (written
 // only by chance).  Returns 0, or -1 for invalid arguments, -5 for a failed
 // launch.
+// Enqueue `blocks` workgroups of exp_lds_kernel, each binning 256 * 16 *
+// rounds scores (rounds in 1..2048).  sink: one device word (written only by
+// chance).  Returns 0, -1 for invalid arguments, -5 for a failed launch.
+int readprobe_exp_lds(int blocks, int rounds, unsigned *sink, void *stream) {
+  if (!sink || blocks < 1 || rounds < 1 || rounds > 2048) return -1;
+  hipLaunchKernelGGL(exp_lds_kernel, dim3(blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), rounds,
+                     sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
 int readprobe_stream(const void *src, size_t bytes, unsigned *sink, int blocks, int unroll, int chunked,
                      int nontemporal, void *stream) {
   if (!src || !sink || (bytes & 15) || (reinterpret_cast<uintptr_t>(src) & 15) || blocks < 1) return -1;
