@@ -200,48 +200,53 @@ __device__ __forceinline__ void attend_rows(const float *q_s, const int *rows, i
   float m = -1.0e30f, l = 0.f, o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
-  constexpr int U = 6;             // rows in flight per 16-lane group: 96 per workgroup per round
-  for (int base = 0; base < cnt; base += 16 * U) {
-    uint4 kr[U], vr[U];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ri = base + u * 16 + wv * 4 + grp;
-      const long long n = ri < cnt ? (long long)rows[ri] : -1;
-      ok[u] = n >= 0 && n < nmax;
-      kr[u] = make_uint4(0, 0, 0, 0);
-      vr[u] = make_uint4(0, 0, 0, 0);
-      if (ok[u]) {
-        kr[u] = ld_stream(kb + n * kD + sub * 8);
-        vr[u] = ld_stream(vb + n * kD + sub * 8);
-      }
+  // U rows in flight per 16-lane group (80 per workgroup), a rolling window:
+  // slot u is refilled with the row U slots ahead as soon as it is consumed
+  constexpr int U = 5;
+  uint4 kr[U], vr[U];
+  bool ok[U];
+  auto fetch = [&](int u, int ri) {
+    const long long n = ri < cnt ? (long long)rows[ri] : -1;
+    ok[u] = n >= 0 && n < nmax;
+    kr[u] = make_uint4(0, 0, 0, 0);
+    vr[u] = make_uint4(0, 0, 0, 0);
+    if (ok[u]) {
+      kr[u] = ld_stream(kb + n * kD + sub * 8);
+      vr[u] = ld_stream(vb + n * kD + sub * 8);
     }
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u) fetch(u, u * 16 + wv * 4 + grp);
+  for (int base = 0; base < cnt; base += 16 * U) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
       const uint32_t vw[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+      const bool oku = ok[u];
       float d = q[0] * bf_lo(kw[0]);
       d = fmaf(q[1], bf_hi(kw[0]), d);
 #pragma unroll
       for (int i = 1; i < 4; ++i) d = fmaf(q[2 * i + 1], bf_hi(kw[i]), fmaf(q[2 * i], bf_lo(kw[i]), d));
       d = row16_sum(d);
-      if (!ok[u]) continue;
-      const bool bump = d > m + 8.f;
-      if (__builtin_amdgcn_ballot_w64(bump)) {
-        const float mn = bump ? d : m;
-        const float a = __builtin_amdgcn_exp2f(m - mn);
-        l *= a;
+      if (oku) {
+        const bool bump = d > m + 8.f;
+        if (__builtin_amdgcn_ballot_w64(bump)) {
+          const float mn = bump ? d : m;
+          const float a = __builtin_amdgcn_exp2f(m - mn);
+          l *= a;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] *= a;
-        m = mn;
-      }
-      const float pw = __builtin_amdgcn_exp2f(d - m);
-      l += pw;
+          for (int i = 0; i < 8; ++i) o[i] *= a;
+          m = mn;
+        }
+        const float pw = __builtin_amdgcn_exp2f(d - m);
+        l += pw;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o[2 * i] = fmaf(pw, bf_lo(vw[i]), o[2 * i]);
-        o[2 * i + 1] = fmaf(pw, bf_hi(vw[i]), o[2 * i + 1]);
+        for (int i = 0; i < 4; ++i) {
+          o[2 * i] = fmaf(pw, bf_lo(vw[i]), o[2 * i]);
+          o[2 * i + 1] = fmaf(pw, bf_hi(vw[i]), o[2 * i + 1]);
+        }
       }
+      fetch(u, base + (U + u) * 16 + wv * 4 + grp);
     }
   }
   // back to natural-log units for the merges (an empty state has m = -inf)

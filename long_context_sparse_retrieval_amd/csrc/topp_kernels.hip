@@ -33,7 +33,8 @@ namespace {
 
 constexpr int kBnd = 254;   // highest regular bin; bin 255 is the clamp bin
 
-constexpr int kCells = 512;      // absolute score cells tracked per tile while streaming (64 logit units)
+constexpr int kCells = 2048;     // absolute score cells tracked per tile while streaming (256 logit units)
+static_assert(4 * kBins <= kCells, "the rebinning reuses the streaming histogram's storage");
 
 // A histogram entry packs the token count (bits 40..63) above the summed
 // in-cell masses (bits 0..39; at most 8192 tokens of < 1.14 * 2^23 each).
@@ -58,7 +59,7 @@ template <int T>
 struct ScanShared {
   static constexpr int TPT = T / kWG;
   uint8_t codes[T];                        // local bin of every position of the tile
-  unsigned long long hist[4][kCells];      // per-wave histograms by absolute cell mod kCells:
+  unsigned long long hist[kCells];         // the tile's histogram by absolute cell mod kCells:
                                            // count << 40 | exact in-cell mass
   double q[kR];
   double qtmp[16][kR];
@@ -245,7 +246,7 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
   float mx = -INFINITY;
   int cmin = INT32_MAX;
   const bool topk = g.topk != 0;
-  for (int x = tid; x < 4 * kCells; x += kWG) (&sm.hist[0][0])[x] = 0ull;
+  for (int x = tid; x < kCells; x += kWG) sm.hist[x] = 0ull;
   // bin one score by its absolute cell and return the cell clamped to 16 bits
   // (kNoCell for an absent score, -inf, which adds nothing when CHECK);
   // branchless, so a whole batch of rows stays one basic block and its loads
@@ -257,7 +258,7 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
     const int cell = score_cell(s);
     const uint32_t w = topk ? kUnitWeight : cell_weight(s, cell);
     const unsigned long long add = ok ? ((unsigned long long)w | (1ull << kCountShift)) : 0ull;
-    atomicAdd(&sm.hist[wv][cell & (kCells - 1)], add);
+    atomicAdd(&sm.hist[cell & (kCells - 1)], add);
     mx = fmaxf(mx, sc);
     cmin = min(cmin, ok ? cell : INT32_MAX);
     const int c16 = min(max(cell, -32767), 32767);
@@ -343,26 +344,20 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
   // local bins j = c_t - cell; cells 255 or more below c_t form the clamp bin 255,
   // weighted relative to its base cell c_t - 255
   unsigned long long packed = 0;
-  // (a span of at most kCells - 2 keeps every cell unique mod kCells and the clamp
-  // cells c_t - 255 .. cmin within the 256 threads below; 16-bit cells are exact)
+  // (a span of at most kCells - 2 keeps every cell unique mod kCells; 16-bit
+  // cells are exact)
   if (c_t != INT32_MIN && (long long)c_t - cmin <= kCells - 2 && c_t <= 32767 && cmin >= -32767) {
     const int j = tid;
-    if (j < kBins - 1) {
-      const int cell = c_t - j;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) packed += sm.hist[w][cell & (kCells - 1)];
-    }
-    // clamp bin: cells c_t - 255 - x for x = 0..(c_t - 255 - cmin), if any
+    if (j < kBins - 1) packed = sm.hist[(c_t - j) & (kCells - 1)];
+    // clamp bin: cells c_t - 255 - x for x = 0..(c_t - 255 - cmin), if any,
+    // thread tid taking x = tid, tid + 256, ...
     if ((long long)cmin <= (long long)c_t - (kBins - 1)) {            // block-uniform
-      const long long cell = (long long)c_t - (kBins - 1) - tid;
       double cm = 0.0;
       unsigned long long cc = 0;
-      if (cell >= cmin) {
-        unsigned long long e = 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) e += sm.hist[w][cell & (kCells - 1)];
-        cm = (double)(e & kMassMask) * bin_scale(g, -(double)tid * 0.125);
-        cc = e >> kCountShift;
+      for (int x = tid; (long long)c_t - (kBins - 1) - x >= cmin; x += kWG) {
+        const unsigned long long e = sm.hist[(c_t - (kBins - 1) - x) & (kCells - 1)];
+        cm += (double)(e & kMassMask) * bin_scale(g, -(double)x * 0.125);
+        cc += e >> kCountShift;
       }
       double tm;
       (void)block_excl_scan<double>(cm, tm, sm.red_d);
@@ -379,9 +374,10 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
           (uint8_t)(cell == kNoCell || jb >= kBins - 1 ? kBins - 1 : jb);
     }
   } else {
-    // rebin relative to c_t, recomputing the scores
+    // rebin relative to c_t, recomputing the scores (per-wave histograms of
+    // the 256 local bins in the same array)
     __syncthreads();
-    for (int x = tid; x < 4 * kBins; x += kWG) sm.hist[x / kBins][x % kBins] = 0ull;
+    for (int x = tid; x < 4 * kBins; x += kWG) sm.hist[x] = 0ull;
     __syncthreads();
     for (int k = 0; k < TPT; ++k) {
       const float sc = rescore(k);
@@ -390,14 +386,14 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
         const int cell = score_cell(sc);
         const int jb = c_t - cell >= kBins - 1 ? kBins - 1 : c_t - cell;
         const uint32_t u = jb == kBins - 1 ? token_weight(g, sc, c_t - (kBins - 1)) : token_weight(g, sc, cell);
-        atomicAdd(&sm.hist[wv][jb], (unsigned long long)u | (1ull << kCountShift));
+        atomicAdd(&sm.hist[wv * kBins + jb], (unsigned long long)u | (1ull << kCountShift));
         code = (uint8_t)jb;
       }
       sm.codes[scan_pos<FROM_LOGITS>(0, k, tid)] = code;
     }
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < 4; ++w) packed += sm.hist[w][tid];
+    for (int w = 0; w < 4; ++w) packed += sm.hist[w * kBins + tid];
   }
   __syncthreads();
   {

@@ -405,6 +405,11 @@ DECODE_CASES = {
     "cfg4-small-topk": (4, dict(N=40000, window=2048, query_scale="unit", top_k=2048), 0.3),
     "cfg4-shared-keys-topk": (4, dict(N=40000, window=2048, query_scale="unit", idx_group=8, top_k=500), 0.3),
     "topk-all": (2, dict(B=1, N=2500, window=300, top_k=2500), None),
+    # scaled queries: tiles whose scores span over 64 logits (clamp cells
+    # summed several per thread) and over 256 logits (the tile recomputes
+    # its scores from the keys)
+    "cfg2-span-200": (2, dict(B=2, N=9000, window=512), 3.0),
+    "cfg2-span-3000": (2, dict(B=2, N=9000, window=512), 60.0),
     "topk-1": (1, dict(top_k=1), None),
 }
 
