@@ -672,13 +672,37 @@ def time_chunked_prefill(calls: int = 3) -> dict:
     split = chunked_prefill_split()
     if split:
         sel_us, attn_us = split["pf_select_kernel"], split["pf_attn_kernel"]
-        out["kernel_split"] = {"source": split["source"], "pf_select_kernel_us": sel_us,
-                               "pf_attn_kernel_us": attn_us,
-                               "pf_select_scores_per_s": round(logits / (sel_us * 1e-6), 1),
-                               "pf_select_frac_of_exp_lds_ceiling": round(logits / (sel_us * 1e-6)
-                                                                          / ceil["scores_per_s"], 4),
-                               "attention_gather_GBps": round(rows * 512 / (attn_us * 1e-6) / 1e9, 1)}
+        out["kernel_split"] = {
+            "source": split["source"], "pf_select_kernel_us": sel_us, "pf_attn_kernel_us": attn_us,
+            "pf_select_passes": 4,
+            "passes": "per-query maximum, exact histogram (the exp + LDS-add work), per-chunk counts, "
+                      "ordered emission; each recomputes the scores on the matrix cores",
+            "pf_select_scores_per_s": round(logits / (sel_us * 1e-6), 1),
+            "pf_select_frac_of_exp_lds_ceiling": round(logits / (sel_us * 1e-6) / ceil["scores_per_s"], 4),
+            "pf_select_score_evaluations_per_s": round(4 * logits / (sel_us * 1e-6), 1),
+            "attention_gather_GBps": round(rows * 512 / (attn_us * 1e-6) / 1e9, 1),
+            "pf_select_matrix_core_busy": counter_line(CP_COUNTERS, "matrix-core busy"),
+            "pf_select_valu_busy": counter_line(CP_COUNTERS, "VALU busy"),
+            "pf_select_lds_bank_conflict_stall": counter_line(CP_COUNTERS, "LDS bank-conflict stall"),
+            "counters_source": os.path.relpath(CP_COUNTERS, ROOT)}
     return out
+
+
+CP_COUNTERS = os.path.join(ROOT, "profiles", "pf_select_kernel.prefill-128k-4096q-4h.counters.txt")
+
+
+def counter_line(path: str, label: str):
+    """The value of a derived line ("<label> ... <value>") of a committed counter summary."""
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as fh:
+        for line in fh:
+            if line.strip().startswith(label):
+                try:
+                    return float(line.split()[-1])
+                except ValueError:
+                    return None
+    return None
 
 
 CP_TRACE = os.path.join(ROOT, "profiles", "pf_select_kernel.prefill-128k-4096q-4h.kernel_trace.txt")
@@ -1032,7 +1056,7 @@ def main():
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "read_ceiling": {"GBps": rc["GBps"], "what": "in-tree streaming-read kernels (libreadprobe.so) over 2 GiB, "
                                                      "best of an access-pattern / grid / loads-in-flight sweep",
-                         "config": rc["config"],
+                         "config": rc["config"], "sweep_GBps": rc["sweep"],
                          "phase_a_frac_of_read_ceiling": round(s["pa_gbps"] / rc["GBps"], 4),
                          "step_frac_of_read_ceiling": round(s["gbps"] / rc["GBps"], 4)},
         "step_us_percentiles": s["pct"],

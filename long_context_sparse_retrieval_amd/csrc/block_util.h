@@ -186,6 +186,10 @@ struct AttnShared {
 // base + n * D.  Rows outside [0, nmax) are skipped.  16 lanes cover one row
 // (8 channels each), a wave holds 4 rows per step.  The workgroup's state is
 // written to *dst (m, l and the unnormalised o).  Ends with a barrier.
+// STREAM: the rows are read once per call (non-temporal loads); otherwise
+// they are cached (many queries of a chunked prefill gather from the same
+// K/V group, which then stays in the L2 and the Infinity Cache).
+template <bool STREAM = true>
 __device__ __forceinline__ void attend_rows(const float *q_s, const int *rows, int cnt, long long nmax,
                                             const rtp_bf16 *__restrict__ kb, const rtp_bf16 *__restrict__ vb,
                                             Partial *dst, AttnShared *sm) {
@@ -211,8 +215,13 @@ __device__ __forceinline__ void attend_rows(const float *q_s, const int *rows, i
     kr[u] = make_uint4(0, 0, 0, 0);
     vr[u] = make_uint4(0, 0, 0, 0);
     if (ok[u]) {
-      kr[u] = ld_stream(kb + n * kD + sub * 8);
-      vr[u] = ld_stream(vb + n * kD + sub * 8);
+      if (STREAM) {
+        kr[u] = ld_stream(kb + n * kD + sub * 8);
+        vr[u] = ld_stream(vb + n * kD + sub * 8);
+      } else {
+        kr[u] = *reinterpret_cast<const uint4 *>(kb + n * kD + sub * 8);
+        vr[u] = *reinterpret_cast<const uint4 *>(vb + n * kD + sub * 8);
+      }
     }
   };
 #pragma unroll

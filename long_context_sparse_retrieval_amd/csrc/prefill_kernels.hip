@@ -485,7 +485,7 @@ __global__ __launch_bounds__(kWG) void pf_attn_kernel(Geo g, int i0, int nqc, co
     __syncthreads();
     for (int x = tid; x < n; x += kWG) sm.list[x] = list[s0 + x];
     __syncthreads();
-    attend_rows(sm.q, sm.list, n, g.N - g.nq + i + 1, kc + cbase, vc + cbase, &sm.extra, &sm.at);
+    attend_rows<false>(sm.q, sm.list, n, g.N - g.nq + i + 1, kc + cbase, vc + cbase, &sm.extra, &sm.at);
     if (tid < kD) merge_state(run_m, run_l, &run_o, sm.extra.m, sm.extra.l, &sm.extra.o[tid], 1);
   }
   Partial *dst = g.part + (size_t)ul * kPfSplit + sp;

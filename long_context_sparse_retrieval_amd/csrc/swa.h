@@ -87,6 +87,13 @@ __device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const 
   const int r1 = r0 + g.swa_chunk < L ? r0 + g.swa_chunk : L;
   const size_t cbase = kv_group_elems<RING_LAYOUT>(g, b, kvg);
   const rtp_bf16 *kb = kc + cbase, *vb = vc + cbase;
+  // one query per sequence reads its window once (non-temporal loads); with
+  // many queries (chunked prefill) consecutive queries share almost every row,
+  // which then stays cached
+  const bool stream = g.nq == 1;
+  auto ld_row = [&](const rtp_bf16 *p) -> uint4 {
+    return stream ? ld_stream(p) : *reinterpret_cast<const uint4 *>(p);
+  };
   // window rows: positions lo.. in rows lo.. of a full group; in a ring group
   // position n >= n_sink sits in row n_sink + (n - n_sink) mod W (below n_sink
   // and, when lo < n_sink, everywhere in the window that is row n as well)
@@ -108,8 +115,8 @@ __device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const 
     kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
     if (ok[u]) {
       const size_t n = (size_t)swa_row<RING>(ri, ns, wbase, wwrap, g.window);
-      kr[u] = ld_stream(kb + n * kD + sub * 8);
-      vr[u] = ld_stream(vb + n * kD + sub * 8);
+      kr[u] = ld_row(kb + n * kD + sub * 8);
+      vr[u] = ld_row(vb + n * kD + sub * 8);
     }
   }
   // every head's query in one round: thread (hh, t) loads and rotates channel
@@ -189,8 +196,8 @@ __device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const 
       ok[u] = ri < r1;
       if (ok[u]) {
         const size_t n = (size_t)swa_row<RING>(ri, ns, wbase, wwrap, g.window);
-        kr[u] = ld_stream(kb + n * kD + sub * 8);
-        vr[u] = ld_stream(vb + n * kD + sub * 8);
+        kr[u] = ld_row(kb + n * kD + sub * 8);
+        vr[u] = ld_row(vb + n * kD + sub * 8);
       }
     }
   }
