@@ -31,6 +31,8 @@ namespace rtp {
 
 namespace {
 
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+
 constexpr int kBnd = 254;   // highest regular bin; bin 255 is the clamp bin
 
 constexpr int kCells = 2048;     // absolute score cells tracked per tile while streaming (256 logit units)
@@ -402,11 +404,11 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
     if constexpr (TPT % 16 == 0) {
 #pragma unroll
       for (int k = 0; k < TPT; k += 16)
-        *reinterpret_cast<uint4 *>(dst + k) = *reinterpret_cast<const uint4 *>(src + k);
+        __builtin_nontemporal_store(*reinterpret_cast<const v4u_t *>(src + k), reinterpret_cast<v4u_t *>(dst + k));
     } else {
 #pragma unroll
       for (int k = 0; k < TPT; k += 4)
-        *reinterpret_cast<uint32_t *>(dst + k) = *reinterpret_cast<const uint32_t *>(src + k);
+        __builtin_nontemporal_store(*reinterpret_cast<const uint32_t *>(src + k), reinterpret_cast<uint32_t *>(dst + k));
     }
   }
 
@@ -416,8 +418,8 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
   const unsigned int cn = (unsigned int)(packed >> kCountShift);
   unsigned int tot;
   const unsigned int ex = block_excl_scan<unsigned int>(cn, tot, sm.red_u32);
-  tsum->mass[tid] = ms;
-  tsum->cum[tid] = ex + cn;
+  __builtin_nontemporal_store(ms, &tsum->mass[tid]);
+  __builtin_nontemporal_store(ex + cn, &tsum->cum[tid]);
   if (tid == 0) {
     tsum->c_t = c_t;
     tsum->nvalid = (int32_t)tot;
