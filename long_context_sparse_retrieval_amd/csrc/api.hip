@@ -86,6 +86,7 @@ int make_geo(const rtp_layer *L, bool dense, Geo &g) {
     L = &LD;
   }
   memset(&g, 0, sizeof(g));
+  g.cstride = 1;
   g.B = L->B;
   g.Hq = L->Hq;
   g.Hkv = L->Hkv;
@@ -199,14 +200,18 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
   const size_t swa_ctrs = std::max((size_t)reg.swa_units * reg.swa_hb, (size_t)den.swa_units * den.swa_hb);
   const size_t o_ring = off;
   off = align_up(off + reg_units * kRing * 8);
+  // control words one 256-byte line apart for decode (few queries, many
+  // workgroups per query); packed for chunked prefill (many queries)
+  const size_t cs = g.nq == 1 ? 64 : 1;
+  g.cstride = (int)cs;
   const size_t o_cmax = off;
-  off = align_up(off + reg_units * 4);
+  off = align_up(off + reg_units * cs * 4);
   const size_t o_cmin = off;
-  off = align_up(off + reg_units * 4);
+  off = align_up(off + reg_units * cs * 4);
   const size_t o_ctr_fin = off;
-  off = align_up(off + reg_units * 4);
+  off = align_up(off + reg_units * cs * 4);
   const size_t o_ctr_swa = off;
-  off = align_up(off + swa_ctrs * 4);
+  off = align_up(off + swa_ctrs * cs * 4);
   // transient regions of this call
   const size_t o_qprep = off;
   out->header_bytes = off;
@@ -240,9 +245,9 @@ int make_plan(const rtp_layer *L, void *ws, Plan *out, bool dense = false) {
     off = align_up(off + (codes_bytes > pf_bytes ? codes_bytes : pf_bytes));
   }
   // regions in order, each inside the workspace and 256-byte aligned
-  RTP_HOST_CHECK(o_ring == 0 && o_cmax >= o_ring + reg_units * kRing * 8 && o_cmin >= o_cmax + reg_units * 4);
-  RTP_HOST_CHECK(o_ctr_fin >= o_cmin + reg_units * 4 && o_ctr_swa >= o_ctr_fin + reg_units * 4);
-  RTP_HOST_CHECK(o_qprep >= o_ctr_swa + swa_ctrs * 4 && o_tsum >= o_qprep + units * sizeof(QPrep));
+  RTP_HOST_CHECK(o_ring == 0 && o_cmax >= o_ring + reg_units * kRing * 8 && o_cmin >= o_cmax + reg_units * cs * 4);
+  RTP_HOST_CHECK(o_ctr_fin >= o_cmin + reg_units * cs * 4 && o_ctr_swa >= o_ctr_fin + reg_units * cs * 4);
+  RTP_HOST_CHECK(o_qprep >= o_ctr_swa + swa_ctrs * cs * 4 && o_tsum >= o_qprep + units * sizeof(QPrep));
   RTP_HOST_CHECK(o_part >= o_tsum + units * nt * sizeof(TileSum));
   RTP_HOST_CHECK(o_swa >= o_part + units * (size_t)std::max(g.fin_nwg, kSpChunks) * sizeof(Partial));
   RTP_HOST_CHECK(o_codes >= o_swa + (size_t)g.swa_units * g.swa_hb * g.swa_nch * kSwaHeads * sizeof(Partial));

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kWG) void sparse_attn_kernel(Geo g, const rtp_bf16 
       st_coherent(&dst->l, run_l);
     }
   }
-  if (!arrive_last(g.ctr_fin + unit, (uint32_t)kSpChunks, &sm.flag)) return;
+  if (!arrive_last(g.ctr_fin + (size_t)unit * g.cstride, (uint32_t)kSpChunks, &sm.flag)) return;
   combine_partials(g.part + (size_t)unit * kSpChunks, kSpChunks, out + (((size_t)b * g.Hq + hq) * g.nq + i) * kD,
                    &sm.cb);
 }

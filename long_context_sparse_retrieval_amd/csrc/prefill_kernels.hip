@@ -496,7 +496,7 @@ __global__ __launch_bounds__(kWG) void pf_attn_kernel(Geo g, int i0, int nqc, co
       st_coherent(&dst->l, run_l);
     }
   }
-  if (!arrive_last(g.ctr_fin + ul, (uint32_t)kPfSplit, &sm.flag)) return;
+  if (!arrive_last(g.ctr_fin + (size_t)ul * g.cstride, (uint32_t)kPfSplit, &sm.flag)) return;
   combine_partials(g.part + (size_t)ul * kPfSplit, kPfSplit, out + (((size_t)b * g.Hq + hq) * g.nq + i) * kD, &sm.cb);
 }
 

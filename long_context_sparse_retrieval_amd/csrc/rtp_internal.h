@@ -120,6 +120,10 @@ struct Geo {
   uint32_t gring[kMaxHq / 32];   // KV groups stored as rings
   int any_ring;                  // any bit of gring set
   long long rows_b;              // cache rows per sequence
+  // per-query control words (cmax, cmin, ctr_fin, ctr_swa): entry i of each
+  // array at word i * cstride.  Decode spreads them one 256-byte line apart:
+  // atomics from many workgroups on one line serialise.
+  int cstride;
 };
 
 // ------------------------------------------------------------------ K/V cache addressing

@@ -240,7 +240,7 @@ __device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const 
     }
   }
   if (defer) return;
-  if (!arrive_last(g.ctr_swa + unit * g.swa_hb + hb, (uint32_t)g.swa_nch, &sm.flag)) return;
+  if (!arrive_last(g.ctr_swa + (size_t)(unit * g.swa_hb + hb) * g.cstride, (uint32_t)g.swa_nch, &sm.flag)) return;
   // wave hh combines head hh's chunk states (all heads in one round of loads)
   const int h = sm.heads[wv];
   if (h >= 0)

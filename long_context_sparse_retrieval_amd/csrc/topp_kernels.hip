@@ -427,8 +427,8 @@ __device__ __forceinline__ void scan_block(const Geo &g, long long blk, const rt
   // absolute-cell histogram of the query: exact integer sums in any order
   if (c_t != INT32_MIN) {
     if (tid == 0) {
-      atomicMax(g.cmax + unit, enc_max(c_t));
-      atomicMax(g.cmin + unit, enc_min(c_t - (kBins - 1)));
+      atomicMax(g.cmax + (size_t)unit * g.cstride, enc_max(c_t));
+      atomicMax(g.cmin + (size_t)unit * g.cstride, enc_min(c_t - (kBins - 1)));
     }
     if (ms) atomicAdd((unsigned long long *)(g.ring + (size_t)unit * kRing + ((c_t - tid) & (kRing - 1))), ms);
   }
@@ -519,7 +519,7 @@ __device__ __forceinline__ void finish_block(const Geo &g, int y, const rtp_bf16
 
   // round one
   const uint64_t *ring = g.ring + (size_t)unit * kRing;
-  const uint32_t ecmax = g.cmax[unit], ecmin = g.cmin[unit];
+  const uint32_t ecmax = g.cmax[(size_t)unit * g.cstride], ecmin = g.cmin[(size_t)unit * g.cstride];
   const int ct0 = tid < g.nt ? ts[tid].c_t : INT32_MIN;
   double qi_v = 0.0;
   float qrot_v = 0.f;
@@ -961,7 +961,7 @@ __device__ __forceinline__ void finish_block(const Geo &g, int y, const rtp_bf16
       }
     }
   }
-  if (!arrive_last(g.ctr_fin + unit, (uint32_t)g.fin_nwg, &sm.flag)) return;
+  if (!arrive_last(g.ctr_fin + (size_t)unit * g.cstride, (uint32_t)g.fin_nwg, &sm.flag)) return;
   // last workgroup of the query (every workgroup has read the ring): leave the
   // query's state zero for the next call, combine the states
   {
@@ -972,8 +972,8 @@ __device__ __forceinline__ void finish_block(const Geo &g, int y, const rtp_bf16
       for (int x = tid; x < kRing; x += kWG) ringw[x] = 0ull;
     }
     if (tid == 0) {
-      g.cmax[unit] = 0u;
-      g.cmin[unit] = 0u;
+      g.cmax[(size_t)unit * g.cstride] = 0u;
+      g.cmin[(size_t)unit * g.cstride] = 0u;
     }
   }
   if (ATTEND)
