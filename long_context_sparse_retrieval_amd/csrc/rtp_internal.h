@@ -326,6 +326,19 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<0x140>(v);   // row_mirror
   return v;
 }
+// row16_sum of N independent values, step by step, so that consecutive DPP
+// reads never wait on the write just before them.
+template <int N>
+__device__ __forceinline__ void row16_sum_n(float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp<0xB1>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp<0x4E>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp<0x141>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp<0x140>(v[i]);
+}
 
 // Inclusive prefix sum over the 64 lanes of a wave, 32-bit integers: sums of
 // four within each row of 16 (row shifts 1-3), then of 8 and 16 (row shifts 4

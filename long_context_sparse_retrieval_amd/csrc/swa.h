@@ -167,27 +167,39 @@ __device__ __forceinline__ void swa_block_rows(const Geo &g, long long x, const 
         vf[2 * e] = bf_lo(vw[e]);
         vf[2 * e + 1] = bf_hi(vw[e]);
       }
+      // every head's score, then the four lane-group sums interleaved
+      float d[kSwaHeads];
 #pragma unroll
       for (int hh = 0; hh < kSwaHeads; ++hh) {
-        float d = q[hh][0] * kf[0];
+        float x = q[hh][0] * kf[0];
 #pragma unroll
-        for (int e = 1; e < 8; ++e) d = fmaf(q[hh][e], kf[e], d);
-        d = row16_sum(d);
-        if (!ok[u]) continue;
-        // online softmax with a lazy reference: the maximum moves only when a
-        // score passes it by more than kSlack (any reference gives the same
-        // o / l; this one keeps every weight below 2^kSlack), for the whole
-        // wave at once, so a row costs one exponential and one FMA per channel
-        const bool bump = d > mm[hh] + kSlack;
-        if (__builtin_amdgcn_ballot_w64(bump)) {
-          const float mn = bump ? d : mm[hh];
+        for (int e = 1; e < 8; ++e) x = fmaf(q[hh][e], kf[e], x);
+        d[hh] = x;
+      }
+      row16_sum_n(d);
+      // online softmax with a lazy reference: a head's maximum moves only
+      // when a score passes it by more than kSlack (any reference gives the
+      // same o / l; this one keeps every weight below 2^kSlack).  One test
+      // for the wave and its four heads; a head that does not move is scaled
+      // by exp2(0) = 1, exactly.  A row past the chunk adds nothing.
+      const bool oku = ok[u];
+      float rise = d[0] - mm[0];
+#pragma unroll
+      for (int hh = 1; hh < kSwaHeads; ++hh) rise = fmaxf(rise, d[hh] - mm[hh]);
+      if (__builtin_amdgcn_ballot_w64(oku && rise > kSlack)) {
+#pragma unroll
+        for (int hh = 0; hh < kSwaHeads; ++hh) {
+          const float mn = oku && d[hh] - mm[hh] > kSlack ? d[hh] : mm[hh];
           const float a = __builtin_amdgcn_exp2f(mm[hh] - mn);
           ll[hh] *= a;
 #pragma unroll
           for (int e = 0; e < 8; ++e) oo[hh][e] *= a;
           mm[hh] = mn;
         }
-        const float pw = __builtin_amdgcn_exp2f(d - mm[hh]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < kSwaHeads; ++hh) {
+        const float pw = oku ? __builtin_amdgcn_exp2f(d[hh] - mm[hh]) : 0.f;
         ll[hh] += pw;
 #pragma unroll
         for (int e = 0; e < 8; ++e) oo[hh][e] = fmaf(pw, vf[e], oo[hh][e]);
