@@ -19,6 +19,8 @@ __device__ __forceinline__ V block_excl_scan(V v, V &total, V *s_buf) {
   V x = v;
   if constexpr (sizeof(V) == 4 && std::is_integral<V>::value) {
     x = (V)wave_incl_scan_u32((uint32_t)v);
+  } else if constexpr (sizeof(V) == 8) {
+    x = wave_incl_scan64(v);
   } else {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {

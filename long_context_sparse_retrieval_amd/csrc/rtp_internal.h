@@ -357,6 +357,45 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
   return (uint32_t)v;
 }
 
+// A DPP move of a 64-bit value (both halves with the same control); lanes
+// without a source, or outside the row and bank masks, read 0.
+template <int CTRL, int RMASK, int BMASK, typename V>
+__device__ __forceinline__ V dpp64(V x) {
+  static_assert(sizeof(V) == 8, "64-bit values");
+  const unsigned long long b = __builtin_bit_cast(unsigned long long, x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)b, CTRL, RMASK, BMASK, true);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), CTRL, RMASK, BMASK, true);
+  return __builtin_bit_cast(V, ((unsigned long long)hi << 32) | lo);
+}
+
+// wave_incl_scan_u32's pattern for 64-bit integers and doubles (a fixed
+// order of additions, so every workgroup gets the same bits).
+template <typename V>
+__device__ __forceinline__ V wave_incl_scan64(V x) {
+  V v = x;
+  v += dpp64<0x111, 0xF, 0xF>(x);   // row_shr:1
+  v += dpp64<0x112, 0xF, 0xF>(x);   // row_shr:2
+  v += dpp64<0x113, 0xF, 0xF>(x);   // row_shr:3
+  v += dpp64<0x114, 0xF, 0xE>(v);   // row_shr:4, banks 1-3
+  v += dpp64<0x118, 0xF, 0xC>(v);   // row_shr:8, banks 2-3
+  v += dpp64<0x142, 0xA, 0xF>(v);   // row_bcast:15 into rows 1, 3
+  v += dpp64<0x143, 0xC, 0xF>(v);   // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// Sum of a double over the wave in a fixed order, in lane 63: the row sums
+// (quad swaps, half-row and row mirrors), then rows 0 + 1 and 2 + 3 (row
+// broadcast 15), then (0 + 1) + (2 + 3) (row broadcast 31).
+__device__ __forceinline__ double wave_sum_f64_last(double v) {
+  v += dpp64<0xB1, 0xF, 0xF>(v);
+  v += dpp64<0x4E, 0xF, 0xF>(v);
+  v += dpp64<0x141, 0xF, 0xF>(v);
+  v += dpp64<0x140, 0xF, 0xF>(v);
+  v += dpp64<0x142, 0xA, 0xF>(v);
+  v += dpp64<0x143, 0xC, 0xF>(v);
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -112,14 +112,13 @@ __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, 
       }
     }
   }
-  // clamp-bin mass, summed in a fixed order (a butterfly inside each wave, the
-  // four wave sums in wave order), so every workgroup gets the same bits
+  // clamp-bin mass, summed in a fixed order (wave_sum_f64_last inside each
+  // wave, the four wave sums in wave order), so every workgroup gets the same
+  // bits
   const int lane = j & 63, wv = j >> 6;
   {
-    double v = w255;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    if (lane == 0) sm.red_d[wv] = v;
+    const double v = wave_sum_f64_last(w255);
+    if (lane == 63) sm.red_d[wv] = v;
   }
   __syncthreads();
   const double W255 = (((sm.red_d[0] + sm.red_d[1]) + sm.red_d[2]) + sm.red_d[3]) * 0x1p-23;
@@ -583,15 +582,7 @@ __device__ __forceinline__ void finish_block(const Geo &g, int y, const rtp_bf16
     // inclusive prefixes inside the wave of the bin-b* mass and of the packed
     // (above b*, in b*) counts, then the wave totals through LDS
     const unsigned long long sbv = ((unsigned long long)sure << 32) | (unsigned)bc;
-    unsigned long long xp = bm, xs = sbv;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const unsigned long long yp = __shfl_up(xp, off), ys = __shfl_up(xs, off);
-      if (lane >= off) {
-        xp += yp;
-        xs += ys;
-      }
-    }
+    const unsigned long long xp = wave_incl_scan64(bm), xs = wave_incl_scan64(sbv);
     if (lane == 63) {
       sm.thr.tot[wv][0] = xp;
       sm.thr.tot[wv][1] = xs;
