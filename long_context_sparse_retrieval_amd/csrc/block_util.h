@@ -263,13 +263,14 @@ __device__ __forceinline__ void attend_rows(const float *q_s, const int *rows, i
   // back to natural-log units for the merges (an empty state has m = -inf)
   m = l > 0.f ? m * 0.6931471805599453f : -INFINITY;
   // merge the 4 row groups of the wave
-#pragma unroll
-  for (int off = 16; off < 64; off <<= 1) {
-    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+  {
     float o2[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o2[i] = __shfl_xor(o[i], off);
-    merge_state(m, l, o, m2, l2, o2, 8);
+    for (int i = 0; i < 8; ++i) o2[i] = lane_xor<16>(o[i]);
+    merge_state(m, l, o, lane_xor<16>(m), lane_xor<16>(l), o2, 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o2[i] = lane_xor<32>(o[i]);
+    merge_state(m, l, o, lane_xor<32>(m), lane_xor<32>(l), o2, 8);
   }
   if (grp == 0) {
 #pragma unroll

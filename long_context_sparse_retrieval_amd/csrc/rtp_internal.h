@@ -357,6 +357,25 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
   return (uint32_t)v;
 }
 
+// The value of lane ^ 16 (OFF = 16) or lane ^ 32 (OFF = 32) of the wave,
+// through gfx950's row swaps: v_permlane16_swap exchanges the odd rows of its
+// first operand with the even rows of its second, v_permlane32_swap the upper
+// half of the first with the lower half of the second.  With both operands v,
+// a lane finds its partner's value in the first result when its OFF bit is set
+// and in the second otherwise.  VALU only, no LDS round trip.
+template <int OFF>
+__device__ __forceinline__ float lane_xor(float v) {
+  static_assert(OFF == 16 || OFF == 32, "row or half swaps");
+  const unsigned u = __float_as_uint(v);
+  if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  }
+}
+
 // A DPP move of a 64-bit value (both halves with the same control); lanes
 // without a source, or outside the row and bank masks, read 0.
 template <int CTRL, int RMASK, int BMASK, typename V>

@@ -49,8 +49,8 @@ struct ThrScratch {
   unsigned long long tot[4][2];            // per-wave totals of the tile prefix
   int cross_t[4], cross_bo[4];             // per-wave last crossing tile and its offset
   int hit_j[4];
-  double hit_before[4];
-  double last_before;
+  double hit_before[4], hit_up[4];
+  double last_before, last_up;
   double red_d[4];
   unsigned long long red_u[4];
   uint32_t red_u32[4];
@@ -81,12 +81,25 @@ __device__ __forceinline__ uint32_t enc_min(int c) { return 0x7fffffffu - (uint3
 __device__ __forceinline__ int dec_min(uint32_t e) { return (int)(0x7fffffffu - e); }
 
 
+// Thread j's bin scales, exp(-j/8), exp(-(255 + j)/8) and exp(j/8) (1 for
+// top-k): they depend on nothing loaded, so the selection computes them while
+// its first loads are in flight.
+struct ThrScales {
+  double down, clamp0, up;
+};
+__device__ __forceinline__ ThrScales thr_scales(const Geo &g) {
+  const int j = threadIdx.x;
+  return ThrScales{bin_scale(g, -(double)j * 0.125), bin_scale(g, (double)(-(kBins - 1) - j) * 0.125),
+                   bin_scale(g, (double)j * 0.125)};
+}
+
 // The query's global histogram from its ring (in LDS; or, when its cells span
 // more than the ring holds, from every tile histogram): boundary bin b*,
 // residual mass in in-cell units of bin b*, and whether every position is
 // taken.  Every workgroup of a query computes identical values: the integer
 // bins are exact and every floating-point sum has a fixed order.
-__device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, int base_min, ThrScratch &sm,
+__device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, int base_min, const ThrScales &scl,
+                                                 ThrScratch &sm,
                                                  int &bstar_out, double &r_u_out, int &all_out) {
   const int tid = threadIdx.x, j = tid;
   const TileSum *ts = g.tsum + (size_t)unit * g.nt;
@@ -98,7 +111,8 @@ __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, 
     H = j <= kBnd ? sm.ring[(c - j) & (kRing - 1)] : 0ull;
     for (long long cell = (long long)c - (kBins - 1) - j; cell >= base_min; cell -= kWG) {
       const unsigned long long mj = sm.ring[cell & (kRing - 1)];
-      if (mj) w255 += (double)mj * bin_scale(g, (double)(cell - c) * 0.125);
+      const bool first = cell == (long long)c - (kBins - 1) - j;
+      if (mj) w255 += (double)mj * (first ? scl.clamp0 : bin_scale(g, (double)(cell - c) * 0.125));
     }
   } else {
     for (int t = 0; t < g.nt; ++t) {
@@ -123,7 +137,7 @@ __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, 
   __syncthreads();
   const double W255 = (((sm.red_d[0] + sm.red_d[1]) + sm.red_d[2]) + sm.red_d[3]) * 0x1p-23;
   __syncthreads();
-  const double Wj = j <= kBnd ? (double)H * 0x1p-23 * bin_scale(g, -(double)j * 0.125) : W255;
+  const double Wj = j <= kBnd ? (double)H * 0x1p-23 * scl.down : W255;
   double Z;
   const double excl = block_excl_scan<double>(Wj, Z, sm.red_d);
   // Top-P needs the mass p Z; top-k needs k tokens (every weight is exactly 1,
@@ -136,16 +150,21 @@ __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, 
   if (bal ? lane == __builtin_ctzll(bal) : lane == 0) {
     sm.hit_j[wv] = bal ? j : kBins;
     sm.hit_before[wv] = excl;
+    sm.hit_up[wv] = scl.up;
   }
-  if (j == kBins - 1) sm.last_before = excl;
+  if (j == kBins - 1) {
+    sm.last_before = excl;
+    sm.last_up = scl.up;
+  }
   __syncthreads();
   int bstar = kBins;
-  double before = sm.last_before;
+  double before = sm.last_before, up = sm.last_up;    // exp(b* / 8)
 #pragma unroll
   for (int w = 3; w >= 0; --w)
     if (sm.hit_j[w] < kBins) {
       bstar = sm.hit_j[w];
       before = sm.hit_before[w];
+      up = sm.hit_up[w];
     }
   if (bstar >= kBins) bstar = kBins - 1;
   __syncthreads();
@@ -153,7 +172,7 @@ __device__ __forceinline__ void global_threshold(const Geo &g, int unit, int c, 
   // have no common scale; its mass is below e^-31.75 of the top cell, so
   // everything is taken).  Top-k: k covers every position.
   all_out = (g.topk ? need >= Z : (g.p >= 1.0 || bstar >= kBins - 1)) ? 1 : 0;
-  r_u_out = (need - before) * 0x1p23 * bin_scale(g, (double)bstar * 0.125);
+  r_u_out = (need - before) * 0x1p23 * up;
   bstar_out = bstar;
 }
 
@@ -547,6 +566,7 @@ __device__ __forceinline__ void finish_block(const Geo &g, int y, const rtp_bf16
                                          16, 0, 0);
     }
   }
+  const ThrScales scl = thr_scales(g);
   if (!FROM_LOGITS && tid < kR) sm.qi[tid] = qi_v;
   if (ATTEND && tid < kD) sm.q[tid] = qrot_v;
   __builtin_amdgcn_s_waitcnt(0);                        // this wave's ring and code loads have landed in LDS
@@ -555,7 +575,7 @@ __device__ __forceinline__ void finish_block(const Geo &g, int y, const rtp_bf16
   const int c = dec_max(ecmax), base_min = dec_min(ecmin);
   int bstar, all;
   double r_u;
-  global_threshold(g, unit, c, base_min, sm.thr, bstar, r_u, all);
+  global_threshold(g, unit, c, base_min, scl, sm.thr, bstar, r_u, all);
 
   // round two: per tile of the query, the bin-b* prefix mass, the counts above
   // b* and in b*, the output offsets; the crossing tile is the last one whose
