@@ -662,9 +662,9 @@ def time_chunked_prefill(calls: int = 3) -> dict:
            "logits_per_s": round(logits / (ms * 1e-3), 1), "gathered_rows": rows,
            "gathered_GB": round(rows * 512 / 1e9, 3),
            "S_mean_per_query": round(rows / c.size, 1),
-           "calibration": ("one query scale per (head, topic), calibrated on the longest prefix to |S| = 500 / "
-                           "2500; every other query carries its own 0.3 xi perturbation, so the sets drift far "
-                           "from the targets: the workload runs at the |S| reported here, not at 500 / 2500"),
+           "calibration": ("one query scale per query, calibrated by the oracle against the query's own causal "
+                           "prefix to |S| = 500 (concentrated topic) / 2500 (diffuse topic), within 2 % where the "
+                           "set size allows (gen/query_scales.json, oracle/calibrate_queries.py)"),
            "S_per_topic": per_topic,
            "exp_lds_ceiling": ceil,
            "histogram_pass_scores": logits}

@@ -178,7 +178,7 @@ class Workload:
     u: np.ndarray = None         # float32 [B, Hq, nq, D] unscaled query draws
     needles: dict = field(default_factory=dict)   # (b, r) -> int64 positions
     classes: dict = field(default_factory=dict)   # (b, r) -> 0 concentrated / 1 diffuse
-    scales: dict = field(default_factory=dict)    # (b, r) -> query scale ((b, r, topic) in topics mode)
+    scales: dict = field(default_factory=dict)    # (b, r) -> query scale ((b, r, topic) or ("q", b, r, i) in topics mode)
     topics: np.ndarray = None    # float32 [B, Hq, 2, D] topic directions (topics mode)
 
     @property
@@ -251,16 +251,19 @@ def make_workload(spec: WorkloadSpec, seed: int, scales: dict | None = None) -> 
     if spec.needle_mode == "topics":
         topics = rng.standard_normal((B, Hq, 2, D), dtype=np.float32)
 
-    # query scales: (b, r) -> s, or (b, r, topic) -> s in topics mode
+    # query scales: (b, r) -> s; in topics mode (b, r, topic) -> s for every
+    # query of a topic, or ("q", b, r, i) -> s for query i alone (the
+    # calibrated table holds one scale per query)
     if scales is None:
         scales = {}
         if spec.query_scale == "table":
-            tab = load_scale_table().get(scale_key(spec, seed))
+            key = scale_key(spec, seed) + ("/per-query" if spec.needle_mode == "topics" else "")
+            tab = load_scale_table().get(key)
             if tab is None:
-                raise KeyError(f"no calibrated query scales for {scale_key(spec, seed)} in {_SCALES_FILE}")
+                raise KeyError(f"no calibrated query scales for {key} in {_SCALES_FILE}")
             for e in tab:
                 if spec.needle_mode == "topics":
-                    scales[(int(e[0]), int(e[1]), int(e[2]))] = float(e[3])
+                    scales[("q", int(e[0]), int(e[1]), int(e[2]))] = float(e[3])
                 else:
                     scales[(int(e[0]), int(e[1]))] = float(e[2])
     if topics is None:
@@ -270,8 +273,12 @@ def make_workload(spec: WorkloadSpec, seed: int, scales: dict | None = None) -> 
     else:
         q = query_directions(u, topics, spec.topic_mix)
         for key, s in scales.items():
-            b, r, tpc = key
-            q[b, rheads[r], tpc::2] *= s
+            if key[0] == "q":
+                _, b, r, i = key
+                q[b, rheads[r], i] *= s
+            else:
+                b, r, tpc = key
+                q[b, rheads[r], tpc::2] *= s
     q_pre = f32_to_bf16_bits(q.astype(np.float32))
 
     # 3. keys (+ needles), 4. values
