@@ -447,7 +447,11 @@ __global__ __launch_bounds__(kWG) void pf_qprep_kernel(Geo g, const rtp_bf16 *__
   rotate_query(q_row, sm.rope, 0.08838834764831845f, qp->qrot);
 }
 
-constexpr int kPfSplit = 8;     // split-K workgroups per query in the prefill attention
+// Split-K workgroups per query in the prefill attention.  One: at 1.5 K rows
+// per query the per-workgroup set-up and the split-K hand-off cost more than
+// the extra parallelism gains (the whole 128K chunked call: 6.9 ms with one
+// workgroup per query, 7.5 ms with 2, 8.4 with 4, 10.0 with 8 or 16).
+constexpr int kPfSplit = 1;
 
 struct PfAttnShared {
   float q[kD];
@@ -459,7 +463,8 @@ struct PfAttnShared {
 };
 
 // Attention of the chunk's retrieval queries over their selected rows:
-// kPfSplit workgroups per query, split-K states combined by the last one.
+// kPfSplit workgroups per query; with more than one, the last combines their
+// split-K states.
 __global__ __launch_bounds__(kWG) void pf_attn_kernel(Geo g, int i0, int nqc, const rtp_bf16 *__restrict__ kc,
                                                       const rtp_bf16 *__restrict__ vc,
                                                       const int32_t *__restrict__ idx_ws, long long capw,
@@ -487,6 +492,10 @@ __global__ __launch_bounds__(kWG) void pf_attn_kernel(Geo g, int i0, int nqc, co
     __syncthreads();
     attend_rows<false>(sm.q, sm.list, n, g.N - g.nq + i + 1, kc + cbase, vc + cbase, &sm.extra, &sm.at);
     if (tid < kD) merge_state(run_m, run_l, &run_o, sm.extra.m, sm.extra.l, &sm.extra.o[tid], 1);
+  }
+  if constexpr (kPfSplit == 1) {      // the query's whole list: normalise in place
+    if (tid < kD) out[(((size_t)b * g.Hq + hq) * g.nq + i) * kD + tid] = run_l > 0.f ? run_o / run_l : 0.f;
+    return;
   }
   Partial *dst = g.part + (size_t)ul * kPfSplit + sp;
   if (tid < kD) {
